@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Throughput of the looped hybrid decoder's forward pass on one MI355X.
+
+Headline: prefill tokens/s through the full 56-execution looped stack
+(32 weight layers run 4 + 24x2 + 4; d 4096, FFN 12288, vocab 248,320;
+bf16 weights N(0, 0.02) drawn on the device by the seeded generator), batch
+1 x 8192 uniform token ids, logits at the last position.  One step = one
+prefill call over the 8192 tokens (every kernel of the path).  Beside it:
+decode tokens/s at batch 64 with 32,768-token contexts (caches pre-filled with
+seeded N(0, 1) bf16 KV and N(0, 0.1) fp32 GDN states), one token per sequence
+per step.
+
+Prints one JSON line (see the repository's benchmark contract).  --gpus N
+with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+PREFILL_T = 8192
+DECODE_B, DECODE_CTX = 64, 32768
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5, help="timed prefill steps")
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--decode-steps", type=int, default=128)
+    p.add_argument("--decode-warmup", type=int, default=3)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    return p.parse_args()
+
+
+# ------------------------------------------------------- algorithmic work
+
+def layer_matrix_params(d, F, kind, Hq=16, Hkv=4, D=256, H=16, Dk=128, Dv=128):
+    ffn = 3 * d * F
+    if kind == "full":
+        return ffn + (2 * Hq * D + 2 * Hkv * D) * d + d * Hq * D
+    return ffn + (2 * H * Dk + 2 * H * Dv + 2 * H) * d + d * H * Dv
+
+
+def prefill_flops(dims, kinds_exec, T):
+    """GEMM 2*M*N*K + causal attention 4*Hq*D*sum(keys <= pos) + GDN
+    6*H*Dk*Dv per token + head at the last position."""
+    d, F = dims["d_model"], dims["d_ff"]
+    gemm = sum(2 * T * layer_matrix_params(d, F, k) for k in kinds_exec)
+    n_full = sum(k == "full" for k in kinds_exec)
+    attn = n_full * 4 * dims["n_q_heads"] * dims["head_dim"] * (T * (T + 1) // 2)
+    gdn = (len(kinds_exec) - n_full) * 6 * dims["gdn_heads"] * dims["gdn_dk"] * dims["gdn_dv"] * T
+    head = 2 * d * dims["vocab"]
+    return dict(gemm=gemm, attn=attn, gdn=gdn, head=head, total=gemm + attn + gdn + head)
+
+
+def decode_bytes(dims, kinds_exec, B, L):
+    """Per step: each executed layer's weights once (bf16), the LM head, all
+    K/V read (L keys) + the appended K/V, GDN state read + write."""
+    d, F = dims["d_model"], dims["d_ff"]
+    weights = sum(2 * layer_matrix_params(d, F, k) for k in kinds_exec) + 2 * d * dims["vocab"]
+    n_full = sum(k == "full" for k in kinds_exec)
+    kv_tok = dims["n_kv_heads"] * dims["head_dim"] * 2 * 2
+    kv = n_full * B * kv_tok * (L + 1)
+    st = (len(kinds_exec) - n_full) * B * dims["gdn_heads"] * dims["gdn_dk"] * dims["gdn_dv"] * 4 * 2
+    return dict(weights=weights, kv=kv, state=st, total=weights + kv + st)
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence or by heads across GPUs, which this build does not run)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import looped_hybrid_attention_amd as L
+    import synth
+    from synth.presets import weight_specs
+
+    dims = synth.preset("full")
+    max_seq = ((DECODE_CTX + args.decode_warmup + args.decode_steps + 1 + 63) // 64) * 64
+    cfg = L.make_config(dims, max_batch=DECODE_B, max_seq=max_seq, max_tokens=PREFILL_T)
+    sched = L.loop_schedule(cfg)
+    kinds_layer = {}
+    for layer, full, *_ in sched:
+        kinds_layer[layer] = "full" if full else "gdn"
+    kinds = [kinds_layer[l] for l in range(dims["n_layers"])]
+    kinds_exec = ["full" if r[1] else "gdn" for r in sched]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    # weights drawn on the device by the seeded generator (same stream names
+    # and recipe as the host generator)
+    t0 = time.time()
+    tensors, ptrs = {}, {}
+    for name, shape, dt, std, mean in weight_specs(dims, kinds):
+        t = torch.empty(shape, dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device="cuda")
+        L.loop_synth_normal(t.data_ptr(), t.numel(), 1 if dt == "bf16" else 0, synth.SEED_W,
+                            synth.fnv1a32(name), 0, std, mean, stream)
+        tensors[name] = t
+        ptrs[name] = t.data_ptr()
+    wstruct = L.make_weights_struct(dims["n_layers"], ptrs)
+    arena_bytes = L.loop_arena_bytes(cfg)
+    ws_bytes = L.loop_workspace_bytes(cfg, PREFILL_T)
+    arena = torch.empty(arena_bytes, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    model = L.loop_model_create(cfg, wstruct, arena.data_ptr(), arena_bytes, ws.data_ptr(), ws_bytes)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    # ------------------------------------------------------------ prefill
+    ids = torch.empty(PREFILL_T, dtype=torch.int32, device="cuda")
+    L.loop_synth_token_ids(ids.data_ptr(), PREFILL_T, dims["vocab"], synth.SEED_X,
+                           synth.fnv1a32("bench.prefill.ids"), stream)
+    logits = torch.empty((1, dims["vocab"]), dtype=torch.float32, device="cuda")
+
+    def prefill_step():
+        L.loop_prefill(model, 1, PREFILL_T, [0], [0], d_tokens=ids.data_ptr(), d_logits=logits.data_ptr(),
+                       stream=stream)
+
+    for _ in range(args.warmup):
+        prefill_step()
+    torch.cuda.synchronize()
+    L.loop_profile(model, L.LOOP_K["gemm_gateup"])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        prefill_step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    k_ms, k_n = L.loop_profile_read(model)
+    L.loop_profile(model, -1)
+    assert torch.isfinite(logits).all().item(), "non-finite logits"
+    fl = prefill_flops(dims, kinds_exec, PREFILL_T)
+    tok_s = PREFILL_T / (ms_step / 1e3)
+    k_avg_ms = k_ms / max(k_n, 1)
+    k_flop = 2 * PREFILL_T * (2 * dims["d_ff"]) * dims["d_model"]
+    k_tflops = k_flop / (k_avg_ms / 1e3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "gemm_kernel<256,256,2,2,SWIGLU> (gate/up projection + SwiGLU epilogue)",
+                "launch_ms": round(k_avg_ms, 4), "launches": k_n,
+                "algorithmic_flop_per_launch": k_flop}
+    step_frac = fl["total"] / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS
+
+    # ------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        nf = sum(k == "full" for k in kinds_exec)
+        ng = len(kinds_exec) - nf
+        for s in range(nf):
+            for which in (0, 1):
+                off = L.loop_cache_offset(cfg, which, s, 0)
+                n = DECODE_B * dims["n_kv_heads"] * max_seq * dims["head_dim"]
+                L.loop_synth_normal(arena.data_ptr() + off, n, 1, synth.SEED_C,
+                                    synth.fnv1a32(f"bench.kv{which}.{s}"), 0, 1.0, 0.0, stream)
+        for s in range(ng):
+            off = L.loop_cache_offset(cfg, 2, s, 0)
+            n = DECODE_B * dims["gdn_heads"] * dims["gdn_dv"] * dims["gdn_dk"]
+            L.loop_synth_normal(arena.data_ptr() + off, n, 0, synth.SEED_C,
+                                synth.fnv1a32(f"bench.state.{s}"), 0, 0.1, 0.0, stream)
+        tok = torch.empty(DECODE_B, dtype=torch.int32, device="cuda")
+        L.loop_synth_token_ids(tok.data_ptr(), DECODE_B, dims["vocab"], synth.SEED_X,
+                               synth.fnv1a32("bench.decode.ids"), stream)
+        nxt = torch.empty(DECODE_B, dtype=torch.int32, device="cuda")
+        slots = list(range(DECODE_B))
+        pos = DECODE_CTX
+
+        def decode_step(p):
+            L.loop_decode_step(model, DECODE_B, slots, [p] * DECODE_B, tok.data_ptr(), d_next=nxt.data_ptr(),
+                               stream=stream)
+            tok.copy_(nxt)
+
+        for _ in range(args.decode_warmup):
+            decode_step(pos)
+            pos += 1
+        torch.cuda.synchronize()
+        L.loop_profile(model, L.LOOP_K["decode_attn"])
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record()
+        p_start = pos
+        for _ in range(args.decode_steps):
+            decode_step(pos)
+            pos += 1
+        d1.record()
+        torch.cuda.synchronize()
+        dms = d0.elapsed_time(d1) / args.decode_steps
+        a_ms, a_n = L.loop_profile_read(model)
+        L.loop_profile(model, -1)
+        L_mid = (p_start + pos) // 2
+        by = decode_bytes(dims, kinds_exec, DECODE_B, L_mid)
+        kv_launch = DECODE_B * dims["n_kv_heads"] * (L_mid + 1) * dims["head_dim"] * 2 * 2
+        a_avg = a_ms / max(a_n, 1)
+        a_gbs = kv_launch / (a_avg / 1e3) / 1e9
+        decode = {"metric": "decode tok/s", "value": round(DECODE_B / (dms / 1e3), 1), "unit": "tok/s",
+                  "ms_per_step": round(dms, 3), "steps": args.decode_steps, "warmup": args.decode_warmup,
+                  "batch": DECODE_B, "context": DECODE_CTX,
+                  "hbm_frac_step": round(by["total"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "algorithmic_bytes_per_step": by["total"],
+                  "roofline": {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": round(a_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                               "kernel": "decode_attn_kernel<256,4> + combine (split-L attention)",
+                               "launch_ms": round(a_avg, 4), "launches": a_n,
+                               "algorithmic_bytes_per_launch": kv_launch}}
+
+    L.loop_model_destroy(model)
+
+    # --------------------------------------------------------- CPU baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_sample_tokens)
+
+    out = {
+        "metric": "prefill tok/s through 56-exec looped stack + decode tok/s; % MFMA/HBM peak",
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform token ids)",
+        "config": {"workload": "full_prefill_8192", "model": "looped hybrid decoder, 32 layers x 56 executions",
+                   "global_batch": 1, "seq_len": PREFILL_T, "parallelism": "none (1 GPU)"},
+        "mfma_frac_step": round(step_frac, 4),
+        "algorithmic_flop_per_step": fl["total"],
+        "roofline": roofline,
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(T: int):
+    """The oracle (NumPy, fp32, as it stands) on the host cores: one 4-layer
+    group at real width (3 GDN + 1 full-attention layers) over T tokens,
+    scaled to the 56-execution stack (x 56/4 of the layer time)."""
+    import numpy as np
+    import oracle
+    from oracle import model as om
+    import synth
+    from synth.presets import make_weights
+    dims = synth.preset("group")
+    cfg = oracle.Config.from_dims(dims)
+    kinds = [oracle.layer_kind(cfg, l) for l in range(cfg.n_layers)]
+    W = om.to_dtype(make_weights(dims, kinds), np.float32)
+    x = synth.normal(synth.SEED_X, "bench.cpu.hidden", (1, T, dims["d_model"]), 1.0)
+    t0 = time.time()
+    om.prefill(cfg, W, [om.SeqState(cfg)], hidden=x, chunked_gdn=True)
+    dt = time.time() - t0
+    per_stack = dt * 56 / 4
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    return {"value": round(T / per_stack, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle fp32 forward of one real-width 4-layer group (3 GDN + 1 full attention, "
+                      f"mHC fork/merge) over {T} tokens took {dt:.2f} s; scaled by 56/4 executions",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+/*
+ * loop.h -- C ABI of the MI355X (gfx950) forward pass of the looped hybrid
+ * decoder.
+ *
+ * What is computed (page citations: [P1] = hncyxsy.com/news/268323, the
+ * technical article; [P2] = yuliuswiki.com/sensenova-loop-9b; [P4] =
+ * yeyulingfeng.com/a/1332585.html):
+ *   - [P1 section 2], [P2 section 2]: n_layers weight layers run as
+ *     head [0, loop_start), the block [loop_start, loop_end) loop_passes times
+ *     (B(B(h)) for two passes), tail [loop_end, n_layers), then the head:
+ *     4 + 24*2 + 4 = 56 executions for the full model.
+ *   - [P1 section 3]: every 4-layer group is 3 Gated-DeltaNet layers then one
+ *     full-attention layer (GQA 16 Q / 4 KV heads x 256, QK-norm, sigmoid
+ *     output gate, rotary on 64 of 256 dims in adjacent pairs).
+ *   - [P1 section 5], [P4 section 02]: a dual-stream mHC residual inside the
+ *     loop, the 2x2 stream mix Sinkhorn-normalised (20 iterations, fp32).
+ *   - [P1 section 4]: every execution keeps its own KV cache / GDN state.
+ *   - [P2 section 4]: greedy decoding with the cache, one token per step.
+ * Every layer has a SwiGLU FFN (d -> F -> d).  Precision: bf16 weights and
+ * GEMM operands with fp32 accumulation, fp32 residual / streams / mHC / GDN
+ * state, bf16 KV cache, fp32 logits.
+ *
+ * Conventions for every entry point:
+ *   - Return 0 on success or a negative LOOP_E* code; loop_last_error()
+ *     then holds a message (thread-local).  No exception crosses the ABI.
+ *   - "device" pointers are HIP device memory (gfx950) owned by the caller;
+ *     "host" pointers are read before the call returns (never kept).
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     null stream) and the call returns without waiting for it.
+ *   - A model handle is not thread-safe; calls on one handle must not
+ *     overlap (they share the workspace).
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call enqueues nothing.
+ */
+#ifndef LOOP_H_
+#define LOOP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LOOP_OK = 0,
+  LOOP_EINVAL = -1,    /* null pointer, bad flag, bad enum */
+  LOOP_ESHAPE = -2,    /* unsupported dimensions or layer layout */
+  LOOP_ECAPACITY = -3, /* arena / workspace / slot / position out of capacity */
+  LOOP_EHIP = -4,      /* a HIP runtime call failed */
+  LOOP_EDEVICE = -5    /* the current device is not gfx950 */
+};
+
+/* Model dimensions and capacities.  Names follow the pages: d_model = hidden
+ * size, d_ff = FFN size, vocab = vocabulary (0 = no embedding / head: the
+ * caller passes hidden states in and reads hidden states out).  Supported:
+ * loop bounds and n_layers multiples of 4, 1 <= loop_passes,
+ * n_streams == 2, head_dim in {64, 256}, rotary_dim even <= head_dim,
+ * n_q_heads multiple of n_kv_heads, gdn_dk == gdn_dv in {64, 128},
+ * gdn_chunk == 64, d_model multiple of 256, max_seq multiple of 64. */
+typedef struct loop_config {
+  int32_t n_layers, loop_start, loop_end, loop_passes;
+  int32_t d_model, d_ff, vocab;
+  int32_t n_q_heads, n_kv_heads, head_dim, rotary_dim;
+  int32_t gdn_heads, gdn_dk, gdn_dv;
+  int32_t n_streams, sinkhorn_iters;
+  float rope_theta, eps;
+  int32_t max_batch;  /* sequence slots held by the cache arena */
+  int32_t max_seq;    /* positions per sequence slot */
+  int32_t max_tokens; /* largest batch*seq_len of one call (workspace size) */
+  int32_t gdn_chunk;  /* chunk length of the chunked GDN prefill (64) */
+} loop_config;
+
+/* Weights of one weight layer; all device pointers, row-major [out, in]
+ * like a linear layer's weight.  bf16 unless marked fp32.
+ *   attn_norm, ffn_norm [d_model]         RMSNorm gains
+ *   full attention layers (layer % 4 == 3):
+ *     w_in  [2*Hq*D + 2*Hkv*D, d_model]   rows [q; gate; k; v]
+ *     w_o   [d_model, Hq*D]
+ *     q_norm, k_norm [D]                  QK-norm gains (shared by heads)
+ *   Gated-DeltaNet layers:
+ *     w_in  [2*H*Dk + 2*H*Dv + 2*H, d_model]  rows [q; k; v; z; a; b]
+ *     w_o   [d_model, H*Dv]
+ *     o_norm [Dv]                         output RMSNorm gain
+ *   w_gateup [2*d_ff, d_model]            rows [gate; up]
+ *   w_down   [d_model, d_ff]
+ *   loop layers only (loop_start <= layer < loop_end), fp32:
+ *     mhc_read_w [2, 2*d_model], mhc_read_b [2],
+ *     mhc_write_w [2, d_model], mhc_write_b [2], mhc_mix [2, 2] (logits)
+ * Unused pointers may be NULL. */
+typedef struct loop_layer_weights {
+  const void *attn_norm, *ffn_norm;
+  const void *w_in, *w_o;
+  const void *q_norm, *k_norm, *o_norm;
+  const void *w_gateup, *w_down;
+  const float *mhc_read_w, *mhc_read_b, *mhc_write_w, *mhc_write_b, *mhc_mix;
+} loop_layer_weights;
+
+typedef struct loop_weights {
+  const void* embed;      /* bf16 [vocab, d_model] (device), NULL if vocab == 0 */
+  const void* final_norm; /* bf16 [d_model] (device) */
+  const void* head;       /* bf16 [vocab, d_model] (device), untied */
+  int32_t n_layers;
+  const loop_layer_weights* layers; /* host array [n_layers], copied at create */
+} loop_weights;
+
+typedef struct loop_model loop_model;
+
+/* ---------------------------------------------------------------- sizes
+ * [P1 section 4]: full-attention KV = n_full_exec * 2 (K, V) * n_kv_heads *
+ * head_dim * 2 bytes per token (57,344 B per token for the full model); GDN
+ * state = n_gdn_exec * H * Dk * Dv * 4 bytes per sequence, independent of
+ * the context length.  All return -1 on an invalid configuration. */
+int64_t loop_kv_bytes(const loop_config* cfg, int32_t batch, int64_t seq_len);
+int64_t loop_state_bytes(const loop_config* cfg, int32_t batch);
+/* Arena for create: kv_bytes(max_batch, max_seq) + state_bytes(max_batch). */
+int64_t loop_arena_bytes(const loop_config* cfg);
+/* Workspace for create, for calls of up to max_tokens tokens. */
+int64_t loop_workspace_bytes(const loop_config* cfg, int32_t max_tokens);
+
+/* Cache layout inside the arena (byte offsets from the arena base):
+ *   K of (kv slot s, sequence slot b): bf16 [n_kv_heads][max_seq][head_dim]
+ *   V of (s, b):                       bf16 [n_kv_heads][head_dim][max_seq]
+ *                                      (transposed: positions contiguous)
+ *   per kv slot s the K blocks of sequence slots 0..max_batch-1 follow each
+ *   other, then the V blocks; the GDN states follow all KV slots.
+ *   GDN state of (gdn slot g, b):      fp32 [gdn_heads][gdn_dv][gdn_dk]
+ * which = 0 for K, 1 for V, 2 for the GDN state (s = gdn slot).  kv slot /
+ * gdn slot = rank of the execution among executions of its kind.  Returns -1
+ * when out of range. */
+int64_t loop_cache_offset(const loop_config* cfg, int32_t which, int32_t slot, int32_t seq_slot);
+
+/* Execution schedule, 0-based ([P1 section 2], [P4 section 03]): writes
+ * n_exec rows of 6 int32 {weight layer, kind (0 GDN, 1 full), slot, loop,
+ * fork, merge} into host `out` (capacity `cap` rows) and returns n_exec, or
+ * a negative code. */
+int32_t loop_schedule(const loop_config* cfg, int32_t* out, int32_t cap);
+
+/* -------------------------------------------------------------- the model
+ * Borrows the caller's device buffers: weights, the cache arena
+ * (loop_arena_bytes) and the workspace (loop_workspace_bytes(cfg,
+ * cfg->max_tokens)); they must stay alive and unmoved until destroy.  No
+ * device memory is allocated.  Checks that the current device is gfx950.
+ * The arena contents are not touched: a sequence slot is reset by a prefill
+ * with start_pos 0. */
+int loop_model_create(const loop_config* cfg, const loop_weights* w, void* d_arena,
+                      size_t arena_bytes, void* d_workspace, size_t ws_bytes,
+                      loop_model** out);
+void loop_model_destroy(loop_model* m);
+
+/* Prefill: seq_len new tokens for each of `batch` sequences, appended to the
+ * caches of their slots at positions start_pos[b] .. start_pos[b]+seq_len-1
+ * (start_pos 0 = fresh sequence: GDN state starts at zero; chunked prefill =
+ * repeated calls).  Exactly one of d_tokens / d_hidden_in is given.
+ *   slots      host [batch]   sequence slot of each sequence (distinct)
+ *   start_pos  host [batch]
+ *   d_tokens   device int32 [batch*seq_len] token ids (vocab > 0; ids
+ *              outside [0, vocab) are clamped into it)
+ *   d_hidden_in device fp32 [batch*seq_len, d_model]
+ *   d_logits   device fp32 [batch, vocab] logits of the last position, or NULL
+ *   d_hidden_out device fp32 [batch*seq_len, d_model]: h after the last
+ *              execution (before the final norm), or NULL
+ *   n_taps / tap_exec (host) / d_taps device fp32 [n_taps, batch, d_model]:
+ *              hidden state after the listed executions at the last position
+ *              (mean of the streams inside the loop), or 0 / NULL.
+ * Requires batch*seq_len <= max_tokens, start_pos+seq_len <= max_seq,
+ * slot < max_batch. */
+typedef struct loop_prefill_args {
+  int32_t batch, seq_len;
+  const int32_t* slots;
+  const int32_t* start_pos;
+  const int32_t* d_tokens;
+  const float* d_hidden_in;
+  float* d_logits;
+  float* d_hidden_out;
+  int32_t n_taps;
+  const int32_t* tap_exec;
+  float* d_taps;
+} loop_prefill_args;
+int loop_prefill(loop_model* m, const loop_prefill_args* a, void* stream);
+
+/* Decode step: one new token per sequence at position pos[b] (its current
+ * length), greedy next token = argmax of the logits, lowest index on ties.
+ *   slots, pos  host [batch]
+ *   d_tokens    device int32 [batch]
+ *   d_logits    device fp32 [batch, vocab] or NULL
+ *   d_next      device int32 [batch] or NULL
+ *   d_hidden_out device fp32 [batch, d_model] (h before the final norm) or NULL */
+typedef struct loop_decode_args {
+  int32_t batch;
+  const int32_t* slots;
+  const int32_t* pos;
+  const int32_t* d_tokens;
+  float* d_logits;
+  int32_t* d_next;
+  float* d_hidden_out;
+} loop_decode_args;
+int loop_decode_step(loop_model* m, const loop_decode_args* a, void* stream);
+
+/* Sinkhorn-normalised stream-mix matrices of every loop layer as the device
+ * computes them ([P1 section 5]): fp32 [loop_end-loop_start, 2, 2] into
+ * device d_out. */
+int loop_debug_mhc(loop_model* m, float* d_out, void* stream);
+
+const char* loop_last_error(void);
+
+/* Kernel timing of one kernel class inside the model calls: with class c
+ * selected (c >= 0), every launch of that class made by loop_prefill /
+ * loop_decode_step is bracketed by two HIP events on the call's stream;
+ * loop_profile_read waits for them and returns the summed duration (ms) and
+ * the number of launches since the last read, then clears them.  c = -1
+ * turns it off.  Classes: */
+enum {
+  LOOP_K_GEMM_GATEUP = 0, LOOP_K_GEMM_DOWN = 1, LOOP_K_GEMM_IN = 2, LOOP_K_GEMM_O = 3,
+  LOOP_K_ATTN_PREP = 4, LOOP_K_FLASH = 5, LOOP_K_GDN = 6, LOOP_K_DECODE_ATTN = 7,
+  LOOP_K_ROWS = 8, LOOP_K_HEAD = 9, LOOP_K_NCLASS = 10
+};
+int loop_profile(loop_model* m, int32_t kernel_class);
+int loop_profile_read(loop_model* m, double* total_ms, int64_t* launches);
+
+/* ------------------------------------------------------ single operations
+ * The kernels of the path, callable one at a time (same kernels the model
+ * launches).  Device pointers; row-major; return codes as above.
+ *
+ * GEMM C[M,N] = A[M,K] . B[N,K]^T (bf16 operands, fp32 accumulation), with
+ * the epilogue `epi`:
+ *   LOOP_EPI_BF16     C bf16 [M, ldc]
+ *   LOOP_EPI_F32      C fp32
+ *   LOOP_EPI_F32_RES  C fp32 = R + A.B^T (R fp32 [M, ldc], may alias C)
+ *   LOOP_EPI_SWIGLU   B holds [gate; up] (2*N rows); C bf16 [M, N] =
+ *                     silu(A.gate^T) * (A.up^T)
+ * Requires K % 64 == 0, lda and ldb multiples of 8, A and B 16-byte aligned. */
+enum { LOOP_EPI_BF16 = 0, LOOP_EPI_F32 = 1, LOOP_EPI_F32_RES = 2, LOOP_EPI_SWIGLU = 3 };
+int loop_op_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                 const float* R, int32_t M, int32_t N, int32_t K, int32_t epi, void* stream);
+
+/* -------------------------------------------------- synthetic inputs
+ * Device implementation of the seeded input generator (Philox4x32-10,
+ * Salmon et al. SC'11, + Box-Muller in float64): element i of stream
+ * (seed, key) takes word i%4 of the Philox block i/4 (counter (i/4 lo,
+ * i/4 hi, 0, 0), key (seed, key)); normals from word pairs (0,1), (2,3),
+ * u = (x + 0.5) 2^-32, value = fp32(z*std + mean), optionally rounded to bf16
+ * (nearest even).  dtype 0 = fp32, 1 = bf16.  Writes n elements to device
+ * `dst`, element i of the call being stream element start+i. */
+int loop_synth_normal(void* dst, int64_t n, int32_t dtype, uint32_t seed, uint32_t key,
+                      int64_t start, double std, double mean, void* stream);
+/* Uniform ids (x * vocab) >> 32, int32, stream elements 0 .. n-1. */
+int loop_synth_token_ids(int32_t* dst, int64_t n, uint32_t vocab, uint32_t seed, uint32_t key,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOOP_H_ */

@@ -1,0 +1,60 @@
+// Shared device helpers for the gfx950 kernels: bf16 conversion, vector
+// types, MFMA wrappers, wave reductions.  CDNA4 only (wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define DEV __device__ __forceinline__
+
+// bf16 <-> fp32.  bf16 -> fp32 is exact (shift); fp32 -> bf16 rounds to
+// nearest even (inputs here are finite).
+DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+DEV float bf2f(bf16 b) { return (float)b; }
+DEV uint16_t f2bf_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (uint16_t)u;
+}
+DEV bf16 f2bf(float f) { return __builtin_bit_cast(bf16, f2bf_bits(f)); }
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%32][(l/32)*8 .. +8]
+// and B^T[l%32][(l/32)*8 .. +8] (k-contiguous); the 16 results of lane l are
+// D[8*(r/4) + 4*(l/32) + r%4][l%32], r = 0..15.
+DEV f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum of one float per thread; `red` = __shared__ float[nwaves].
+// All threads get the result.  Deterministic (fixed order).
+template <int NT>
+DEV float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += red[i];
+  return s;
+}
+
+DEV float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+DEV float siluf_(float x) { return x / (1.0f + __expf(-x)); }

@@ -1,0 +1,98 @@
+// Host-side launchers of the kernels (one per kernel family).  Each enqueues
+// on stream `s` and returns the launch status; argument checks are done by
+// the callers in host.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "../../include/loop.h"
+
+hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                       const float* R, int M, int N, int K, int epi, hipStream_t s);
+
+hipError_t launch_synth_normal(void* dst, int64_t n, int dtype, uint32_t seed, uint32_t key,
+                               int64_t start, double std, double mean, hipStream_t s);
+hipError_t launch_synth_token_ids(int32_t* dst, int64_t n, uint32_t vocab, uint32_t seed,
+                                  uint32_t key, hipStream_t s);
+
+// ---- row kernels
+hipError_t launch_embed(const int32_t* ids, const void* E, float* h, int M, int d, int vocab, hipStream_t s);
+// y[i] = bf16(RMSNorm(x[row_i] (+ x2[row_i])) * g); rows = NULL: row i = i.
+hipError_t launch_rmsnorm(const float* x, const float* x2, const int32_t* rows, int64_t x_stride,
+                          const void* g, void* y, int M, int d, float eps, hipStream_t s);
+
+enum { TR_IN_H = 0, TR_IN_WRITE = 1 };
+enum { TR_OUT_NORM = 0, TR_OUT_READ = 1, TR_OUT_NONE = 2 };
+struct TransitionArgs {
+  int in_mode, out_mode, M, d, iters, rows_per_block;
+  float eps;
+  const float* h;    // in = H: current state
+  const float* out;  // in = WRITE: layer branch a + f
+  const float* s0;   // in = WRITE: streams before the write
+  const float* s1;
+  const float* write_w; const float* write_b; const float* mix;  // this exec's write params
+  const float* read_w; const float* read_b;                      // next exec's read params
+  const uint16_t* norm_g;  // next exec's attn_norm gain (bf16)
+  float* s0_out; float* s1_out; float* x_out;  // out = READ
+  float* h_out;            // in = WRITE, out != READ: merged h
+  uint16_t* xn;            // normed input of the next exec (bf16)
+};
+hipError_t launch_transition(TransitionArgs t, hipStream_t s);
+hipError_t launch_tap(const float* h, const float* s0, const float* s1, float* dst, int B, int T, int d,
+                      hipStream_t s);
+hipError_t launch_sinkhorn(const float* mix, int iters, float* out, hipStream_t s);
+int argmax_chunks(int64_t n);
+hipError_t launch_argmax(const float* x, int rows, int64_t n, float* pv, int* pi, int32_t* out, hipStream_t s);
+
+// ---- attention
+struct AttnPrepArgs {
+  const uint16_t* proj; int64_t proj_stride;  // [M][..]: q | gate | k | v
+  int T, Hq, Hkv, D, R, max_seq;
+  float theta, eps;
+  const int32_t* pos;       // device [B] first position of the call
+  const int32_t* seq_slot;  // device [B]
+  const uint16_t* q_norm; const uint16_t* k_norm;
+  uint16_t* q_out;          // [M][Hq][D]
+  uint16_t* k_cache;        // K block of the exec slot: [max_batch][Hkv][max_seq][D]
+  uint16_t* v_cache;        // V block: [max_batch][Hkv][D][max_seq]
+};
+hipError_t launch_attn_prep(const AttnPrepArgs& a, int M, hipStream_t s);
+
+struct FlashArgs {
+  const uint16_t* q; int T, Hq, Hkv, D, max_seq;
+  const int32_t* pos; const int32_t* seq_slot;
+  const uint16_t* k_cache; const uint16_t* v_cache;
+  float scale_log2;
+  const uint16_t* gate; int64_t gate_stride;
+  uint16_t* out; int64_t out_stride;
+};
+hipError_t launch_flash_prefill(const FlashArgs& a, int B, hipStream_t s);
+
+struct DecodeAttnArgs {
+  const uint16_t* q; int Hq, Hkv, D, max_seq;
+  const int32_t* pos;  // device [B]: position of the new token (keys 0..pos)
+  const int32_t* seq_slot;
+  const uint16_t* k_cache; const uint16_t* v_cache;
+  float scale_log2;
+  int split_len, n_split;
+  float* partial;      // [B][Hq][n_split][D + 2]
+  const uint16_t* gate; int64_t gate_stride;
+  uint16_t* out; int64_t out_stride;
+};
+hipError_t launch_decode_attn(const DecodeAttnArgs& a, int B, hipStream_t s);
+
+// ---- Gated-DeltaNet
+struct GdnArgs {
+  const uint16_t* proj; int64_t proj_stride;
+  int off_q, off_k, off_v, off_z, off_a, off_b;
+  int H, Dk, T, n_chunks;
+  float eps, q_scale;
+  const int32_t* pos; const int32_t* seq_slot;
+  float* state;  // state block of the exec slot: [max_batch][H][Dv][Dk]
+  float* W; float* Ut; float* Qg; float* Kd; float* Mqk; float* gC;  // chunk workspace
+  float* o;      // [M][H][Dv] fp32
+  const uint16_t* o_norm;
+  uint16_t* out; int64_t out_stride;
+};
+int gdn_chunks(int T);
+hipError_t launch_gdn_prefill(const GdnArgs& a, int B, hipStream_t s);
+hipError_t launch_gdn_recurrent(const GdnArgs& a, int B, hipStream_t s);

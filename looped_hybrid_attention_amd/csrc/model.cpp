@@ -1,0 +1,542 @@
+// The model entry points: create / destroy, prefill, decode step, and the
+// executor that replays the execution schedule over the shared weights.
+//
+// [P1 section 2], [P2 section 2]: the schedule runs the head layers, the
+// shared block loop_passes times with the same weights, the tail layers,
+// then the head.  [P1 section 4]: every execution owns its KV cache (full
+// attention) or state (Gated-DeltaNet) slot in the arena.  [P1 section 5],
+// [P1 section 6]: inside the loop the residual is the pair of mHC streams:
+// fork on entry, read / mix / write per execution, merge on exit.
+//
+// Per execution (M = batch * tokens rows):
+//   in-proj GEMM (xn -> proj, bf16)
+//   mixer: full attention (prep + flash or split decode) or GDN (chunked or
+//          recurrent) -> o (bf16, gated / normed)
+//   O-proj GEMM: plain hmid = h + o W_o^T; loop a = o W_o^T
+//   RMSNorm of hmid (plain) or x + a (loop) -> hn
+//   gate/up GEMM with SwiGLU epilogue -> act
+//   down GEMM: plain h = hmid + act W_down^T; loop out = a + act W_down^T
+//   transition to the next execution (mHC write / fork / read / merge + the
+//   next pre-norm) -> xn
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <set>
+
+#include "host.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+constexpr int DEC_SPLIT = 256;  // keys per decode-attention split
+
+size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+  size_t meta, h, hmid, x, a, s0, s1, xn, hn, proj, qbuf, obuf, act, gdn_o;
+  size_t gW, gUt, gQg, gKd, gM, gC;
+  size_t xf, logits, am_v, am_i, dec_part, mhc;
+  size_t total;
+  int n_in_max, chunk_slots, n_split_max;
+};
+
+int n_in_full(const loop_config& c) { return 2 * c.n_q_heads * c.head_dim + 2 * c.n_kv_heads * c.head_dim; }
+int n_in_gdn(const loop_config& c) { return 2 * c.gdn_heads * c.gdn_dk + 2 * c.gdn_heads * c.gdn_dv + 2 * c.gdn_heads; }
+
+Layout layout(const loop_config& c, int64_t M) {
+  Layout L{};
+  const int64_t d = c.d_model, B = c.max_batch;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
+  L.n_in_max = std::max(n_in_full(c), n_in_gdn(c));
+  L.meta = take(4 * B * sizeof(int32_t));
+  L.h = take(M * d * 4);
+  L.hmid = take(M * d * 4);
+  L.x = take(M * d * 4);
+  L.a = take(M * d * 4);
+  L.s0 = take(M * d * 4);
+  L.s1 = take(M * d * 4);
+  L.xn = take(M * d * 2);
+  L.hn = take(M * d * 2);
+  L.proj = take(M * (int64_t)L.n_in_max * 2);
+  L.qbuf = take(M * (int64_t)c.n_q_heads * c.head_dim * 2);
+  L.obuf = take(M * (int64_t)std::max(c.n_q_heads * c.head_dim, c.gdn_heads * c.gdn_dv) * 2);
+  L.act = take(M * (int64_t)c.d_ff * 2);
+  L.gdn_o = take(M * (int64_t)c.gdn_heads * c.gdn_dv * 4);
+  // chunk workspace: (sum over sequences of their chunks) * heads
+  L.chunk_slots = (int)((M + 63) / 64 + B);
+  const int64_t cs = (int64_t)L.chunk_slots * c.gdn_heads;
+  L.gW = take(cs * 64 * c.gdn_dk * 4);
+  L.gUt = take(cs * 64 * c.gdn_dv * 4);
+  L.gQg = take(cs * 64 * c.gdn_dk * 4);
+  L.gKd = take(cs * 64 * c.gdn_dk * 4);
+  L.gM = take(cs * 64 * 64 * 4);
+  L.gC = take(cs * 4);
+  L.xf = take(B * d * 2);
+  L.logits = take(B * (int64_t)std::max(c.vocab, 1) * 4);
+  L.am_v = take(B * (int64_t)argmax_chunks(std::max(c.vocab, 1)) * 4);
+  L.am_i = take(B * (int64_t)argmax_chunks(std::max(c.vocab, 1)) * 4);
+  L.n_split_max = (c.max_seq + DEC_SPLIT - 1) / DEC_SPLIT;
+  L.dec_part = take(B * (int64_t)c.n_q_heads * L.n_split_max * (c.head_dim + 2) * 4);
+  L.mhc = take(std::max(c.loop_end - c.loop_start, 1) * 4 * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct loop_model {
+  loop_config cfg;
+  std::vector<loop_layer_weights> lw;
+  const void *embed, *final_norm, *head;
+  char* arena;
+  size_t arena_bytes;
+  char* ws;
+  size_t ws_bytes;
+  Layout L;
+  std::vector<ExecDesc> sched;
+  std::vector<int32_t> meta_host;
+  // kernel-class timing
+  int prof_class = -1;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_events;
+  size_t prof_used = 0;
+};
+
+extern "C" int64_t loop_workspace_bytes(const loop_config* c, int32_t max_tokens) {
+  if (validate_config(c) || max_tokens <= 0) return -1;
+  return (int64_t)layout(*c, max_tokens).total;
+}
+
+static int check_weights(const loop_config& c, const loop_weights* w, const std::vector<ExecDesc>& s) {
+  if (!w) return loop_fail(LOOP_EINVAL, "weights are NULL");
+  if (w->n_layers != c.n_layers || !w->layers) return loop_fail(LOOP_EINVAL, "weights: n_layers mismatch or no layer array");
+  if (!w->final_norm) return loop_fail(LOOP_EINVAL, "weights: final_norm is NULL");
+  if (c.vocab > 0 && (!w->embed || !w->head)) return loop_fail(LOOP_EINVAL, "weights: embed / head NULL with vocab > 0");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const loop_layer_weights& x = w->layers[l];
+    if (!x.attn_norm || !x.ffn_norm || !x.w_in || !x.w_o || !x.w_gateup || !x.w_down)
+      return loop_fail(LOOP_EINVAL, "weights: layer %d misses a matrix or norm gain", l);
+    const bool full = l % 4 == 3;
+    if (full && (!x.q_norm || !x.k_norm)) return loop_fail(LOOP_EINVAL, "weights: layer %d needs q_norm, k_norm", l);
+    if (!full && !x.o_norm) return loop_fail(LOOP_EINVAL, "weights: layer %d needs o_norm", l);
+    const bool loop = l >= c.loop_start && l < c.loop_end;
+    if (loop && (!x.mhc_read_w || !x.mhc_read_b || !x.mhc_write_w || !x.mhc_write_b || !x.mhc_mix))
+      return loop_fail(LOOP_EINVAL, "weights: loop layer %d needs its mHC parameters", l);
+  }
+  (void)s;
+  return 0;
+}
+
+extern "C" int loop_model_create(const loop_config* cfg, const loop_weights* w, void* d_arena,
+                                 size_t arena_bytes, void* d_workspace, size_t ws_bytes,
+                                 loop_model** out) {
+  if (!out) return loop_fail(LOOP_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (int e = validate_config(cfg)) return e;
+  std::vector<ExecDesc> sched;
+  build_schedule(*cfg, sched);
+  if (int e = check_weights(*cfg, w, sched)) return e;
+  const int64_t need_arena = loop_arena_bytes(cfg);
+  const Layout L = layout(*cfg, cfg->max_tokens);
+  if (!d_arena || arena_bytes < (size_t)need_arena)
+    return loop_fail(LOOP_ECAPACITY, "arena: %zu bytes given, %lld needed", arena_bytes, (long long)need_arena);
+  if (!d_workspace || ws_bytes < L.total)
+    return loop_fail(LOOP_ECAPACITY, "workspace: %zu bytes given, %zu needed", ws_bytes, L.total);
+  if (((uintptr_t)d_arena | (uintptr_t)d_workspace) % ALIGN)
+    return loop_fail(LOOP_EINVAL, "arena and workspace must be %zu-byte aligned", ALIGN);
+  int dev = 0;
+  hipDeviceProp_t prop;
+  hipError_t he = hipGetDevice(&dev);
+  if (he == hipSuccess) he = hipGetDeviceProperties(&prop, dev);
+  if (he != hipSuccess) return loop_hip_fail(he, "device query");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return loop_fail(LOOP_EDEVICE, "device is %s, gfx950 required", prop.gcnArchName);
+  loop_model* m = new loop_model();
+  m->cfg = *cfg;
+  m->lw.assign(w->layers, w->layers + cfg->n_layers);
+  m->embed = w->embed;
+  m->final_norm = w->final_norm;
+  m->head = w->head;
+  m->arena = (char*)d_arena;
+  m->arena_bytes = arena_bytes;
+  m->ws = (char*)d_workspace;
+  m->ws_bytes = ws_bytes;
+  m->L = L;
+  m->sched = sched;
+  *out = m;
+  return 0;
+}
+
+extern "C" void loop_model_destroy(loop_model* m) {
+  if (!m) return;
+  for (auto& p : m->prof_events) {
+    (void)hipEventDestroy(p.first);
+    (void)hipEventDestroy(p.second);
+  }
+  delete m;
+}
+
+namespace {
+// Scoped timing of one launch group of the selected class.
+struct Prof {
+  loop_model* m;
+  hipStream_t s;
+  int idx = -1;
+  Prof(loop_model* m_, int cls, hipStream_t s_) : m(m_), s(s_) {
+    if (m->prof_class != cls) return;
+    if (m->prof_used == m->prof_events.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) { (void)hipEventDestroy(a); return; }
+      m->prof_events.push_back({a, b});
+    }
+    idx = (int)m->prof_used++;
+    (void)hipEventRecord(m->prof_events[idx].first, s);
+  }
+  ~Prof() {
+    if (idx >= 0) (void)hipEventRecord(m->prof_events[idx].second, s);
+  }
+};
+}  // namespace
+
+extern "C" int loop_profile(loop_model* m, int32_t kernel_class) {
+  if (!m) return loop_fail(LOOP_EINVAL, "model is NULL");
+  if (kernel_class < -1 || kernel_class >= LOOP_K_NCLASS) return loop_fail(LOOP_EINVAL, "bad kernel class %d", kernel_class);
+  m->prof_class = kernel_class;
+  m->prof_used = 0;
+  return 0;
+}
+
+extern "C" int loop_profile_read(loop_model* m, double* total_ms, int64_t* launches) {
+  if (!m || !total_ms || !launches) return loop_fail(LOOP_EINVAL, "NULL argument");
+  double t = 0;
+  for (size_t i = 0; i < m->prof_used; ++i) {
+    hipError_t e = hipEventSynchronize(m->prof_events[i].second);
+    if (e != hipSuccess) return loop_hip_fail(e, "profile event");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, m->prof_events[i].first, m->prof_events[i].second);
+    if (e != hipSuccess) return loop_hip_fail(e, "profile elapsed");
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = (int64_t)m->prof_used;
+  m->prof_used = 0;
+  return 0;
+}
+
+namespace {
+
+struct Call {
+  int B, T, M;
+  bool decode;
+  const int32_t* d_pos;
+  const int32_t* d_slot;
+  const int32_t* d_last;
+};
+
+#define HIP_TRY(x)                                              \
+  do {                                                          \
+    hipError_t e_ = (x);                                        \
+    if (e_ != hipSuccess) return loop_hip_fail(e_, #x);         \
+  } while (0)
+
+template <typename T>
+T* at(loop_model* m, size_t off) { return reinterpret_cast<T*>(m->ws + off); }
+
+int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
+  const loop_config& c = m->cfg;
+  const Layout& L = m->L;
+  const ExecDesc& d = m->sched[e];
+  const loop_layer_weights& w = m->lw[d.layer];
+  const int M = k.M, dm = c.d_model;
+  uint16_t* xn = at<uint16_t>(m, L.xn);
+  uint16_t* proj = at<uint16_t>(m, L.proj);
+  uint16_t* obuf = at<uint16_t>(m, L.obuf);
+  float* h = at<float>(m, L.h);
+  float* hmid = at<float>(m, L.hmid);
+  float* x = at<float>(m, L.x);
+  float* a = at<float>(m, L.a);
+  const int n_in = d.full ? n_in_full(c) : n_in_gdn(c);
+
+  {
+    Prof p(m, LOOP_K_GEMM_IN, s);
+    HIP_TRY(launch_gemm(xn, dm, w.w_in, dm, proj, L.n_in_max, nullptr, M, n_in, dm, LOOP_EPI_BF16, s));
+  }
+  int mix_width;
+  if (d.full) {
+    const int Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim;
+    mix_width = Hq * D;
+    const int64_t kv_off = loop_cache_offset(&c, 0, d.slot, 0);
+    const int64_t v_off = loop_cache_offset(&c, 1, d.slot, 0);
+    AttnPrepArgs p{};
+    p.proj = proj; p.proj_stride = L.n_in_max;
+    p.T = k.T; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.R = c.rotary_dim; p.max_seq = c.max_seq;
+    p.theta = c.rope_theta; p.eps = c.eps;
+    p.pos = k.d_pos; p.seq_slot = k.d_slot;
+    p.q_norm = (const uint16_t*)w.q_norm; p.k_norm = (const uint16_t*)w.k_norm;
+    p.q_out = at<uint16_t>(m, L.qbuf);
+    p.k_cache = (uint16_t*)(m->arena + kv_off);
+    p.v_cache = (uint16_t*)(m->arena + v_off);
+    {
+      Prof pr(m, LOOP_K_ATTN_PREP, s);
+      HIP_TRY(launch_attn_prep(p, M, s));
+    }
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    if (!k.decode) {
+      FlashArgs f{};
+      f.q = p.q_out; f.T = k.T; f.Hq = Hq; f.Hkv = Hkv; f.D = D; f.max_seq = c.max_seq;
+      f.pos = k.d_pos; f.seq_slot = k.d_slot; f.k_cache = p.k_cache; f.v_cache = p.v_cache;
+      f.scale_log2 = scale_log2;
+      f.gate = proj + Hq * D; f.gate_stride = L.n_in_max;
+      f.out = obuf; f.out_stride = mix_width;
+      Prof pr(m, LOOP_K_FLASH, s);
+      HIP_TRY(launch_flash_prefill(f, k.B, s));
+    } else {
+      DecodeAttnArgs g{};
+      g.q = p.q_out; g.Hq = Hq; g.Hkv = Hkv; g.D = D; g.max_seq = c.max_seq;
+      g.pos = k.d_pos; g.seq_slot = k.d_slot; g.k_cache = p.k_cache; g.v_cache = p.v_cache;
+      g.scale_log2 = scale_log2;
+      g.split_len = DEC_SPLIT; g.n_split = L.n_split_max;
+      g.partial = at<float>(m, L.dec_part);
+      g.gate = proj + Hq * D; g.gate_stride = L.n_in_max;
+      g.out = obuf; g.out_stride = mix_width;
+      Prof pr(m, LOOP_K_DECODE_ATTN, s);
+      HIP_TRY(launch_decode_attn(g, k.B, s));
+    }
+  } else {
+    const int H = c.gdn_heads, Dk = c.gdn_dk, Dv = c.gdn_dv;
+    mix_width = H * Dv;
+    GdnArgs g{};
+    g.proj = proj; g.proj_stride = L.n_in_max;
+    g.off_q = 0; g.off_k = H * Dk; g.off_v = 2 * H * Dk; g.off_z = 2 * H * Dk + H * Dv;
+    g.off_a = 2 * H * Dk + 2 * H * Dv; g.off_b = g.off_a + H;
+    g.H = H; g.Dk = Dk; g.T = k.T; g.n_chunks = gdn_chunks(k.T);
+    g.eps = c.eps; g.q_scale = (float)(1.0 / sqrt((double)Dk));
+    g.pos = k.d_pos; g.seq_slot = k.d_slot;
+    g.state = (float*)(m->arena + loop_cache_offset(&c, 2, d.slot, 0));
+    g.W = at<float>(m, L.gW); g.Ut = at<float>(m, L.gUt); g.Qg = at<float>(m, L.gQg);
+    g.Kd = at<float>(m, L.gKd); g.Mqk = at<float>(m, L.gM); g.gC = at<float>(m, L.gC);
+    g.o = at<float>(m, L.gdn_o);
+    g.o_norm = (const uint16_t*)w.o_norm;
+    g.out = obuf; g.out_stride = mix_width;
+    Prof pr(m, LOOP_K_GDN, s);
+    if (k.decode) HIP_TRY(launch_gdn_recurrent(g, k.B, s));
+    else HIP_TRY(launch_gdn_prefill(g, k.B, s));
+  }
+  // O-proj, mid norm, FFN
+  uint16_t* hn = at<uint16_t>(m, L.hn);
+  uint16_t* act = at<uint16_t>(m, L.act);
+  {
+    Prof p(m, LOOP_K_GEMM_O, s);
+    if (!d.loop)
+      HIP_TRY(launch_gemm(obuf, mix_width, w.w_o, mix_width, hmid, dm, h, M, dm, mix_width, LOOP_EPI_F32_RES, s));
+    else
+      HIP_TRY(launch_gemm(obuf, mix_width, w.w_o, mix_width, a, dm, nullptr, M, dm, mix_width, LOOP_EPI_F32, s));
+  }
+  {
+    Prof p(m, LOOP_K_ROWS, s);
+    if (!d.loop) HIP_TRY(launch_rmsnorm(hmid, nullptr, nullptr, dm, w.ffn_norm, hn, M, dm, c.eps, s));
+    else HIP_TRY(launch_rmsnorm(x, a, nullptr, dm, w.ffn_norm, hn, M, dm, c.eps, s));
+  }
+  {
+    Prof p(m, LOOP_K_GEMM_GATEUP, s);
+    HIP_TRY(launch_gemm(hn, dm, w.w_gateup, dm, act, c.d_ff, nullptr, M, c.d_ff, dm, LOOP_EPI_SWIGLU, s));
+  }
+  {
+    Prof p(m, LOOP_K_GEMM_DOWN, s);
+    if (!d.loop) HIP_TRY(launch_gemm(act, c.d_ff, w.w_down, c.d_ff, h, dm, hmid, M, dm, c.d_ff, LOOP_EPI_F32_RES, s));
+    else HIP_TRY(launch_gemm(act, c.d_ff, w.w_down, c.d_ff, a, dm, a, M, dm, c.d_ff, LOOP_EPI_F32_RES, s));
+  }
+  Prof prow(m, LOOP_K_ROWS, s);
+
+  // transition to the next execution
+  TransitionArgs t{};
+  t.M = M; t.d = dm; t.iters = c.sinkhorn_iters; t.eps = c.eps;
+  float* s0 = at<float>(m, L.s0);
+  float* s1 = at<float>(m, L.s1);
+  t.h = h; t.out = a; t.s0 = s0; t.s1 = s1;
+  t.s0_out = s0; t.s1_out = s1; t.x_out = x; t.h_out = h; t.xn = xn;
+  if (d.loop) {
+    t.in_mode = TR_IN_WRITE;
+    t.write_w = w.mhc_write_w; t.write_b = w.mhc_write_b; t.mix = w.mhc_mix;
+  } else {
+    t.in_mode = TR_IN_H;
+  }
+  const bool last = e + 1 == (int)m->sched.size();
+  if (last) {
+    if (d.loop) {
+      t.out_mode = TR_OUT_NONE;
+      HIP_TRY(launch_transition(t, s));
+    }
+    return 0;
+  }
+  const ExecDesc& nd = m->sched[e + 1];
+  const loop_layer_weights& nw = m->lw[nd.layer];
+  t.norm_g = (const uint16_t*)nw.attn_norm;
+  if (nd.loop && !nd.fork) {  // stay inside the loop
+    t.out_mode = TR_OUT_READ;
+    t.read_w = nw.mhc_read_w; t.read_b = nw.mhc_read_b;
+    HIP_TRY(launch_transition(t, s));
+  } else if (nd.fork) {       // enter the loop
+    t.out_mode = TR_OUT_READ;
+    t.read_w = nw.mhc_read_w; t.read_b = nw.mhc_read_b;
+    HIP_TRY(launch_transition(t, s));
+  } else if (d.loop) {        // leave the loop: merge + norm
+    t.out_mode = TR_OUT_NORM;
+    HIP_TRY(launch_transition(t, s));
+  } else {                    // plain -> plain
+    HIP_TRY(launch_rmsnorm(h, nullptr, nullptr, dm, nw.attn_norm, xn, M, dm, c.eps, s));
+  }
+  return 0;
+}
+
+// First transition: embedded (or given) h -> the first execution's input.
+int run_entry(loop_model* m, const Call& k, hipStream_t s) {
+  const loop_config& c = m->cfg;
+  const Layout& L = m->L;
+  const ExecDesc& d = m->sched[0];
+  const loop_layer_weights& w = m->lw[d.layer];
+  float* h = at<float>(m, L.h);
+  if (!d.loop) {
+    HIP_TRY(launch_rmsnorm(h, nullptr, nullptr, c.d_model, w.attn_norm, at<uint16_t>(m, L.xn), k.M, c.d_model, c.eps, s));
+    return 0;
+  }
+  TransitionArgs t{};
+  t.M = k.M; t.d = c.d_model; t.iters = c.sinkhorn_iters; t.eps = c.eps;
+  t.in_mode = TR_IN_H; t.out_mode = TR_OUT_READ;
+  t.h = h; t.s0_out = at<float>(m, L.s0); t.s1_out = at<float>(m, L.s1); t.x_out = at<float>(m, L.x);
+  t.read_w = w.mhc_read_w; t.read_b = w.mhc_read_b; t.norm_g = (const uint16_t*)w.attn_norm;
+  t.xn = at<uint16_t>(m, L.xn);
+  HIP_TRY(launch_transition(t, s));
+  return 0;
+}
+
+int run_forward(loop_model* m, const Call& k, const int32_t* taps, int n_taps, float* d_taps, hipStream_t s) {
+  const loop_config& c = m->cfg;
+  const Layout& L = m->L;
+  if (int r = run_entry(m, k, s)) return r;
+  for (int e = 0; e < (int)m->sched.size(); ++e) {
+    if (int r = run_exec(m, k, e, s)) return r;
+    for (int i = 0; i < n_taps; ++i) {
+      if (taps[i] != e) continue;
+      const ExecDesc& d = m->sched[e];
+      const bool streams = d.loop && !d.merge;
+      HIP_TRY(launch_tap(at<float>(m, L.h), streams ? at<float>(m, L.s0) : nullptr,
+                         streams ? at<float>(m, L.s1) : nullptr, d_taps + (int64_t)i * k.B * c.d_model,
+                         k.B, k.T, c.d_model, s));
+    }
+  }
+  return 0;
+}
+
+int upload_meta(loop_model* m, int B, int T, const int32_t* pos, const int32_t* slots, hipStream_t s) {
+  m->meta_host.assign(4 * m->cfg.max_batch, 0);
+  for (int b = 0; b < B; ++b) {
+    m->meta_host[b] = pos[b];
+    m->meta_host[m->cfg.max_batch + b] = slots[b];
+    m->meta_host[2 * m->cfg.max_batch + b] = b * T + T - 1;
+  }
+  HIP_TRY(hipMemcpyAsync(m->ws + m->L.meta, m->meta_host.data(), m->meta_host.size() * 4,
+                         hipMemcpyHostToDevice, s));
+  return 0;
+}
+
+int head_logits(loop_model* m, const Call& k, float* logits, hipStream_t s) {
+  const loop_config& c = m->cfg;
+  const Layout& L = m->L;
+  uint16_t* xf = at<uint16_t>(m, L.xf);
+  Prof p(m, LOOP_K_HEAD, s);
+  HIP_TRY(launch_rmsnorm(at<float>(m, L.h), nullptr, k.d_last, c.d_model, m->final_norm, xf, k.B, c.d_model, c.eps, s));
+  HIP_TRY(launch_gemm(xf, c.d_model, m->head, c.d_model, logits, c.vocab, nullptr, k.B, c.vocab, c.d_model,
+                      LOOP_EPI_F32, s));
+  return 0;
+}
+
+int check_slots(const loop_config& c, int B, const int32_t* slots) {
+  if (!slots) return loop_fail(LOOP_EINVAL, "slots is NULL");
+  std::set<int> seen;
+  for (int b = 0; b < B; ++b) {
+    if (slots[b] < 0 || slots[b] >= c.max_batch) return loop_fail(LOOP_ECAPACITY, "slot %d out of [0, %d)", slots[b], c.max_batch);
+    if (!seen.insert(slots[b]).second) return loop_fail(LOOP_EINVAL, "slot %d used twice", slots[b]);
+  }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" int loop_prefill(loop_model* m, const loop_prefill_args* a, void* stream) {
+  if (!m || !a) return loop_fail(LOOP_EINVAL, "model or args NULL");
+  const loop_config& c = m->cfg;
+  const int B = a->batch, T = a->seq_len;
+  if (B < 1 || B > c.max_batch) return loop_fail(LOOP_ECAPACITY, "batch %d out of [1, %d]", B, c.max_batch);
+  if (T < 1) return loop_fail(LOOP_EINVAL, "seq_len must be >= 1");
+  if ((int64_t)B * T > c.max_tokens) return loop_fail(LOOP_ECAPACITY, "batch*seq_len %lld > max_tokens %d", (long long)B * T, c.max_tokens);
+  if (int r = check_slots(c, B, a->slots)) return r;
+  if (!a->start_pos) return loop_fail(LOOP_EINVAL, "start_pos is NULL");
+  for (int b = 0; b < B; ++b)
+    if (a->start_pos[b] < 0 || (int64_t)a->start_pos[b] + T > c.max_seq)
+      return loop_fail(LOOP_ECAPACITY, "start_pos %d + seq_len %d exceeds max_seq %d", a->start_pos[b], T, c.max_seq);
+  if ((a->d_tokens != nullptr) == (a->d_hidden_in != nullptr))
+    return loop_fail(LOOP_EINVAL, "exactly one of d_tokens / d_hidden_in must be given");
+  if (a->d_tokens && c.vocab == 0) return loop_fail(LOOP_EINVAL, "token input needs vocab > 0");
+  if (a->d_logits && c.vocab == 0) return loop_fail(LOOP_EINVAL, "logits need vocab > 0");
+  if (a->n_taps < 0 || (a->n_taps > 0 && (!a->tap_exec || !a->d_taps))) return loop_fail(LOOP_EINVAL, "bad taps");
+  for (int i = 0; i < a->n_taps; ++i)
+    if (a->tap_exec[i] < 0 || a->tap_exec[i] >= (int)m->sched.size()) return loop_fail(LOOP_EINVAL, "tap %d out of range", a->tap_exec[i]);
+  hipStream_t s = (hipStream_t)stream;
+  Call k{B, T, B * T, false, nullptr, nullptr, nullptr};
+  const int32_t* meta = at<int32_t>(m, m->L.meta);
+  k.d_pos = meta;
+  k.d_slot = meta + c.max_batch;
+  k.d_last = meta + 2 * c.max_batch;
+  if (int r = upload_meta(m, B, T, a->start_pos, a->slots, s)) return r;
+  float* h = at<float>(m, m->L.h);
+  if (a->d_tokens) HIP_TRY(launch_embed(a->d_tokens, m->embed, h, k.M, c.d_model, c.vocab, s));
+  else HIP_TRY(hipMemcpyAsync(h, a->d_hidden_in, (size_t)k.M * c.d_model * 4, hipMemcpyDeviceToDevice, s));
+  if (int r = run_forward(m, k, a->tap_exec, a->n_taps, a->d_taps, s)) return r;
+  if (a->d_hidden_out)
+    HIP_TRY(hipMemcpyAsync(a->d_hidden_out, h, (size_t)k.M * c.d_model * 4, hipMemcpyDeviceToDevice, s));
+  if (a->d_logits)
+    if (int r = head_logits(m, k, a->d_logits, s)) return r;
+  return 0;
+}
+
+extern "C" int loop_decode_step(loop_model* m, const loop_decode_args* a, void* stream) {
+  if (!m || !a) return loop_fail(LOOP_EINVAL, "model or args NULL");
+  const loop_config& c = m->cfg;
+  const int B = a->batch;
+  if (B < 1 || B > c.max_batch || B > c.max_tokens) return loop_fail(LOOP_ECAPACITY, "batch %d out of range", B);
+  if (c.vocab == 0) return loop_fail(LOOP_EINVAL, "decode needs vocab > 0");
+  if (!a->d_tokens || !a->pos) return loop_fail(LOOP_EINVAL, "d_tokens and pos are required");
+  if (int r = check_slots(c, B, a->slots)) return r;
+  for (int b = 0; b < B; ++b)
+    if (a->pos[b] < 0 || a->pos[b] >= c.max_seq) return loop_fail(LOOP_ECAPACITY, "pos %d out of [0, %d)", a->pos[b], c.max_seq);
+  hipStream_t s = (hipStream_t)stream;
+  Call k{B, 1, B, true, nullptr, nullptr, nullptr};
+  const int32_t* meta = at<int32_t>(m, m->L.meta);
+  k.d_pos = meta;
+  k.d_slot = meta + c.max_batch;
+  k.d_last = meta + 2 * c.max_batch;
+  if (int r = upload_meta(m, B, 1, a->pos, a->slots, s)) return r;
+  float* h = at<float>(m, m->L.h);
+  HIP_TRY(launch_embed(a->d_tokens, m->embed, h, B, c.d_model, c.vocab, s));
+  if (int r = run_forward(m, k, nullptr, 0, nullptr, s)) return r;
+  if (a->d_hidden_out) HIP_TRY(hipMemcpyAsync(a->d_hidden_out, h, (size_t)B * c.d_model * 4, hipMemcpyDeviceToDevice, s));
+  if (a->d_logits || a->d_next) {
+    float* logits = a->d_logits ? a->d_logits : at<float>(m, m->L.logits);
+    if (int r = head_logits(m, k, logits, s)) return r;
+    if (a->d_next)
+      HIP_TRY(launch_argmax(logits, B, c.vocab, at<float>(m, m->L.am_v), at<int>(m, m->L.am_i), a->d_next, s));
+  }
+  return 0;
+}
+
+extern "C" int loop_debug_mhc(loop_model* m, float* d_out, void* stream) {
+  if (!m || !d_out) return loop_fail(LOOP_EINVAL, "model or output NULL");
+  const loop_config& c = m->cfg;
+  for (int l = c.loop_start; l < c.loop_end; ++l)
+    HIP_TRY(launch_sinkhorn(m->lw[l].mhc_mix, c.sinkhorn_iters, d_out + 4 * (l - c.loop_start), (hipStream_t)stream));
+  return 0;
+}

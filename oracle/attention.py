@@ -17,6 +17,7 @@ from __future__ import annotations
 import numpy as np
 
 from .ops import rmsnorm, apply_rope, softmax, sigmoid
+from .precision import maybe_bf16, round_bf16
 
 
 class KVCache:
@@ -36,9 +37,12 @@ class KVCache:
         self.v = np.concatenate([self.v, v.transpose(1, 0, 2)], axis=1)
 
 
-def attention_core(q: np.ndarray, K: np.ndarray, V: np.ndarray, q_pos: np.ndarray) -> np.ndarray:
+def attention_core(q: np.ndarray, K: np.ndarray, V: np.ndarray, q_pos: np.ndarray,
+                   bf16: bool = False) -> np.ndarray:
     """softmax(q K^T / sqrt(D), keys at positions <= q_pos) V per query head.
-    ``q``: [T, Hq, D]; ``K``, ``V``: [Hkv, L, D] for key positions 0..L-1."""
+    ``q``: [T, Hq, D]; ``K``, ``V``: [Hkv, L, D] for key positions 0..L-1.
+    ``bf16``: the (unnormalised) probabilities exp(s - max) that multiply V
+    are stored in bf16; the normaliser is summed in full precision."""
     T, Hq, D = q.shape
     Hkv, L, _ = K.shape
     group = Hq // Hkv
@@ -50,16 +54,22 @@ def attention_core(q: np.ndarray, K: np.ndarray, V: np.ndarray, q_pos: np.ndarra
         kv = j // group
         s = (q[:, j, :] @ K[kv].T) * scale                        # [T, L]
         s = np.where(mask, s, -np.inf)
-        out[:, j, :] = softmax(s, axis=-1) @ V[kv]
+        if not bf16:
+            out[:, j, :] = softmax(s, axis=-1) @ V[kv]
+        else:
+            e = np.exp(s - np.max(s, axis=-1, keepdims=True))
+            out[:, j, :] = (round_bf16(e) @ V[kv]) / np.sum(e, axis=-1, keepdims=True)
     return out
 
 
-def full_attention(xn: np.ndarray, w: dict, cache: KVCache, pos0: int, cfg) -> np.ndarray:
+def full_attention(xn: np.ndarray, w: dict, cache: KVCache, pos0: int, cfg,
+                   bf16: bool = False) -> np.ndarray:
     """Mixer output ``a`` [T, d] for one sequence whose new tokens sit at
-    positions pos0 .. pos0+T-1; appends their K, V to ``cache``."""
+    positions pos0 .. pos0+T-1; appends their K, V to ``cache``.  ``bf16``:
+    the backbone precision policy of ``oracle.precision``."""
     T = xn.shape[0]
     Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    proj = xn @ w["w_in"].T
+    proj = maybe_bf16(xn @ w["w_in"].T, bf16)
     q = proj[:, :Hq * D].reshape(T, Hq, D)
     g = proj[:, Hq * D:2 * Hq * D]
     k = proj[:, 2 * Hq * D:2 * Hq * D + Hkv * D].reshape(T, Hkv, D)
@@ -69,8 +79,9 @@ def full_attention(xn: np.ndarray, w: dict, cache: KVCache, pos0: int, cfg) -> n
     pos = np.arange(pos0, pos0 + T)
     q = apply_rope(q, pos, cfg.rotary_dim, cfg.rope_theta)
     k = apply_rope(k, pos, cfg.rotary_dim, cfg.rope_theta)
+    q, k = maybe_bf16(q, bf16), maybe_bf16(k, bf16)
     assert cache.length == pos0, "cache length must equal the first new position"
     cache.append(k, v)
-    o = attention_core(q, cache.k, cache.v, pos)
-    o = o.reshape(T, Hq * D) * sigmoid(g)
+    o = attention_core(q, cache.k, cache.v, pos, bf16=bf16)
+    o = maybe_bf16(o.reshape(T, Hq * D) * sigmoid(g), bf16)
     return o @ w["w_o"].T

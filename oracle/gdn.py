@@ -25,6 +25,7 @@ from __future__ import annotations
 import numpy as np
 
 from .ops import rmsnorm, silu, sigmoid, softplus
+from .precision import maybe_bf16
 
 
 def gdn_recurrent(q, k, v, alpha, beta, S0):
@@ -87,11 +88,13 @@ def gdn_chunked(q, k, v, log_alpha, beta, S0, chunk: int = 64):
 
 
 def gdn_layer(xn: np.ndarray, w: dict, S0: np.ndarray, cfg, chunked: bool = False,
-              chunk: int = 64):
-    """Mixer output ``a`` [T, d] and the new state for one sequence."""
+              chunk: int = 64, bf16: bool = False):
+    """Mixer output ``a`` [T, d] and the new state for one sequence.  ``bf16``:
+    the backbone precision policy of ``oracle.precision`` (projection outputs
+    and the gated output in bf16; the recurrence and its state in fp32)."""
     T = xn.shape[0]
     H, Dk, Dv = cfg.gdn_heads, cfg.gdn_dk, cfg.gdn_dv
-    proj = xn @ w["w_in"].T
+    proj = maybe_bf16(xn @ w["w_in"].T, bf16)
     o0 = 0
     q = proj[:, o0:o0 + H * Dk].reshape(T, H, Dk); o0 += H * Dk
     k = proj[:, o0:o0 + H * Dk].reshape(T, H, Dk); o0 += H * Dk
@@ -108,5 +111,5 @@ def gdn_layer(xn: np.ndarray, w: dict, S0: np.ndarray, cfg, chunked: bool = Fals
         o, S = gdn_chunked(qh, kh, v, log_alpha, beta, S0, chunk)
     else:
         o, S = gdn_recurrent(qh, kh, v, np.exp(log_alpha), beta, S0)
-    o = rmsnorm(o, w["o_norm"], cfg.eps) * silu(z)
+    o = maybe_bf16(rmsnorm(o, w["o_norm"], cfg.eps) * silu(z), bf16)
     return o.reshape(T, H * Dv) @ w["w_o"].T, S

@@ -25,6 +25,7 @@ from .attention import KVCache, full_attention
 from .gdn import gdn_layer
 from .ops import rmsnorm, swiglu_ffn
 from . import mhc
+from .precision import maybe_bf16
 
 
 class SeqState:
@@ -65,20 +66,23 @@ def layer_weights(W: dict, l: int) -> dict:
     return {k[len(p):]: v for k, v in W.items() if k.startswith(p)}
 
 
-def _layer_body(cfg, row, lw, x, st, pos0, chunked_gdn):
-    xn = rmsnorm(x, lw["attn_norm"], cfg.eps)
+def _layer_body(cfg, row, lw, x, st, pos0, chunked_gdn, bf16):
+    xn = maybe_bf16(rmsnorm(x, lw["attn_norm"], cfg.eps), bf16)
     if row.kind == "full":
-        a = full_attention(xn, lw, st.kv[row.slot], pos0, cfg)
+        a = full_attention(xn, lw, st.kv[row.slot], pos0, cfg, bf16=bf16)
     else:
-        a, st.S[row.slot] = gdn_layer(xn, lw, st.S[row.slot], cfg, chunked=chunked_gdn)
+        a, st.S[row.slot] = gdn_layer(xn, lw, st.S[row.slot], cfg, chunked=chunked_gdn, bf16=bf16)
     hmid = x + a
-    f = swiglu_ffn(rmsnorm(hmid, lw["ffn_norm"], cfg.eps), lw["w_gateup"], lw["w_down"])
+    hn = maybe_bf16(rmsnorm(hmid, lw["ffn_norm"], cfg.eps), bf16)
+    f = swiglu_ffn(hn, lw["w_gateup"], lw["w_down"], bf16=bf16)
     return a, hmid, f
 
 
 def forward_seq(cfg: Config, W: dict, st: SeqState, ids=None, hidden=None,
-                chunked_gdn: bool = False, write_full: bool = False, taps=()):
+                chunked_gdn: bool = False, write_full: bool = False, taps=(),
+                bf16: bool = False):
     """One sequence: T new tokens at positions st.length .. st.length+T-1.
+    ``bf16``: the backbone precision policy of ``oracle.precision``.
 
     Returns (h [T, d] after the last execution, logits [V] of the last position
     or None, {tap exec: hidden [d] at the last position}).  A tap at a loop
@@ -96,7 +100,7 @@ def forward_seq(cfg: Config, W: dict, st: SeqState, ids=None, hidden=None,
     for row in schedule(cfg):
         lw = layer_weights(W, row.layer)
         if not row.loop:
-            a, hmid, f = _layer_body(cfg, row, lw, h, st, pos0, chunked_gdn)
+            a, hmid, f = _layer_body(cfg, row, lw, h, st, pos0, chunked_gdn, bf16)
             h = hmid + f
             if row.e in taps:
                 tapped[row.e] = h[-1].copy()
@@ -104,7 +108,7 @@ def forward_seq(cfg: Config, W: dict, st: SeqState, ids=None, hidden=None,
         if row.fork:
             streams = mhc.fork(h, cfg.n_streams)
         x, _ = mhc.read(streams, lw["mhc.read_w"], lw["mhc.read_b"])
-        a, hmid, f = _layer_body(cfg, row, lw, x, st, pos0, chunked_gdn)
+        a, hmid, f = _layer_body(cfg, row, lw, x, st, pos0, chunked_gdn, bf16)
         out = (hmid + f) if write_full else (a + f)
         P = mhc.sinkhorn(lw["mhc.mix"], cfg.sinkhorn_iters)
         streams = mhc.write(streams, out, lw["mhc.write_w"], lw["mhc.write_b"], P)
@@ -115,7 +119,7 @@ def forward_seq(cfg: Config, W: dict, st: SeqState, ids=None, hidden=None,
     st.length += h.shape[0]
     logits = None
     if cfg.vocab:
-        logits = rmsnorm(h[-1:], W["final_norm"], cfg.eps)[0] @ W["head"].T
+        logits = maybe_bf16(rmsnorm(h[-1:], W["final_norm"], cfg.eps), bf16)[0] @ W["head"].T
     return h, logits, tapped
 
 

@@ -68,8 +68,11 @@ def apply_rope(x: np.ndarray, positions: np.ndarray, rotary_dim: int, theta: flo
     return out
 
 
-def swiglu_ffn(hn: np.ndarray, w_gateup: np.ndarray, w_down: np.ndarray) -> np.ndarray:
-    """``(silu(hn W_gate^T) * (hn W_up^T)) W_down^T``; ``w_gateup`` = [gate; up]."""
+def swiglu_ffn(hn: np.ndarray, w_gateup: np.ndarray, w_down: np.ndarray,
+               bf16: bool = False) -> np.ndarray:
+    """``(silu(hn W_gate^T) * (hn W_up^T)) W_down^T``; ``w_gateup`` = [gate; up].
+    ``bf16``: the activation entering W_down is stored in bf16."""
+    from .precision import maybe_bf16
     F = w_down.shape[1]
     gu = hn @ w_gateup.T
-    return (silu(gu[:, :F]) * gu[:, F:]) @ w_down.T
+    return maybe_bf16(silu(gu[:, :F]) * gu[:, F:], bf16) @ w_down.T

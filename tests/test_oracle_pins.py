@@ -568,3 +568,47 @@ def test_planted_mistake_gdn_missing_gate_caught():
     o1, _ = gdn.gdn_recurrent(q, k, v, np.exp(la), beta, S0)
     o2, _ = gdn.gdn_chunked(q, k, v, 0 * la, beta, S0, 16)   # gate dropped in one form
     assert np.abs(o1 - o2).max() > 1e-3
+
+
+# ------------------------------------------------------ precision policy
+
+def test_round_bf16_matches_library_cast():
+    """round_bf16 against torch's float32 -> bfloat16 conversion (round to
+    nearest even), including exact ties."""
+    import torch
+    from oracle.precision import round_bf16
+    rng = np.random.default_rng(13)
+    x = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 10.0 ** rng.integers(-8, 8, 10000),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0, -0.0], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(round_bf16(x), ref)
+    assert round_bf16(np.float32(1.0 + 2 ** -8)) == 1.0            # tie -> even
+    assert round_bf16(np.float32(1.0 + 3 * 2 ** -8)) == 1.0 + 2 ** -6  # tie -> even (up)
+
+
+def test_bf16_policy_is_a_perturbation_of_the_definition():
+    """The bf16 policy rounds stored tensors only: at one token through the
+    first execution it moves the result by about the bf16 unit roundoff
+    (2^-9 relative), and with rounding disabled it is the fp32 definition."""
+    cfg = cfg_of("tiny")
+    W = weights(cfg, np.float32)
+    ids = _ids(1, cfg.vocab).reshape(1, -1)
+    _, _, t32 = model.prefill(cfg, W, [model.SeqState(cfg)], ids=ids, taps=(0,))
+    _, _, t16 = model.prefill(cfg, W, [model.SeqState(cfg)], ids=ids, taps=(0,), bf16=True)
+    r = np.abs(t16[0] - t32[0]).max() / np.abs(t32[0]).max()
+    assert 2 ** -12 < r < 2 ** -6
+    h1, l1, _ = model.prefill(cfg, W, [model.SeqState(cfg)], ids=ids)
+    h2, l2, _ = model.prefill(cfg, W, [model.SeqState(cfg)], ids=ids, bf16=False)
+    assert np.array_equal(h1, h2) and np.array_equal(l1, l2)
+
+
+def test_bf16_policy_keeps_structural_invariants():
+    """Looped = unrolled bit for bit, and chunked prefill = whole prefill,
+    hold in the bf16 policy too (rounding acts on the same tensors)."""
+    cfg = cfg_of("tiny")
+    W = weights(cfg, np.float32)
+    ids = _ids(24, cfg.vocab).reshape(1, -1)
+    h1, l1, _ = model.prefill(cfg, W, [model.SeqState(cfg)], ids=ids, bf16=True)
+    ucfg, UW = model.unrolled(cfg, W)
+    h2, l2, _ = model.prefill(ucfg, UW, [model.SeqState(ucfg)], ids=ids, bf16=True)
+    assert np.array_equal(h1, h2) and np.array_equal(l1, l2)
