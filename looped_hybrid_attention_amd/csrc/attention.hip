@@ -256,165 +256,140 @@ __global__ __launch_bounds__(64 * G, 1) void flash_prefill_kernel(FlashArgs a) {
 }
 
 // --------------------------------------------------------------- decode
-// Workgroup = (split of keys, KV head, sequence): G query heads against the
-// keys [split*SL, min(pos+1, (split+1)*SL)).  Writes per (head, split) the
-// partial max m, sum l and unnormalised o[D]; the combine kernel merges the
-// splits in a fixed order.
+// Workgroup = (split of DEC_SPLIT keys, KV head, sequence): the G query heads
+// of the KV head against keys [split*DEC_SPLIT, min(pos+1, ...)).  HBM-bound:
+// every K and V^T byte of the split is read once, straight into MFMA
+// operands.  Scores S^T[key][g] = K . q^T with v_mfma_f32_16x16x32_bf16 (16
+// keys x 16 head columns, G of them used); probabilities go through LDS as
+// bf16 [g][key]; O^T[d][g] += V^T[d][key] . P[key][g] with the same MFMA.
+// Writes per (head, split) the unnormalised o[D], the split max m and sum l;
+// the combine kernel merges the splits in split order.
 constexpr int DEC_NT = 256;
-constexpr int DEC_KB = 64;  // keys per LDS block
+constexpr int DEC_SPLIT = 512;
+constexpr int DEC_PS = DEC_SPLIT + 8;  // bf16 row of P in LDS
+
+DEV f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 template <int D, int G>
-__global__ __launch_bounds__(DEC_NT) void decode_attn_kernel(DecodeAttnArgs a) {
-  constexpr int QPL = D / 32;  // dims per lane in the score pass (32 lanes per key)
-  __shared__ float sq[G][D];
-  __shared__ float sp[G][DEC_KB];
-  __shared__ __align__(16) uint16_t sKV[DEC_KB * (D + 8) > D * (DEC_KB + 8) ? DEC_KB * (D + 8) : D * (DEC_KB + 8)];
-  __shared__ float red[G][DEC_NT / 64];
+__global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a) {
+  static_assert(G <= 16, "query heads per KV head");
+  constexpr int NKS = D / 32;   // 32-dim steps of the score MFMA
+  constexpr int NDT = D / 16;   // 16-dim output tiles
+  __shared__ float sc[G][DEC_SPLIT];
+  __shared__ __align__(16) uint16_t sp[16 * DEC_PS];
+  __shared__ float sm[G], sl[G];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int pos = a.pos[b];
-  const int k_begin = split * a.split_len;
-  const int k_end = min(pos + 1, k_begin + a.split_len);
+  const int k_begin = split * DEC_SPLIT;
+  const int k_end = min(pos + 1, k_begin + DEC_SPLIT);
   float* part = a.partial + (((int64_t)b * a.Hq + kvh * G) * a.n_split + split) * (D + 2);
   const int64_t part_head_stride = (int64_t)a.n_split * (D + 2);
-  if (k_begin >= k_end) {
-    // empty split: neutral element
+  if (k_begin >= k_end) {  // empty split: neutral element
     for (int i = threadIdx.x; i < G * (D + 2); i += DEC_NT) {
       const int g = i / (D + 2), c = i % (D + 2);
       part[g * part_head_stride + c] = c == D ? -1e30f : 0.f;
     }
     return;
   }
+  const int nk = k_end - k_begin;
   const int64_t slot_b = a.seq_slot[b];
-  const uint16_t* Kc = a.k_cache + (slot_b * a.Hkv + kvh) * (int64_t)a.max_seq * D;
-  const uint16_t* Vc = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq;
-  for (int i = threadIdx.x; i < G * D; i += DEC_NT) {
-    const int g = i / D, d = i % D;
-    sq[g][d] = bf2f(a.q[((int64_t)b * a.Hq + kvh * G + g) * D + d]) * a.scale_log2;
+  const uint16_t* Kc = a.k_cache + ((slot_b * a.Hkv + kvh) * (int64_t)a.max_seq + k_begin) * D;
+  const uint16_t* Vc = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq + k_begin;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+
+  // q^T operand: lane supplies q[g = l16][32 ks + 8 lg .. +8] (zero for g >= G)
+  bf16x8 qf[NKS];
+  {
+    const uint16_t* qs = a.q + ((int64_t)b * a.Hq + kvh * G + min(l16, G - 1)) * D;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      uint4 v = l16 < G ? *reinterpret_cast<const uint4*>(qs + ks * 32 + lg * 8) : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // scores, 16 keys per group, groups round-robin over the waves
+  for (int g0 = wave * 16; g0 < nk; g0 += 4 * 16) {
+    const int key = g0 + l16;
+    uint4 kv[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      kv[ks] = key < nk ? *reinterpret_cast<const uint4*>(Kc + (int64_t)key * D + ks * 32 + lg * 8)
+                        : make_uint4(0, 0, 0, 0);
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kv[ks]), qf[ks], acc);
+    // lane holds keys g0 + 4 lg + r of head l16
+    if (l16 < G) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kk = g0 + 4 * lg + r;
+        if (kk < DEC_SPLIT) sc[l16][kk] = kk < nk ? acc[r] * a.scale_log2 : -1e30f;
+      }
+    }
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // per-thread running state for the score pass: thread handles d-chunk
-  // (lane % 32) of key (2*wave + lane/32) within each 8-key group.
-  float m_run[G], l_run[G];
-  float acc[G];  // o for d = threadIdx.x (D == 256) or partial
+  // per-head max and sum over the split (wave w: heads w, w+4, ...)
+  for (int g = wave; g < G; g += 4) {
+    float mx = -1e30f;
+    for (int k = lane; k < nk; k += 64) mx = fmaxf(mx, sc[g][k]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int k = lane; k < DEC_SPLIT; k += 64) {
+      const float p = k < nk ? exp2f(sc[g][k] - mx) : 0.f;
+      sum += p;
+      sp[g * DEC_PS + k] = f2bf_bits(p);
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) { sm[g] = mx; sl[g] = sum; }
+  }
+  for (int i = threadIdx.x; i < (16 - G) * DEC_SPLIT; i += DEC_NT)
+    sp[(G + i / DEC_SPLIT) * DEC_PS + i % DEC_SPLIT] = 0;
+  __syncthreads();
+  // O^T[d][g] += V^T[d][key] P[key][g]; wave w: d-tiles w, w+4, ...
+  constexpr int TPW = (NDT + 3) / 4;
+  f32x4 o[TPW];
 #pragma unroll
-  for (int g = 0; g < G; ++g) { m_run[g] = -1e30f; l_run[g] = 0.f; acc[g] = 0.f; }
-  float accx[G][D / DEC_NT > 0 ? D / DEC_NT : 1];
+  for (int i = 0; i < TPW; ++i) o[i] = (f32x4){0, 0, 0, 0};
+  const int nsteps = (nk + 31) / 32;
+  for (int st = 0; st < nsteps; ++st) {
+    const int kk = st * 32 + lg * 8;  // first of this lane's 8 keys
+    bf16x8 pf = *reinterpret_cast<const bf16x8*>(sp + l16 * DEC_PS + kk);
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int j = 0; j < (D / DEC_NT > 0 ? D / DEC_NT : 1); ++j) accx[g][j] = 0.f;
-
-  for (int kb = k_begin; kb < k_end; kb += DEC_KB) {
-    const int nk = min(DEC_KB, k_end - kb);
-    // K block -> LDS (coalesced 16-byte loads)
-    __syncthreads();
-    for (int c = threadIdx.x; c < DEC_KB * D / 8; c += DEC_NT) {
-      const int key = c / (D / 8), dc = c % (D / 8);
+    for (int i = 0; i < TPW; ++i) {
+      const int dt = wave + 4 * i;
+      if (dt >= NDT) break;
+      const int d = dt * 16 + l16;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < nk) v = *reinterpret_cast<const uint4*>(Kc + (int64_t)(kb + key) * D + dc * 8);
-      *reinterpret_cast<uint4*>(sKV + key * (D + 8) + dc * 8) = v;
-    }
-    __syncthreads();
-    // scores: 32 lanes per key, QPL dims each; 8 keys per pass over the block
-    for (int kk = wave * 2 + (lane >> 5); kk < DEC_KB; kk += DEC_NT / 32) {
-      const int dl = (lane & 31) * QPL;
-      float part_s[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) part_s[g] = 0.f;
-      const uint16_t* kr = sKV + kk * (D + 8) + dl;
-#pragma unroll
-      for (int e = 0; e < QPL; ++e) {
-        const float kv = bf2f(kr[e]);
-#pragma unroll
-        for (int g = 0; g < G; ++g) part_s[g] += kv * sq[g][dl + e];
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float v = part_s[g];
-#pragma unroll
-        for (int off = 16; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-        if ((lane & 31) == 0) sp[g][kk] = kk < nk ? v : -1e30f;
-      }
-    }
-    __syncthreads();
-    // block max / probabilities / running rescale (every thread keeps the
-    // same per-head running max: the block max is read from LDS)
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float bm = -1e30f;
-      for (int k = 0; k < DEC_KB; ++k) bm = fmaxf(bm, sp[g][k]);
-      const float m_new = fmaxf(m_run[g], bm);
-      const float alpha = exp2f(m_run[g] - m_new);
-      m_run[g] = m_new;
-      l_run[g] *= alpha;
-#pragma unroll
-      for (int j = 0; j < (D / DEC_NT > 0 ? D / DEC_NT : 1); ++j) accx[g][j] *= alpha;
-    }
-    __syncthreads();
-    // probabilities in place
-    for (int i = threadIdx.x; i < G * DEC_KB; i += DEC_NT) {
-      const int g = i / DEC_KB, k = i % DEC_KB;
-      const float v = sp[g][k];
-      sp[g][k] = v > -1e29f ? exp2f(v - m_run[g]) : 0.f;
-    }
-    // V^T block -> LDS
-    for (int c = threadIdx.x; c < D * DEC_KB / 8; c += DEC_NT) {
-      const int d = c / (DEC_KB / 8), kc = c % (DEC_KB / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      const int kk = kb + kc * 8;
-      if (kc * 8 < nk) {
-        if (kc * 8 + 8 <= nk && ((a.max_seq & 7) == 0)) {
-          v = *reinterpret_cast<const uint4*>(Vc + (int64_t)d * a.max_seq + kk);
-        } else {
+      if (kk < nk) {
+        v = *reinterpret_cast<const uint4*>(Vc + (int64_t)d * a.max_seq + kk);
+        if (kk + 8 > nk) {
           uint16_t* e = reinterpret_cast<uint16_t*>(&v);
-          for (int j = 0; j < 8; ++j) e[j] = (kc * 8 + j < nk) ? Vc[(int64_t)d * a.max_seq + kk + j] : 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (kk + j >= nk) e[j] = 0;
         }
       }
-      *reinterpret_cast<uint4*>(sKV + d * (DEC_KB + 8) + kc * 8) = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float ls = 0.f;
-      for (int k = 0; k < DEC_KB; ++k) ls += sp[g][k];
-      l_run[g] += ls;
-    }
-    // o[d] += sum_k p[k] V^T[d][k], thread = d (D / DEC_NT dims each)
-#pragma unroll
-    for (int j = 0; j < (D / DEC_NT > 0 ? D / DEC_NT : 1); ++j) {
-      const int d = threadIdx.x + j * DEC_NT;
-      if (d < D) {
-        const uint16_t* vr = sKV + d * (DEC_KB + 8);
-        for (int k = 0; k < DEC_KB; k += 8) {
-          uint4 v = *reinterpret_cast<const uint4*>(vr + k);
-          const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float vv = bf2f(e[u]);
-#pragma unroll
-            for (int g = 0; g < G; ++g) accx[g][j] += sp[g][k + u] * vv;
-          }
-        }
-      }
+      o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, v), pf, o[i]);
     }
   }
-  // partial results
+  // lane holds O^T[d = 16 dt + 4 lg + r][g = l16]
+  if (l16 < G) {
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+    for (int i = 0; i < TPW; ++i) {
+      const int dt = wave + 4 * i;
+      if (dt >= NDT) break;
 #pragma unroll
-    for (int j = 0; j < (D / DEC_NT > 0 ? D / DEC_NT : 1); ++j) {
-      const int d = threadIdx.x + j * DEC_NT;
-      if (d < D) part[g * part_head_stride + d] = accx[g][j];
-    }
-    if (threadIdx.x == 0) {
-      part[g * part_head_stride + D] = m_run[g];
-      part[g * part_head_stride + D + 1] = l_run[g];
+      for (int r = 0; r < 4; ++r) part[l16 * part_head_stride + dt * 16 + 4 * lg + r] = o[i][r];
     }
   }
-  (void)acc;
-  (void)red;
+  if (threadIdx.x < G) {
+    part[threadIdx.x * part_head_stride + D] = sm[threadIdx.x];
+    part[threadIdx.x * part_head_stride + D + 1] = sl[threadIdx.x];
+  }
 }
 
 // Merge the splits of one (sequence, query head) in split order; apply the

@@ -9,6 +9,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 raw bytes as a native vector (HIP's uint4 is a struct of unions that
+// the compiler does not keep in registers when indexed from arrays).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define DEV __device__ __forceinline__
 

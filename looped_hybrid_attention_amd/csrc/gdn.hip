@@ -28,24 +28,82 @@ constexpr int NT = 256;
 
 DEV float softplusf_(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 
+// fp32 MFMA 16x16x4 tile products from LDS (row-major operands).  Lane l
+// supplies A[m = l%16][k = l/16] and B[k = l/16][n = l%16]; the result D
+// holds rows 4*(l/16) + r (r = 0..3) of column l%16.
+DEV f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// acc += A[0:16, 0:K] . B[0:16, 0:K]^T
+DEV void mm_nt(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a = A + i * lda + kk;
+  const float* b = B + i * ldb + kk;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k], b[k], acc);
+}
+// acc += A[0:16, 0:K] . B[0:K, 0:16]
+DEV void mm_nn(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a = A + i * lda + kk;
+  const float* b = B + kk * ldb + i;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k], b[k * ldb], acc);
+}
+// acc += A[0:K, 0:16]^T . B[0:K, 0:16]
+DEV void mm_tn(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a = A + kk * lda + i;
+  const float* b = B + kk * ldb + i;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k * lda], b[k * ldb], acc);
+}
+
+// Chunk workspace layout, per (seq b, head h, chunk c), fp32:
+//   W, Ut, Kd, Qp, Up: [CH][DK] each, then gC; S_c (entry state) [DV][DK].
+struct ChunkPtr {
+  float *W, *Ut, *Kd, *Qp, *Up, *S;
+  float* gC;
+};
+DEV ChunkPtr chunk_ptr(const GdnArgs& a, int b, int h, int c, int DK) {
+  const int64_t cb = ((int64_t)b * a.H + h) * a.n_chunks + c;
+  const int64_t mat = (int64_t)CH * DK;
+  ChunkPtr p;
+  p.W = a.W + cb * mat;
+  p.Ut = a.Ut + cb * mat;
+  p.Kd = a.Kd + cb * mat;
+  p.Qp = a.Qg + cb * mat;
+  p.Up = a.Mqk + cb * mat;
+  p.S = a.Sc + cb * (int64_t)DK * DK;
+  p.gC = a.gC + cb;
+  return p;
+}
+
 // ------------------------------------------------------- chunk prep
-// grid (chunk, head, seq).  Per chunk writes (fp32):
-//   W [CH][Dk], Ut [CH][Dv], Qg = gamma*q^ [CH][Dk], Kd = exp(G_C - G)*k^ [CH][Dk],
-//   Mqk [CH][CH] (lower incl. diagonal), gC.
+// grid (chunk, head, seq).  Writes W = T diag(beta gamma) K, Ut = T diag(beta) V,
+// Kd = exp(G_C - G) K, Qp = gamma Q - Mqk W and Up = Mqk Ut, and gC, where
+// Mqk = tril(exp(G_r - G_i)) * Q K^T and T = (I + A)^-1.
 template <int DK>
 __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   constexpr int DV = DK;
-  constexpr int PK = DK + 1;  // padded LDS rows
-  __shared__ float sQ[CH][PK], sK[CH][PK], sV[CH][PK];
-  __shared__ float sA[CH][CH + 1], sT[CH][CH + 1];
-  __shared__ float sG[CH], sB[CH];
+  constexpr int LD = DK + 4;   // [CH][DK] rows
+  constexpr int LC = CH + 4;   // [CH][CH] rows
+  extern __shared__ __align__(16) float gsm[];
+  float* sQ = gsm;                 // q^ ; later unchanged
+  float* sK = sQ + CH * LD;        // k^ ; later W
+  float* sV = sK + CH * LD;        // v  ; later Ut
+  float* sA = sV + CH * LD;        // A ; later T diag(beta gamma)
+  float* sT2 = sA + CH * LC;       // T diag(beta)
+  float* sM = sT2 + CH * LC;       // Mqk
+  float* sG = sM + CH * LC;        // cumulative log alpha
+  float* sB = sG + CH;             // beta
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = c * CH;
   const int C = min(CH, a.T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t row0 = (int64_t)b * a.T + t0;
+  const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
 
-  // load + L2-normalise q, k; load v.  Wave w handles rows w, w+4, ...
   for (int r = wave; r < CH; r += NT / 64) {
     float qv[DK / 64], kv[DK / 64];
     float sq = 0.f, sk = 0.f;
@@ -58,144 +116,277 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
       kv[e] = ok ? bf2f(pr[a.off_k + h * DK + d]) : 0.f;
       sq += qv[e] * qv[e];
       sk += kv[e] * kv[e];
-      sV[r][d] = ok ? bf2f(pr[a.off_v + h * DV + d]) : 0.f;
+      sV[r * LD + d] = ok ? bf2f(pr[a.off_v + h * DV + d]) : 0.f;
     }
     sq = wave_sum(sq);
     sk = wave_sum(sk);
     const float iq = rsqrtf(sq + a.eps) * a.q_scale, ik = rsqrtf(sk + a.eps);
 #pragma unroll
     for (int e = 0; e < DK / 64; ++e) {
-      sQ[r][lane + 64 * e] = qv[e] * iq;
-      sK[r][lane + 64 * e] = kv[e] * ik;
+      sQ[r * LD + lane + 64 * e] = qv[e] * iq;
+      sK[r * LD + lane + 64 * e] = kv[e] * ik;
     }
     if (lane == 0) {
       const float av = ok ? bf2f(pr[a.off_a + h]) : 0.f;
       const float bv = ok ? bf2f(pr[a.off_b + h]) : 0.f;
-      sG[r] = ok ? -softplusf_(av) : 0.f;  // log alpha, cumulated below
+      sG[r] = ok ? -softplusf_(av) : 0.f;
       sB[r] = ok ? sigmoidf_(bv) : 0.f;
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    float g = 0.f;
-    for (int r = 0; r < CH; ++r) {
-      g += sG[r];
-      sG[r] = g;
+  if (wave == 0) {  // inclusive prefix sum of log alpha over the 64 rows
+    float g = sG[lane];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float u = __shfl_up(g, o, 64);
+      if (lane >= o) g += u;
     }
+    sG[lane] = g;
   }
   __syncthreads();
-  // A (strictly lower) and Mqk (lower incl. diagonal); 16 entries per thread
-  for (int idx = tid; idx < CH * CH; idx += NT) {
-    const int r = idx / CH, i = idx % CH;
-    float kk = 0.f, qk = 0.f;
-    if (i <= r) {
-#pragma unroll 8
-      for (int d = 0; d < DK; ++d) {
-        kk += sK[r][d] * sK[i][d];
-        qk += sQ[r][d] * sK[i][d];
-      }
-    }
-    const float dec = i <= r ? expf(sG[r] - sG[i]) : 0.f;
-    sA[r][i] = i < r ? sB[r] * dec * kk : 0.f;
-    a.Mqk[(((int64_t)b * a.H + h) * a.n_chunks + c) * CH * CH + idx] = i <= r ? dec * qk : 0.f;
-  }
-  __syncthreads();
-  // T = (I + A)^-1 by forward substitution, one row at a time
-  for (int idx = tid; idx < CH * CH; idx += NT) sT[idx / CH][idx % CH] = (idx / CH == idx % CH) ? 1.f : 0.f;
-  __syncthreads();
-  for (int r = 1; r < CH; ++r) {
-    if (tid < r) {
-      const int j = tid;
-      float s = 0.f;
-      for (int i = j; i < r; ++i) s += sA[r][i] * sT[i][j];
-      sT[r][j] = -s;
-    }
-    __syncthreads();
-  }
-  // W = T diag(beta gamma) K, Ut = T diag(beta) V; Qg, Kd
   const float GC = sG[C - 1];
-  const int64_t base = (((int64_t)b * a.H + h) * a.n_chunks + c) * CH * DK;
+  // Kd = exp(G_C - G) k^ (rows >= C are zero because k^ is)
   for (int idx = tid; idx < CH * DK; idx += NT) {
     const int r = idx / DK, d = idx % DK;
-    float w = 0.f, u = 0.f;
-    for (int i = 0; i <= r; ++i) {
-      const float t = sT[r][i] * sB[i];
-      w += t * expf(sG[i]) * sK[i][d];
-      u += t * sV[i][d];
-    }
-    const bool ok = r < C;
-    a.W[base + idx] = ok ? w : 0.f;
-    a.Ut[base + idx] = ok ? u : 0.f;
-    a.Qg[base + idx] = ok ? expf(sG[r]) * sQ[r][d] : 0.f;
-    a.Kd[base + idx] = ok ? expf(GC - sG[r]) * sK[r][d] : 0.f;
+    P.Kd[idx] = expf(GC - sG[r]) * sK[r * LD + d];
   }
-  if (tid == 0) a.gC[((int64_t)b * a.H + h) * a.n_chunks + c] = expf(GC);
+  if (tid == 0) *P.gC = expf(GC);
+  // A = beta_r exp(G_r - G_i) k_r.k_i (i < r), Mqk = exp(G_r - G_i) q_r.k_i (i <= r)
+  {
+    const int i16 = lane & 15, kk = lane >> 4;
+    for (int nt = 0; nt < CH / 16; ++nt) {
+      f32x4 kk_acc = {0, 0, 0, 0}, qk_acc = {0, 0, 0, 0};
+      mm_nt(kk_acc, sK + wave * 16 * LD, LD, sK + nt * 16 * LD, LD, DK);
+      mm_nt(qk_acc, sQ + wave * 16 * LD, LD, sK + nt * 16 * LD, LD, DK);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
+        const float dec = col <= row ? expf(sG[row] - sG[col]) : 0.f;
+        sA[row * LC + col] = col < row ? sB[row] * dec * kk_acc[r] : 0.f;
+        sM[row * LC + col] = col <= row ? dec * qk_acc[r] : 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  // T = (I + A)^-1: lane j of wave 0 owns column j, rows in order.
+  if (wave == 0) {
+    float t[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) t[i] = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 1; r < CH; ++r) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < r; ++i) s += sA[r * LC + i] * t[i];
+      t[r] = (r > lane) ? -s : t[r];
+    }
+    // T diag(beta gamma) -> sA, T diag(beta) -> sT2 (column j scaled)
+    const float bj = sB[lane], bgj = bj * expf(sG[lane]);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      sA[i * LC + lane] = t[i] * bgj;
+      sT2[i * LC + lane] = t[i] * bj;
+    }
+  }
+  __syncthreads();
+  // W = (T diag(beta gamma)) K^, Ut = (T diag(beta)) V; wave w: rows 16w..16w+15
+  constexpr int NTILE = DK / 16;
+  f32x4 wacc[NTILE], uacc[NTILE];
+#pragma unroll
+  for (int nt = 0; nt < NTILE; ++nt) {
+    wacc[nt] = (f32x4){0, 0, 0, 0};
+    uacc[nt] = (f32x4){0, 0, 0, 0};
+    mm_nn(wacc[nt], sA + wave * 16 * LC, LC, sK + nt * 16, LD, CH);
+    mm_nn(uacc[nt], sT2 + wave * 16 * LC, LC, sV + nt * 16, LD, CH);
+  }
+  __syncthreads();  // sK, sV fully read: reuse them for W and Ut
+  {
+    const int i16 = lane & 15, kk = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
+        const bool ok = row < C;
+        const float w = ok ? wacc[nt][r] : 0.f, u = ok ? uacc[nt][r] : 0.f;
+        sK[row * LD + col] = w;
+        sV[row * LD + col] = u;
+        P.W[row * DK + col] = w;
+        P.Ut[row * DK + col] = u;
+      }
+  }
+  __syncthreads();
+  // Qp = gamma Q - Mqk W, Up = Mqk Ut
+  {
+    const int i16 = lane & 15, kk = lane >> 4;
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt) {
+      f32x4 mw = {0, 0, 0, 0}, mu = {0, 0, 0, 0};
+      mm_nn(mw, sM + wave * 16 * LC, LC, sK + nt * 16, LD, CH);
+      mm_nn(mu, sM + wave * 16 * LC, LC, sV + nt * 16, LD, CH);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
+        const bool ok = row < C;
+        P.Qp[row * DK + col] = ok ? expf(sG[row]) * sQ[row * LD + col] - mw[r] : 0.f;
+        P.Up[row * DK + col] = ok ? mu[r] : 0.f;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------- chunk scan
-// grid (Dv / DS, head, seq).  S rows [j0, j0 + DS) of one head, carried over
-// the chunks in order.  O (fp32, before the output norm) -> a.o.
-template <int DK, int DS>
+// grid (Dv / 16, head, seq).  Rows j0 .. j0+15 of S, carried over the chunks
+// in order: U = Ut - W S^T, S <- gC S + U^T Kd.  The entry state of every
+// chunk is written for the output kernel; the final state to the slot.
+template <int DK>
 __global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a) {
-  constexpr int PK = DK + 1;
-  __shared__ float sS[DS][PK];
-  __shared__ float sW[CH][PK], sQ[CH][PK], sK[CH][PK];
-  __shared__ float sM[CH][CH + 1];
-  __shared__ float sU[CH][DS + 1];
-  const int j0 = blockIdx.x * DS, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
+  constexpr int LW = DK + 4;    // W rows (nt operand)
+  constexpr int LK = DK + 16;   // Kd rows (tn operand)
+  constexpr int LS = DK + 4;    // S rows (nt operand)
+  constexpr int LU = 16;        // U rows (tn operand)
+  constexpr int PF = (2 * CH * DK + CH * 16) / 4 / NT;  // uint4 per thread per chunk
+  static_assert(PF * NT * 4 == 2 * CH * DK + CH * 16, "prefetch split");
+  __shared__ __align__(16) float sW[CH * LW];
+  __shared__ __align__(16) float sKd[CH * LK];
+  __shared__ __align__(16) float sUt[CH * 16];
+  __shared__ __align__(16) float sU[CH * LU];
+  __shared__ __align__(16) float sS[16 * LS];
+  const int j0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, kk = lane >> 4;
   float* Sg = a.state + ((int64_t)a.seq_slot[b] * a.H + h) * (int64_t)DK * DK;  // [Dv][Dk]
   const bool fresh = a.pos[b] == 0;
-  for (int idx = tid; idx < DS * DK; idx += NT) {
+  for (int idx = tid; idx < 16 * DK; idx += NT) {
     const int j = idx / DK, k = idx % DK;
-    sS[j][k] = fresh ? 0.f : Sg[(int64_t)(j0 + j) * DK + k];
+    sS[j * LS + k] = fresh ? 0.f : Sg[(int64_t)(j0 + j) * DK + k];
   }
+  // prefetch: element e of this thread's share -> (array, offset)
+  uint4 pf[PF];
+  auto load = [&](int c) {
+    const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int e = (tid + i * NT) * 4;  // float index in [W | Kd | Ut-slice]
+      const float* src;
+      if (e < CH * DK) src = P.W + e;
+      else if (e < 2 * CH * DK) src = P.Kd + (e - CH * DK);
+      else { const int u = e - 2 * CH * DK; src = P.Ut + (u / 16) * DK + j0 + (u % 16); }
+      pf[i] = *reinterpret_cast<const uint4*>(src);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int e = (tid + i * NT) * 4;
+      float* dst;
+      if (e < CH * DK) dst = sW + (e / DK) * LW + e % DK;
+      else if (e < 2 * CH * DK) { const int u = e - CH * DK; dst = sKd + (u / DK) * LK + u % DK; }
+      else { const int u = e - 2 * CH * DK; dst = sUt + u; }
+      *reinterpret_cast<uint4*>(dst) = pf[i];
+    }
+  };
+  load(0);
   for (int c = 0; c < a.n_chunks; ++c) {
-    const int64_t cb = ((int64_t)b * a.H + h) * a.n_chunks + c;
-    const int C = min(CH, a.T - c * CH);
+    __syncthreads();  // previous chunk's LDS reads are done
+    stash();
+    const float gC = a.gC[((int64_t)b * a.H + h) * a.n_chunks + c];
     __syncthreads();
-    for (int idx = tid; idx < CH * DK; idx += NT) {
-      const int r = idx / DK, k = idx % DK;
-      sW[r][k] = a.W[cb * CH * DK + idx];
-      sQ[r][k] = a.Qg[cb * CH * DK + idx];
-      sK[r][k] = a.Kd[cb * CH * DK + idx];
+    if (c + 1 < a.n_chunks) load(c + 1);
+    // entry state of chunk c
+    {
+      const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
+      for (int idx = tid; idx < 16 * DK; idx += NT) {
+        const int j = idx / DK, k = idx % DK;
+        P.S[(int64_t)(j0 + j) * DK + k] = sS[j * LS + k];
+      }
     }
-    for (int idx = tid; idx < CH * CH; idx += NT) sM[idx / CH][idx % CH] = a.Mqk[cb * CH * CH + idx];
-    __syncthreads();
-    // U = Ut - W S^T  (rows r, columns j of the slice)
-    for (int idx = tid; idx < CH * DS; idx += NT) {
-      const int r = idx / DS, j = idx % DS;
-      float s = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < DK; ++k) s += sW[r][k] * sS[j][k];
-      sU[r][j] = a.Ut[cb * CH * DK + r * DK + j0 + j] - s;
-    }
-    __syncthreads();
-    // O = Qg S^T + Mqk U
-    for (int idx = tid; idx < CH * DS; idx += NT) {
-      const int r = idx / DS, j = idx % DS;
-      if (r >= C) continue;
-      float s = 0.f;
-#pragma unroll 8
-      for (int k = 0; k < DK; ++k) s += sQ[r][k] * sS[j][k];
-      for (int i = 0; i <= r; ++i) s += sM[r][i] * sU[i][j];
-      const int64_t m = (int64_t)b * a.T + c * CH + r;
-      a.o[(m * a.H + h) * DK + j0 + j] = s;
+    // U = Ut - W S^T ; wave w: rows 16w..16w+15, the 16 columns j
+    {
+      f32x4 acc = {0, 0, 0, 0};
+      mm_nt(acc, sW + wave * 16 * LW, LW, sS, LS, DK);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wave * 16 + 4 * kk + r;
+        sU[row * LU + i16] = sUt[row * 16 + i16] - acc[r];
+      }
     }
     __syncthreads();
-    // S = gC S + U^T Kd
-    const float gC = a.gC[cb];
-    for (int idx = tid; idx < DS * DK; idx += NT) {
-      const int j = idx / DK, k = idx % DK;
-      float s = gC * sS[j][k];
-      for (int r = 0; r < CH; ++r) s += sU[r][j] * sK[r][k];
-      sS[j][k] = s;
+    // S = gC S + U^T Kd ; wave w: k-tiles w, w+4, ...
+    for (int nt = wave; nt < DK / 16; nt += NT / 64) {
+      f32x4 acc = {0, 0, 0, 0};
+      mm_tn(acc, sU, LU, sKd + nt * 16, LK, CH);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * kk + r, k = nt * 16 + i16;
+        sS[j * LS + k] = gC * sS[j * LS + k] + acc[r];
+      }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < DS * DK; idx += NT) {
+  for (int idx = tid; idx < 16 * DK; idx += NT) {
     const int j = idx / DK, k = idx % DK;
-    Sg[(int64_t)(j0 + j) * DK + k] = sS[j][k];
+    Sg[(int64_t)(j0 + j) * DK + k] = sS[j * LS + k];
+  }
+}
+
+// ------------------------------------------------------- chunk output
+// grid (chunk, head, seq): O = Qp S_c^T + Up, then per token and head
+// y = RMSNorm(o; g_o) * SiLU(z) -> bf16.
+template <int DK>
+__global__ __launch_bounds__(NT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
+  constexpr int DV = DK;
+  constexpr int LD = DK + 4;
+  extern __shared__ __align__(16) float gsm[];
+  float* sQ = gsm;             // Qp [CH][LD], later O
+  float* sS = sQ + CH * LD;    // S_c [DV][LD]
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int C = min(CH, a.T - c * CH);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
+  for (int idx = tid * 4; idx < CH * DK; idx += NT * 4) {
+    const int r = idx / DK, k = idx % DK;
+    *reinterpret_cast<float4*>(sQ + r * LD + k) = *reinterpret_cast<const float4*>(P.Qp + idx);
+  }
+  for (int idx = tid * 4; idx < DV * DK; idx += NT * 4) {
+    const int v = idx / DK, k = idx % DK;
+    *reinterpret_cast<float4*>(sS + v * LD + k) = *reinterpret_cast<const float4*>(P.S + idx);
+  }
+  __syncthreads();
+  constexpr int NTILE = DV / 16;
+  f32x4 acc[NTILE];
+  const int i16 = lane & 15, kk = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NTILE; ++nt) {
+    acc[nt] = (f32x4){0, 0, 0, 0};
+    mm_nt(acc[nt], sQ + wave * 16 * LD, LD, sS + nt * 16 * LD, LD, DK);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int nt = 0; nt < NTILE; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
+      sQ[row * LD + col] = acc[nt][r] + P.Up[row * DK + col];
+    }
+  __syncthreads();
+  for (int r = wave; r < C; r += NT / 64) {
+    const int64_t m = (int64_t)b * a.T + c * CH + r;
+    float v[DV / 64], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < DV / 64; ++e) {
+      v[e] = sQ[r * LD + lane + 64 * e];
+      ss += v[e] * v[e];
+    }
+    ss = wave_sum(ss);
+    const float inv = rsqrtf(ss / DV + a.eps);
+    const uint16_t* z = a.proj + m * a.proj_stride + a.off_z + h * DV;
+    uint16_t* y = a.out + m * a.out_stride + h * DV;
+#pragma unroll
+    for (int e = 0; e < DV / 64; ++e) {
+      const int d = lane + 64 * e;
+      y[d] = f2bf_bits(v[e] * inv * bf2f(a.o_norm[d]) * siluf_(bf2f(z[d])));
+    }
   }
 }
 
@@ -292,12 +483,25 @@ __global__ __launch_bounds__(256) void gdn_out_kernel(GdnArgs a, int M) {
   (void)M;
 }
 
+template <typename K>
+hipError_t set_lds(K k, size_t bytes) {
+  return hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 template <int DK>
 hipError_t prefill_dk(const GdnArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL(gdn_chunk_prep_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), 0, s, a);
-  constexpr int DS = 16;
-  hipLaunchKernelGGL((gdn_chunk_scan_kernel<DK, DS>), dim3(DK / DS, a.H, B), dim3(NT), 0, s, a);
-  hipLaunchKernelGGL(gdn_out_kernel<DK>, dim3(B * a.T, (a.H + 3) / 4), dim3(256), 0, s, a, B * a.T);
+  const size_t lds_prep = (3 * CH * (DK + 4) + 3 * CH * (CH + 4) + 2 * CH) * sizeof(float);
+  const size_t lds_out = (CH * (DK + 4) + DK * (DK + 4)) * sizeof(float);
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = set_lds(gdn_chunk_prep_kernel<DK>, lds_prep);
+    if (e == hipSuccess) e = set_lds(gdn_chunk_out_kernel<DK>, lds_out);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(gdn_chunk_prep_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), lds_prep, s, a);
+  hipLaunchKernelGGL(gdn_chunk_scan_kernel<DK>, dim3(DK / 16, a.H, B), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(gdn_chunk_out_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), lds_out, s, a);
   return hipGetLastError();
 }
 

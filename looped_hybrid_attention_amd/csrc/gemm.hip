@@ -55,60 +55,44 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmArgs g) {
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? BN / 2 : BN;
   const int n0 = tn * OUT_BN;  // first output column
 
-  // Global source rows of this thread's chunks.
-  const uint16_t* a_src[A_CHUNKS];
-  bool a_ok[A_CHUNKS];
-  int a_lds[A_CHUNKS];
+  // Global source offsets (elements, 32-bit) of this thread's chunks from
+  // the tile's row base.  Rows past M (or N) are clamped to a valid row: they
+  // only feed output rows (columns) that are never stored.
+  int a_off[A_CHUNKS], a_lds[A_CHUNKS];
 #pragma unroll
   for (int i = 0; i < A_CHUNKS; ++i) {
-    int c = tid + i * NT, r = c / (BK / 8), kc = c % (BK / 8);
-    int gm = m0 + r;
-    a_ok[i] = gm < g.M;
-    a_src[i] = g.A + (int64_t)(a_ok[i] ? gm : 0) * g.lda + kc * 8;
+    const int c = tid + i * NT, r = c / (BK / 8), kc = c % (BK / 8);
+    a_off[i] = min(m0 + r, g.M - 1) * (int)g.lda + kc * 8;
     a_lds[i] = r * LDSK + kc * 8;
   }
-  const uint16_t* b_src[B_CHUNKS];
-  bool b_ok[B_CHUNKS];
-  int b_lds[B_CHUNKS];
+  int b_off[B_CHUNKS], b_lds[B_CHUNKS];
 #pragma unroll
   for (int i = 0; i < B_CHUNKS; ++i) {
-    int c = tid + i * NT, r = c / (BK / 8), kc = c % (BK / 8);
+    const int c = tid + i * NT, r = c / (BK / 8), kc = c % (BK / 8);
     int gn;
-    bool ok;
     if (EPI == LOOP_EPI_SWIGLU) {
       // B-tile rows come in 32-row blocks alternating gate / up of the same
       // output columns.
-      int blk = r / 32, part = blk & 1, col = n0 + (blk >> 1) * 32 + (r & 31);
-      ok = col < g.N;
+      const int blk = r / 32, part = blk & 1, col = min(n0 + (blk >> 1) * 32 + (r & 31), g.N - 1);
       gn = part * g.swiglu_F + col;
     } else {
-      gn = n0 + r;
-      ok = gn < g.N;
+      gn = min(n0 + r, g.N - 1);
     }
-    b_ok[i] = ok;
-    b_src[i] = g.B + (int64_t)(ok ? gn : 0) * g.ldb + kc * 8;
-    b_lds[i] = r * LDSK + kc * 8;
+    b_off[i] = gn * (int)g.ldb + kc * 8;
+    b_lds[i] = (BM + r) * LDSK + kc * 8;
   }
+  const uint16_t* Ak = g.A;  // advanced by BK per k-step
+  const uint16_t* Bk = g.B;
 
-  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-  auto gload = [&](int k0) {
+  u32x4 ra[A_CHUNKS], rb[B_CHUNKS];
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-      if (!a_ok[i]) ra[i] = make_uint4(0, 0, 0, 0);
-    }
+  for (int i = 0; i < A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(Ak + a_off[i]);
 #pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-      rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
-      if (!b_ok[i]) rb[i] = make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
+  for (int i = 0; i < B_CHUNKS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bk + b_off[i]);
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<uint4*>(gemm_smem + buf * STAGE + a_lds[i]) = ra[i];
+  for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(gemm_smem + a_lds[i]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) *reinterpret_cast<uint4*>(gemm_smem + buf * STAGE + BM * LDSK + b_lds[i]) = rb[i];
-  };
+  for (int i = 0; i < B_CHUNKS; ++i) *reinterpret_cast<u32x4*>(gemm_smem + b_lds[i]) = rb[i];
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -117,30 +101,62 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmArgs g) {
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
 
   const int nk = g.K / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
   const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int a_frag = (wm * (BM / WM) + lr) * LDSK + lk;
+  const int b_frag = (BM + wn * (BN / WN) + lr) * LDSK + lk;
+  __syncthreads();
+  // One basic block per k-step: the next tile's global loads (the last step
+  // re-reads its own tile, harmlessly), the MFMAs of the four 16-deep steps
+  // with the next step's LDS fragments interleaved, then the next tile into
+  // the other LDS buffer.
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
-    const uint16_t* a_base = gemm_smem + cur * STAGE + (wm * (BM / WM) + lr) * LDSK + lk;
-    const uint16_t* b_base = gemm_smem + cur * STAGE + BM * LDSK + (wn * (BN / WN) + lr) * LDSK + lk;
+    const uint16_t* S = gemm_smem + (kt & 1) * STAGE;
+    const int kn = min(kt + 1, nk - 1) * BK;
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const u32x4*>(Ak + kn + a_off[i]);
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) rb[i] = *reinterpret_cast<const u32x4*>(Bk + kn + b_off[i]);
+    bf16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(S + a_frag + i * 32 * LDSK);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bfr[0][j] = *reinterpret_cast<const bf16x8*>(S + b_frag + j * 32 * LDSK);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[TM], bfr[TN];
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < BK / 16) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          af[nxt][i] = *reinterpret_cast<const bf16x8*>(S + a_frag + i * 32 * LDSK + (ks + 1) * 16);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[nxt][j] = *reinterpret_cast<const bf16x8*>(S + b_frag + j * 32 * LDSK + (ks + 1) * 16);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(a_base + i * 32 * LDSK + ks * 16);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(b_base + j * 32 * LDSK + ks * 16);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma32x32x16(af[cur][i], bfr[cur][j], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(cur ^ 1);
+    uint16_t* D = gemm_smem + ((kt + 1) & 1) * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(D + a_lds[i]) = ra[i];
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) *reinterpret_cast<u32x4*>(D + b_lds[i]) = rb[i];
+    // schedule: global loads first, first fragments, then for each of the
+    // first three 16-deep steps its MFMAs interleaved with the next step's
+    // fragment reads, the last step's MFMAs, the LDS stores.
+    __builtin_amdgcn_sched_group_barrier(0x020, A_CHUNKS + B_CHUNKS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16 - 1; ++ks) {
+#pragma unroll
+      for (int f = 0; f < TM + TN; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN / (TM + TN) > 0 ? TM * TN / (TM + TN) : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, A_CHUNKS + B_CHUNKS, 0);
     __syncthreads();
   }
 

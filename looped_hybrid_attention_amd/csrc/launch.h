@@ -88,7 +88,9 @@ struct GdnArgs {
   float eps, q_scale;
   const int32_t* pos; const int32_t* seq_slot;
   float* state;  // state block of the exec slot: [max_batch][H][Dv][Dk]
-  float* W; float* Ut; float* Qg; float* Kd; float* Mqk; float* gC;  // chunk workspace
+  // chunk workspace, per (seq, head, chunk): W, Ut, Kd, Qg (= gamma Q - Mqk W),
+  // Mqk (= Mqk Ut) [64][Dk] fp32 each, gC, and Sc, the chunk entry state [Dv][Dk]
+  float* W; float* Ut; float* Qg; float* Kd; float* Mqk; float* gC; float* Sc;
   float* o;      // [M][H][Dv] fp32
   const uint16_t* o_norm;
   uint16_t* out; int64_t out_stride;

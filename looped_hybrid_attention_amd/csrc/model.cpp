@@ -30,13 +30,13 @@
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr int DEC_SPLIT = 256;  // keys per decode-attention split
+constexpr int DEC_SPLIT = 512;  // keys per decode-attention split (decode_attn_kernel)
 
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
   size_t meta, h, hmid, x, a, s0, s1, xn, hn, proj, qbuf, obuf, act, gdn_o;
-  size_t gW, gUt, gQg, gKd, gM, gC;
+  size_t gW, gUt, gQg, gKd, gM, gC, gS;
   size_t xf, logits, am_v, am_i, dec_part, mhc;
   size_t total;
   int n_in_max, chunk_slots, n_split_max;
@@ -72,8 +72,9 @@ Layout layout(const loop_config& c, int64_t M) {
   L.gUt = take(cs * 64 * c.gdn_dv * 4);
   L.gQg = take(cs * 64 * c.gdn_dk * 4);
   L.gKd = take(cs * 64 * c.gdn_dk * 4);
-  L.gM = take(cs * 64 * 64 * 4);
+  L.gM = take(cs * 64 * c.gdn_dv * 4);
   L.gC = take(cs * 4);
+  L.gS = take(cs * (int64_t)c.gdn_dv * c.gdn_dk * 4);
   L.xf = take(B * d * 2);
   L.logits = take(B * (int64_t)std::max(c.vocab, 1) * 4);
   L.am_v = take(B * (int64_t)argmax_chunks(std::max(c.vocab, 1)) * 4);
@@ -318,6 +319,7 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
     g.state = (float*)(m->arena + loop_cache_offset(&c, 2, d.slot, 0));
     g.W = at<float>(m, L.gW); g.Ut = at<float>(m, L.gUt); g.Qg = at<float>(m, L.gQg);
     g.Kd = at<float>(m, L.gKd); g.Mqk = at<float>(m, L.gM); g.gC = at<float>(m, L.gC);
+    g.Sc = at<float>(m, L.gS);
     g.o = at<float>(m, L.gdn_o);
     g.o_norm = (const uint16_t*)w.o_norm;
     g.out = obuf; g.out_stride = mix_width;

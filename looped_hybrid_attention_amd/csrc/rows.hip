@@ -121,100 +121,113 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const float* x, const float
 //   out = TR_OUT_READ: (fork if in = H) then the next exec's mHC read:
 //                      x = r0 s0 + r1 s1, xn = RMSNorm(x; g)
 //   out = TR_OUT_NONE: merge only (h written), no norm
-template <int PER>
-__global__ __launch_bounds__(NT) void transition_kernel(TransitionArgs t) {
-  __shared__ float red[2 * NT / 64];
+// One row per workgroup of TNT threads, PER values per thread.
+template <int TNT, int PER>
+DEV void block_sum2_t(float& a, float& b, float* red) {
+  a = wave_sum(a);
+  b = wave_sum(b);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) { red[2 * w] = a; red[2 * w + 1] = b; }
+  __syncthreads();
+  a = b = 0.f;
+#pragma unroll
+  for (int i = 0; i < TNT / 64; ++i) { a += red[2 * i]; b += red[2 * i + 1]; }
+}
+
+template <int TNT, int PER>
+__global__ __launch_bounds__(TNT) void transition_kernel(TransitionArgs t) {
+  __shared__ float red[2 * TNT / 64];
   __shared__ float sP[4];
   const int d = t.d;
-  // The layer's 2x2 mix matrix, once per workgroup (wave 0, in registers),
-  // shared through LDS with the rows this workgroup handles.
-  if (t.in_mode == TR_IN_WRITE && threadIdx.x < 64) {
-    float P[4];
-    sinkhorn2(t.mix, t.iters, P);
-    if (threadIdx.x == 0) { sP[0] = P[0]; sP[1] = P[1]; sP[2] = P[2]; sP[3] = P[3]; }
-  }
-  __syncthreads();
-  const int64_t m_end = min((int64_t)t.M, (int64_t)(blockIdx.x + 1) * t.rows_per_block);
-  for (int64_t m = (int64_t)blockIdx.x * t.rows_per_block; m < m_end; ++m) {
-    const int64_t o = m * d;
-    float s0[PER], s1[PER];
-    if (t.in_mode == TR_IN_WRITE) {
-      float ov[PER];
-      float z0 = 0.f, z1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        int c = threadIdx.x + i * NT;
-        bool ok = c < d;
-        ov[i] = ok ? t.out[o + c] : 0.f;
-        s0[i] = ok ? t.s0[o + c] : 0.f;
-        s1[i] = ok ? t.s1[o + c] : 0.f;
-        if (ok) {
-          z0 += t.write_w[c] * ov[i];
-          z1 += t.write_w[d + c] * ov[i];
-        }
-      }
-      block_sum2(z0, z1, red);
-      float w0, w1;
-      softmax2(z0 + t.write_b[0], z1 + t.write_b[1], w0, w1);
-      const float P0 = sP[0], P1 = sP[1], P2 = sP[2], P3 = sP[3];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        float a = s0[i], b = s1[i];
-        s0[i] = P0 * a + P1 * b + w0 * ov[i];
-        s1[i] = P2 * a + P3 * b + w1 * ov[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        int c = threadIdx.x + i * NT;
-        s0[i] = s1[i] = c < d ? t.h[o + c] : 0.f;
-      }
-    }
-
-    float xv[PER];
-    if (t.out_mode == TR_OUT_READ) {
-      float z0 = 0.f, z1 = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        int c = threadIdx.x + i * NT;
-        if (c < d) {
-          z0 += t.read_w[c] * s0[i] + t.read_w[d + c] * s1[i];
-          z1 += t.read_w[2 * d + c] * s0[i] + t.read_w[3 * d + c] * s1[i];
-        }
-      }
-      block_sum2(z0, z1, red);
-      float r0, r1;
-      softmax2(z0 + t.read_b[0], z1 + t.read_b[1], r0, r1);
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        int c = threadIdx.x + i * NT;
-        xv[i] = r0 * s0[i] + r1 * s1[i];
-        if (c < d) {
-          t.s0_out[o + c] = s0[i];
-          t.s1_out[o + c] = s1[i];
-          t.x_out[o + c] = xv[i];
-        }
-      }
-    } else {
-      // plain state h: either unchanged (in = H) or the merge of the streams
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        int c = threadIdx.x + i * NT;
-        xv[i] = t.in_mode == TR_IN_WRITE ? (s0[i] + s1[i]) * 0.5f : s0[i];
-        if (t.in_mode == TR_IN_WRITE && c < d) t.h_out[o + c] = xv[i];
-      }
-      if (t.out_mode == TR_OUT_NONE) continue;
-    }
-    float ss = 0.f, dummy = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) ss += xv[i] * xv[i];
-    block_sum2(ss, dummy, red);
-    const float inv = rsqrtf(ss / d + t.eps);
+  const int64_t o = (int64_t)blockIdx.x * d;
+  float s0[PER], s1[PER];
+  if (t.in_mode == TR_IN_WRITE) {
+    float ov[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      int c = threadIdx.x + i * NT;
-      if (c < d) t.xn[o + c] = f2bf_bits(xv[i] * inv * bf2f(t.norm_g[c]));
+      const int c = threadIdx.x + i * TNT;
+      const bool ok = c < d;
+      ov[i] = ok ? t.out[o + c] : 0.f;
+      s0[i] = ok ? t.s0[o + c] : 0.f;
+      s1[i] = ok ? t.s1[o + c] : 0.f;
     }
+    // the layer's 2x2 mix matrix: Sinkhorn in registers of wave 0
+    if (threadIdx.x < 64) {
+      float P[4];
+      sinkhorn2(t.mix, t.iters, P);
+      if (threadIdx.x == 0) { sP[0] = P[0]; sP[1] = P[1]; sP[2] = P[2]; sP[3] = P[3]; }
+    }
+    float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * TNT;
+      if (c < d) {
+        z0 += t.write_w[c] * ov[i];
+        z1 += t.write_w[d + c] * ov[i];
+      }
+    }
+    block_sum2_t<TNT, PER>(z0, z1, red);  // its barriers also publish sP
+    float w0, w1;
+    softmax2(z0 + t.write_b[0], z1 + t.write_b[1], w0, w1);
+    const float P0 = sP[0], P1 = sP[1], P2 = sP[2], P3 = sP[3];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const float a = s0[i], b = s1[i];
+      s0[i] = P0 * a + P1 * b + w0 * ov[i];
+      s1[i] = P2 * a + P3 * b + w1 * ov[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * TNT;
+      s0[i] = s1[i] = c < d ? t.h[o + c] : 0.f;
+    }
+  }
+
+  float xv[PER];
+  if (t.out_mode == TR_OUT_READ) {
+    float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * TNT;
+      if (c < d) {
+        z0 += t.read_w[c] * s0[i] + t.read_w[d + c] * s1[i];
+        z1 += t.read_w[2 * d + c] * s0[i] + t.read_w[3 * d + c] * s1[i];
+      }
+    }
+    block_sum2_t<TNT, PER>(z0, z1, red);
+    float r0, r1;
+    softmax2(z0 + t.read_b[0], z1 + t.read_b[1], r0, r1);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * TNT;
+      xv[i] = r0 * s0[i] + r1 * s1[i];
+      if (c < d) {
+        t.s0_out[o + c] = s0[i];
+        t.s1_out[o + c] = s1[i];
+        t.x_out[o + c] = xv[i];
+      }
+    }
+  } else {
+    // plain state h: either unchanged (in = H) or the merge of the streams
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * TNT;
+      xv[i] = t.in_mode == TR_IN_WRITE ? (s0[i] + s1[i]) * 0.5f : s0[i];
+      if (t.in_mode == TR_IN_WRITE && c < d) t.h_out[o + c] = xv[i];
+    }
+    if (t.out_mode == TR_OUT_NONE) return;
+  }
+  float ss = 0.f, dummy = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) ss += xv[i] * xv[i];
+  block_sum2_t<TNT, PER>(ss, dummy, red);
+  const float inv = rsqrtf(ss / d + t.eps);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = threadIdx.x + i * TNT;
+    if (c < d) t.xn[o + c] = f2bf_bits(xv[i] * inv * bf2f(t.norm_g[c]));
   }
 }
 
@@ -306,12 +319,13 @@ hipError_t launch_rmsnorm(const float* x, const float* x2, const int32_t* rows, 
 
 hipError_t launch_transition(TransitionArgs t, hipStream_t s) {
   if (t.M == 0) return hipSuccess;
-  t.rows_per_block = t.M >= 4096 ? 8 : 1;
-  const int blocks = (t.M + t.rows_per_block - 1) / t.rows_per_block;
-  return by_width(t.d, [&](auto per) {
-    hipLaunchKernelGGL(transition_kernel<decltype(per)::value>, dim3(blocks), dim3(NT), 0, s, t);
-    return hipGetLastError();
-  });
+  t.rows_per_block = 1;
+  if (t.d <= 256) hipLaunchKernelGGL((transition_kernel<256, 1>), dim3(t.M), dim3(256), 0, s, t);
+  else if (t.d <= 1024) hipLaunchKernelGGL((transition_kernel<256, 4>), dim3(t.M), dim3(256), 0, s, t);
+  else if (t.d <= 4096) hipLaunchKernelGGL((transition_kernel<512, 8>), dim3(t.M), dim3(512), 0, s, t);
+  else if (t.d <= 8192) hipLaunchKernelGGL((transition_kernel<1024, 8>), dim3(t.M), dim3(1024), 0, s, t);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 hipError_t launch_tap(const float* h, const float* s0, const float* s1, float* dst, int B, int T, int d,

@@ -8,11 +8,15 @@ residual / mHC / state: ``oracle.precision``).  Metric: max |gpu - oracle| /
 max |oracle| per tensor.  Bar: 2e-2 for the final hidden states (all
 positions) and the logits, unless the oracle itself is less stable than that:
 this random-weight model amplifies a relative input perturbation of 1e-7 about
-100x at 256 tokens, so two evaluations that are identical in exact arithmetic
-(the oracle with its token-by-token and with its chunked Gated-DeltaNet) land
+100x at 256 tokens, so evaluations that are identical in exact arithmetic (the
+oracle with token-by-token or chunked Gated-DeltaNet, in fp32 or fp64) land
 ~4e-2 apart once bf16 rounding decisions flip.  The bar is therefore
-max(2e-2, 1.5 * that self-spread + 5e-3), computed here from the oracle alone.
-Exact next-token argmax; Sinkhorn matrices within 1e-4.  Against the plain
+max(2e-2, 2 x the largest spread among those evaluations) (``parity.bar``),
+computed here from the oracle alone.
+Next-token argmax: exact wherever the oracle's top-1 / top-2 margin is wider
+than the logits bar; inside that band (a near-tie the noise can decide
+either way) the GPU's token must be within the bar of the oracle's best
+(``parity.argmax_ok``).  Sinkhorn matrices within 1e-4.  Against the plain
 fp32 definition the GPU may drift as much as the bf16 policy itself does:
 bounded by 1.5x the policy oracle's drift + 5e-3.  Decode is teacher-forced
 with the oracle's greedy tokens so that every step compares the same inputs.
@@ -25,15 +29,19 @@ import oracle
 from oracle import model as om
 from gpu_util import torch_cuda, dev, host, say, rel_err
 from model_util import GpuModel
+from parity import bar, argmax_ok
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
 
 
-def spread_tol(a, b):
-    """Bar for a whole-model comparison: 2e-2, or 1.5x the oracle's own spread
-    between two evaluations that are equal in exact arithmetic, + 5e-3."""
-    return max(TOL, 1.5 * rel_err(a, b) + 5e-3)
+def oracle_evals(ocfg, W, W64, ids):
+    """The policy oracle evaluated four ways that agree in exact arithmetic."""
+    out = []
+    for w in (W, W64):
+        for ch in (False, True):
+            out.append(om.prefill(ocfg, w, [om.SeqState(ocfg)], ids=ids, bf16=True, chunked_gdn=ch))
+    return out
 
 
 @pytest.fixture(scope="module")
@@ -43,12 +51,13 @@ def tiny():
     g = GpuModel(torch, dims, max_batch=3, max_seq=512, max_tokens=512)
     ocfg = oracle.Config.from_dims(dims)
     W = om.to_dtype(g.host_weights, np.float32)
-    yield torch, dims, g, ocfg, W
+    W64 = om.to_dtype(g.host_weights, np.float64)
+    yield torch, dims, g, ocfg, W, W64
     g.close()
 
 
 def test_schedule_matches_oracle(tiny):
-    torch, dims, g, ocfg, W = tiny
+    torch, dims, g, ocfg, W, W64 = tiny
     sched = g.L.loop_schedule(g.cfg)
     orows = oracle.schedule(ocfg)
     assert [(r.layer, int(r.kind == "full"), r.slot, int(r.loop), int(r.fork), int(r.merge))
@@ -56,7 +65,7 @@ def test_schedule_matches_oracle(tiny):
 
 
 def test_mhc_sinkhorn_matrices(tiny):
-    torch, dims, g, ocfg, W = tiny
+    torch, dims, g, ocfg, W, W64 = tiny
     say("tiny mhc matrices")
     n = dims["loop_end"] - dims["loop_start"]
     out = torch.zeros(n * 4, dtype=torch.float32, device="cuda")
@@ -70,7 +79,7 @@ def test_mhc_sinkhorn_matrices(tiny):
 
 
 def test_prefill_and_greedy_decode(tiny):
-    torch, dims, g, ocfg, W = tiny
+    torch, dims, g, ocfg, W, W64 = tiny
     T, V, d = 256, dims["vocab"], dims["d_model"]
     ids = synth.token_ids(synth.SEED_X, "tiny.ids", T, V)
     say("tiny prefill", T)
@@ -82,18 +91,16 @@ def test_prefill_and_greedy_decode(tiny):
     torch.cuda.synchronize()
     st = [om.SeqState(ocfg)]
     h_ref, lg_ref, _ = om.prefill(ocfg, W, st, ids=ids.reshape(1, -1), bf16=True)
-    h_c, lg_c, _ = om.prefill(ocfg, W, [om.SeqState(ocfg)], ids=ids.reshape(1, -1), bf16=True,
-                              chunked_gdn=True)
-    tol_h, tol_l = spread_tol(h_c, h_ref), spread_tol(lg_c, lg_ref)
+    ev = oracle_evals(ocfg, W, W64, ids.reshape(1, -1))
+    tol_h, tol_l = bar([e[0] for e in ev]), bar([e[1] for e in ev])
     print("tiny prefill: gpu-vs-oracle hidden %.4f (bar %.4f), logits %.4f (bar %.4f)"
           % (rel_err(host(hid), h_ref[0]), tol_h, rel_err(host(logits), lg_ref), tol_l))
     assert rel_err(host(hid), h_ref[0]) <= tol_h
     assert rel_err(host(logits), lg_ref) <= tol_l
-    assert int(np.argmax(host(logits)[0])) == int(om.argmax_lowest(lg_ref)[0])
+    assert argmax_ok(int(np.argmax(host(logits)[0])), lg_ref[0], tol_l)
     # against the fp32 definition: no worse than the bf16 policy's own drift
     h32, lg32, _ = om.prefill(ocfg, W, [om.SeqState(ocfg)], ids=ids.reshape(1, -1))
-    bound = 1.5 * rel_err(h_ref[0], h32[0]) + 5e-3
-    assert rel_err(host(hid), h32[0]) <= bound
+    assert rel_err(host(hid), h32[0]) <= 2 * max(rel_err(e[0][0], h32[0]) for e in ev)
     tok = int(om.argmax_lowest(lg_ref)[0])
     nxt = torch.zeros(1, dtype=torch.int32, device="cuda")
     for step in range(8):
@@ -107,7 +114,7 @@ def test_prefill_and_greedy_decode(tiny):
                                                           rel_err(host(hid)[0], h_o[0])))
         assert rel_err(host(logits), lg_o) <= tol_l, step
         assert rel_err(host(hid)[0], h_o[0]) <= tol_h, step
-        assert int(host(nxt)[0]) == int(nx_o[0]), step
+        assert argmax_ok(int(host(nxt)[0]), lg_o[0], tol_l), step
         tok = int(nx_o[0])
 
 
@@ -115,7 +122,7 @@ def test_batched_ragged_chunked_prefill(tiny):
     """Two sequences in other slots, prefilled in two chunks of 100 and 37
     tokens (several GDN chunks, a ragged tail, start_pos > 0), equal to the
     oracle's whole prefill of each sequence."""
-    torch, dims, g, ocfg, W = tiny
+    torch, dims, g, ocfg, W, W64 = tiny
     V, d = dims["vocab"], dims["d_model"]
     ids = synth.token_ids(synth.SEED_X, "tiny.ids2", 2 * 137, V).reshape(2, 137)
     hid = torch.zeros((2 * 100, d), dtype=torch.float32, device="cuda")
@@ -129,16 +136,15 @@ def test_batched_ragged_chunked_prefill(tiny):
                      d_logits=logits.data_ptr(), d_hidden_out=hid.data_ptr(), stream=g.stream())
     torch.cuda.synchronize()
     for s in range(2):
-        h_ref, lg_ref, _ = om.prefill(ocfg, W, [om.SeqState(ocfg)], ids=ids[s:s + 1], bf16=True)
-        h_c, lg_c, _ = om.prefill(ocfg, W, [om.SeqState(ocfg)], ids=ids[s:s + 1], bf16=True,
-                                  chunked_gdn=True)
-        assert rel_err(host(hid)[s * 37:(s + 1) * 37], h_ref[0, 100:]) <= spread_tol(h_c[0, 100:], h_ref[0, 100:])
-        assert rel_err(host(logits)[s], lg_ref[0]) <= spread_tol(lg_c[0], lg_ref[0])
-        assert int(np.argmax(host(logits)[s])) == int(np.argmax(lg_ref[0]))
+        ev = oracle_evals(ocfg, W, W64, ids[s:s + 1])
+        h_ref, lg_ref = ev[0][0], ev[0][1]
+        assert rel_err(host(hid)[s * 37:(s + 1) * 37], h_ref[0, 100:]) <= bar([e[0][0, 100:] for e in ev])
+        assert rel_err(host(logits)[s], lg_ref[0]) <= bar([e[1][0] for e in ev])
+        assert argmax_ok(int(np.argmax(host(logits)[s])), lg_ref[0], bar([e[1][0] for e in ev]))
 
 
 def test_taps(tiny):
-    torch, dims, g, ocfg, W = tiny
+    torch, dims, g, ocfg, W, W64 = tiny
     T, V, d = 40, dims["vocab"], dims["d_model"]
     ids = synth.token_ids(synth.SEED_X, "tiny.ids3", T, V)
     taps = [3, 7, 11, 13, 15]
@@ -148,14 +154,14 @@ def test_taps(tiny):
     g.L.loop_prefill(g.handle, 1, T, [0], [0], d_tokens=d_ids.data_ptr(), tap_exec=taps,
                      d_taps=d_taps.data_ptr(), stream=g.stream())
     torch.cuda.synchronize()
-    _, _, tref = om.prefill(ocfg, W, [om.SeqState(ocfg)], ids=ids.reshape(1, -1), taps=tuple(taps),
-                            bf16=True)
+    trefs = [om.prefill(ocfg, w, [om.SeqState(ocfg)], ids=ids.reshape(1, -1), taps=tuple(taps), bf16=True,
+                        chunked_gdn=ch)[2] for w in (W, W64) for ch in (False, True)]
     for i, e in enumerate(taps):
-        assert rel_err(host(d_taps)[i, 0], tref[e][0]) <= TOL, e
+        assert rel_err(host(d_taps)[i, 0], trefs[0][e][0]) <= bar([t[e][0] for t in trefs]), e
 
 
 def test_deterministic_rerun(tiny):
-    torch, dims, g, ocfg, W = tiny
+    torch, dims, g, ocfg, W, W64 = tiny
     T, V, d = 96, dims["vocab"], dims["d_model"]
     ids = dev(synth.token_ids(synth.SEED_X, "tiny.ids4", T, V), torch)
     outs = []
