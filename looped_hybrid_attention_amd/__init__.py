@@ -87,7 +87,7 @@ def _load():
         "loop_profile": (ctypes.c_int, [_vp, _i32]),
         "loop_profile_read": (ctypes.c_int, [_vp, P(_f64), P(_i64)]),
         "loop_op_gemm": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
-                                        _i32, _vp]),
+                                        _i32, _vp, _sz, _vp]),
         "loop_synth_normal": (ctypes.c_int, [_vp, _i64, _i32, _u32, _u32, _i64, _f64, _f64, _vp]),
         "loop_synth_token_ids": (ctypes.c_int, [_vp, _i64, _u32, _u32, _u32, _vp]),
     }
@@ -157,8 +157,9 @@ def loop_schedule(cfg: loop_config) -> list:
 
 
 def loop_op_gemm(A: int, lda: int, B: int, ldb: int, C: int, ldc: int, R: int, M: int, N: int,
-                 K: int, epi: int, stream: int = 0) -> None:
-    _check(_lib.loop_op_gemm(A, lda, B, ldb, C, ldc, R or None, M, N, K, epi, stream or None))
+                 K: int, epi: int, stream: int = 0, ws: int = 0, ws_bytes: int = 0) -> None:
+    _check(_lib.loop_op_gemm(A, lda, B, ldb, C, ldc, R or None, M, N, K, epi, ws or None, ws_bytes,
+                             stream or None))
 
 
 def loop_synth_normal(dst: int, n: int, dtype: int, seed: int, key: int, start: int, std: float,

@@ -311,23 +311,30 @@ __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // scores, 16 keys per group, groups round-robin over the waves
-  for (int g0 = wave * 16; g0 < nk; g0 += 4 * 16) {
-    const int key = g0 + l16;
-    uint4 kv[NKS];
+  // scores: each wave takes two 16-key groups at a time (32 loads per lane in
+  // flight for D = 256), groups round-robin over the waves
+  for (int g0 = wave * 32; g0 < nk; g0 += 4 * 32) {
+    u32x4 kv[2][NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      kv[ks] = key < nk ? *reinterpret_cast<const uint4*>(Kc + (int64_t)key * D + ks * 32 + lg * 8)
-                        : make_uint4(0, 0, 0, 0);
-    f32x4 acc = {0, 0, 0, 0};
+    for (int u = 0; u < 2; ++u) {
+      const int key = g0 + 16 * u + l16;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kv[ks]), qf[ks], acc);
-    // lane holds keys g0 + 4 lg + r of head l16
-    if (l16 < G) {
+      for (int ks = 0; ks < NKS; ++ks)
+        kv[u][ks] = key < nk ? *reinterpret_cast<const u32x4*>(Kc + (int64_t)key * D + ks * 32 + lg * 8)
+                             : (u32x4){0, 0, 0, 0};
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kk = g0 + 4 * lg + r;
-        if (kk < DEC_SPLIT) sc[l16][kk] = kk < nk ? acc[r] * a.scale_log2 : -1e30f;
+    for (int u = 0; u < 2; ++u) {
+      f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kv[u][ks]), qf[ks], acc);
+      // lane holds keys g0 + 16u + 4 lg + r of head l16
+      if (l16 < G) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kk = g0 + 16 * u + 4 * lg + r;
+          if (kk < DEC_SPLIT) sc[l16][kk] = kk < nk ? acc[r] * a.scale_log2 : -1e30f;
+        }
       }
     }
   }
@@ -355,26 +362,36 @@ __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a
 #pragma unroll
   for (int i = 0; i < TPW; ++i) o[i] = (f32x4){0, 0, 0, 0};
   const int nsteps = (nk + 31) / 32;
-  for (int st = 0; st < nsteps; ++st) {
-    const int kk = st * 32 + lg * 8;  // first of this lane's 8 keys
-    bf16x8 pf = *reinterpret_cast<const bf16x8*>(sp + l16 * DEC_PS + kk);
+  // four 32-key steps per iteration: their V^T loads are all in flight
+  // before the MFMAs
+  for (int st0 = 0; st0 < nsteps; st0 += 4) {
+    u32x4 vv[4][TPW];
+    bf16x8 pf[4];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int dt = wave + 4 * i;
-      if (dt >= NDT) break;
-      const int d = dt * 16 + l16;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kk < nk) {
-        v = *reinterpret_cast<const uint4*>(Vc + (int64_t)d * a.max_seq + kk);
-        if (kk + 8 > nk) {
-          uint16_t* e = reinterpret_cast<uint16_t*>(&v);
+    for (int u = 0; u < 4; ++u) {
+      const int kk = (st0 + u) * 32 + lg * 8;  // first of this lane's 8 keys
+      pf[u] = kk < DEC_SPLIT ? *reinterpret_cast<const bf16x8*>(sp + l16 * DEC_PS + kk) : (bf16x8){};
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (kk + j >= nk) e[j] = 0;
+      for (int i = 0; i < TPW; ++i) {
+        const int dt = wave + 4 * i;
+        u32x4 v = {0, 0, 0, 0};
+        if (dt < NDT && kk < nk) {
+          const int d = dt * 16 + l16;
+          v = *reinterpret_cast<const u32x4*>(Vc + (int64_t)d * a.max_seq + kk);
+          if (kk + 8 > nk) {
+            uint16_t* e = reinterpret_cast<uint16_t*>(&v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (kk + j >= nk) e[j] = 0;
+          }
         }
+        vv[u][i] = v;
       }
-      o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, v), pf, o[i]);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, vv[u][i]), pf[u], o[i]);
   }
   // lane holds O^T[d = 16 dt + 4 lg + r][g = l16]
   if (l16 < G) {

@@ -14,6 +14,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace {
 
 constexpr int BK = 64;
@@ -26,9 +28,11 @@ struct GemmArgs {
   const float* R;
   int M, N, K;   // N = output columns
   int swiglu_F;  // SwiGLU: offset of the up rows in B (= N)
+  float* part;   // split-K: fp32 partials [splits][M][N] ([splits][M][2][N] for SwiGLU)
+  int kslice;    // split-K: K per split (blockIdx.y)
 };
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, bool SPLIT>
 __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmArgs g) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM / 32;  // 32x32 tiles per wave along M
@@ -81,8 +85,9 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmArgs g) {
     b_off[i] = gn * (int)g.ldb + kc * 8;
     b_lds[i] = (BM + r) * LDSK + kc * 8;
   }
-  const uint16_t* Ak = g.A;  // advanced by BK per k-step
-  const uint16_t* Bk = g.B;
+  // split-K: this workgroup's K range starts at blockIdx.y * kslice
+  const uint16_t* Ak = g.A + (SPLIT ? blockIdx.y * g.kslice : 0);
+  const uint16_t* Bk = g.B + (SPLIT ? blockIdx.y * g.kslice : 0);
 
   u32x4 ra[A_CHUNKS], rb[B_CHUNKS];
 #pragma unroll
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
 
-  const int nk = g.K / BK;
+  const int nk = (SPLIT ? g.kslice : g.K) / BK;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   const int a_frag = (wm * (BM / WM) + lr) * LDSK + lk;
   const int b_frag = (BM + wn * (BN / WN) + lr) * LDSK + lk;
@@ -163,6 +168,31 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmArgs g) {
   // Epilogue.  Lane holds column lr of each 32x32 tile and rows
   // 8*(r/4) + 4*(lane/32) + r%4.
   const int row_base = m0 + wm * (BM / WM) + 4 * (lane >> 5);
+  if (SPLIT) {
+    // raw fp32 partials; SwiGLU keeps gate and up apart
+    float* P = g.part + (int64_t)blockIdx.y * g.M * (EPI == LOOP_EPI_SWIGLU ? 2 * g.N : g.N);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      int col, part = 0;
+      if (EPI == LOOP_EPI_SWIGLU) {
+        col = n0 + (wn * (BN / WN)) / 2 + (j / 2) * 32 + lr;
+        part = j & 1;
+      } else {
+        col = n0 + wn * (BN / WN) + j * 32 + lr;
+      }
+      if (col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+          if (row >= g.M) continue;
+          if (EPI == LOOP_EPI_SWIGLU) P[((int64_t)row * 2 + part) * g.N + col] = acc[i][j][r];
+          else P[(int64_t)row * g.N + col] = acc[i][j][r];
+        }
+    }
+    return;
+  }
   if (EPI == LOOP_EPI_SWIGLU) {
 #pragma unroll
     for (int j = 0; j < TN; j += 2) {
@@ -204,38 +234,80 @@ __global__ __launch_bounds__(WM * WN * 64, 1) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
-hipError_t launch_cfg(const GemmArgs& g, hipStream_t s) {
+// Sum of the split-K partials in split order, then the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int splits) {
+  const int64_t n_out = (int64_t)g.M * g.N;
+  const int64_t stride = (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * n_out;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n_out; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / g.N, col = i % g.N;
+    if (EPI == LOOP_EPI_SWIGLU) {
+      float gt = 0.f, up = 0.f;
+      for (int sp = 0; sp < splits; ++sp) {
+        gt += g.part[sp * stride + (row * 2) * g.N + col];
+        up += g.part[sp * stride + (row * 2 + 1) * g.N + col];
+      }
+      reinterpret_cast<uint16_t*>(g.C)[row * g.ldc + col] = f2bf_bits(siluf_(gt) * up);
+    } else {
+      float v = 0.f;
+      for (int sp = 0; sp < splits; ++sp) v += g.part[sp * stride + i];
+      const int64_t o = row * g.ldc + col;
+      if (EPI == LOOP_EPI_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = f2bf_bits(v);
+      else if (EPI == LOOP_EPI_F32) reinterpret_cast<float*>(g.C)[o] = v;
+      else reinterpret_cast<float*>(g.C)[o] = g.R[o] + v;
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EPI, bool SPLIT>
+hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t s) {
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? BN / 2 : BN;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + OUT_BN - 1) / OUT_BN);
   const size_t lds = 2 * (size_t)(BM + BN) * LDSK * sizeof(uint16_t);
-  auto k = gemm_kernel<BM, BN, WM, WN, EPI>;
+  auto k = gemm_kernel<BM, BN, WM, WN, EPI, SPLIT>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k, dim3(tiles), dim3(WM * WN * 64), lds, s, g);
+  hipLaunchKernelGGL(k, dim3(tiles, SPLIT ? splits : 1), dim3(WM * WN * 64), lds, s, g);
+  if (SPLIT) {
+    const int64_t n_out = (int64_t)g.M * g.N;
+    const int blocks = (int)std::min<int64_t>((n_out + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, splits);
+  }
   return hipGetLastError();
 }
 
+// Small-M calls (decode) get too few output tiles to fill the chip: split K
+// so that tiles * splits >= ~512 workgroups, if a partial buffer is given.
 template <int EPI>
-hipError_t launch_epi(const GemmArgs& g, hipStream_t s) {
-  if (g.M >= 512) return launch_cfg<256, 256, 2, 2, EPI>(g, s);
-  return launch_cfg<64, 128, 2, 2, EPI>(g, s);
+hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
+  if (g.M >= 512) return launch_cfg<256, 256, 2, 2, EPI, false>(g, 1, s);
+  constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? 64 : 128;
+  const int tiles = ((g.M + 63) / 64) * ((g.N + OUT_BN - 1) / OUT_BN);
+  int splits = 1;
+  while (tiles * splits < 512 && g.K % (64 * splits * 2) == 0 && g.K / (splits * 2) >= 256) splits *= 2;
+  const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
+  if (splits > 1 && g.part && need <= ws_bytes) {
+    g.kslice = g.K / splits;
+    return launch_cfg<64, 128, 2, 2, EPI, true>(g, splits, s);
+  }
+  return launch_cfg<64, 128, 2, 2, EPI, false>(g, 1, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-                       const float* R, int M, int N, int K, int epi, hipStream_t s) {
-  GemmArgs g{(const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, R, M, N, K, N};
+                       const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws,
+                       size_t ws_bytes) {
+  GemmArgs g{(const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, R, M, N, K, N, ws, K};
   switch (epi) {
-    case LOOP_EPI_BF16: return launch_epi<LOOP_EPI_BF16>(g, s);
-    case LOOP_EPI_F32: return launch_epi<LOOP_EPI_F32>(g, s);
-    case LOOP_EPI_F32_RES: return launch_epi<LOOP_EPI_F32_RES>(g, s);
-    case LOOP_EPI_SWIGLU: return launch_epi<LOOP_EPI_SWIGLU>(g, s);
+    case LOOP_EPI_BF16: return launch_epi<LOOP_EPI_BF16>(g, ws_bytes, s);
+    case LOOP_EPI_F32: return launch_epi<LOOP_EPI_F32>(g, ws_bytes, s);
+    case LOOP_EPI_F32_RES: return launch_epi<LOOP_EPI_F32_RES>(g, ws_bytes, s);
+    case LOOP_EPI_SWIGLU: return launch_epi<LOOP_EPI_SWIGLU>(g, ws_bytes, s);
   }
   return hipErrorInvalidValue;
 }

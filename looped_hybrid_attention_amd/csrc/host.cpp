@@ -145,7 +145,7 @@ extern "C" int32_t loop_schedule(const loop_config* c, int32_t* out, int32_t cap
 
 extern "C" int loop_op_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                             int64_t ldc, const float* R, int32_t M, int32_t N, int32_t K,
-                            int32_t epi, void* stream) {
+                            int32_t epi, float* d_ws, size_t ws_bytes, void* stream) {
   if (!A || !B || !C) return loop_fail(LOOP_EINVAL, "gemm: null operand");
   if (epi < 0 || epi > 3) return loop_fail(LOOP_EINVAL, "gemm: bad epilogue %d", epi);
   if (epi == LOOP_EPI_F32_RES && !R) return loop_fail(LOOP_EINVAL, "gemm: residual epilogue needs R");
@@ -154,7 +154,8 @@ extern "C" int loop_op_gemm(const void* A, int64_t lda, const void* B, int64_t l
     return loop_fail(LOOP_ESHAPE, "gemm: lda, ldb must be multiples of 8 and cover K; ldc >= N");
   if (((uintptr_t)A | (uintptr_t)B) % 16) return loop_fail(LOOP_EINVAL, "gemm: A and B must be 16-byte aligned");
   if (M == 0) return 0;
-  hipError_t e = launch_gemm(A, lda, B, ldb, C, ldc, R, M, N, K, epi, (hipStream_t)stream);
+  hipError_t e = launch_gemm(A, lda, B, ldb, C, ldc, R, M, N, K, epi, (hipStream_t)stream, d_ws,
+                             d_ws ? ws_bytes : 0);
   return e == hipSuccess ? 0 : loop_hip_fail(e, "gemm launch");
 }
 

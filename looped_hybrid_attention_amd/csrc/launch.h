@@ -6,8 +6,11 @@
 #include <stdint.h>
 #include "../../include/loop.h"
 
+// ws / ws_bytes: optional fp32 buffer for split-K partials (small M); NULL
+// or too small = no split.
 hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-                       const float* R, int M, int N, int K, int epi, hipStream_t s);
+                       const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws = nullptr,
+                       size_t ws_bytes = 0);
 
 hipError_t launch_synth_normal(void* dst, int64_t n, int dtype, uint32_t seed, uint32_t key,
                                int64_t start, double std, double mean, hipStream_t s);

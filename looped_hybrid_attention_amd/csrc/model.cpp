@@ -37,7 +37,8 @@ size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 struct Layout {
   size_t meta, h, hmid, x, a, s0, s1, xn, hn, proj, qbuf, obuf, act, gdn_o;
   size_t gW, gUt, gQg, gKd, gM, gC, gS;
-  size_t xf, logits, am_v, am_i, dec_part, mhc;
+  size_t xf, logits, am_v, am_i, dec_part, mhc, splitk;
+  size_t splitk_bytes;
   size_t total;
   int n_in_max, chunk_slots, n_split_max;
 };
@@ -82,6 +83,14 @@ Layout layout(const loop_config& c, int64_t M) {
   L.n_split_max = (c.max_seq + DEC_SPLIT - 1) / DEC_SPLIT;
   L.dec_part = take(B * (int64_t)c.n_q_heads * L.n_split_max * (c.head_dim + 2) * 4);
   L.mhc = take(std::max(c.loop_end - c.loop_start, 1) * 4 * 4);
+  // split-K partials of the small-M (decode) projections: up to 16 splits of
+  // [64 rows][widest output] (SwiGLU keeps gate and up: 2 x d_ff)
+  {
+    const int64_t rows = std::min<int64_t>(M, 512);
+    const int64_t widest = std::max<int64_t>({2LL * c.d_ff, (int64_t)L.n_in_max, (int64_t)c.d_model});
+    L.splitk_bytes = (size_t)(16 * rows * widest * 4);
+    L.splitk = take(L.splitk_bytes);
+  }
   L.total = off;
   return L;
 }
@@ -260,10 +269,11 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   float* x = at<float>(m, L.x);
   float* a = at<float>(m, L.a);
   const int n_in = d.full ? n_in_full(c) : n_in_gdn(c);
+#define SK at<float>(m, L.splitk), L.splitk_bytes
 
   {
     Prof p(m, LOOP_K_GEMM_IN, s);
-    HIP_TRY(launch_gemm(xn, dm, w.w_in, dm, proj, L.n_in_max, nullptr, M, n_in, dm, LOOP_EPI_BF16, s));
+    HIP_TRY(launch_gemm(xn, dm, w.w_in, dm, proj, L.n_in_max, nullptr, M, n_in, dm, LOOP_EPI_BF16, s, SK));
   }
   int mix_width;
   if (d.full) {
@@ -333,9 +343,9 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   {
     Prof p(m, LOOP_K_GEMM_O, s);
     if (!d.loop)
-      HIP_TRY(launch_gemm(obuf, mix_width, w.w_o, mix_width, hmid, dm, h, M, dm, mix_width, LOOP_EPI_F32_RES, s));
+      HIP_TRY(launch_gemm(obuf, mix_width, w.w_o, mix_width, hmid, dm, h, M, dm, mix_width, LOOP_EPI_F32_RES, s, SK));
     else
-      HIP_TRY(launch_gemm(obuf, mix_width, w.w_o, mix_width, a, dm, nullptr, M, dm, mix_width, LOOP_EPI_F32, s));
+      HIP_TRY(launch_gemm(obuf, mix_width, w.w_o, mix_width, a, dm, nullptr, M, dm, mix_width, LOOP_EPI_F32, s, SK));
   }
   {
     Prof p(m, LOOP_K_ROWS, s);
@@ -344,12 +354,12 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   }
   {
     Prof p(m, LOOP_K_GEMM_GATEUP, s);
-    HIP_TRY(launch_gemm(hn, dm, w.w_gateup, dm, act, c.d_ff, nullptr, M, c.d_ff, dm, LOOP_EPI_SWIGLU, s));
+    HIP_TRY(launch_gemm(hn, dm, w.w_gateup, dm, act, c.d_ff, nullptr, M, c.d_ff, dm, LOOP_EPI_SWIGLU, s, SK));
   }
   {
     Prof p(m, LOOP_K_GEMM_DOWN, s);
-    if (!d.loop) HIP_TRY(launch_gemm(act, c.d_ff, w.w_down, c.d_ff, h, dm, hmid, M, dm, c.d_ff, LOOP_EPI_F32_RES, s));
-    else HIP_TRY(launch_gemm(act, c.d_ff, w.w_down, c.d_ff, a, dm, a, M, dm, c.d_ff, LOOP_EPI_F32_RES, s));
+    if (!d.loop) HIP_TRY(launch_gemm(act, c.d_ff, w.w_down, c.d_ff, h, dm, hmid, M, dm, c.d_ff, LOOP_EPI_F32_RES, s, SK));
+    else HIP_TRY(launch_gemm(act, c.d_ff, w.w_down, c.d_ff, a, dm, a, M, dm, c.d_ff, LOOP_EPI_F32_RES, s, SK));
   }
   Prof prow(m, LOOP_K_ROWS, s);
 
@@ -452,7 +462,7 @@ int head_logits(loop_model* m, const Call& k, float* logits, hipStream_t s) {
   Prof p(m, LOOP_K_HEAD, s);
   HIP_TRY(launch_rmsnorm(at<float>(m, L.h), nullptr, k.d_last, c.d_model, m->final_norm, xf, k.B, c.d_model, c.eps, s));
   HIP_TRY(launch_gemm(xf, c.d_model, m->head, c.d_model, logits, c.vocab, nullptr, k.B, c.vocab, c.d_model,
-                      LOOP_EPI_F32, s));
+                      LOOP_EPI_F32, s, at<float>(m, L.splitk), L.splitk_bytes));
   return 0;
 }
 

@@ -109,3 +109,42 @@ def test_gemm_real_shapes_sampled(M, N, K, epi):
         assert rel_err(got, ref) < 2 ** -7
     else:
         assert rel_err(got, gu) < (2 ** -8 if epi == 0 else 1e-5)
+
+
+# The decode projections (64 sequences): split-K with fp32 partials summed in
+# split order, against the float64 product; also bit-identical reruns.
+DECODE = [(64, 10240, 4096, 0), (64, 8224, 4096, 0), (64, 4096, 4096, 2), (64, 4096, 2048, 1),
+          (64, 12288, 4096, 3), (64, 4096, 12288, 2), (1, 4096, 12288, 2), (37, 520, 768, 3)]
+
+
+@pytest.mark.parametrize("M,N,K,epi", DECODE)
+def test_gemm_split_k(M, N, K, epi):
+    import looped_hybrid_attention_amd as L
+    torch = torch_cuda()
+    say("gemm split-k", M, N, K, epi)
+    nB = 2 * N if epi == 3 else N
+    a, b = _inputs(M, N, K, f"sk{N}.{K}", nB=nB)
+    ref = _ref(a, b)
+    A, B = dev(a, torch), dev(b, torch)
+    ws = torch.empty(16 * M * 2 * N, dtype=torch.float32, device="cuda")
+    outs = []
+    for rep in range(2):
+        C = torch.zeros((M, N), dtype=torch.bfloat16 if epi in (0, 3) else torch.float32, device="cuda")
+        R = None
+        if epi == 2:
+            r = synth.normal(synth.SEED_X, f"gemmRsk{N}", (M, N), 1.0)
+            C.copy_(dev(r, torch))
+            R = C
+        L.loop_op_gemm(A.data_ptr(), K, B.data_ptr(), K, C.data_ptr(), N, R.data_ptr() if R is not None else 0,
+                       M, N, K, epi, stream(torch), ws.data_ptr(), ws.numel() * 4)
+        torch.cuda.synchronize()
+        outs.append(host(C))
+    assert np.array_equal(outs[0], outs[1])
+    got = outs[0]
+    if epi == 3:
+        g, u = ref[:, :N], ref[:, N:]
+        assert rel_err(got, g / (1 + np.exp(-g)) * u) < 2 ** -7
+    elif epi == 2:
+        assert rel_err(got, ref + r) < 1e-5
+    else:
+        assert rel_err(got, ref) < (2 ** -8 if epi == 0 else 1e-5)
