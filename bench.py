@@ -16,6 +16,7 @@ with N > 1 exits: this build runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,6 +31,37 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PREFILL_T = 8192
 DECODE_B, DECODE_CTX = 64, 32768
 
+# HBM bytes per launch of the roofline kernels, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes scaled by the same counters on a plain 1 GiB copy
+# (--copy-calibration).  Each record carries the SHA-256 of the sources the
+# kernel was built from; once they change the figure no longer applies and
+# ``traffic`` is reported as null.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CSRC = os.path.join(ROOT, "looped_hybrid_attention_amd", "csrc")
+TRAFFIC_SOURCES = {
+    "gemm_gateup": ["gemm.hip", "common.h"],
+    "decode_attn": ["attention.hip", "common.h"],
+}
+
+
+def sources_sha256(key: str) -> str:
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES[key]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key: str):
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)[key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256(key):
+        return None
+    return rec["hbm_bytes_per_launch"]
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -39,8 +71,11 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=128)
     p.add_argument("--decode-warmup", type=int, default=3)
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-prefill", action="store_true", help="decode only (for kernel profiles)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run one plain 1 GiB device-to-device copy (scale for HBM byte counters)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return p.parse_args()
 
 
@@ -102,6 +137,14 @@ def main():
     kinds_exec = ["full" if r[1] else "gdn" for r in sched]
     stream = torch.cuda.current_stream().cuda_stream
 
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # weights drawn on the device by the seeded generator (same stream names
     # and recipe as the host generator)
     t0 = time.time()
@@ -131,32 +174,35 @@ def main():
         L.loop_prefill(model, 1, PREFILL_T, [0], [0], d_tokens=ids.data_ptr(), d_logits=logits.data_ptr(),
                        stream=stream)
 
-    for _ in range(args.warmup):
-        prefill_step()
-    torch.cuda.synchronize()
-    L.loop_profile(model, L.LOOP_K["gemm_gateup"])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        prefill_step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    k_ms, k_n = L.loop_profile_read(model)
-    L.loop_profile(model, -1)
-    assert torch.isfinite(logits).all().item(), "non-finite logits"
-    fl = prefill_flops(dims, kinds_exec, PREFILL_T)
-    tok_s = PREFILL_T / (ms_step / 1e3)
-    k_avg_ms = k_ms / max(k_n, 1)
-    k_flop = 2 * PREFILL_T * (2 * dims["d_ff"]) * dims["d_model"]
-    k_tflops = k_flop / (k_avg_ms / 1e3) / 1e12
-    roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "gemm_kernel<256,256,2,2,SWIGLU> (gate/up projection + SwiGLU epilogue)",
-                "launch_ms": round(k_avg_ms, 4), "launches": k_n,
-                "algorithmic_flop_per_launch": k_flop}
-    step_frac = fl["total"] / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS
+    tok_s = ms_step = step_frac = roofline = fl = None
+    if not args.no_prefill:
+        for _ in range(args.warmup):
+            prefill_step()
+        torch.cuda.synchronize()
+        L.loop_profile(model, L.LOOP_K["gemm_gateup"])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            prefill_step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_step = e0.elapsed_time(e1) / args.steps
+        k_ms, k_n = L.loop_profile_read(model)
+        L.loop_profile(model, -1)
+        assert torch.isfinite(logits).all().item(), "non-finite logits"
+        fl = prefill_flops(dims, kinds_exec, PREFILL_T)
+        tok_s = PREFILL_T / (ms_step / 1e3)
+        k_avg_ms = k_ms / max(k_n, 1)
+        k_flop = 2 * PREFILL_T * (2 * dims["d_ff"]) * dims["d_model"]
+        k_tflops = k_flop / (k_avg_ms / 1e3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic("gemm_gateup"),
+                    "kernel": "gemm_kernel<256,256,2,4,SWIGLU> (gate/up projection + SwiGLU epilogue)",
+                    "launch_ms": round(k_avg_ms, 4), "launches": k_n,
+                    "algorithmic_flop_per_launch": k_flop}
+        step_frac = fl["total"] / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS
 
     # ------------------------------------------------------------- decode
     decode = None
@@ -213,7 +259,8 @@ def main():
                   "hbm_frac_step": round(by["total"] / (dms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
                   "algorithmic_bytes_per_step": by["total"],
                   "roofline": {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": PEAK_HBM_GBS,
-                               "unit": "GB/s", "frac": round(a_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                               "unit": "GB/s", "frac": round(a_gbs / PEAK_HBM_GBS, 4),
+                               "traffic": measured_traffic("decode_attn"),
                                "kernel": "decode_attn_kernel<256,4> + combine (split-L attention)",
                                "launch_ms": round(a_avg, 4), "launches": a_n,
                                "algorithmic_bytes_per_launch": kv_launch}}
@@ -227,12 +274,12 @@ def main():
 
     out = {
         "metric": "prefill tok/s through 56-exec looped stack + decode tok/s; % MFMA/HBM peak",
-        "value": round(tok_s, 1),
+        "value": round(tok_s, 1) if tok_s else None,
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 3),
+        "ms_per_step": round(ms_step, 3) if ms_step else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -240,8 +287,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) bf16 weights, uniform token ids)",
         "config": {"workload": "full_prefill_8192", "model": "looped hybrid decoder, 32 layers x 56 executions",
                    "global_batch": 1, "seq_len": PREFILL_T, "parallelism": "none (1 GPU)"},
-        "mfma_frac_step": round(step_frac, 4),
-        "algorithmic_flop_per_step": fl["total"],
+        "mfma_frac_step": round(step_frac, 4) if step_frac else None,
+        "algorithmic_flop_per_step": fl["total"] if fl else None,
         "roofline": roofline,
         "decode": decode,
         "cpu_baseline": cpu,

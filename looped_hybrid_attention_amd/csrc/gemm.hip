@@ -284,7 +284,9 @@ hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t s) {
 // so that tiles * splits >= ~512 workgroups, if a partial buffer is given.
 template <int EPI>
 hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
-  if (g.M >= 512) return launch_cfg<256, 256, 2, 2, EPI, false>(g, 1, s);
+  // Large M: 256 x 256 tiles, eight waves (two per SIMD, so that one wave's
+  // barrier and load waits are covered by the other's MFMAs).
+  if (g.M >= 512) return launch_cfg<256, 256, 2, 4, EPI, false>(g, 1, s);
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? 64 : 128;
   const int tiles = ((g.M + 63) / 64) * ((g.N + OUT_BN - 1) / OUT_BN);
   int splits = 1;
