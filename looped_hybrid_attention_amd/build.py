@@ -66,8 +66,10 @@ def build(jobs: int = 8) -> str:
     clang = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang++")
     if not os.path.exists(clang):
         clang = "/opt/rocm/lib/llvm/bin/clang++"
+    # -z defs: an unresolved symbol (e.g. a kernel whose host stub the
+    # compiler did not emit) fails the link instead of the first dlopen
     subprocess.run([clang, "-shared", "-fPIC", "-o", tmp, *objs, "-L", rt, "-l:libamdhip64.so",
-                    "-Wl,-rpath," + rt], check=True)
+                    "-Wl,-rpath," + rt, "-Wl,-z,defs"], check=True)
     os.replace(tmp, LIB)
     return LIB
 

@@ -95,37 +95,114 @@ __global__ __launch_bounds__(256) void qk_prep_kernel(AttnPrepArgs a) {
 }
 
 // ------------------------------------------------------- flash prefill
-// Workgroup = (32-query tile, KV head, sequence); G waves, wave w = query head
-// kvh*G + w.  Lane (h = lane/32, q = lane%32) owns query q of the tile.
+// Workgroup = (query tile, KV head, sequence) with W = max(G, 4) waves; wave
+// w takes query head kvh*G + w%G and 32 queries (w/G)*32 .. of the tile of
+// QT = 32*W/G queries.  Lane (h = lane/32, q = lane%32) owns query q.
 // S^T = K . Q^T (32 keys x 32 queries per MFMA tile) leaves each lane with
 // the scores of its own query, so the online softmax is lane-local (plus one
-// exchange with lane ^ 32) and the probabilities feed O^T += V^T . P^T as the
-// B operand without leaving registers; the key order inside a 16-key MFMA
-// step is permuted identically on both operands.
-constexpr int KT = 64;          // keys per LDS tile
+// exchange with lane ^ 32), and the probabilities feed O^T += V^T . P^T as
+// the B operand straight from registers.  That operand wants keys
+// 16j + 8h .. +8 of 16-key step j in lane (q, h), while the score MFMA leaves
+// the lane rows 8(r/4) + 4h + r%4; storing the K rows in LDS with bits 2 and
+// 3 of their in-tile index swapped makes the two coincide.
+//
+// K [64 keys][D] and V^T [D][64 keys] tiles go global -> LDS directly
+// (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS, lane i
+// at byte 16 i), double-buffered: the next tile's copies are issued before
+// the current tile's MFMAs, waited for and fenced by one barrier after them.
+// Rows are unpadded and their 16-byte chunks swizzled so that the operand
+// reads of 16 consecutive rows (one LDS cycle of a 128-bit read: 64 banks)
+// hit distinct banks: chunk c of K row r sits at c ^ (r % 16) (512-byte rows),
+// chunk c of V^T row d at c ^ ((d / 2) % 8) (128-byte rows, two per bank
+// sweep).  The loads pick their global source to realise both the swizzle and
+// the K row order.
+constexpr int KT = 64;  // keys per LDS tile
 template <int D>
 struct FlashLds {
-  static constexpr int KS = D + 8;   // padded K row (bf16)
-  static constexpr int VS = KT + 8;  // padded V^T row (bf16)
-  static constexpr int bytes = (KT * KS + D * VS) * 2;
+  static constexpr int KROW = D * 2;                   // bytes per K row
+  static constexpr int VROW = KT * 2;                  // bytes per V^T row
+  static constexpr int STAGE = KT * KROW + D * VROW;   // bytes per buffer
+  static constexpr int bytes = 2 * STAGE;
 };
+DEV int swap_bits23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+template <int CR>
+DEV int k_swz(int r) { return CR >= 16 ? (r & 15) : (r & 7); }
+DEV int v_swz(int d) { return (d >> 1) & 7; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+// Raw buffer resource over `bytes` bytes at `base` (word 3: 32-bit data
+// format, no swizzle, as CDNA expects for raw buffer loads).
+DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16-byte copy global -> LDS: lane i's 16 bytes at `src` + voffset land at
+// LDS byte `dst` + 16 i (dst wave-uniform).
+DEV void copy16_to_lds(__amdgpu_buffer_rsrc_t src, int voffset, lds_void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, voffset, 0, 0, 0);
+}
+
+// Probabilities of a score tile against reference max m (log2 units), their
+// row sum into l, and O^T += V^T . P^T over the tile's 64 keys in 4 steps of
+// 16 (V^T fragment reads FD steps ahead of the MFMAs).  `vr` = the lane's
+// V^T row in LDS (swizzle vsw).
+template <int NDT, int FD, int VROW>
+DEV void flash_pv(f32x16 (&o)[NDT], f32x16 (&s)[2], float& l, float m, float scale, const uint8_t* vr, int h,
+                  int vsw) {
+  float lsum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], scale, -m));
+      s[kt][r] = p;
+      lsum += p;
+    }
+  l += __shfl_xor(lsum, 32, 64) + lsum;
+  bf16x8 pf[4];
+#pragma unroll
+  for (int ks2 = 0; ks2 < 4; ++ks2)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[ks2][e] = f2bf(s[ks2 >> 1][(ks2 & 1) * 8 + e]);
+  bf16x8 vf[4 * NDT];
+#define FLASH_VREAD(g_) \
+  vf[g_] = *reinterpret_cast<const bf16x8*>(vr + ((g_) % NDT) * 32 * VROW + (((2 * ((g_) / NDT) + h) ^ vsw) << 4))
+#pragma unroll
+  for (int g = 0; g < FD; ++g) FLASH_VREAD(g);
+#pragma unroll
+  for (int g = 0; g < 4 * NDT; ++g) {
+    if (g + FD < 4 * NDT) FLASH_VREAD(g + FD);
+    o[g % NDT] = mfma32x32x16(vf[g], pf[g / NDT], o[g % NDT]);
+  }
+#undef FLASH_VREAD
+  __builtin_amdgcn_sched_group_barrier(0x100, FD, 0);
+#pragma unroll
+  for (int g = 0; g < 4 * NDT; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (g + FD < 4 * NDT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
 
 template <int D, int G>
-__global__ __launch_bounds__(64 * G, 1) void flash_prefill_kernel(FlashArgs a) {
-  constexpr int NT = 64 * G;
+__global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(FlashArgs a) {
+  constexpr int W = G < 4 ? 4 : G;
+  constexpr int QT = 32 * W / G;
   constexpr int NKS = D / 16;  // 16-dim MFMA steps of Q.K
   constexpr int NDT = D / 32;  // 32-dim output tiles
+  constexpr int CR = D / 8;    // 16-byte chunks per K row
+  constexpr int KI = KT * CR / 64 / W;  // K copy instructions per wave and tile
+  constexpr int VI = D * 8 / 64 / W;    // V^T copy instructions per wave and tile
+  static_assert(KI * 64 * W == KT * CR && VI * 64 * W == D * 8, "tile / wave split");
+  static_assert(CR >= 8, "swizzle needs 8 chunks per row");
+  constexpr int FD = 4;  // LDS operand reads in flight ahead of the MFMAs
   using L = FlashLds<D>;
-  extern __shared__ __align__(16) uint16_t flash_smem[];
-  uint16_t* sK = flash_smem;
-  uint16_t* sV = flash_smem + KT * L::KS;
+  extern __shared__ __align__(16) uint8_t flash_smem[];
 
   const int tile = (gridDim.x - 1) - blockIdx.x;  // heaviest (latest) tiles first
   const int kvh = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int h = lane >> 5, ql = lane & 31;
-  const int head = kvh * G + wave;
-  const int t = tile * 32 + ql;
+  const int head = kvh * G + wave % G;
+  const int t = tile * QT + (wave / G) * 32 + ql;
   const bool qvalid = t < a.T;
   const int p0 = a.pos[b];
   const int qpos = p0 + t;
@@ -134,13 +211,60 @@ __global__ __launch_bounds__(64 * G, 1) void flash_prefill_kernel(FlashArgs a) {
   const uint16_t* Kc = a.k_cache + (slot_b * a.Hkv + kvh) * (int64_t)a.max_seq * D;
   const uint16_t* Vc = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq;
   const int L_valid = p0 + a.T;
+  const int kv_end = p0 + min(a.T, (tile + 1) * QT);
+  const int nkt = (kv_end + KT - 1) / KT;
+
+  // Global element offsets (from the tile's first key) of this lane's chunk
+  // in each copy instruction of the wave.
+  int k_src[KI], v_src[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int n = wave * KI + i;  // instruction index within the tile
+    const int r = (n * 64 + lane) / CR, p = (n * 64 + lane) % CR;
+    const int key = (r & ~31) | swap_bits23(r & 31);
+    k_src[i] = key * D + (p ^ k_swz<CR>(r)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int n = wave * VI + i;
+    const int d = (n * 64 + lane) / 8, p = (n * 64 + lane) % 8;
+    v_src[i] = d * a.max_seq + (p ^ v_swz(d)) * 8;
+  }
+  // Buffer resources over this (sequence, KV head)'s K and V^T blocks.  The
+  // MUBUF form of the LDS copy keeps the compiler's LDS-read waits counted
+  // (the FLAT form makes it wait for every outstanding LDS read).
+  const auto k_rsrc = buffer_rsrc(Kc, a.max_seq * D * 2);
+  const auto v_rsrc = buffer_rsrc(Vc, a.max_seq * D * 2);
+#define FLASH_COPY(k0_, stage_)                                                               \
+  {                                                                                           \
+    uint8_t* S_ = flash_smem + (stage_) * L::STAGE;                                           \
+    _Pragma("unroll") for (int i = 0; i < KI; ++i)                                            \
+        copy16_to_lds(k_rsrc, ((k0_) * D + k_src[i]) * 2, (lds_void*)(S_ + (wave * KI + i) * 1024)); \
+    _Pragma("unroll") for (int i = 0; i < VI; ++i)                                            \
+        copy16_to_lds(v_rsrc, ((k0_) + v_src[i]) * 2,                                        \
+                      (lds_void*)(S_ + KT * L::KROW + (wave * VI + i) * 1024));               \
+  }
+  // V^T keys at or past L_valid may hold anything; P is 0 there but 0 * NaN
+  // is not, so they are zeroed once the tile holding them has landed.
+#define FLASH_ZERO_TAIL(k0_, stage_)                                                         \
+  {                                                                                          \
+    uint8_t* V_ = flash_smem + (stage_) * L::STAGE + KT * L::KROW;                           \
+    const int first = max(L_valid - (k0_), 0);                                               \
+    for (int d = tid; d < D; d += 64 * W)                                                    \
+      for (int kk = first; kk < KT; ++kk)                                                    \
+        *reinterpret_cast<uint16_t*>(V_ + d * L::VROW + (((kk >> 3) ^ v_swz(d)) << 4) + (kk & 7) * 2) = 0; \
+  }
+  // vmcnt(0): this wave's LDS copies have landed
+#define FLASH_WAIT_COPIES() __builtin_amdgcn_s_waitcnt(0x0F70)
+
+  FLASH_COPY(0, 0);
 
   bf16x8 qf[NKS];
   {
     const uint16_t* qs = a.q + (m * a.Hq + head) * D;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      uint4 v = qvalid ? *reinterpret_cast<const uint4*>(qs + ks * 16 + h * 8) : make_uint4(0, 0, 0, 0);
+      u32x4 v = qvalid ? *reinterpret_cast<const u32x4*>(qs + ks * 16 + h * 8) : (u32x4){0, 0, 0, 0};
       qf[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -149,94 +273,107 @@ __global__ __launch_bounds__(64 * G, 1) void flash_prefill_kernel(FlashArgs a) {
   for (int i = 0; i < NDT; ++i) o[i] = (f32x16){};
   float m_i = -1e30f, l_i = 0.f;
   const float scale = a.scale_log2;
-
-  const int last_t = min(a.T, tile * 32 + 32) - 1;
-  const int kv_end = min(p0 + last_t + 1, L_valid);
-  for (int k0 = 0; k0 < kv_end; k0 += KT) {
+  const int ksw = k_swz<CR>(ql), vsw = v_swz(ql);  // swizzles of the rows this lane reads
+  const int qpos_lo = p0 + tile * QT + (wave / G) * 32;  // first query of the wave
+  FLASH_WAIT_COPIES();
+  __syncthreads();
+  if (KT > L_valid) {
+    FLASH_ZERO_TAIL(0, 0);
     __syncthreads();
-    // K tile: 64 keys x D
-    for (int c = threadIdx.x; c < KT * D / 8; c += NT) {
-      const int key = c / (D / 8), dc = c % (D / 8);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (k0 + key < L_valid) v = *reinterpret_cast<const uint4*>(Kc + (int64_t)(k0 + key) * D + dc * 8);
-      *reinterpret_cast<uint4*>(sK + key * L::KS + dc * 8) = v;
-    }
-    // V^T tile: D rows x 64 keys
-    for (int c = threadIdx.x; c < D * KT / 8; c += NT) {
-      const int d = c / (KT / 8), kc = c % (KT / 8);
-      const int kk = k0 + kc * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kk < L_valid) {
-        v = *reinterpret_cast<const uint4*>(Vc + (int64_t)d * a.max_seq + kk);
-        if (kk + 8 > L_valid) {
-          uint16_t* e = reinterpret_cast<uint16_t*>(&v);
+  }
+
+  // Tile loop.  The reference max moves rarely; when a tile needs it moved
+  // the inner loop is left, O and l are rescaled outside it and the tile is
+  // finished there, so that inside the loop O is only ever an MFMA
+  // accumulator (no copies out of the accumulation registers).
+  f32x16 s[2];
+  float mloc;
+  bool bump;
+#define FLASH_SYNC(j_)                                                 \
+  {                                                                    \
+    FLASH_WAIT_COPIES();                                               \
+    __syncthreads();                                                   \
+    if ((j_) + 1 < nkt && ((j_) + 2) * KT > L_valid) {                 \
+      FLASH_ZERO_TAIL(((j_) + 1) * KT, ((j_) + 1) & 1);                \
+      __syncthreads();                                                 \
+    }                                                                  \
+  }
+  int j = 0;
+  for (;;) {
+    for (; j < nkt; ++j) {
+      const uint8_t* sK = flash_smem + (j & 1) * L::STAGE;
+      const int k0 = j * KT;
+      if (j + 1 < nkt) FLASH_COPY(k0 + KT, (j + 1) & 1);
+
+      // S^T for the two 32-key halves: 2 NKS MFMAs, the K fragment reads
+      // kept FD steps ahead of them
+      s[0] = (f32x16){};
+      s[1] = (f32x16){};
+      {
+        const uint8_t* kr = sK + ql * L::KROW;
+        bf16x8 kf[2 * NKS];
+#define FLASH_KREAD(g_) \
+  kf[g_] = *reinterpret_cast<const bf16x8*>(kr + ((g_) / NKS) * 32 * L::KROW + (((2 * ((g_) % NKS) + h) ^ ksw) << 4))
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (kk + j >= L_valid) e[j] = 0;
+        for (int g = 0; g < FD; ++g) FLASH_KREAD(g);
+#pragma unroll
+        for (int g = 0; g < 2 * NKS; ++g) {
+          if (g + FD < 2 * NKS) FLASH_KREAD(g + FD);
+          s[g / NKS] = mfma32x32x16(kf[g], qf[g % NKS], s[g / NKS]);
+        }
+#undef FLASH_KREAD
+        __builtin_amdgcn_sched_group_barrier(0x100, FD, 0);
+#pragma unroll
+        for (int g = 0; g < 2 * NKS; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (g + FD < 2 * NKS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
-      *reinterpret_cast<uint4*>(sV + d * L::VS + kc * 8) = v;
+      // causal mask, only on tiles that reach past the wave's first query;
+      // register r of half kt holds key k0 + 32 kt + swap_bits23(8 (r/4) + 4 h + r%4)
+      if (k0 + KT - 1 > qpos_lo) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kt * 32 + swap_bits23(8 * (r >> 2) + 4 * h + (r & 3));
+            s[kt][r] = (key <= qpos) ? s[kt][r] : -1e30f;
+          }
+      }
+      // online softmax, lane-local for query ql (plus lane ^ 32), in log2
+      // units.  The reference max m_i moves only when a tile's max exceeds
+      // it by more than 8, so probabilities stay below 2^8 (O and l share
+      // the reference: their ratio is exact).  Key 0 is in every query's
+      // range, so the first tile sets m_i.
+      mloc = -1e30f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * scale;
+      bump = mloc > m_i + 8.f;
+      if (__builtin_amdgcn_read_exec() & __ballot(bump)) break;
+      flash_pv<NDT, FD, L::VROW>(o, s, l_i, m_i, scale, sK + KT * L::KROW + ql * L::VROW, h, vsw);
+      FLASH_SYNC(j);
     }
-    __syncthreads();
-
-    f32x16 s[2];
+    if (j >= nkt) break;
+    {
+      const float m_new = bump ? mloc : m_i;
+      const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
+      l_i *= alpha;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      s[kt] = (f32x16){};
-      const uint16_t* kr = sK + (kt * 32 + ql) * L::KS + h * 8;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        bf16x8 kf = *reinterpret_cast<const bf16x8*>(kr + ks * 16);
-        s[kt] = mfma32x32x16(kf, qf[ks], s[kt]);
-      }
+      for (int i = 0; i < NDT; ++i) o[i] *= alpha;
+      m_i = m_new;
     }
-    // mask + online softmax (lane-local for query ql)
-    float mloc = -1e30f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + kt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        float v = s[kt][r] * scale;
-        v = (key <= qpos) ? v : -1e30f;
-        s[kt][r] = v;
-        mloc = fmaxf(mloc, v);
-      }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_i, mloc);
-    const float alpha = exp2f(m_i - m_new);
-    float lsum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = s[kt][r] > -1e29f ? exp2f(s[kt][r] - m_new) : 0.f;
-        s[kt][r] = p;
-        lsum += p;
-      }
-    lsum += __shfl_xor(lsum, 32, 64);
-    l_i = l_i * alpha + lsum;
-    m_i = m_new;
-#pragma unroll
-    for (int i = 0; i < NDT; ++i) o[i] *= alpha;
-    // O^T += V^T . P^T over the 64 keys in 4 steps of 16
-#pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2) {
-      const int kt = ks2 >> 1, sh = (ks2 & 1) * 8;
-      bf16x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = f2bf(s[kt][sh + e]);
-      const uint16_t* vr = sV + ql * L::VS + ks2 * 16 + 4 * h;
-#pragma unroll
-      for (int i = 0; i < NDT; ++i) {
-        const uint16_t* vp = vr + i * 32 * L::VS;
-        uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
-        uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        o[i] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), pf, o[i]);
-      }
-    }
+    flash_pv<NDT, FD, L::VROW>(o, s, l_i, m_i, scale, flash_smem + (j & 1) * L::STAGE + KT * L::KROW + ql * L::VROW,
+                               h, vsw);
+    FLASH_SYNC(j);
+    ++j;
   }
+#undef FLASH_SYNC
+#undef FLASH_COPY
+#undef FLASH_ZERO_TAIL
+#undef FLASH_WAIT_COPIES
   if (!qvalid) return;
   const float inv_l = 1.f / l_i;
   const uint16_t* g = a.gate + m * a.gate_stride + head * D;
@@ -445,7 +582,9 @@ hipError_t flash_dg(const FlashArgs& a, int B, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(k, dim3((a.T + 31) / 32, a.Hkv, B), dim3(64 * G), lds, s, a);
+  constexpr int W = G < 4 ? 4 : G;
+  constexpr int QT = 32 * W / G;
+  hipLaunchKernelGGL(k, dim3((a.T + QT - 1) / QT, a.Hkv, B), dim3(64 * W), lds, s, a);
   return hipGetLastError();
 }
 

@@ -16,15 +16,11 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define DEV __device__ __forceinline__
 
 // bf16 <-> fp32.  bf16 -> fp32 is exact (shift); fp32 -> bf16 rounds to
-// nearest even (inputs here are finite).
+// nearest even (gfx950's v_cvt_pk_bf16_f32).
 DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 DEV float bf2f(bf16 b) { return (float)b; }
-DEV uint16_t f2bf_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  return (uint16_t)u;
-}
-DEV bf16 f2bf(float f) { return __builtin_bit_cast(bf16, f2bf_bits(f)); }
+DEV bf16 f2bf(float f) { return (bf16)f; }
+DEV uint16_t f2bf_bits(float f) { return __builtin_bit_cast(uint16_t, f2bf(f)); }
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%32][(l/32)*8 .. +8]
 // and B^T[l%32][(l/32)*8 .. +8] (k-contiguous); the 16 results of lane l are
