@@ -59,6 +59,65 @@ DEV void mm_tn(f32x4& acc, const float* A, int lda, const float* B, int ldb, int
   for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k * lda], b[k * ldb], acc);
 }
 
+// Two products in one pass (independent MFMA chains, so the second issues
+// while the first is in flight).
+// acc0 += A0[0:16, 0:K] . B[0:16, 0:K]^T, acc1 += A1[0:16, 0:K] . B[0:16, 0:K]^T
+DEV void mm_nt2(f32x4& acc0, f32x4& acc1, const float* A0, const float* A1, int lda, const float* B, int ldb,
+                int K) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a0 = A0 + i * lda + kk;
+  const float* a1 = A1 + i * lda + kk;
+  const float* b = B + i * ldb + kk;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 4) {
+    const float bk = b[k];
+    acc0 = mfma16x16x4f32(a0[k], bk, acc0);
+    acc1 = mfma16x16x4f32(a1[k], bk, acc1);
+  }
+}
+// acc0 += A0[0:16, 0:K] . B0[0:K, 0:16], acc1 += A1[0:16, 0:K] . B1[0:K, 0:16]
+DEV void mm_nn2(f32x4& acc0, f32x4& acc1, const float* A0, const float* A1, int lda, const float* B0,
+                const float* B1, int ldb, int K) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a0 = A0 + i * lda + kk;
+  const float* a1 = A1 + i * lda + kk;
+  const float* b0 = B0 + kk * ldb + i;
+  const float* b1 = B1 + kk * ldb + i;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 4) {
+    acc0 = mfma16x16x4f32(a0[k], b0[k * ldb], acc0);
+    acc1 = mfma16x16x4f32(a1[k], b1[k * ldb], acc1);
+  }
+}
+
+// acc += A[0:16, 0:K] . B[0:16, 0:K]^T as two interleaved chains (K % 8 == 0)
+DEV void mm_nt_ilp(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a = A + i * lda + kk;
+  const float* b = B + i * ldb + kk;
+  f32x4 acc1 = {0, 0, 0, 0};
+#pragma unroll 8
+  for (int k = 0; k < K; k += 8) {
+    acc = mfma16x16x4f32(a[k], b[k], acc);
+    acc1 = mfma16x16x4f32(a[k + 4], b[k + 4], acc1);
+  }
+  acc += acc1;
+}
+// acc0 += A[0:K, 0:16]^T . B0[0:K, 0:16], acc1 += A[0:K, 0:16]^T . B1[0:K, 0:16]
+DEV void mm_tn2(f32x4& acc0, f32x4& acc1, const float* A, int lda, const float* B0, const float* B1, int ldb,
+                int K) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a = A + kk * lda + i;
+  const float* b0 = B0 + kk * ldb + i;
+  const float* b1 = B1 + kk * ldb + i;
+#pragma unroll 8
+  for (int k = 0; k < K; k += 4) {
+    const float ak = a[k * lda];
+    acc0 = mfma16x16x4f32(ak, b0[k * ldb], acc0);
+    acc1 = mfma16x16x4f32(ak, b1[k * ldb], acc1);
+  }
+}
+
 // Chunk workspace layout, per (seq b, head h, chunk c), fp32:
 //   W, Ut, Kd, Qp, Up: [CH][DK] each, then gC; S_c (entry state) [DV][DK].
 struct ChunkPtr {
@@ -88,6 +147,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   constexpr int DV = DK;
   constexpr int LD = DK + 4;   // [CH][DK] rows
   constexpr int LC = CH + 4;   // [CH][CH] rows
+  constexpr int XS = 20;       // rows of the 16x16 inverse scratch
   extern __shared__ __align__(16) float gsm[];
   float* sQ = gsm;                 // q^ ; later unchanged
   float* sK = sQ + CH * LD;        // k^ ; later W
@@ -97,6 +157,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   float* sM = sT2 + CH * LC;       // Mqk
   float* sG = sM + CH * LC;        // cumulative log alpha
   float* sB = sG + CH;             // beta
+  float* sEG = sB + CH;            // exp(G_r)
+  float* sEK = sEG + CH;           // exp(G_C - G_r)
+  float* sX = sEK + CH;            // [4][16][XS] products of the blocked inverse
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = c * CH;
   const int C = min(CH, a.T - t0);
@@ -104,31 +167,54 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   const int64_t row0 = (int64_t)b * a.T + t0;
   const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
 
-  for (int r = wave; r < CH; r += NT / 64) {
-    float qv[DK / 64], kv[DK / 64];
-    float sq = 0.f, sk = 0.f;
+  // q, k, v of the chunk's rows: 4 threads per row, DK/4 dims each, every
+  // load issued before any is used; q and k L2-normalised per row.
+  {
+    static_assert(CH * 4 == NT, "4 threads per row");
+    constexpr int PER = DK / 4;      // dims per thread
+    constexpr int NV = PER / 8;      // 16-byte loads per tensor
+    const int r = tid >> 2, part = tid & 3;
     const bool ok = r < C;
-    const uint16_t* pr = a.proj + (row0 + r) * a.proj_stride;
+    const uint16_t* pr = a.proj + (row0 + min(r, C - 1)) * a.proj_stride;
+    const int d0 = part * PER;
+    u32x4 vq[NV], vk[NV], vv[NV];
 #pragma unroll
-    for (int e = 0; e < DK / 64; ++e) {
-      const int d = lane + 64 * e;
-      qv[e] = ok ? bf2f(pr[a.off_q + h * DK + d]) : 0.f;
-      kv[e] = ok ? bf2f(pr[a.off_k + h * DK + d]) : 0.f;
-      sq += qv[e] * qv[e];
-      sk += kv[e] * kv[e];
-      sV[r * LD + d] = ok ? bf2f(pr[a.off_v + h * DV + d]) : 0.f;
+    for (int i = 0; i < NV; ++i) {
+      vq[i] = *reinterpret_cast<const u32x4*>(pr + a.off_q + h * DK + d0 + 8 * i);
+      vk[i] = *reinterpret_cast<const u32x4*>(pr + a.off_k + h * DK + d0 + 8 * i);
+      vv[i] = *reinterpret_cast<const u32x4*>(pr + a.off_v + h * DV + d0 + 8 * i);
     }
-    sq = wave_sum(sq);
-    sk = wave_sum(sk);
-    const float iq = rsqrtf(sq + a.eps) * a.q_scale, ik = rsqrtf(sk + a.eps);
+    float av = 0.f, bv = 0.f;
+    if (part == 0) {
+      av = bf2f(pr[a.off_a + h]);
+      bv = bf2f(pr[a.off_b + h]);
+    }
+    float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < DK / 64; ++e) {
-      sQ[r * LD + lane + 64 * e] = qv[e] * iq;
-      sK[r * LD + lane + 64 * e] = kv[e] * ik;
-    }
-    if (lane == 0) {
-      const float av = ok ? bf2f(pr[a.off_a + h]) : 0.f;
-      const float bv = ok ? bf2f(pr[a.off_b + h]) : 0.f;
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float q = bf2f((uint16_t)(vq[i][e >> 1] >> ((e & 1) * 16)));
+        const float k = bf2f((uint16_t)(vk[i][e >> 1] >> ((e & 1) * 16)));
+        sq += q * q;
+        sk += k * k;
+      }
+    sq += __shfl_xor(sq, 1, 64);
+    sq += __shfl_xor(sq, 2, 64);
+    sk += __shfl_xor(sk, 1, 64);
+    sk += __shfl_xor(sk, 2, 64);
+    const float iq = ok ? rsqrtf(sq + a.eps) * a.q_scale : 0.f;
+    const float ik = ok ? rsqrtf(sk + a.eps) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = d0 + 8 * i + e;
+        sQ[r * LD + d] = bf2f((uint16_t)(vq[i][e >> 1] >> ((e & 1) * 16))) * iq;
+        sK[r * LD + d] = bf2f((uint16_t)(vk[i][e >> 1] >> ((e & 1) * 16))) * ik;
+        sV[r * LD + d] = ok ? bf2f((uint16_t)(vv[i][e >> 1] >> ((e & 1) * 16))) : 0.f;
+      }
+    if (part == 0) {
       sG[r] = ok ? -softplusf_(av) : 0.f;
       sB[r] = ok ? sigmoidf_(bv) : 0.f;
     }
@@ -145,48 +231,83 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   }
   __syncthreads();
   const float GC = sG[C - 1];
-  // Kd = exp(G_C - G) k^ (rows >= C are zero because k^ is)
-  for (int idx = tid; idx < CH * DK; idx += NT) {
-    const int r = idx / DK, d = idx % DK;
-    P.Kd[idx] = expf(GC - sG[r]) * sK[r * LD + d];
+  if (tid < CH) {
+    sEG[tid] = __expf(sG[tid]);
+    sEK[tid] = __expf(GC - sG[tid]);
   }
-  if (tid == 0) *P.gC = expf(GC);
+  if (tid == 0) *P.gC = __expf(GC);
   // A = beta_r exp(G_r - G_i) k_r.k_i (i < r), Mqk = exp(G_r - G_i) q_r.k_i (i <= r)
   {
     const int i16 = lane & 15, kk = lane >> 4;
     for (int nt = 0; nt < CH / 16; ++nt) {
       f32x4 kk_acc = {0, 0, 0, 0}, qk_acc = {0, 0, 0, 0};
-      mm_nt(kk_acc, sK + wave * 16 * LD, LD, sK + nt * 16 * LD, LD, DK);
-      mm_nt(qk_acc, sQ + wave * 16 * LD, LD, sK + nt * 16 * LD, LD, DK);
+      mm_nt2(kk_acc, qk_acc, sK + wave * 16 * LD, sQ + wave * 16 * LD, LD, sK + nt * 16 * LD, LD, DK);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
-        const float dec = col <= row ? expf(sG[row] - sG[col]) : 0.f;
+        const float dec = col <= row ? __expf(sG[row] - sG[col]) : 0.f;
         sA[row * LC + col] = col < row ? sB[row] * dec * kk_acc[r] : 0.f;
         sM[row * LC + col] = col <= row ? dec * qk_acc[r] : 0.f;
       }
     }
   }
   __syncthreads();
-  // T = (I + A)^-1: lane j of wave 0 owns column j, rows in order.
-  if (wave == 0) {
-    float t[CH];
+  // Kd = exp(G_C - G) k^ (rows >= C are zero because k^ is)
+  for (int idx = tid; idx < CH * DK; idx += NT) {
+    const int r = idx / DK, d = idx % DK;
+    P.Kd[idx] = sEK[r] * sK[r * LD + d];
+  }
+  // T = (I + A)^-1 (unit lower triangular) into sT2, in 16 x 16 blocks.
+  // Diagonal blocks by forward substitution (wave w: block w, lane j < 16
+  // owns column j); then, by block diagonal d = I - J = 1, 2, 3 (one block
+  // per wave), T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ on the MFMA.
+  {
+    const int I = wave, j = lane & 15;
+    const float* Ab = sA + (16 * I) * LC + 16 * I;
+    float t[16];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) t[i] = (i == lane) ? 1.f : 0.f;
+    for (int i = 0; i < 16; ++i) t[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-    for (int r = 1; r < CH; ++r) {
-      float s = 0.f;
+    for (int r = 1; r < 16; ++r) {
+      float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) s += sA[r * LC + i] * t[i];
-      t[r] = (r > lane) ? -s : t[r];
+      for (int i = 0; i < r; ++i) acc += Ab[r * LC + i] * t[i];
+      t[r] = (r > j) ? -acc : t[r];
     }
-    // T diag(beta gamma) -> sA, T diag(beta) -> sT2 (column j scaled)
-    const float bj = sB[lane], bgj = bj * expf(sG[lane]);
+    if (lane < 16) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      sA[i * LC + lane] = t[i] * bgj;
-      sT2[i * LC + lane] = t[i] * bj;
+      for (int i = 0; i < 16; ++i) sT2[(16 * I + i) * LC + 16 * I + j] = t[i];
     }
+    for (int idx = tid; idx < CH * CH; idx += NT) {  // blocks above the diagonal
+      const int r = idx / CH, cc = idx % CH;
+      if ((cc >> 4) > (r >> 4)) sT2[r * LC + cc] = 0.f;
+    }
+  }
+  __syncthreads();
+  {
+    const int i16 = lane & 15, kk = lane >> 4;
+    float* X = sX + wave * 16 * XS;
+    for (int d = 1; d < CH / 16; ++d) {
+      if (wave < CH / 16 - d) {
+        const int J = wave, I = wave + d;
+        f32x4 x = {0, 0, 0, 0};
+        for (int K = J; K < I; ++K) mm_nn(x, sA + 16 * I * LC + 16 * K, LC, sT2 + 16 * K * LC + 16 * J, LC, 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X[(4 * kk + r) * XS + i16] = x[r];
+        f32x4 y = {0, 0, 0, 0};
+        mm_nn(y, sT2 + 16 * I * LC + 16 * I, LC, X, XS, 16);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sT2[(16 * I + 4 * kk + r) * LC + 16 * J + i16] = -y[r];
+      }
+      __syncthreads();
+    }
+  }
+  // T diag(beta gamma) -> sA (A is no longer needed), T diag(beta) -> sT2
+  for (int idx = tid; idx < CH * CH; idx += NT) {
+    const int r = idx / CH, cc = idx % CH;
+    const float tv = sT2[r * LC + cc];
+    sA[r * LC + cc] = tv * sB[cc] * sEG[cc];
+    sT2[r * LC + cc] = tv * sB[cc];
   }
   __syncthreads();
   // W = (T diag(beta gamma)) K^, Ut = (T diag(beta)) V; wave w: rows 16w..16w+15
@@ -196,8 +317,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   for (int nt = 0; nt < NTILE; ++nt) {
     wacc[nt] = (f32x4){0, 0, 0, 0};
     uacc[nt] = (f32x4){0, 0, 0, 0};
-    mm_nn(wacc[nt], sA + wave * 16 * LC, LC, sK + nt * 16, LD, CH);
-    mm_nn(uacc[nt], sT2 + wave * 16 * LC, LC, sV + nt * 16, LD, CH);
+    mm_nn2(wacc[nt], uacc[nt], sA + wave * 16 * LC, sT2 + wave * 16 * LC, LC, sK + nt * 16, sV + nt * 16, LD, CH);
   }
   __syncthreads();  // sK, sV fully read: reuse them for W and Ut
   {
@@ -222,13 +342,12 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
 #pragma unroll
     for (int nt = 0; nt < NTILE; ++nt) {
       f32x4 mw = {0, 0, 0, 0}, mu = {0, 0, 0, 0};
-      mm_nn(mw, sM + wave * 16 * LC, LC, sK + nt * 16, LD, CH);
-      mm_nn(mu, sM + wave * 16 * LC, LC, sV + nt * 16, LD, CH);
+      mm_nn2(mw, mu, sM + wave * 16 * LC, sM + wave * 16 * LC, LC, sK + nt * 16, sV + nt * 16, LD, CH);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
         const bool ok = row < C;
-        P.Qp[row * DK + col] = ok ? expf(sG[row]) * sQ[row * LD + col] - mw[r] : 0.f;
+        P.Qp[row * DK + col] = ok ? sEG[row] * sQ[row * LD + col] - mw[r] : 0.f;
         P.Up[row * DK + col] = ok ? mu[r] : 0.f;
       }
     }
@@ -236,23 +355,31 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
 }
 
 // ------------------------------------------------------- chunk scan
-// grid (Dv / 16, head, seq).  Rows j0 .. j0+15 of S, carried over the chunks
-// in order: U = Ut - W S^T, S <- gC S + U^T Kd.  The entry state of every
-// chunk is written for the output kernel; the final state to the slot.
+// One workgroup per (16 rows of S, head, seq): rows j0 .. j0+15 of S,
+// carried over the chunks in order: U = Ut - W S^T, S <- gC S + U^T Kd.
+// The entry state of every chunk is written for the output kernel; the final
+// state to the slot.  All Dv/16 row blocks of a (seq, head) read the same W
+// and Kd, so they are placed on one XCD (workgroups go to XCDs round-robin
+// by linear index): index = x + 8 ((g / 8) Dv/16 + jb) for group g = seq*H + head.
+constexpr int N_XCD = 8;
 template <int DK>
-__global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a) {
+__global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, int n_groups) {
   constexpr int LW = DK + 4;    // W rows (nt operand)
   constexpr int LK = DK + 16;   // Kd rows (tn operand)
   constexpr int LS = DK + 4;    // S rows (nt operand)
   constexpr int LU = 16;        // U rows (tn operand)
-  constexpr int PF = (2 * CH * DK + CH * 16) / 4 / NT;  // uint4 per thread per chunk
-  static_assert(PF * NT * 4 == 2 * CH * DK + CH * 16, "prefetch split");
+  constexpr int PW = CH * DK / (4 * NT);  // 16-byte pieces of W (and of Kd) per thread
+  static_assert(PW * 4 * NT == CH * DK && CH * 16 == 4 * NT, "prefetch split");
   __shared__ __align__(16) float sW[CH * LW];
   __shared__ __align__(16) float sKd[CH * LK];
   __shared__ __align__(16) float sUt[CH * 16];
   __shared__ __align__(16) float sU[CH * LU];
   __shared__ __align__(16) float sS[16 * LS];
-  const int j0 = blockIdx.x * 16, h = blockIdx.y, b = blockIdx.z;
+  constexpr int NJB = DK / 16;
+  const int xcd = blockIdx.x % N_XCD, q = blockIdx.x / N_XCD;
+  const int g = (q / NJB) * N_XCD + xcd;
+  if (g >= n_groups) return;
+  const int j0 = (q % NJB) * 16, h = g % a.H, b = g / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, kk = lane >> 4;
   float* Sg = a.state + ((int64_t)a.seq_slot[b] * a.H + h) * (int64_t)DK * DK;  // [Dv][Dk]
@@ -261,38 +388,36 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a) {
     const int j = idx / DK, k = idx % DK;
     sS[j * LS + k] = fresh ? 0.f : Sg[(int64_t)(j0 + j) * DK + k];
   }
-  // prefetch: element e of this thread's share -> (array, offset)
-  uint4 pf[PF];
-  auto load = [&](int c) {
-    const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int e = (tid + i * NT) * 4;  // float index in [W | Kd | Ut-slice]
-      const float* src;
-      if (e < CH * DK) src = P.W + e;
-      else if (e < 2 * CH * DK) src = P.Kd + (e - CH * DK);
-      else { const int u = e - 2 * CH * DK; src = P.Ut + (u / 16) * DK + j0 + (u % 16); }
-      pf[i] = *reinterpret_cast<const uint4*>(src);
-    }
-  };
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      const int e = (tid + i * NT) * 4;
-      float* dst;
-      if (e < CH * DK) dst = sW + (e / DK) * LW + e % DK;
-      else if (e < 2 * CH * DK) { const int u = e - CH * DK; dst = sKd + (u / DK) * LK + u % DK; }
-      else { const int u = e - 2 * CH * DK; dst = sUt + u; }
-      *reinterpret_cast<uint4*>(dst) = pf[i];
-    }
-  };
-  load(0);
+  // prefetch of the next chunk: this thread's 16-byte pieces of W and Kd
+  // (PW each) and of its 16 columns of Ut, one chunk ahead in registers
+  u32x4 pf[2 * PW + 1];
+  float gC_next;
+#define SCAN_LOAD(c_)                                                                        \
+  {                                                                                          \
+    const ChunkPtr P_ = chunk_ptr(a, b, h, (c_), DK);                                        \
+    gC_next = *P_.gC;                                                                        \
+    _Pragma("unroll") for (int i = 0; i < PW; ++i)                                           \
+        pf[i] = *reinterpret_cast<const u32x4*>(P_.W + (tid + i * NT) * 4);                  \
+    _Pragma("unroll") for (int i = 0; i < PW; ++i)                                           \
+        pf[PW + i] = *reinterpret_cast<const u32x4*>(P_.Kd + (tid + i * NT) * 4);            \
+    pf[2 * PW] = *reinterpret_cast<const u32x4*>(P_.Ut + (tid / 4) * DK + j0 + (tid % 4) * 4); \
+  }
+#define SCAN_STASH()                                                                         \
+  {                                                                                          \
+    _Pragma("unroll") for (int i = 0; i < PW; ++i) {                                         \
+      const int e = (tid + i * NT) * 4;                                                      \
+      *reinterpret_cast<u32x4*>(sW + (e / DK) * LW + e % DK) = pf[i];                        \
+      *reinterpret_cast<u32x4*>(sKd + (e / DK) * LK + e % DK) = pf[PW + i];                  \
+    }                                                                                        \
+    *reinterpret_cast<u32x4*>(sUt + tid * 4) = pf[2 * PW];                                   \
+  }
+  SCAN_LOAD(0);
   for (int c = 0; c < a.n_chunks; ++c) {
     __syncthreads();  // previous chunk's LDS reads are done
-    stash();
-    const float gC = a.gC[((int64_t)b * a.H + h) * a.n_chunks + c];
+    SCAN_STASH();
+    const float gC = gC_next;
     __syncthreads();
-    if (c + 1 < a.n_chunks) load(c + 1);
+    if (c + 1 < a.n_chunks) SCAN_LOAD(c + 1);
     // entry state of chunk c
     {
       const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
@@ -304,7 +429,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a) {
     // U = Ut - W S^T ; wave w: rows 16w..16w+15, the 16 columns j
     {
       f32x4 acc = {0, 0, 0, 0};
-      mm_nt(acc, sW + wave * 16 * LW, LW, sS, LS, DK);
+      mm_nt_ilp(acc, sW + wave * 16 * LW, LW, sS, LS, DK);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wave * 16 + 4 * kk + r;
@@ -312,17 +437,31 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a) {
       }
     }
     __syncthreads();
-    // S = gC S + U^T Kd ; wave w: k-tiles w, w+4, ...
-    for (int nt = wave; nt < DK / 16; nt += NT / 64) {
-      f32x4 acc = {0, 0, 0, 0};
-      mm_tn(acc, sU, LU, sKd + nt * 16, LK, CH);
+    // S = gC S + U^T Kd ; wave w: k-tile w (and w + 4 when Dk = 128)
+    constexpr int TPW = DK / 16 / (NT / 64);
+    static_assert(TPW == 1 || TPW == 2, "k-tiles per wave");
+    if constexpr (TPW == 2) {
+      const int nt0 = wave, nt1 = wave + NT / 64;
+      f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+      mm_tn2(acc0, acc1, sU, LU, sKd + nt0 * 16, sKd + nt1 * 16, LK, CH);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 4 * kk + r, k = nt * 16 + i16;
-        sS[j * LS + k] = gC * sS[j * LS + k] + acc[r];
+        const int j = 4 * kk + r;
+        sS[j * LS + nt0 * 16 + i16] = gC * sS[j * LS + nt0 * 16 + i16] + acc0[r];
+        sS[j * LS + nt1 * 16 + i16] = gC * sS[j * LS + nt1 * 16 + i16] + acc1[r];
+      }
+    } else {
+      f32x4 acc = {0, 0, 0, 0};
+      mm_tn(acc, sU, LU, sKd + wave * 16, LK, CH);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 4 * kk + r;
+        sS[j * LS + wave * 16 + i16] = gC * sS[j * LS + wave * 16 + i16] + acc[r];
       }
     }
   }
+#undef SCAN_LOAD
+#undef SCAN_STASH
   __syncthreads();
   for (int idx = tid; idx < 16 * DK; idx += NT) {
     const int j = idx / DK, k = idx % DK;
@@ -490,7 +629,7 @@ hipError_t set_lds(K k, size_t bytes) {
 
 template <int DK>
 hipError_t prefill_dk(const GdnArgs& a, int B, hipStream_t s) {
-  const size_t lds_prep = (3 * CH * (DK + 4) + 3 * CH * (CH + 4) + 2 * CH) * sizeof(float);
+  const size_t lds_prep = (3 * CH * (DK + 4) + 3 * CH * (CH + 4) + 4 * CH + 4 * 16 * 20) * sizeof(float);
   const size_t lds_out = (CH * (DK + 4) + DK * (DK + 4)) * sizeof(float);
   static bool attr = false;
   if (!attr) {
@@ -500,7 +639,8 @@ hipError_t prefill_dk(const GdnArgs& a, int B, hipStream_t s) {
     attr = true;
   }
   hipLaunchKernelGGL(gdn_chunk_prep_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), lds_prep, s, a);
-  hipLaunchKernelGGL(gdn_chunk_scan_kernel<DK>, dim3(DK / 16, a.H, B), dim3(NT), 0, s, a);
+  const int groups = (a.H * B + N_XCD - 1) / N_XCD * N_XCD;
+  hipLaunchKernelGGL(gdn_chunk_scan_kernel<DK>, dim3(groups * (DK / 16)), dim3(NT), 0, s, a, a.H * B);
   hipLaunchKernelGGL(gdn_chunk_out_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), lds_out, s, a);
   return hipGetLastError();
 }

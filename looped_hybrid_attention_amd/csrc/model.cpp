@@ -51,7 +51,8 @@ Layout layout(const loop_config& c, int64_t M) {
   const int64_t d = c.d_model, B = c.max_batch;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
-  L.n_in_max = std::max(n_in_full(c), n_in_gdn(c));
+  // rows of the input projection padded to 8 elements: 16-byte vector reads
+  L.n_in_max = (std::max(n_in_full(c), n_in_gdn(c)) + 7) / 8 * 8;
   L.meta = take(4 * B * sizeof(int32_t));
   L.h = take(M * d * 4);
   L.hmid = take(M * d * 4);
