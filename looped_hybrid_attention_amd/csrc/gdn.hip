@@ -39,7 +39,7 @@ DEV void mm_nt(f32x4& acc, const float* A, int lda, const float* B, int ldb, int
   const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
   const float* a = A + i * lda + kk;
   const float* b = B + i * ldb + kk;
-#pragma unroll 8
+#pragma unroll
   for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k], b[k], acc);
 }
 // acc += A[0:16, 0:K] . B[0:K, 0:16]
@@ -47,7 +47,7 @@ DEV void mm_nn(f32x4& acc, const float* A, int lda, const float* B, int ldb, int
   const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
   const float* a = A + i * lda + kk;
   const float* b = B + kk * ldb + i;
-#pragma unroll 8
+#pragma unroll
   for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k], b[k * ldb], acc);
 }
 // acc += A[0:K, 0:16]^T . B[0:K, 0:16]
@@ -55,7 +55,7 @@ DEV void mm_tn(f32x4& acc, const float* A, int lda, const float* B, int ldb, int
   const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
   const float* a = A + kk * lda + i;
   const float* b = B + kk * ldb + i;
-#pragma unroll 8
+#pragma unroll
   for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k * lda], b[k * ldb], acc);
 }
 
@@ -68,7 +68,7 @@ DEV void mm_nt2(f32x4& acc0, f32x4& acc1, const float* A0, const float* A1, int 
   const float* a0 = A0 + i * lda + kk;
   const float* a1 = A1 + i * lda + kk;
   const float* b = B + i * ldb + kk;
-#pragma unroll 8
+#pragma unroll
   for (int k = 0; k < K; k += 4) {
     const float bk = b[k];
     acc0 = mfma16x16x4f32(a0[k], bk, acc0);
@@ -83,20 +83,34 @@ DEV void mm_nn2(f32x4& acc0, f32x4& acc1, const float* A0, const float* A1, int 
   const float* a1 = A1 + i * lda + kk;
   const float* b0 = B0 + kk * ldb + i;
   const float* b1 = B1 + kk * ldb + i;
-#pragma unroll 8
+#pragma unroll
   for (int k = 0; k < K; k += 4) {
     acc0 = mfma16x16x4f32(a0[k], b0[k * ldb], acc0);
     acc1 = mfma16x16x4f32(a1[k], b1[k * ldb], acc1);
   }
 }
 
+// acc0 += A . B0^T, acc1 += A . B1^T (shared A, [16][K] row-major operands)
+DEV void mm_nt2s(f32x4& acc0, f32x4& acc1, const float* A, int lda, const float* B0, const float* B1, int ldb,
+                 int K) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a = A + i * lda + kk;
+  const float* b0 = B0 + i * ldb + kk;
+  const float* b1 = B1 + i * ldb + kk;
+#pragma unroll
+  for (int k = 0; k < K; k += 4) {
+    const float ak = a[k];
+    acc0 = mfma16x16x4f32(ak, b0[k], acc0);
+    acc1 = mfma16x16x4f32(ak, b1[k], acc1);
+  }
+}
 // acc += A[0:16, 0:K] . B[0:16, 0:K]^T as two interleaved chains (K % 8 == 0)
 DEV void mm_nt_ilp(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
   const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
   const float* a = A + i * lda + kk;
   const float* b = B + i * ldb + kk;
   f32x4 acc1 = {0, 0, 0, 0};
-#pragma unroll 8
+#pragma unroll
   for (int k = 0; k < K; k += 8) {
     acc = mfma16x16x4f32(a[k], b[k], acc);
     acc1 = mfma16x16x4f32(a[k + 4], b[k + 4], acc1);
@@ -110,7 +124,7 @@ DEV void mm_tn2(f32x4& acc0, f32x4& acc1, const float* A, int lda, const float* 
   const float* a = A + kk * lda + i;
   const float* b0 = B0 + kk * ldb + i;
   const float* b1 = B1 + kk * ldb + i;
-#pragma unroll 8
+#pragma unroll
   for (int k = 0; k < K; k += 4) {
     const float ak = a[k * lda];
     acc0 = mfma16x16x4f32(ak, b0[k * ldb], acc0);
@@ -476,6 +490,10 @@ template <int DK>
 __global__ __launch_bounds__(NT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
   constexpr int DV = DK;
   constexpr int LD = DK + 4;
+  constexpr int NQ = CH * DK / 4 / NT;   // 16-byte pieces of Qp per thread
+  constexpr int NS = DV * DK / 4 / NT;   // of S_c
+  constexpr int PER = DV / 4;            // output dims per thread (4 threads per row)
+  static_assert(NQ * 4 * NT == CH * DK && NS * 4 * NT == DV * DK && CH * 4 == NT, "thread split");
   extern __shared__ __align__(16) float gsm[];
   float* sQ = gsm;             // Qp [CH][LD], later O
   float* sS = sQ + CH * LD;    // S_c [DV][LD]
@@ -483,48 +501,78 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
   const int C = min(CH, a.T - c * CH);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
-  for (int idx = tid * 4; idx < CH * DK; idx += NT * 4) {
-    const int r = idx / DK, k = idx % DK;
-    *reinterpret_cast<float4*>(sQ + r * LD + k) = *reinterpret_cast<const float4*>(P.Qp + idx);
+  // every global read first: Qp and S_c (for LDS), this thread's row piece
+  // of Up and of the gate z
+  const int r = tid >> 2, d0 = (tid & 3) * PER;
+  const int64_t m = (int64_t)b * a.T + c * CH + min(r, C - 1);
+  u32x4 rq[NQ], rs[NS], ru[PER / 4], rz[PER / 8];
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) rq[i] = *reinterpret_cast<const u32x4*>(P.Qp + (tid + i * NT) * 4);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) rs[i] = *reinterpret_cast<const u32x4*>(P.S + (tid + i * NT) * 4);
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) ru[i] = *reinterpret_cast<const u32x4*>(P.Up + r * DK + d0 + 4 * i);
+  const uint16_t* z = a.proj + m * a.proj_stride + a.off_z + h * DV + d0;
+#pragma unroll
+  for (int i = 0; i < PER / 8; ++i) rz[i] = *reinterpret_cast<const u32x4*>(z + 8 * i);
+#pragma unroll
+  for (int i = 0; i < NQ; ++i) {
+    const int e = (tid + i * NT) * 4;
+    *reinterpret_cast<u32x4*>(sQ + (e / DK) * LD + e % DK) = rq[i];
   }
-  for (int idx = tid * 4; idx < DV * DK; idx += NT * 4) {
-    const int v = idx / DK, k = idx % DK;
-    *reinterpret_cast<float4*>(sS + v * LD + k) = *reinterpret_cast<const float4*>(P.S + idx);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int e = (tid + i * NT) * 4;
+    *reinterpret_cast<u32x4*>(sS + (e / DK) * LD + e % DK) = rs[i];
   }
   __syncthreads();
+  // O = Qp S_c^T (+ Up below); wave w: rows 16w .. 16w+15, tiles in pairs
   constexpr int NTILE = DV / 16;
+  static_assert(NTILE % 2 == 0, "tile pairs");
   f32x4 acc[NTILE];
   const int i16 = lane & 15, kk = lane >> 4;
 #pragma unroll
-  for (int nt = 0; nt < NTILE; ++nt) {
+  for (int nt = 0; nt < NTILE; nt += 2) {
     acc[nt] = (f32x4){0, 0, 0, 0};
-    mm_nt(acc[nt], sQ + wave * 16 * LD, LD, sS + nt * 16 * LD, LD, DK);
+    acc[nt + 1] = (f32x4){0, 0, 0, 0};
+    mm_nt2s(acc[nt], acc[nt + 1], sQ + wave * 16 * LD, LD, sS + nt * 16 * LD, sS + (nt + 1) * 16 * LD, LD, DK);
   }
-  __syncthreads();
+  __syncthreads();  // sQ fully read: reuse it for O
 #pragma unroll
   for (int nt = 0; nt < NTILE; ++nt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
-      sQ[row * LD + col] = acc[nt][r] + P.Up[row * DK + col];
-    }
+    for (int q = 0; q < 4; ++q) sQ[(wave * 16 + 4 * kk + q) * LD + nt * 16 + i16] = acc[nt][q];
   __syncthreads();
-  for (int r = wave; r < C; r += NT / 64) {
-    const int64_t m = (int64_t)b * a.T + c * CH + r;
-    float v[DV / 64], ss = 0.f;
+  // per token and head: y = RMSNorm(O + Up; g_o) * SiLU(z) -> bf16
+  float v[PER];
+  float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < DV / 64; ++e) {
-      v[e] = sQ[r * LD + lane + 64 * e];
-      ss += v[e] * v[e];
+  for (int i = 0; i < PER / 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[4 * i + e] = sQ[r * LD + d0 + 4 * i + e] + __uint_as_float(ru[i][e]);
+      ss += v[4 * i + e] * v[4 * i + e];
     }
-    ss = wave_sum(ss);
-    const float inv = rsqrtf(ss / DV + a.eps);
-    const uint16_t* z = a.proj + m * a.proj_stride + a.off_z + h * DV;
-    uint16_t* y = a.out + m * a.out_stride + h * DV;
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  const float inv = rsqrtf(ss / DV + a.eps);
+  if (r < C) {
+    uint16_t* y = a.out + m * a.out_stride + h * DV + d0;
 #pragma unroll
-    for (int e = 0; e < DV / 64; ++e) {
-      const int d = lane + 64 * e;
-      y[d] = f2bf_bits(v[e] * inv * bf2f(a.o_norm[d]) * siluf_(bf2f(z[d])));
+    for (int i = 0; i < PER / 8; ++i) {
+      u32x4 o;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float f[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int k = 8 * i + 2 * w + e;
+          const float zf = bf2f((uint16_t)(rz[i][w] >> (16 * e)));
+          f[e] = v[k] * inv * bf2f(a.o_norm[d0 + k]) * siluf_(zf);
+        }
+        o[w] = (uint32_t)f2bf_bits(f[0]) | ((uint32_t)f2bf_bits(f[1]) << 16);
+      }
+      *reinterpret_cast<u32x4*>(y + 8 * i) = o;
     }
   }
 }
