@@ -199,7 +199,7 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(k_tflops, 1), "peak": PEAK_BF16_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_BF16_TFLOPS, 4),
                     "traffic": measured_traffic("gemm_gateup"),
-                    "kernel": "gemm_kernel<256,256,2,4,SWIGLU> (gate/up projection + SwiGLU epilogue)",
+                    "kernel": "gemm_db_kernel<SWIGLU> (256x256 tiles, LDS-copy fed; gate/up projection + SwiGLU epilogue)",
                     "launch_ms": round(k_avg_ms, 4), "launches": k_n,
                     "algorithmic_flop_per_launch": k_flop}
         step_frac = fl["total"] / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS

@@ -129,22 +129,6 @@ template <int CR>
 DEV int k_swz(int r) { return CR >= 16 ? (r & 15) : (r & 7); }
 DEV int v_swz(int d) { return (d >> 1) & 7; }
 
-typedef __attribute__((address_space(3))) void lds_void;
-// Raw buffer resource over `bytes` bytes at `base` (word 3: 32-bit data
-// format, no swizzle, as CDNA expects for raw buffer loads).
-DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-// 16-byte copy global -> LDS: lane i's 16 bytes at `src` + voffset land at
-// LDS byte `dst` + 16 i (dst wave-uniform).
-DEV void copy16_to_lds(__amdgpu_buffer_rsrc_t src, int voffset, lds_void* dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, voffset, 0, 0, 0);
-}
-
-// Probabilities of a score tile against reference max m (log2 units), their
-// row sum into l, and O^T += V^T . P^T over the tile's 64 keys in 4 steps of
-// 16 (V^T fragment reads FD steps ahead of the MFMAs).  `vr` = the lane's
-// V^T row in LDS (swizzle vsw).
 template <int NDT, int FD, int VROW>
 DEV void flash_pv(f32x16 (&o)[NDT], f32x16 (&s)[2], float& l, float m, float scale, const uint8_t* vr, int h,
                   int vsw) {
@@ -239,9 +223,9 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
   {                                                                                           \
     uint8_t* S_ = flash_smem + (stage_) * L::STAGE;                                           \
     _Pragma("unroll") for (int i = 0; i < KI; ++i)                                            \
-        copy16_to_lds(k_rsrc, ((k0_) * D + k_src[i]) * 2, (lds_void*)(S_ + (wave * KI + i) * 1024)); \
+        copy16_to_lds(k_rsrc, ((k0_) * D + k_src[i]) * 2, 0, (lds_void*)(S_ + (wave * KI + i) * 1024)); \
     _Pragma("unroll") for (int i = 0; i < VI; ++i)                                            \
-        copy16_to_lds(v_rsrc, ((k0_) + v_src[i]) * 2,                                        \
+        copy16_to_lds(v_rsrc, ((k0_) + v_src[i]) * 2, 0,                                      \
                       (lds_void*)(S_ + KT * L::KROW + (wave * VI + i) * 1024));               \
   }
   // V^T keys at or past L_valid may hold anything; P is 0 there but 0 * NaN
@@ -255,7 +239,7 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
         *reinterpret_cast<uint16_t*>(V_ + d * L::VROW + (((kk >> 3) ^ v_swz(d)) << 4) + (kk & 7) * 2) = 0; \
   }
   // vmcnt(0): this wave's LDS copies have landed
-#define FLASH_WAIT_COPIES() __builtin_amdgcn_s_waitcnt(0x0F70)
+#define FLASH_WAIT_COPIES() wait_vmem()
 
   FLASH_COPY(0, 0);
 

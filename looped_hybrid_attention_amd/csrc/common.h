@@ -57,3 +57,21 @@ DEV float block_sum(float v, float* red) {
 
 DEV float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 DEV float siluf_(float x) { return x / (1.0f + __expf(-x)); }
+
+// Global -> LDS copies that bypass registers (buffer_load ... lds, gfx950
+// 16-byte form).  MUBUF rather than the FLAT form: with a FLAT LDS copy in
+// flight the compiler waits for every outstanding LDS read at each use.
+typedef __attribute__((address_space(3))) void lds_void;
+// Raw buffer resource over `bytes` bytes at `base` (word 3: 32-bit data
+// format, no swizzle, as CDNA expects for raw buffer loads).
+DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Lane i's 16 bytes at `src` + voffset + soffset land at LDS byte `dst` + 16 i
+// (dst and soffset wave-uniform).  Completion is counted by vmcnt.
+DEV void copy16_to_lds(__amdgpu_buffer_rsrc_t src, int voffset, int soffset, lds_void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, voffset, soffset, 0, 0);
+}
+// s_waitcnt vmcnt(0): this wave's vector memory operations (LDS copies
+// included) have completed.
+DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -280,13 +280,224 @@ hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------- large-M tiles, LDS copy
+// 256 x 256 output tile, K in steps of 64, four waves (one per SIMD), each
+// computing 128 x 128 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with the
+// accumulators in AGPRs.  A and B tiles go global -> LDS with buffer_load
+// ... lds, double-buffered: the next tile's copies are issued at the top of
+// a tile; its barrier sits before the MFMAs of the last 16-deep step, so the
+// next tile's first operand reads overlap them.  Operand reads run one
+// 16-deep step ahead of the MFMAs.  Rows are unpadded (128 bytes); chunk c of
+// row r sits at c ^ ((r / 2) % 8) so that the 128-bit operand reads of 16
+// consecutive rows hit distinct banks.
+constexpr int DB_BM = 256, DB_BN = 256;
+constexpr int DB_TILE = 256 * BK * 2;        // bytes of one operand tile
+constexpr int DB_STAGE = 2 * DB_TILE;        // A then B
+constexpr int DB_LDS = 2 * DB_STAGE;
+DEV int db_swz(int row) { return (row >> 1) & 7; }
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes) {
+  constexpr int TM = 4, TN = 4;
+  extern __shared__ __align__(16) uint8_t db_smem[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (g.M + DB_BM - 1) / DB_BM;
+  const int m0 = (blockIdx.x % tiles_m) * DB_BM;
+  const int tn = blockIdx.x / tiles_m;
+  constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? DB_BN / 2 : DB_BN;
+  const int n0 = tn * OUT_BN;
+
+  // Byte offsets (k = 0) of this lane's 16-byte piece in each of the wave's
+  // 8 copy instructions per operand tile: instruction n fills rows
+  // 8n .. 8n+7, lane l row 8n + l/8 at chunk l%8 (holding logical chunk
+  // (l%8) ^ swizzle).  Rows past M (N) are clamped: they feed outputs that
+  // are never stored.
+  int a_off[8], b_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = (wave * 8 + i) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ db_swz(row);
+    a_off[i] = (min(m0 + row, g.M - 1) * (int)g.lda + c * 8) * 2;
+    int gn;
+    if (EPI == LOOP_EPI_SWIGLU) {
+      const int blk = row / 32, part = blk & 1, col = min(n0 + (blk >> 1) * 32 + (row & 31), g.N - 1);
+      gn = part * g.swiglu_F + col;
+    } else {
+      gn = min(n0 + row, g.N - 1);
+    }
+    b_off[i] = (gn * (int)g.ldb + c * 8) * 2;
+  }
+  const auto a_rsrc = buffer_rsrc(g.A, a_bytes);
+  const auto b_rsrc = buffer_rsrc(g.B, b_bytes);
+#define DB_COPY(k0_, stage_)                                                                       \
+  {                                                                                                \
+    uint8_t* S_ = db_smem + (stage_) * DB_STAGE;                                                   \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                  \
+        copy16_to_lds(a_rsrc, a_off[i], (k0_) * 2, (lds_void*)(S_ + (wave * 8 + i) * 1024));      \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                  \
+        copy16_to_lds(b_rsrc, b_off[i], (k0_) * 2, (lds_void*)(S_ + DB_TILE + (wave * 8 + i) * 1024)); \
+  }
+  // operand reads: lane (lr, half) row lr of each 32-row tile, chunk 2 ks + half
+  const int lr = lane & 31, half = lane >> 5, sw = db_swz(lr);
+  const int a_row = (wm * 128 + lr) * (BK * 2), b_row = DB_TILE + (wn * 128 + lr) * (BK * 2);
+  bf16x8 fa[2][TM], fb[2][TN];
+#define DB_READ(stage_, ks_, buf_)                                                                 \
+  {                                                                                                \
+    const uint8_t* S_ = db_smem + (stage_) * DB_STAGE + (((2 * (ks_) + half) ^ sw) << 4);          \
+    _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                 \
+        fa[buf_][i] = *reinterpret_cast<const bf16x8*>(S_ + a_row + i * 32 * (BK * 2));            \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
+        fb[buf_][j] = *reinterpret_cast<const bf16x8*>(S_ + b_row + j * 32 * (BK * 2));            \
+  }
+#define DB_MFMA(buf_)                                                                              \
+  _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                               \
+          acc[i][j] = mfma32x32x16(fa[buf_][i], fb[buf_][j], acc[i][j]);
+// interleave: the 8 reads of the next step spread over the 16 MFMAs
+#define DB_SCHED()                                                                                 \
+  _Pragma("unroll") for (int q = 0; q < TM + TN; ++q) {                                            \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                             \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
+
+  const int nk = g.K / BK;
+  DB_COPY(0, 0);
+  wait_vmem();
+  __syncthreads();
+  DB_READ(0, 0, 0);
+  for (int t = 0; t < nk; ++t) {
+    const int s = t & 1;
+    // next tile's copies (the last tile re-copies itself into the idle
+    // buffer, harmlessly: nothing reads it afterwards)
+    DB_COPY(min(t + 1, nk - 1) * BK, s ^ 1);
+    DB_READ(s, 1, 1);
+    DB_MFMA(0);
+    DB_SCHED();
+    DB_READ(s, 2, 0);
+    DB_MFMA(1);
+    DB_SCHED();
+    DB_READ(s, 3, 1);
+    DB_MFMA(0);
+    DB_SCHED();
+    // all of this tile's reads and the next tile's copies are done in every
+    // wave past this barrier
+    wait_vmem();
+    __syncthreads();
+    DB_READ(s ^ 1, 0, 0);
+    DB_MFMA(1);
+    DB_SCHED();
+  }
+#undef DB_COPY
+#undef DB_READ
+#undef DB_MFMA
+#undef DB_SCHED
+
+  // Epilogue.  Lane holds column lr of each 32x32 tile and rows
+  // 8*(r/4) + 4*(lane/32) + r%4.  Tiles wholly inside the output take a
+  // branch-free path whose loads (residual) are issued a row block at a time.
+  const int row_base = m0 + wm * 128 + 4 * half;
+  const bool full = m0 + DB_BM <= g.M && n0 + OUT_BN <= g.N;
+  if (EPI == LOOP_EPI_SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < TN; j += 2) {
+      const int col = n0 + wn * 64 + (j / 2) * 32 + lr;
+      if (!full && col >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+          if (full || row < g.M) {
+            const float gt = acc[i][j][r], up = acc[i][j + 1][r];
+            reinterpret_cast<uint16_t*>(g.C)[(int64_t)row * g.ldc + col] = f2bf_bits(siluf_(gt) * up);
+          }
+        }
+    }
+    return;
+  }
+  if (full) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float rv[TN][16];
+      if (EPI == LOOP_EPI_F32_RES) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+            rv[j][r] = g.R[(int64_t)row * g.ldc + n0 + wn * 128 + j * 32 + lr];
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+          const int64_t o = (int64_t)row * g.ldc + n0 + wn * 128 + j * 32 + lr;
+          const float v = acc[i][j][r];
+          if (EPI == LOOP_EPI_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = f2bf_bits(v);
+          else if (EPI == LOOP_EPI_F32) reinterpret_cast<float*>(g.C)[o] = v;
+          else reinterpret_cast<float*>(g.C)[o] = rv[j][r] + v;
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int col = n0 + wn * 128 + j * 32 + lr;
+    if (col >= g.N) continue;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+        if (row >= g.M) continue;
+        const int64_t o = (int64_t)row * g.ldc + col;
+        const float v = acc[i][j][r];
+        if (EPI == LOOP_EPI_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = f2bf_bits(v);
+        else if (EPI == LOOP_EPI_F32) reinterpret_cast<float*>(g.C)[o] = v;
+        else reinterpret_cast<float*>(g.C)[o] = g.R[o] + v;
+      }
+  }
+}
+
+template <int EPI>
+hipError_t launch_db(const GemmArgs& g, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
+  constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? DB_BN / 2 : DB_BN;
+  const int tiles = ((g.M + DB_BM - 1) / DB_BM) * ((g.N + OUT_BN - 1) / OUT_BN);
+  auto k = gemm_db_kernel<EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, DB_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k, dim3(tiles), dim3(256), DB_LDS, s, g, a_bytes, b_bytes);
+  return hipGetLastError();
+}
+
 // Small-M calls (decode) get too few output tiles to fill the chip: split K
 // so that tiles * splits >= ~512 workgroups, if a partial buffer is given.
 template <int EPI>
 hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
-  // Large M: 256 x 256 tiles, eight waves (two per SIMD, so that one wave's
-  // barrier and load waits are covered by the other's MFMAs).
-  if (g.M >= 512) return launch_cfg<256, 256, 2, 4, EPI, false>(g, 1, s);
+  // Large M: 256 x 256 tiles fed by LDS copies; operands whose byte range
+  // does not fit the 32-bit buffer offsets use the register-staged kernel
+  // (eight waves, two per SIMD).
+  if (g.M >= 512) {
+    const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
+    const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
+    if (g.K % BK == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31))
+      return launch_db<EPI>(g, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+    return launch_cfg<256, 256, 2, 4, EPI, false>(g, 1, s);
+  }
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? 64 : 128;
   const int tiles = ((g.M + 63) / 64) * ((g.N + OUT_BN - 1) / OUT_BN);
   int splits = 1;
