@@ -20,78 +20,109 @@
 namespace {
 
 // ---------------------------------------------------------------- prep
-// One wave per (token, item); items: Hq query heads, Hkv key heads, Hkv
-// value heads.  Lane holds D/64 consecutive dims.
+// One workgroup per token: the rotary cos / sin of the token's position are
+// computed once (angle in double, rounded to fp32) into LDS, then the four
+// waves take the Hq query and Hkv key heads in turn; lane holds D/64
+// consecutive dims.
 template <int D>
 __global__ __launch_bounds__(256) void qk_prep_kernel(AttnPrepArgs a) {
   constexpr int EPL = D / 64;
+  __shared__ float rc[D / 2], rs[D / 2];
   const int m = blockIdx.x;  // token row
-  const int item = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int n_items = a.Hq + 2 * a.Hkv;
-  if (item >= n_items) return;
   const int b = m / a.T, t = m % a.T;
   const int pos = a.pos[b] + t;
   const int64_t slot_b = a.seq_slot[b];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < a.R / 2) {
+    const double th = pow((double)a.theta, -2.0 * tid / a.R);
+    const double ang = (double)pos * th;
+    rc[tid] = (float)cos(ang);
+    rs[tid] = (float)sin(ang);
+  }
+  __syncthreads();
   const uint16_t* row = a.proj + (int64_t)m * a.proj_stride;
   const int d0 = lane * EPL;
-  float x[EPL];
-  if (item >= a.Hq + a.Hkv) {
-    // value head: raw copy into the transposed cache
-    const int kvh = item - a.Hq - a.Hkv;
-    const uint16_t* src = row + 2 * a.Hq * D + a.Hkv * D + kvh * D + d0;
-    uint16_t* vt = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq;
+  for (int item = wave; item < a.Hq + a.Hkv; item += 4) {
+    const bool is_q = item < a.Hq;
+    const int head = is_q ? item : item - a.Hq;
+    const uint16_t* src = (is_q ? row + head * D : row + 2 * a.Hq * D + head * D) + d0;
+    const uint16_t* gain = (is_q ? a.q_norm : a.k_norm) + d0;
+    float x[EPL];
+    float ss = 0.f;
+    if constexpr (EPL == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      x[0] = bf2f((uint16_t)v.x); x[1] = bf2f((uint16_t)(v.x >> 16));
+      x[2] = bf2f((uint16_t)v.y); x[3] = bf2f((uint16_t)(v.y >> 16));
+    } else {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) vt[(int64_t)(d0 + e) * a.max_seq + pos] = src[e];
-    return;
-  }
-  const bool is_q = item < a.Hq;
-  const int head = is_q ? item : item - a.Hq;
-  const uint16_t* src = is_q ? row + head * D : row + 2 * a.Hq * D + head * D;
-  const uint16_t* gain = is_q ? a.q_norm : a.k_norm;
-  float ss = 0.f;
+      for (int e = 0; e < EPL; ++e) x[e] = bf2f(src[e]);
+    }
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    x[e] = bf2f(src[d0 + e]);
-    ss += x[e] * x[e];
-  }
-  ss = wave_sum(ss);
-  const float inv = rsqrtf(ss / D + a.eps);
+    for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+    ss = wave_sum(ss);
+    const float inv = rsqrtf(ss / D + a.eps);
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) x[e] = x[e] * inv * bf2f(gain[d0 + e]);
-  // rotary on dims < R, adjacent pairs
-  if (EPL >= 2) {
+    for (int e = 0; e < EPL; ++e) x[e] = x[e] * inv * bf2f(gain[e]);
+    // rotary on dims < R, adjacent pairs (2i, 2i+1)
+    if (EPL >= 2) {
 #pragma unroll
-    for (int e = 0; e < EPL; e += 2) {
-      const int d = d0 + e;
-      if (d < a.R) {
-        const int i = d >> 1;
-        const double th = pow((double)a.theta, -2.0 * i / a.R);
-        const double ang = (double)pos * th;
-        const float c = (float)cos(ang), s = (float)sin(ang);
-        const float x0 = x[e], x1 = x[e + 1];
-        x[e] = x0 * c - x1 * s;
-        x[e + 1] = x0 * s + x1 * c;
+      for (int e = 0; e < EPL; e += 2) {
+        const int d = d0 + e;
+        if (d < a.R) {
+          const float c = rc[d >> 1], sn = rs[d >> 1];
+          const float x0 = x[e], x1 = x[e + 1];
+          x[e] = x0 * c - x1 * sn;
+          x[e + 1] = x0 * sn + x1 * c;
+        }
+      }
+    } else {
+      const float partner = __shfl_xor(x[0], 1, 64);
+      if (d0 < a.R) {
+        const float c = rc[d0 >> 1], sn = rs[d0 >> 1];
+        x[0] = (d0 & 1) ? partner * sn + x[0] * c : x[0] * c - partner * sn;
       }
     }
-  } else {
-    const float partner = __shfl_xor(x[0], 1, 64);
-    if (d0 < a.R) {
-      const int i = d0 >> 1;
-      const double th = pow((double)a.theta, -2.0 * i / a.R);
-      const double ang = (double)pos * th;
-      const float c = (float)cos(ang), s = (float)sin(ang);
-      x[0] = (d0 & 1) ? partner * s + x[0] * c : x[0] * c - partner * s;
+    uint16_t* dst = is_q ? a.q_out + ((int64_t)m * a.Hq + head) * D + d0
+                         : a.k_cache + ((slot_b * a.Hkv + head) * (int64_t)a.max_seq + pos) * D + d0;
+    if constexpr (EPL == 4) {
+      uint2 o;
+      o.x = (uint32_t)f2bf_bits(x[0]) | ((uint32_t)f2bf_bits(x[1]) << 16);
+      o.y = (uint32_t)f2bf_bits(x[2]) | ((uint32_t)f2bf_bits(x[3]) << 16);
+      *reinterpret_cast<uint2*>(dst) = o;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dst[e] = f2bf_bits(x[e]);
     }
   }
-  uint16_t* dst;
-  if (is_q) {
-    dst = a.q_out + ((int64_t)m * a.Hq + head) * D + d0;
-  } else {
-    dst = a.k_cache + ((slot_b * a.Hkv + head) * (int64_t)a.max_seq + pos) * D + d0;
-  }
+}
+
+// V of a block of 64 tokens of one sequence and KV head into the transposed
+// cache: rows of the projection in, staged in LDS, written out as 128-byte
+// runs of each V^T row (the cache keeps V transposed for the PV products).
+constexpr int VT_TOK = 64;
+template <int D>
+__global__ __launch_bounds__(256) void v_transpose_kernel(AttnPrepArgs a) {
+  constexpr int LS = D + 2;  // bf16 row in LDS (odd word stride: the column reads hit distinct banks)
+  __shared__ __align__(4) uint16_t tile[VT_TOK * LS];
+  const int t0 = blockIdx.x * VT_TOK, kvh = blockIdx.y, b = blockIdx.z;
+  const int nt = min(VT_TOK, a.T - t0);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < VT_TOK * (D / 8); i += 256) {
+    const int t = i / (D / 8), c = i % (D / 8);
+    if (t < nt) {
+      const uint16_t* src = a.proj + ((int64_t)b * a.T + t0 + t) * a.proj_stride + 2 * a.Hq * D + a.Hkv * D +
+                            kvh * D + c * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[e] = f2bf_bits(x[e]);
+      for (int w = 0; w < 4; ++w) *reinterpret_cast<uint32_t*>(tile + t * LS + c * 8 + 2 * w) = v[w];
+    }
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t slot_b = a.seq_slot[b];
+  uint16_t* vt = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq + a.pos[b] + t0;
+  if (lane < nt)
+    for (int d = wave; d < D; d += 4) vt[(int64_t)d * a.max_seq + lane] = tile[lane * LS + d];
 }
 
 // ------------------------------------------------------- flash prefill
@@ -551,8 +582,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
 
 template <int D>
 hipError_t prep_d(const AttnPrepArgs& a, int M, hipStream_t s) {
-  const int items = a.Hq + 2 * a.Hkv;
-  hipLaunchKernelGGL(qk_prep_kernel<D>, dim3(M, (items + 3) / 4), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(qk_prep_kernel<D>, dim3(M), dim3(256), 0, s, a);
+  const int B = M / a.T;
+  hipLaunchKernelGGL(v_transpose_kernel<D>, dim3((a.T + VT_TOK - 1) / VT_TOK, a.Hkv, B), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
