@@ -69,6 +69,7 @@ int validate_config(const loop_config* c) {
     return loop_fail(LOOP_ESHAPE, "gdn_dk == gdn_dv in {64, 128} required");
   if (c->gdn_chunk != 64) return loop_fail(LOOP_ESHAPE, "gdn_chunk must be 64");
   if (c->d_model <= 0 || c->d_model % 256) return loop_fail(LOOP_ESHAPE, "d_model must be a multiple of 256");
+  if (c->loop_end - c->loop_start > 64) return loop_fail(LOOP_ESHAPE, "at most 64 layers in the loop block");
   if (c->d_ff <= 0 || c->d_ff % 64) return loop_fail(LOOP_ESHAPE, "d_ff must be a multiple of 64");
   if ((c->n_q_heads * c->head_dim) % 64 || (c->gdn_heads * c->gdn_dv) % 64)
     return loop_fail(LOOP_ESHAPE, "attention / GDN widths must be multiples of 64");

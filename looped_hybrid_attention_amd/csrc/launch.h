@@ -32,7 +32,8 @@ struct TransitionArgs {
   const float* out;  // in = WRITE: layer branch a + f
   const float* s0;   // in = WRITE: streams before the write
   const float* s1;
-  const float* write_w; const float* write_b; const float* mix;  // this exec's write params
+  const float* write_w; const float* write_b;  // this exec's write params
+  const float* P;          // this exec's 2x2 mix matrix (row-major), precomputed
   const float* read_w; const float* read_b;                      // next exec's read params
   const uint16_t* norm_g;  // next exec's attn_norm gain (bf16)
   float* s0_out; float* s1_out; float* x_out;  // out = READ
@@ -43,6 +44,13 @@ hipError_t launch_transition(TransitionArgs t, hipStream_t s);
 hipError_t launch_tap(const float* h, const float* s0, const float* s1, float* dst, int B, int T, int d,
                       hipStream_t s);
 hipError_t launch_sinkhorn(const float* mix, int iters, float* out, hipStream_t s);
+// mix matrices of up to 64 layers in one launch: out[4 l ..] = Sinkhorn(mix[l])
+struct SinkhornBatch {
+  const float* mix[64];
+  int n, iters;
+  float* out;
+};
+hipError_t launch_sinkhorn_layers(const SinkhornBatch& sb, hipStream_t s);
 int argmax_chunks(int64_t n);
 hipError_t launch_argmax(const float* x, int rows, int64_t n, float* pv, int* pi, int32_t* out, hipStream_t s);
 

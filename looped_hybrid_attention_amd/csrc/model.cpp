@@ -373,7 +373,8 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   t.s0_out = s0; t.s1_out = s1; t.x_out = x; t.h_out = h; t.xn = xn;
   if (d.loop) {
     t.in_mode = TR_IN_WRITE;
-    t.write_w = w.mhc_write_w; t.write_b = w.mhc_write_b; t.mix = w.mhc_mix;
+    t.write_w = w.mhc_write_w; t.write_b = w.mhc_write_b;
+    t.P = at<float>(m, L.mhc) + 4 * (d.layer - c.loop_start);
   } else {
     t.in_mode = TR_IN_H;
   }
@@ -429,6 +430,15 @@ int run_entry(loop_model* m, const Call& k, hipStream_t s) {
 int run_forward(loop_model* m, const Call& k, const int32_t* taps, int n_taps, float* d_taps, hipStream_t s) {
   const loop_config& c = m->cfg;
   const Layout& L = m->L;
+  // the loop layers' mix matrices, once per call (they depend on weights only)
+  if (c.loop_end > c.loop_start) {
+    SinkhornBatch sb{};
+    sb.n = c.loop_end - c.loop_start;
+    sb.iters = c.sinkhorn_iters;
+    sb.out = at<float>(m, L.mhc);
+    for (int l = 0; l < sb.n; ++l) sb.mix[l] = m->lw[c.loop_start + l].mhc_mix;
+    HIP_TRY(launch_sinkhorn_layers(sb, s));
+  }
   if (int r = run_entry(m, k, s)) return r;
   for (int e = 0; e < (int)m->sched.size(); ++e) {
     if (int r = run_exec(m, k, e, s)) return r;

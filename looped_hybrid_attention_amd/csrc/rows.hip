@@ -137,40 +137,56 @@ DEV void block_sum2_t(float& a, float& b, float* red) {
 
 template <int TNT, int PER>
 __global__ __launch_bounds__(TNT) void transition_kernel(TransitionArgs t) {
+  // Element i of this thread: with PER >= 4, contiguous groups of four
+  // (16-byte accesses), columns 4 (tid + (i/4) TNT) + i%4; else tid + i TNT.
+  constexpr bool VEC = PER % 4 == 0;
   __shared__ float red[2 * TNT / 64];
-  __shared__ float sP[4];
   const int d = t.d;
   const int64_t o = (int64_t)blockIdx.x * d;
+  auto col = [](int i) { return VEC ? 4 * ((int)threadIdx.x + (i / 4) * TNT) + (i & 3) : (int)threadIdx.x + i * TNT; };
+#define TR_LOAD(dst_, src_, off_)                                                                  \
+  {                                                                                                \
+    if (VEC) {                                                                                     \
+      _Pragma("unroll") for (int q = 0; q < PER / 4; ++q) {                                        \
+        const int c_ = col(4 * q);                                                                 \
+        const float4 v_ = c_ < d ? *reinterpret_cast<const float4*>((src_) + (off_) + c_) : make_float4(0, 0, 0, 0); \
+        dst_[4 * q] = v_.x; dst_[4 * q + 1] = v_.y; dst_[4 * q + 2] = v_.z; dst_[4 * q + 3] = v_.w; \
+      }                                                                                            \
+    } else {                                                                                       \
+      _Pragma("unroll") for (int i = 0; i < PER; ++i) dst_[i] = col(i) < d ? (src_)[(off_) + col(i)] : 0.f; \
+    }                                                                                              \
+  }
+#define TR_STORE(dst_, off_, val_)                                                                 \
+  {                                                                                                \
+    if (VEC) {                                                                                     \
+      _Pragma("unroll") for (int q = 0; q < PER / 4; ++q) {                                        \
+        const int c_ = col(4 * q);                                                                 \
+        if (c_ < d) *reinterpret_cast<float4*>((dst_) + (off_) + c_) =                             \
+            make_float4(val_[4 * q], val_[4 * q + 1], val_[4 * q + 2], val_[4 * q + 3]);           \
+      }                                                                                            \
+    } else {                                                                                       \
+      _Pragma("unroll") for (int i = 0; i < PER; ++i) if (col(i) < d) (dst_)[(off_) + col(i)] = val_[i]; \
+    }                                                                                              \
+  }
   float s0[PER], s1[PER];
   if (t.in_mode == TR_IN_WRITE) {
-    float ov[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * TNT;
-      const bool ok = c < d;
-      ov[i] = ok ? t.out[o + c] : 0.f;
-      s0[i] = ok ? t.s0[o + c] : 0.f;
-      s1[i] = ok ? t.s1[o + c] : 0.f;
-    }
-    // the layer's 2x2 mix matrix: Sinkhorn in registers of wave 0
-    if (threadIdx.x < 64) {
-      float P[4];
-      sinkhorn2(t.mix, t.iters, P);
-      if (threadIdx.x == 0) { sP[0] = P[0]; sP[1] = P[1]; sP[2] = P[2]; sP[3] = P[3]; }
-    }
+    float ov[PER], w0v[PER], w1v[PER];
+    TR_LOAD(ov, t.out, o);
+    TR_LOAD(s0, t.s0, o);
+    TR_LOAD(s1, t.s1, o);
+    TR_LOAD(w0v, t.write_w, 0);
+    TR_LOAD(w1v, t.write_w, d);
     float z0 = 0.f, z1 = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * TNT;
-      if (c < d) {
-        z0 += t.write_w[c] * ov[i];
-        z1 += t.write_w[d + c] * ov[i];
-      }
+      z0 += w0v[i] * ov[i];
+      z1 += w1v[i] * ov[i];
     }
-    block_sum2_t<TNT, PER>(z0, z1, red);  // its barriers also publish sP
+    block_sum2_t<TNT, PER>(z0, z1, red);
     float w0, w1;
     softmax2(z0 + t.write_b[0], z1 + t.write_b[1], w0, w1);
-    const float P0 = sP[0], P1 = sP[1], P2 = sP[2], P3 = sP[3];
+    // the layer's 2x2 mix matrix (Sinkhorn of its logits, computed once per call)
+    const float P0 = t.P[0], P1 = t.P[1], P2 = t.P[2], P3 = t.P[3];
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const float a = s0[i], b = s1[i];
@@ -178,45 +194,37 @@ __global__ __launch_bounds__(TNT) void transition_kernel(TransitionArgs t) {
       s1[i] = P2 * a + P3 * b + w1 * ov[i];
     }
   } else {
+    TR_LOAD(s0, t.h, o);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * TNT;
-      s0[i] = s1[i] = c < d ? t.h[o + c] : 0.f;
-    }
+    for (int i = 0; i < PER; ++i) s1[i] = s0[i];
   }
 
   float xv[PER];
   if (t.out_mode == TR_OUT_READ) {
+    float r00[PER], r01[PER], r10[PER], r11[PER];
+    TR_LOAD(r00, t.read_w, 0);
+    TR_LOAD(r01, t.read_w, d);
+    TR_LOAD(r10, t.read_w, 2 * d);
+    TR_LOAD(r11, t.read_w, 3 * d);
     float z0 = 0.f, z1 = 0.f;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * TNT;
-      if (c < d) {
-        z0 += t.read_w[c] * s0[i] + t.read_w[d + c] * s1[i];
-        z1 += t.read_w[2 * d + c] * s0[i] + t.read_w[3 * d + c] * s1[i];
-      }
+      z0 += r00[i] * s0[i] + r01[i] * s1[i];
+      z1 += r10[i] * s0[i] + r11[i] * s1[i];
     }
     block_sum2_t<TNT, PER>(z0, z1, red);
     float r0, r1;
     softmax2(z0 + t.read_b[0], z1 + t.read_b[1], r0, r1);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * TNT;
-      xv[i] = r0 * s0[i] + r1 * s1[i];
-      if (c < d) {
-        t.s0_out[o + c] = s0[i];
-        t.s1_out[o + c] = s1[i];
-        t.x_out[o + c] = xv[i];
-      }
-    }
+    for (int i = 0; i < PER; ++i) xv[i] = r0 * s0[i] + r1 * s1[i];
+    TR_STORE(t.s0_out, o, s0);
+    TR_STORE(t.s1_out, o, s1);
+    TR_STORE(t.x_out, o, xv);
   } else {
     // plain state h: either unchanged (in = H) or the merge of the streams
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = threadIdx.x + i * TNT;
-      xv[i] = t.in_mode == TR_IN_WRITE ? (s0[i] + s1[i]) * 0.5f : s0[i];
-      if (t.in_mode == TR_IN_WRITE && c < d) t.h_out[o + c] = xv[i];
-    }
+    for (int i = 0; i < PER; ++i) xv[i] = t.in_mode == TR_IN_WRITE ? (s0[i] + s1[i]) * 0.5f : s0[i];
+    if (t.in_mode == TR_IN_WRITE) TR_STORE(t.h_out, o, xv);
     if (t.out_mode == TR_OUT_NONE) return;
   }
   float ss = 0.f, dummy = 0.f;
@@ -224,11 +232,33 @@ __global__ __launch_bounds__(TNT) void transition_kernel(TransitionArgs t) {
   for (int i = 0; i < PER; ++i) ss += xv[i] * xv[i];
   block_sum2_t<TNT, PER>(ss, dummy, red);
   const float inv = rsqrtf(ss / d + t.eps);
+  if (VEC) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int c = threadIdx.x + i * TNT;
-    if (c < d) t.xn[o + c] = f2bf_bits(xv[i] * inv * bf2f(t.norm_g[c]));
+    for (int q = 0; q < PER / 4; ++q) {
+      const int c = col(4 * q);
+      if (c >= d) continue;
+      const uint2 gv = *reinterpret_cast<const uint2*>(t.norm_g + c);
+      const float g4[4] = {bf2f((uint16_t)gv.x), bf2f((uint16_t)(gv.x >> 16)), bf2f((uint16_t)gv.y),
+                           bf2f((uint16_t)(gv.y >> 16))};
+      uint2 y;
+      y.x = (uint32_t)f2bf_bits(xv[4 * q] * inv * g4[0]) | ((uint32_t)f2bf_bits(xv[4 * q + 1] * inv * g4[1]) << 16);
+      y.y = (uint32_t)f2bf_bits(xv[4 * q + 2] * inv * g4[2]) | ((uint32_t)f2bf_bits(xv[4 * q + 3] * inv * g4[3]) << 16);
+      *reinterpret_cast<uint2*>(t.xn + o + c) = y;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (col(i) < d) t.xn[o + col(i)] = f2bf_bits(xv[i] * inv * bf2f(t.norm_g[col(i)]));
   }
+#undef TR_LOAD
+#undef TR_STORE
+}
+
+// The 2x2 mix matrices of the loop layers (Sinkhorn of each layer's mix
+// logits): one thread per layer.
+__global__ void sinkhorn_layers_kernel(SinkhornBatch sb) {
+  const int l = threadIdx.x;
+  if (l < sb.n) sinkhorn2(sb.mix[l], sb.iters, sb.out + 4 * l);
 }
 
 // Hidden state at the last position of each sequence: h, or the mean of the
@@ -331,6 +361,12 @@ hipError_t launch_transition(TransitionArgs t, hipStream_t s) {
 hipError_t launch_tap(const float* h, const float* s0, const float* s1, float* dst, int B, int T, int d,
                       hipStream_t s) {
   hipLaunchKernelGGL(tap_kernel, dim3(B), dim3(NT), 0, s, h, s0, s1, dst, T, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_sinkhorn_layers(const SinkhornBatch& sb, hipStream_t s) {
+  if (sb.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(sinkhorn_layers_kernel, dim3(1), dim3(64), 0, s, sb);
   return hipGetLastError();
 }
 
