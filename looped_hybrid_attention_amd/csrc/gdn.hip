@@ -432,18 +432,46 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, int n_
     const float gC = gC_next;
     __syncthreads();
     if (c + 1 < a.n_chunks) SCAN_LOAD(c + 1);
-    // entry state of chunk c
+    // entry state of chunk c (16-byte pieces; all LDS reads before the stores)
     {
       const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
-      for (int idx = tid; idx < 16 * DK; idx += NT) {
-        const int j = idx / DK, k = idx % DK;
-        P.S[(int64_t)(j0 + j) * DK + k] = sS[j * LS + k];
+      constexpr int NE = 16 * DK / 4 / NT;
+      static_assert(NE * 4 * NT == 16 * DK, "entry-state split");
+      f32x4 ev[NE];
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const int e = (tid + i * NT) * 4;
+        ev[i] = *reinterpret_cast<const f32x4*>(sS + (e / DK) * LS + e % DK);
+      }
+#pragma unroll
+      for (int i = 0; i < NE; ++i) {
+        const int e = (tid + i * NT) * 4;
+        *reinterpret_cast<f32x4*>(P.S + (int64_t)(j0 + e / DK) * DK + e % DK) = ev[i];
       }
     }
-    // U = Ut - W S^T ; wave w: rows 16w..16w+15, the 16 columns j
+    // U = Ut - W S^T ; wave w: rows 16w..16w+15, the 16 columns j.  Lane
+    // group kk contributes k = kk DK/4 + i at MFMA step i (a permutation of
+    // K, the same on both operands), so its operands are contiguous runs
+    // read with 128-bit loads, all before the MFMAs.
     {
-      f32x4 acc = {0, 0, 0, 0};
-      mm_nt_ilp(acc, sW + wave * 16 * LW, LW, sS, LS, DK);
+      constexpr int KQ = DK / 4;
+      float av[KQ], bv[KQ];
+      const float* ar = sW + (wave * 16 + i16) * LW + kk * KQ;
+      const float* br = sS + i16 * LS + kk * KQ;
+#pragma unroll
+      for (int q = 0; q < KQ / 4; ++q) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(ar + 4 * q);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(br + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { av[4 * q + e] = x[e]; bv[4 * q + e] = y[e]; }
+      }
+      f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < KQ; i += 2) {
+        acc = mfma16x16x4f32(av[i], bv[i], acc);
+        acc1 = mfma16x16x4f32(av[i + 1], bv[i + 1], acc1);
+      }
+      acc += acc1;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wave * 16 + 4 * kk + r;
@@ -457,7 +485,19 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, int n_
     if constexpr (TPW == 2) {
       const int nt0 = wave, nt1 = wave + NT / 64;
       f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-      mm_tn2(acc0, acc1, sU, LU, sKd + nt0 * 16, sKd + nt1 * 16, LK, CH);
+      float ua[CH / 4], k0v[CH / 4], k1v[CH / 4];
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q) {
+        const int k = kk + 4 * q;
+        ua[q] = sU[k * LU + i16];
+        k0v[q] = sKd[k * LK + nt0 * 16 + i16];
+        k1v[q] = sKd[k * LK + nt1 * 16 + i16];
+      }
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q) {
+        acc0 = mfma16x16x4f32(ua[q], k0v[q], acc0);
+        acc1 = mfma16x16x4f32(ua[q], k1v[q], acc1);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 4 * kk + r;
