@@ -132,6 +132,41 @@ DEV void mm_tn2(f32x4& acc0, f32x4& acc1, const float* A, int lda, const float* 
   }
 }
 
+// Operand staging for the fp32 MFMA with K read ahead: lane group kk takes
+// the contiguous quarter k = kk K/4 .. of K (a permutation of K, applied to
+// both operands of a product), so row operands are 128-bit LDS reads and all
+// reads are issued before the MFMAs.
+// this lane's quarter of row l%16 of a [16][K] row-major operand
+template <int K>
+DEV void row_quarter(float (&v)[K / 4], const float* A, int lda) {
+  const int l = threadIdx.x & 63;
+  const float* r = A + (l & 15) * lda + (l >> 4) * (K / 4);
+#pragma unroll
+  for (int q = 0; q < K / 16; ++q) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(r + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+  }
+}
+// this lane's quarter of column l%16 of a [K][16] row-major operand
+template <int K>
+DEV void col_quarter(float (&v)[K / 4], const float* B, int ldb) {
+  const int l = threadIdx.x & 63;
+  const float* c = B + (l >> 4) * (K / 4) * ldb + (l & 15);
+#pragma unroll
+  for (int q = 0; q < K / 4; ++q) v[q] = c[q * ldb];
+}
+// acc0 += a0 . b0, acc1 += a1 . b1 over staged quarters (two chains)
+template <int K>
+DEV void mma2(f32x4& acc0, f32x4& acc1, const float (&a0)[K / 4], const float (&b0)[K / 4],
+              const float (&a1)[K / 4], const float (&b1)[K / 4]) {
+#pragma unroll
+  for (int q = 0; q < K / 4; ++q) {
+    acc0 = mfma16x16x4f32(a0[q], b0[q], acc0);
+    acc1 = mfma16x16x4f32(a1[q], b1[q], acc1);
+  }
+}
+
 // Chunk workspace layout, per (seq b, head h, chunk c), fp32:
 //   W, Ut, Kd, Qp, Up: [CH][DK] each, then gC; S_c (entry state) [DV][DK].
 struct ChunkPtr {
@@ -253,9 +288,14 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   // A = beta_r exp(G_r - G_i) k_r.k_i (i < r), Mqk = exp(G_r - G_i) q_r.k_i (i <= r)
   {
     const int i16 = lane & 15, kk = lane >> 4;
+    float aK[DK / 4], aQ[DK / 4];
+    row_quarter<DK>(aK, sK + wave * 16 * LD, LD);
+    row_quarter<DK>(aQ, sQ + wave * 16 * LD, LD);
     for (int nt = 0; nt < CH / 16; ++nt) {
       f32x4 kk_acc = {0, 0, 0, 0}, qk_acc = {0, 0, 0, 0};
-      mm_nt2(kk_acc, qk_acc, sK + wave * 16 * LD, sQ + wave * 16 * LD, LD, sK + nt * 16 * LD, LD, DK);
+      float bK[DK / 4];
+      row_quarter<DK>(bK, sK + nt * 16 * LD, LD);
+      mma2<DK>(kk_acc, qk_acc, aK, bK, aQ, bK);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
@@ -327,11 +367,19 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   // W = (T diag(beta gamma)) K^, Ut = (T diag(beta)) V; wave w: rows 16w..16w+15
   constexpr int NTILE = DK / 16;
   f32x4 wacc[NTILE], uacc[NTILE];
+  {
+    float a0[CH / 4], a1[CH / 4];
+    row_quarter<CH>(a0, sA + wave * 16 * LC, LC);
+    row_quarter<CH>(a1, sT2 + wave * 16 * LC, LC);
 #pragma unroll
-  for (int nt = 0; nt < NTILE; ++nt) {
-    wacc[nt] = (f32x4){0, 0, 0, 0};
-    uacc[nt] = (f32x4){0, 0, 0, 0};
-    mm_nn2(wacc[nt], uacc[nt], sA + wave * 16 * LC, sT2 + wave * 16 * LC, LC, sK + nt * 16, sV + nt * 16, LD, CH);
+    for (int nt = 0; nt < NTILE; ++nt) {
+      wacc[nt] = (f32x4){0, 0, 0, 0};
+      uacc[nt] = (f32x4){0, 0, 0, 0};
+      float b0[CH / 4], b1[CH / 4];
+      col_quarter<CH>(b0, sK + nt * 16, LD);
+      col_quarter<CH>(b1, sV + nt * 16, LD);
+      mma2<CH>(wacc[nt], uacc[nt], a0, b0, a1, b1);
+    }
   }
   __syncthreads();  // sK, sV fully read: reuse them for W and Ut
   {
@@ -353,10 +401,15 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   // Qp = gamma Q - Mqk W, Up = Mqk Ut
   {
     const int i16 = lane & 15, kk = lane >> 4;
+    float am[CH / 4];
+    row_quarter<CH>(am, sM + wave * 16 * LC, LC);
 #pragma unroll
     for (int nt = 0; nt < NTILE; ++nt) {
       f32x4 mw = {0, 0, 0, 0}, mu = {0, 0, 0, 0};
-      mm_nn2(mw, mu, sM + wave * 16 * LC, sM + wave * 16 * LC, LC, sK + nt * 16, sV + nt * 16, LD, CH);
+      float b0[CH / 4], b1[CH / 4];
+      col_quarter<CH>(b0, sK + nt * 16, LD);
+      col_quarter<CH>(b1, sV + nt * 16, LD);
+      mma2<CH>(mw, mu, am, b0, am, b1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
