@@ -231,8 +231,9 @@ int loop_profile_read(loop_model* m, double* total_ms, int64_t* launches);
  *                     silu(A.gate^T) * (A.up^T)
  * Requires K % 64 == 0, lda and ldb multiples of 8, A and B 16-byte aligned.
  * d_ws / ws_bytes (device, optional): fp32 scratch for split-K partials,
- * used when M is small (< 512) and the buffer is large enough; the partials
- * are summed in split order (deterministic).  NULL = no split. */
+ * used when M is small (< 512), or for the last N % 256 columns (at most 128)
+ * of a large-M call, and the buffer is large enough; the partials are summed
+ * in split order (deterministic).  NULL = no split. */
 enum { LOOP_EPI_BF16 = 0, LOOP_EPI_F32 = 1, LOOP_EPI_F32_RES = 2, LOOP_EPI_SWIGLU = 3 };
 int loop_op_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                  const float* R, int32_t M, int32_t N, int32_t K, int32_t epi, float* d_ws,

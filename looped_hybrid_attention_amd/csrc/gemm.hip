@@ -282,24 +282,46 @@ hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t s) {
 
 
 // ------------------------------------------------- large-M tiles, LDS copy
-// 256 x 256 output tile, K in steps of 64, four waves (one per SIMD), each
+// 256 x 256 output tile, K in steps of KB, four waves (one per SIMD), each
 // computing 128 x 128 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with the
 // accumulators in AGPRs.  A and B tiles go global -> LDS with buffer_load
-// ... lds, double-buffered: the next tile's copies are issued at the top of
-// a tile; its barrier sits before the MFMAs of the last 16-deep step, so the
-// next tile's first operand reads overlap them.  Operand reads run one
-// 16-deep step ahead of the MFMAs.  Rows are unpadded (128 bytes); chunk c of
-// row r sits at c ^ ((r / 2) % 8) so that the 128-bit operand reads of 16
-// consecutive rows hit distinct banks.
+// ... lds through an NS-stage ring: the copies of step t + NS - 1 are issued
+// at the top of step t, so NS - 1 steps of copies are in flight while a step
+// computes.  The barrier that publishes step t + 1 sits before the MFMAs of
+// step t's last 16-deep slice, so the next step's first operand reads overlap
+// them.  Operand reads run one 16-deep slice ahead of the MFMAs.  Rows are
+// unpadded (KB * 2 bytes); 16-byte chunk c of row r sits at c ^ swz(r), which
+// puts the 128-bit operand reads of 16 consecutive rows on distinct banks.
+template <int KB>
+struct DbShape {
+  static constexpr int ROW = KB * 2;               // bytes of one operand row
+  static constexpr int CPR = ROW / 16;             // 16-byte chunks per row
+  static constexpr int RPI = 1024 / ROW;           // rows per 1 KB copy instruction
+  static constexpr int CPW = 256 / RPI / 4;        // copy instructions per wave per operand
+  static constexpr int TILE = 256 * ROW;           // bytes of one operand tile
+  static constexpr int STAGE = 2 * TILE;           // A then B
+  static DEV int swz(int row) { return (row / (16 / CPR)) % CPR; }
+};
 constexpr int DB_BM = 256, DB_BN = 256;
-constexpr int DB_TILE = 256 * BK * 2;        // bytes of one operand tile
-constexpr int DB_STAGE = 2 * DB_TILE;        // A then B
-constexpr int DB_LDS = 2 * DB_STAGE;
-DEV int db_swz(int row) { return (row >> 1) & 7; }
+constexpr int db_lds(int kb, int ns) { return ns * 2 * 256 * kb * 2; }
 
-template <int EPI>
+// s_waitcnt with vmcnt(N), other counters untouched
+template <int N>
+DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Workgroup barrier after this wave's LDS reads have returned.  Copies still
+// in flight to other ring stages stay in flight: a fence would make the
+// compiler drain them (it counts them as pending LDS writes).  The memory
+// clobber keeps LDS accesses on their side of the barrier.
+DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int EPI, int KB, int NS>
 __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes) {
-  constexpr int TM = 4, TN = 4;
+  using S = DbShape<KB>;
+  static_assert(NS >= 2 && KB % 32 == 0 && S::CPW * 2 * (NS - 2) < 64, "ring shape");
+  constexpr int TM = 4, TN = 4, KS = KB / 16;
   extern __shared__ __align__(16) uint8_t db_smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
@@ -310,15 +332,15 @@ __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_
   const int n0 = tn * OUT_BN;
 
   // Byte offsets (k = 0) of this lane's 16-byte piece in each of the wave's
-  // 8 copy instructions per operand tile: instruction n fills rows
-  // 8n .. 8n+7, lane l row 8n + l/8 at chunk l%8 (holding logical chunk
-  // (l%8) ^ swizzle).  Rows past M (N) are clamped: they feed outputs that
-  // are never stored.
-  int a_off[8], b_off[8];
+  // copy instructions per operand tile: instruction n fills rows RPI n ..
+  // RPI n + RPI - 1, lane l row RPI n + l / CPR at chunk l % CPR (holding
+  // logical chunk (l % CPR) ^ swz).  Rows past M (N) are clamped: they feed
+  // outputs that are never stored.
+  int a_off[S::CPW], b_off[S::CPW];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = (wave * 8 + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ db_swz(row);
+  for (int i = 0; i < S::CPW; ++i) {
+    const int row = (wave * S::CPW + i) * S::RPI + lane / S::CPR;
+    const int c = (lane % S::CPR) ^ S::swz(row);
     a_off[i] = (min(m0 + row, g.M - 1) * (int)g.lda + c * 8) * 2;
     int gn;
     if (EPI == LOOP_EPI_SWIGLU) {
@@ -333,29 +355,30 @@ __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_
   const auto b_rsrc = buffer_rsrc(g.B, b_bytes);
 #define DB_COPY(k0_, stage_)                                                                       \
   {                                                                                                \
-    uint8_t* S_ = db_smem + (stage_) * DB_STAGE;                                                   \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                  \
-        copy16_to_lds(a_rsrc, a_off[i], (k0_) * 2, (lds_void*)(S_ + (wave * 8 + i) * 1024));      \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                  \
-        copy16_to_lds(b_rsrc, b_off[i], (k0_) * 2, (lds_void*)(S_ + DB_TILE + (wave * 8 + i) * 1024)); \
+    uint8_t* S_ = db_smem + (stage_) * S::STAGE;                                                   \
+    _Pragma("unroll") for (int i = 0; i < S::CPW; ++i)                                             \
+        copy16_to_lds(a_rsrc, a_off[i], (k0_) * 2, (lds_void*)(S_ + (wave * S::CPW + i) * 1024));  \
+    _Pragma("unroll") for (int i = 0; i < S::CPW; ++i)                                             \
+        copy16_to_lds(b_rsrc, b_off[i], (k0_) * 2,                                                 \
+                      (lds_void*)(S_ + S::TILE + (wave * S::CPW + i) * 1024));                     \
   }
   // operand reads: lane (lr, half) row lr of each 32-row tile, chunk 2 ks + half
-  const int lr = lane & 31, half = lane >> 5, sw = db_swz(lr);
-  const int a_row = (wm * 128 + lr) * (BK * 2), b_row = DB_TILE + (wn * 128 + lr) * (BK * 2);
+  const int lr = lane & 31, half = lane >> 5, sw = S::swz(lr);
+  const int a_row = (wm * 128 + lr) * S::ROW, b_row = S::TILE + (wn * 128 + lr) * S::ROW;
   bf16x8 fa[2][TM], fb[2][TN];
 #define DB_READ(stage_, ks_, buf_)                                                                 \
   {                                                                                                \
-    const uint8_t* S_ = db_smem + (stage_) * DB_STAGE + (((2 * (ks_) + half) ^ sw) << 4);          \
+    const uint8_t* S_ = db_smem + (stage_) * S::STAGE + (((2 * (ks_) + half) ^ sw) << 4);          \
     _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                 \
-        fa[buf_][i] = *reinterpret_cast<const bf16x8*>(S_ + a_row + i * 32 * (BK * 2));            \
+        fa[buf_][i] = *reinterpret_cast<const bf16x8*>(S_ + a_row + i * 32 * S::ROW);              \
     _Pragma("unroll") for (int j = 0; j < TN; ++j)                                                 \
-        fb[buf_][j] = *reinterpret_cast<const bf16x8*>(S_ + b_row + j * 32 * (BK * 2));            \
+        fb[buf_][j] = *reinterpret_cast<const bf16x8*>(S_ + b_row + j * 32 * S::ROW);              \
   }
 #define DB_MFMA(buf_)                                                                              \
   _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
       _Pragma("unroll") for (int j = 0; j < TN; ++j)                                               \
           acc[i][j] = mfma32x32x16(fa[buf_][i], fb[buf_][j], acc[i][j]);
-// interleave: the 8 reads of the next step spread over the 16 MFMAs
+// interleave: the 8 reads of the next slice spread over the 16 MFMAs
 #define DB_SCHED()                                                                                 \
   _Pragma("unroll") for (int q = 0; q < TM + TN; ++q) {                                            \
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                             \
@@ -368,33 +391,44 @@ __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
 
-  const int nk = g.K / BK;
-  DB_COPY(0, 0);
-  wait_vmem();
-  __syncthreads();
+  // Copies complete in issue order, so "at most CPW*2*(NS-2) outstanding"
+  // means every stage but the NS-2 newest has landed.  Steps past the end
+  // re-copy the last step into an idle stage, harmlessly: nothing reads it.
+  constexpr int IN_FLIGHT = S::CPW * 2 * (NS - 2);
+  const int nk = g.K / KB;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p) DB_COPY(min(p, nk - 1) * KB, p);
+  wait_vmcnt<IN_FLIGHT>();
+  lds_barrier();
   DB_READ(0, 0, 0);
+  int s = 0, s_fill = NS - 1;
   for (int t = 0; t < nk; ++t) {
-    const int s = t & 1;
-    // next tile's copies (the last tile re-copies itself into the idle
-    // buffer, harmlessly: nothing reads it afterwards)
-    DB_COPY(min(t + 1, nk - 1) * BK, s ^ 1);
+    // the stage refilled here was last read before the previous barrier
     DB_READ(s, 1, 1);
+    DB_COPY(min(t + NS - 1, nk - 1) * KB, s_fill);
     DB_MFMA(0);
-    DB_SCHED();
-    DB_READ(s, 2, 0);
-    DB_MFMA(1);
-    DB_SCHED();
-    DB_READ(s, 3, 1);
-    DB_MFMA(0);
-    DB_SCHED();
-    // all of this tile's reads and the next tile's copies are done in every
-    // wave past this barrier
-    wait_vmem();
-    __syncthreads();
-    DB_READ(s ^ 1, 0, 0);
-    DB_MFMA(1);
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+    _Pragma("unroll") for (int q = 0; q < TM * TN; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2 * S::CPW / (TM * TN), 0);
+    }
+#pragma unroll
+    for (int ks = 2; ks < KS; ++ks) {
+      DB_READ(s, ks, ks & 1);
+      DB_MFMA((ks - 1) & 1);
+      DB_SCHED();
+    }
+    // step t + 1 has landed and every wave is done reading step t - 1 past
+    // this barrier
+    wait_vmcnt<IN_FLIGHT>();
+    lds_barrier();
+    s = (s + 1 == NS) ? 0 : s + 1;
+    s_fill = (s_fill + 1 == NS) ? 0 : s_fill + 1;
+    DB_READ(s, 0, 0);
+    DB_MFMA((KS - 1) & 1);
     DB_SCHED();
   }
+  wait_vmem();
 #undef DB_COPY
 #undef DB_READ
 #undef DB_MFMA
@@ -469,35 +503,29 @@ __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_
   }
 }
 
+// Ring shape: two stages of K = 64 (128 KB of LDS).  Deeper rings of K = 32
+// steps (up to 5 stages, the whole 160 KB) measured slower on every shape.
+constexpr int DB_KB = 64, DB_NS = 2;
 template <int EPI>
 hipError_t launch_db(const GemmArgs& g, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? DB_BN / 2 : DB_BN;
+  constexpr int lds = db_lds(DB_KB, DB_NS);
   const int tiles = ((g.M + DB_BM - 1) / DB_BM) * ((g.N + OUT_BN - 1) / OUT_BN);
-  auto k = gemm_db_kernel<EPI>;
+  auto k = gemm_db_kernel<EPI, DB_KB, DB_NS>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, DB_LDS);
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k, dim3(tiles), dim3(256), DB_LDS, s, g, a_bytes, b_bytes);
+  hipLaunchKernelGGL(k, dim3(tiles), dim3(256), lds, s, g, a_bytes, b_bytes);
   return hipGetLastError();
 }
 
-// Small-M calls (decode) get too few output tiles to fill the chip: split K
-// so that tiles * splits >= ~512 workgroups, if a partial buffer is given.
+// 64 x 128 tiles; calls with too few tiles to fill the chip split K so that
+// tiles * splits >= ~512 workgroups, if a large enough partial buffer is given.
 template <int EPI>
-hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
-  // Large M: 256 x 256 tiles fed by LDS copies; operands whose byte range
-  // does not fit the 32-bit buffer offsets use the register-staged kernel
-  // (eight waves, two per SIMD).
-  if (g.M >= 512) {
-    const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
-    const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
-    if (g.K % BK == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31))
-      return launch_db<EPI>(g, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
-    return launch_cfg<256, 256, 2, 4, EPI, false>(g, 1, s);
-  }
+hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? 64 : 128;
   const int tiles = ((g.M + 63) / 64) * ((g.N + OUT_BN - 1) / OUT_BN);
   int splits = 1;
@@ -508,6 +536,40 @@ hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
     return launch_cfg<64, 128, 2, 2, EPI, true>(g, splits, s);
   }
   return launch_cfg<64, 128, 2, 2, EPI, false>(g, 1, s);
+}
+
+// Large M: 256 x 256 tiles; small M (decode): 64 x 128 tiles, split K.
+template <int EPI>
+hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
+  // Large M: 256 x 256 tiles fed by LDS copies; operands whose byte range
+  // does not fit the 32-bit buffer offsets use the register-staged kernel
+  // (eight waves, two per SIMD).
+  if (g.M >= 512) {
+    const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
+    const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
+    if (g.K % DB_KB == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31)) {
+      // A strip of at most 128 columns past the last whole 256-column tile
+      // would cost a full extra round of 256 x 256 tiles (e.g. 8224 columns:
+      // 1024 whole tiles, then 32 more on an otherwise idle chip); 64 x 128
+      // tiles with split K cover it in a fraction of that.
+      const int rem = g.N % DB_BN;
+      if (EPI != LOOP_EPI_SWIGLU && rem != 0 && rem <= 128 && g.N > DB_BN) {
+        const int nm = g.N - rem;
+        GemmArgs main = g, tail = g;
+        main.N = main.swiglu_F = nm;
+        hipError_t e = launch_db<EPI>(main, (uint32_t)a_bytes, (uint32_t)((int64_t)nm * g.ldb * 2), s);
+        if (e != hipSuccess) return e;
+        tail.B = g.B + (int64_t)nm * g.ldb;
+        tail.C = (uint8_t*)g.C + (int64_t)nm * (EPI == LOOP_EPI_BF16 ? 2 : 4);
+        tail.R = g.R ? g.R + nm : nullptr;
+        tail.N = tail.swiglu_F = rem;
+        return launch_small<EPI>(tail, ws_bytes, s);
+      }
+      return launch_db<EPI>(g, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+    }
+    return launch_cfg<256, 256, 2, 4, EPI, false>(g, 1, s);
+  }
+  return launch_small<EPI>(g, ws_bytes, s);
 }
 
 }  // namespace

@@ -26,7 +26,7 @@ def _ref(a, b, rows=None):
 
 
 SMALL = [(1, 64, 64), (37, 100, 128), (300, 520, 256), (64, 256, 64), (513, 300, 192),
-         (1000, 1032, 256), (700, 768, 768)]
+         (1000, 1032, 256), (700, 768, 768), (600, 280, 64), (530, 300, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
@@ -99,8 +99,9 @@ def test_gemm_real_shapes_sampled(M, N, K, epi):
         R = C
         gu = gu + r[rows]
     A, B = dev(a, torch), dev(b, torch)
+    ws = torch.empty(16 * M * 128, dtype=torch.float32, device="cuda")   # as the model passes one
     L.loop_op_gemm(A.data_ptr(), K, B.data_ptr(), K, C.data_ptr(), N,
-                   R.data_ptr() if R is not None else 0, M, N, K, epi, stream(torch))
+                   R.data_ptr() if R is not None else 0, M, N, K, epi, stream(torch), ws.data_ptr(), ws.numel() * 4)
     torch.cuda.synchronize()
     got = host(C)[rows]
     if epi == 3:
@@ -112,9 +113,11 @@ def test_gemm_real_shapes_sampled(M, N, K, epi):
 
 
 # The decode projections (64 sequences): split-K with fp32 partials summed in
-# split order, against the float64 product; also bit-identical reruns.
+# split order, against the float64 product; also bit-identical reruns.  The
+# large-M shapes with a narrow column remainder run that strip split-K.
 DECODE = [(64, 10240, 4096, 0), (64, 8224, 4096, 0), (64, 4096, 4096, 2), (64, 4096, 2048, 1),
-          (64, 12288, 4096, 3), (64, 4096, 12288, 2), (1, 4096, 12288, 2), (37, 520, 768, 3)]
+          (64, 12288, 4096, 3), (64, 4096, 12288, 2), (1, 4096, 12288, 2), (37, 520, 768, 3),
+          (1024, 288, 1024, 0), (1024, 288, 1024, 2), (600, 1032, 512, 1)]
 
 
 @pytest.mark.parametrize("M,N,K,epi", DECODE)
