@@ -55,8 +55,11 @@ DEV float block_sum(float v, float* red) {
   return s;
 }
 
-DEV float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
-DEV float siluf_(float x) { return x / (1.0f + __expf(-x)); }
+// Hardware exp2 and reciprocal (about 1 ulp each): far below the bf16
+// rounding that every consumer applies, and a fraction of the cost of an
+// IEEE division.  Large |x| saturates correctly (rcp(inf) = 0).
+DEV float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+DEV float siluf_(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Global -> LDS copies that bypass registers (buffer_load ... lds, gfx950
 // 16-byte form).  MUBUF rather than the FLAT form: with a FLAT LDS copy in

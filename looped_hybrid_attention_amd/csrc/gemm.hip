@@ -440,19 +440,33 @@ __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_
   const int row_base = m0 + wm * 128 + 4 * half;
   const bool full = m0 + DB_BM <= g.M && n0 + OUT_BN <= g.N;
   if (EPI == LOOP_EPI_SWIGLU) {
+    uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < TN; j += 2) {
+        const int col = n0 + wn * 64 + (j / 2) * 32 + lr;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          uint16_t o[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[r] = f2bf_bits(siluf_(acc[i][j][r]) * acc[i][j + 1][r]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            C[(int64_t)(row_base + i * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc + col] = o[r];
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < TN; j += 2) {
       const int col = n0 + wn * 64 + (j / 2) * 32 + lr;
-      if (!full && col >= g.N) continue;
+      if (col >= g.N) continue;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-          if (full || row < g.M) {
-            const float gt = acc[i][j][r], up = acc[i][j + 1][r];
-            reinterpret_cast<uint16_t*>(g.C)[(int64_t)row * g.ldc + col] = f2bf_bits(siluf_(gt) * up);
-          }
+          if (row < g.M) C[(int64_t)row * g.ldc + col] = f2bf_bits(siluf_(acc[i][j][r]) * acc[i][j + 1][r]);
         }
     }
     return;
