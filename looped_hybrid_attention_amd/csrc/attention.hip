@@ -410,42 +410,38 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
 // --------------------------------------------------------------- decode
 // Workgroup = (split of DEC_SPLIT keys, KV head, sequence): the G query heads
 // of the KV head against keys [split*DEC_SPLIT, min(pos+1, ...)).  HBM-bound:
-// every K and V^T byte of the split is read once, straight into MFMA
-// operands.  Scores S^T[key][g] = K . q^T with v_mfma_f32_16x16x32_bf16 (16
-// keys x 16 head columns, G of them used); probabilities go through LDS as
-// bf16 [g][key]; O^T[d][g] += V^T[d][key] . P[key][g] with the same MFMA.
-// Writes per (head, split) the unnormalised o[D], the split max m and sum l;
-// the combine kernel merges the splits in split order.
+// every K and V^T byte of the split is read once, straight from HBM into MFMA
+// operands, and nothing else touches memory inside the loop.
+//
+// Each wave takes 32-key steps (waves interleaved over the split) and keeps
+// its own online softmax in registers.  Scores S^T[key][g] = K . q^T on
+// v_mfma_f32_16x16x32_bf16 (16 keys x 16 head columns, G used), two passes
+// per step.  The A-operand lane of row i loads key 8*(i/4) + 4u + i%4 in pass
+// u, so the lane holding head g (= lane % 16) and row group lg (= lane / 16)
+// ends up with exactly keys 8 lg .. 8 lg + 7: the bf16 probabilities of those
+// keys are the B operand of O^T[d][g] += V^T[d][key] P[key][g] as they stand,
+// with no exchange between lanes.  O^T accumulates in the same lanes (head g
+// = lane % 16), so the softmax rescale is lane-local.  At the end the four
+// waves merge through LDS and the workgroup writes, per head, the
+// unnormalised o[D], its max m (log2 units) and its sum l; the combine kernel
+// merges the splits in split order.
 constexpr int DEC_NT = 256;
-constexpr int DEC_SPLIT = 512;
-constexpr int DEC_PS = DEC_SPLIT + 8;  // bf16 row of P in LDS
-
-DEV f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
+constexpr int DEC_SPLIT = DEC_SPLIT_KEYS;
 
 template <int D, int G>
 __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a) {
   static_assert(G <= 16, "query heads per KV head");
   constexpr int NKS = D / 32;   // 32-dim steps of the score MFMA
   constexpr int NDT = D / 16;   // 16-dim output tiles
-  __shared__ float sc[G][DEC_SPLIT];
-  __shared__ __align__(16) uint16_t sp[16 * DEC_PS];
-  __shared__ float sm[G], sl[G];
+  __shared__ float wm[4][G], wl[4][G];
+  __shared__ float wo[4][G][D];
+  __shared__ u32x4 sq[16 * D / 8];
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int pos = a.pos[b];
   const int k_begin = split * DEC_SPLIT;
   const int k_end = min(pos + 1, k_begin + DEC_SPLIT);
-  float* part = a.partial + (((int64_t)b * a.Hq + kvh * G) * a.n_split + split) * (D + 2);
-  const int64_t part_head_stride = (int64_t)a.n_split * (D + 2);
-  if (k_begin >= k_end) {  // empty split: neutral element
-    for (int i = threadIdx.x; i < G * (D + 2); i += DEC_NT) {
-      const int g = i / (D + 2), c = i % (D + 2);
-      part[g * part_head_stride + c] = c == D ? -1e30f : 0.f;
-    }
-    return;
-  }
+  if (k_begin >= k_end) return;  // past the sequence: the combine never reads it
   const int nk = k_end - k_begin;
   const int64_t slot_b = a.seq_slot[b];
   const uint16_t* Kc = a.k_cache + ((slot_b * a.Hkv + kvh) * (int64_t)a.max_seq + k_begin) * D;
@@ -453,129 +449,155 @@ __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
 
-  // q^T operand: lane supplies q[g = l16][32 ks + 8 lg .. +8] (zero for g >= G)
-  bf16x8 qf[NKS];
-  {
-    const uint16_t* qs = a.q + ((int64_t)b * a.Hq + kvh * G + min(l16, G - 1)) * D;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      uint4 v = l16 < G ? *reinterpret_cast<const uint4*>(qs + ks * 32 + lg * 8) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+  // q^T operand, kept in LDS (registers go to the loads in flight): lane
+  // supplies q[g = l16][32 ks + 8 lg .. +8], zero for g >= G
+  for (int i = threadIdx.x; i < 16 * D / 8; i += DEC_NT) {
+    const int g = i / (D / 8), c = i % (D / 8);
+    sq[i] = g < G ? *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.Hq + kvh * G + g) * D + c * 8)
+                  : (u32x4){0, 0, 0, 0};
   }
-  // scores: each wave takes two 16-key groups at a time (32 loads per lane in
-  // flight for D = 256), groups round-robin over the waves
-  for (int g0 = wave * 32; g0 < nk; g0 += 4 * 32) {
-    u32x4 kv[2][NKS];
+  __syncthreads();
+  // Buffer loads: one 32-bit lane offset per step, the per-load displacements
+  // in the instruction's immediate (K) or a scalar offset (V^T tiles).  The K
+  // range ends at key nk, so K rows past it read as zero (and are masked).
+  const int krow = 8 * (l16 >> 2) + (l16 & 3);  // key of this A-operand row in pass 0 (pass 1: + 4)
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kc, (uint32_t)nk * D * 2);
+  // V^T range: to the end of this (sequence, head) block
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vc, (uint32_t)((int64_t)D * a.max_seq - k_begin) * 2);
+  const int kvo = (krow * D + lg * 8) * 2;
+  const int vvo = (l16 * a.max_seq + lg * 8) * 2;
+  const int vtile = 16 * a.max_seq * 2;  // bytes between 16-dim tiles of V^T
+
+  float m = -1e30f, l = 0.f;  // running max (log2 units) and this lane's partial sum
+  f32x4 o[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) o[i] = (f32x4){0, 0, 0, 0};
+
+  for (int kb = wave * 32; kb < nk; kb += 4 * 32) {
+    u32x4 kv[2][NKS], vv[NDT];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) kv[u][ks] = buffer_load16(krs, kvo + (kb * D + u * 4 * D + ks * 32) * 2, 0);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vv[dt] = buffer_load16(vrs, vvo + kb * 2, dt * vtile);
+    if (kb + 32 > nk) {
+      // ragged last step: V^T entries of keys at or past nk are zeroed (their
+      // probabilities are zero, but the cache there may hold anything)
+      const int kk = kb + lg * 8;  // first of this lane's 8 keys
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t w = vv[dt][j];
+          if (kk + 2 * j >= nk) w &= 0xFFFF0000u;
+          if (kk + 2 * j + 1 >= nk) w &= 0x0000FFFFu;
+          vv[dt][j] = w;
+        }
+    }
+    f32x4 sacc[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int key = g0 + 16 * u + l16;
+      sacc[u] = (f32x4){0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
-        kv[u][ks] = key < nk ? *reinterpret_cast<const u32x4*>(Kc + (int64_t)key * D + ks * 32 + lg * 8)
-                             : (u32x4){0, 0, 0, 0};
+        sacc[u] = mfma16x16x32(__builtin_bit_cast(bf16x8, kv[u][ks]),
+                               __builtin_bit_cast(bf16x8, sq[l16 * (D / 8) + ks * 4 + lg]), sacc[u]);
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      f32x4 acc = {0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) acc = mfma16x16x32(__builtin_bit_cast(bf16x8, kv[u][ks]), qf[ks], acc);
-      // lane holds keys g0 + 16u + 4 lg + r of head l16
-      if (l16 < G) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kk = g0 + 16 * u + 4 * lg + r;
-          if (kk < DEC_SPLIT) sc[l16][kk] = kk < nk ? acc[r] * a.scale_log2 : -1e30f;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // per-head max and sum over the split (wave w: heads w, w+4, ...)
-  for (int g = wave; g < G; g += 4) {
+    // lane holds keys kb + 8 lg + 4 u + r of head l16
+    float sv[8];
     float mx = -1e30f;
-    for (int k = lane; k < nk; k += 64) mx = fmaxf(mx, sc[g][k]);
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int k = lane; k < DEC_SPLIT; k += 64) {
-      const float p = k < nk ? exp2f(sc[g][k] - mx) : 0.f;
-      sum += p;
-      sp[g * DEC_PS + k] = f2bf_bits(p);
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) { sm[g] = mx; sl[g] = sum; }
-  }
-  for (int i = threadIdx.x; i < (16 - G) * DEC_SPLIT; i += DEC_NT)
-    sp[(G + i / DEC_SPLIT) * DEC_PS + i % DEC_SPLIT] = 0;
-  __syncthreads();
-  // O^T[d][g] += V^T[d][key] P[key][g]; wave w: d-tiles w, w+4, ...
-  constexpr int TPW = (NDT + 3) / 4;
-  f32x4 o[TPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) o[i] = (f32x4){0, 0, 0, 0};
-  const int nsteps = (nk + 31) / 32;
-  // four 32-key steps per iteration: their V^T loads are all in flight
-  // before the MFMAs
-  for (int st0 = 0; st0 < nsteps; st0 += 4) {
-    u32x4 vv[4][TPW];
-    bf16x8 pf[4];
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kk = (st0 + u) * 32 + lg * 8;  // first of this lane's 8 keys
-      pf[u] = kk < DEC_SPLIT ? *reinterpret_cast<const bf16x8*>(sp + l16 * DEC_PS + kk) : (bf16x8){};
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int dt = wave + 4 * i;
-        u32x4 v = {0, 0, 0, 0};
-        if (dt < NDT && kk < nk) {
-          const int d = dt * 16 + l16;
-          v = *reinterpret_cast<const u32x4*>(Vc + (int64_t)d * a.max_seq + kk);
-          if (kk + 8 > nk) {
-            uint16_t* e = reinterpret_cast<uint16_t*>(&v);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (kk + j >= nk) e[j] = 0;
-          }
-        }
-        vv[u][i] = v;
+      for (int r = 0; r < 4; ++r) {
+        const int key = kb + 8 * lg + 4 * u + r;
+        sv[4 * u + r] = key < nk ? sacc[u][r] * a.scale_log2 : -1e30f;
+        mx = fmaxf(mx, sv[4 * u + r]);
       }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m, mx);
+    const float alpha = exp2f(m - m_new);
+    m = m_new;
+    bf16x8 pf;
+    float ps = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = l16 < G ? exp2f(sv[j] - m_new) : 0.f;
+      ps += p;
+      pf[j] = f2bf(p);
     }
+    l = l * alpha + ps;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) o[i] = mfma16x16x32(__builtin_bit_cast(bf16x8, vv[u][i]), pf[u], o[i]);
+    for (int dt = 0; dt < NDT; ++dt) {
+      o[dt] *= alpha;
+      o[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vv[dt]), pf, o[dt]);
+    }
   }
-  // lane holds O^T[d = 16 dt + 4 lg + r][g = l16]
+  // this wave's sum over its keys: the four row groups of head l16
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
   if (l16 < G) {
+    if (lg == 0) { wm[wave][l16] = m; wl[wave][l16] = l; }
+    // lane holds O^T[d = 16 dt + 4 lg + r][g = l16]
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int dt = wave + 4 * i;
-      if (dt >= NDT) break;
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part[l16 * part_head_stride + dt * 16 + 4 * lg + r] = o[i][r];
-    }
+      for (int r = 0; r < 4; ++r) wo[wave][l16][dt * 16 + 4 * lg + r] = o[dt][r];
   }
-  if (threadIdx.x < G) {
-    part[threadIdx.x * part_head_stride + D] = sm[threadIdx.x];
-    part[threadIdx.x * part_head_stride + D + 1] = sl[threadIdx.x];
+  __syncthreads();
+  float* part = a.partial + (((int64_t)b * a.Hq + kvh * G) * a.n_split + split) * (D + 2);
+  const int64_t part_head_stride = (int64_t)a.n_split * (D + 2);
+  for (int i = threadIdx.x; i < G * D; i += DEC_NT) {
+    const int g = i / D, dd = i % D;
+    const float M = fmaxf(fmaxf(wm[0][g], wm[1][g]), fmaxf(wm[2][g], wm[3][g]));
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc += wo[w][g][dd] * exp2f(wm[w][g] - M);
+    part[g * part_head_stride + dd] = acc;
+    if (dd == 0) {
+      float Ls = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) Ls += wl[w][g] * exp2f(wm[w][g] - M);
+      part[g * part_head_stride + D] = M;
+      part[g * part_head_stride + D + 1] = Ls;
+    }
   }
 }
 
-// Merge the splits of one (sequence, query head) in split order; apply the
-// output gate; store bf16.
+// Merge the splits of one (sequence, query head) in split order (only the
+// splits that hold keys of the sequence); apply the output gate; store bf16.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeAttnArgs a) {
+  __shared__ float wsplit[DEC_MAX_SPLITS];
+  __shared__ float red[4];
   const int hq = blockIdx.x, b = blockIdx.y;
+  const int ns = (a.pos[b] + DEC_SPLIT) / DEC_SPLIT;  // splits holding keys 0..pos
   const float* part = a.partial + ((int64_t)b * a.Hq + hq) * a.n_split * (D + 2);
-  float M = -1e30f;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, part[s * (D + 2) + D]);
+  float mloc = -1e30f;
+  for (int s = threadIdx.x; s < ns; s += 256) mloc = fmaxf(mloc, part[s * (D + 2) + D]);
+  mloc = wave_max(mloc);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mloc;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  for (int s = threadIdx.x; s < ns; s += 256) wsplit[s] = exp2f(part[s * (D + 2) + D] - M);
+  __syncthreads();
   float Lsum = 0.f;
-  for (int s = 0; s < a.n_split; ++s) Lsum += part[s * (D + 2) + D + 1] * exp2f(part[s * (D + 2) + D] - M);
+  for (int s = 0; s < ns; ++s) Lsum += part[s * (D + 2) + D + 1] * wsplit[s];
   const uint16_t* g = a.gate + (int64_t)b * a.gate_stride + hq * D;
   uint16_t* out = a.out + (int64_t)b * a.out_stride + hq * D;
   for (int d = threadIdx.x; d < D; d += 256) {
     float o = 0.f;
-    for (int s = 0; s < a.n_split; ++s) o += part[s * (D + 2) + d] * exp2f(part[s * (D + 2) + D] - M);
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[(s + j) * (D + 2) + d];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o += v[j] * wsplit[s + j];
+    }
+    for (; s < ns; ++s) o += part[s * (D + 2) + d] * wsplit[s];
     out[d] = f2bf_bits(o / Lsum * sigmoidf_(bf2f(g[d])));
   }
 }
@@ -617,6 +639,8 @@ hipError_t flash_d(const FlashArgs& a, int B, hipStream_t s) {
 
 template <int D, int G>
 hipError_t decode_dg(const DecodeAttnArgs& a, int B, hipStream_t s) {
+  if (a.split_len != DEC_SPLIT || a.n_split > DEC_MAX_SPLITS || (int64_t)a.n_split * DEC_SPLIT < a.max_seq)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(a.n_split, a.Hkv, B), dim3(DEC_NT), 0, s, a);
   hipLaunchKernelGGL(decode_combine_kernel<D>, dim3(a.Hq, B), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -29,6 +29,12 @@ DEV f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%16][(l/16)*8 .. +8]
+// and B^T[l%16][(l/16)*8 .. +8]; its 4 results are D[4*(l/16) + r][l%16].
+DEV f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 DEV float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -74,6 +80,10 @@ DEV __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
 // (dst and soffset wave-uniform).  Completion is counted by vmcnt.
 DEV void copy16_to_lds(__amdgpu_buffer_rsrc_t src, int voffset, int soffset, lds_void* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, dst, 16, voffset, soffset, 0, 0);
+}
+// 16 bytes at byte voffset + soffset of a raw buffer (zero past its size).
+DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
 }
 // s_waitcnt vmcnt(0): this wave's vector memory operations (LDS copies
 // included) have completed.

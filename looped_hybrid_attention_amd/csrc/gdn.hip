@@ -670,33 +670,47 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
   }
 }
 
-// ------------------------------------------------ token recurrence (decode)
-// grid (Dv / 16, head, seq); 16 rows of S per workgroup, 16 threads per row.
-// Tokens of the call in order (T = 1 for decode).
+// ------------------------------------------------------------- decode
+// Token-by-token recurrence (decode: one token per sequence; the tokens of a
+// call in order).  One workgroup per (sequence, head) keeps the whole state
+// S [Dv][Dk] in registers (eight waves): load j of wave w covers RPI whole
+// rows, lane l holding the 4 entries k = 4 (l % CPR) .. of row
+// w Dv/8 + j RPI + l / CPR,
+// so every load and store is a contiguous 1 KB per wave.  Per row the two
+// dot products S k and S q are reduced over the row's CPR lanes; then
+//   u = beta (v - alpha S k),  S <- alpha S + u k^T,  o = S q,
+// and wave 0 applies the output RMSNorm over Dv (gain g_o) times SiLU(z).
+constexpr int DEC_W = 8;             // waves per workgroup of the decode recurrence
+
 template <int DK>
-__global__ __launch_bounds__(NT) void gdn_recurrent_kernel(GdnArgs a) {
-  constexpr int RPW = 16;             // rows per workgroup
-  constexpr int KPT = DK / 16;        // k per thread
-  __shared__ float sq[DK], sk[DK];
-  __shared__ float sred[2];
+__global__ __launch_bounds__(64 * DEC_W) void gdn_decode_kernel(GdnArgs a) {
+  constexpr int CPR = DK / 4;           // 16-byte pieces per row of S
+  constexpr int RPI = 64 / CPR;         // rows per wave load
+  constexpr int NI = DK / DEC_W / RPI;  // loads per lane (each wave holds DK / DEC_W rows)
+  static_assert(NI >= 1, "rows per wave");
+  __shared__ float sq[DK], sk[DK], sv[DK], so[DK];
   __shared__ float sab[2];
-  const int j0 = blockIdx.x * RPW, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, j = tid / 16, kq = (tid % 16) * KPT;
-  float* Sg = a.state + ((int64_t)a.seq_slot[b] * a.H + h) * (int64_t)DK * DK + (int64_t)(j0 + j) * DK + kq;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kq = (lane % CPR) * 4;
+  const int row0 = wave * (DK / DEC_W) + lane / CPR;  // row of load j: row0 + j * RPI
+  float* Sg = a.state + ((int64_t)a.seq_slot[b] * a.H + h) * (int64_t)DK * DK + (int64_t)row0 * DK + kq;
   const bool fresh = a.pos[b] == 0;
-  float S[KPT];
+  f32x4 S[NI];
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) S[e] = fresh ? 0.f : Sg[e];
+  for (int j = 0; j < NI; ++j)
+    S[j] = fresh ? (f32x4){0, 0, 0, 0} : *reinterpret_cast<const f32x4*>(Sg + (int64_t)j * RPI * DK);
   for (int t = 0; t < a.T; ++t) {
     const int64_t m = (int64_t)b * a.T + t;
     const uint16_t* pr = a.proj + m * a.proj_stride;
-    __syncthreads();
-    if (tid < 64) {
+    __syncthreads();  // the previous token's vectors are consumed
+    if (wave == 0) {
       float qv[DK / 64], kv[DK / 64], s1 = 0.f, s2 = 0.f;
 #pragma unroll
       for (int e = 0; e < DK / 64; ++e) {
-        qv[e] = bf2f(pr[a.off_q + h * DK + tid + 64 * e]);
-        kv[e] = bf2f(pr[a.off_k + h * DK + tid + 64 * e]);
+        qv[e] = bf2f(pr[a.off_q + h * DK + lane + 64 * e]);
+        kv[e] = bf2f(pr[a.off_k + h * DK + lane + 64 * e]);
+        sv[lane + 64 * e] = bf2f(pr[a.off_v + h * DK + lane + 64 * e]);
         s1 += qv[e] * qv[e];
         s2 += kv[e] * kv[e];
       }
@@ -705,62 +719,52 @@ __global__ __launch_bounds__(NT) void gdn_recurrent_kernel(GdnArgs a) {
       const float iq = rsqrtf(s1 + a.eps) * a.q_scale, ik = rsqrtf(s2 + a.eps);
 #pragma unroll
       for (int e = 0; e < DK / 64; ++e) {
-        sq[tid + 64 * e] = qv[e] * iq;
-        sk[tid + 64 * e] = kv[e] * ik;
+        sq[lane + 64 * e] = qv[e] * iq;
+        sk[lane + 64 * e] = kv[e] * ik;
       }
-      if (tid == 0) {
+      if (lane == 0) {
         sab[0] = expf(-softplusf_(bf2f(pr[a.off_a + h])));
         sab[1] = sigmoidf_(bf2f(pr[a.off_b + h]));
       }
     }
     __syncthreads();
     const float alpha = sab[0], beta = sab[1];
-    float sk_part = 0.f;
+    const f32x4 kk = *reinterpret_cast<const f32x4*>(sk + kq);
+    const f32x4 qq = *reinterpret_cast<const f32x4*>(sq + kq);
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) sk_part += S[e] * sk[kq + e];
+    for (int j = 0; j < NI; ++j) {
+      float p = S[j][0] * kk[0] + S[j][1] * kk[1] + S[j][2] * kk[2] + S[j][3] * kk[3];
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) sk_part += __shfl_xor(sk_part, off, 64);
-    const float v = bf2f(pr[a.off_v + h * DK + j0 + j]);
-    const float u = beta * (v - alpha * sk_part);
-    float oq = 0.f;
+      for (int off = 1; off < CPR; off <<= 1) p += __shfl_xor(p, off, 64);
+      const int row = row0 + j * RPI;
+      const float u = beta * (sv[row] - alpha * p);
+      S[j] = alpha * S[j] + u * kk;
+      float o = S[j][0] * qq[0] + S[j][1] * qq[1] + S[j][2] * qq[2] + S[j][3] * qq[3];
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) {
-      S[e] = alpha * S[e] + u * sk[kq + e];
-      oq += S[e] * sq[kq + e];
+      for (int off = 1; off < CPR; off <<= 1) o += __shfl_xor(o, off, 64);
+      if (lane % CPR == 0) so[row] = o;
     }
+    __syncthreads();
+    if (wave == 0) {
+      float v[DK / 64], ss = 0.f;
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) oq += __shfl_xor(oq, off, 64);
-    if ((tid & 15) == 0) a.o[(m * a.H + h) * DK + j0 + j] = oq;
+      for (int e = 0; e < DK / 64; ++e) {
+        v[e] = so[lane + 64 * e];
+        ss += v[e] * v[e];
+      }
+      ss = wave_sum(ss);
+      const float inv = rsqrtf(ss / DK + a.eps);
+      const uint16_t* z = pr + a.off_z + h * DK;
+      uint16_t* y = a.out + m * a.out_stride + h * DK;
+#pragma unroll
+      for (int e = 0; e < DK / 64; ++e) {
+        const int d = lane + 64 * e;
+        y[d] = f2bf_bits(v[e] * inv * bf2f(a.o_norm[d]) * siluf_(bf2f(z[d])));
+      }
+    }
   }
 #pragma unroll
-  for (int e = 0; e < KPT; ++e) Sg[e] = S[e];
-  (void)sred;
-}
-
-// ------------------------------------------------------- output norm
-// One wave per (token, head): y = RMSNorm(o; g_o) * SiLU(z) -> bf16.
-template <int DV>
-__global__ __launch_bounds__(256) void gdn_out_kernel(GdnArgs a, int M) {
-  const int m = blockIdx.x;
-  const int h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (h >= a.H) return;
-  const float* o = a.o + ((int64_t)m * a.H + h) * DV;
-  const uint16_t* z = a.proj + (int64_t)m * a.proj_stride + a.off_z + h * DV;
-  float v[DV / 64], ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < DV / 64; ++e) {
-    v[e] = o[lane + 64 * e];
-    ss += v[e] * v[e];
-  }
-  ss = wave_sum(ss);
-  const float inv = rsqrtf(ss / DV + a.eps);
-  uint16_t* y = a.out + (int64_t)m * a.out_stride + h * DV;
-#pragma unroll
-  for (int e = 0; e < DV / 64; ++e) {
-    const int d = lane + 64 * e;
-    y[d] = f2bf_bits(v[e] * inv * bf2f(a.o_norm[d]) * siluf_(bf2f(z[d])));
-  }
-  (void)M;
+  for (int j = 0; j < NI; ++j) *reinterpret_cast<f32x4*>(Sg + (int64_t)j * RPI * DK) = S[j];
 }
 
 template <typename K>
@@ -788,8 +792,7 @@ hipError_t prefill_dk(const GdnArgs& a, int B, hipStream_t s) {
 
 template <int DK>
 hipError_t recurrent_dk(const GdnArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL(gdn_recurrent_kernel<DK>, dim3(DK / 16, a.H, B), dim3(NT), 0, s, a);
-  hipLaunchKernelGGL(gdn_out_kernel<DK>, dim3(B * a.T, (a.H + 3) / 4), dim3(256), 0, s, a, B * a.T);
+  hipLaunchKernelGGL(gdn_decode_kernel<DK>, dim3(a.H, B), dim3(64 * DEC_W), 0, s, a);
   return hipGetLastError();
 }
 

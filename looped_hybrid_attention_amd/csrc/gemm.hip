@@ -517,6 +517,182 @@ __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_
   }
 }
 
+// ------------------------------------------------------- decode (M <= 64)
+// Weight streaming for a batch of at most 64 rows: C^T[n][m] = B[n][k] .
+// A[m][k]^T on v_mfma_f32_16x16x32_bf16.  Workgroup = 64 weight rows, wave w
+// the 16 rows 16w.. (its A operand), walking K in 128-deep chunks: each wave
+// streams its own rows front to back (16 rows x 64 bytes per load), loaded
+// straight into registers three chunks ahead of the MFMAs.  The activations
+// (B operand, all 64 rows of a chunk, hot in L2) are shared through LDS, also
+// three chunks ahead: copied global -> LDS by buffer_load ... lds into a
+// four-stage ring, 16-byte piece c of row r at c ^ (r % 16) so that the
+// operand reads of 16 consecutive rows hit distinct banks.  SwiGLU takes 32 output columns per
+// workgroup, each wave 8 gate rows then the 8 matching up rows, so a lane's
+// partner in the pair sits 32 lanes away.  Calls with too few row tiles to
+// fill the chip split K across workgroups (fp32 partials, summed in split
+// order by splitk_reduce_kernel).
+constexpr int SK_KC = 128;                    // K per chunk
+constexpr int SK_ROWB = SK_KC * 2;            // bytes of one activation row in LDS
+constexpr int SK_STAGE = 64 * SK_ROWB;        // 16 KB
+constexpr int SK_NSET = 4;                    // ring stages / weight register sets (3 chunks ahead)
+constexpr int SK_WAVES = 4;                   // waves (16 weight rows each) per workgroup
+
+template <int EPI, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes) {
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  constexpr int CPW = 16 / NW;  // activation copies per wave per chunk
+  __shared__ __align__(16) uint8_t sk_smem[SK_NSET * SK_STAGE];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int tile = blockIdx.x;
+  // weight row of this lane's A-operand row (rows past N clamped: never stored)
+  int wrow;
+  if (EPI == LOOP_EPI_SWIGLU) {
+    const int col = min(8 * NW * tile + 8 * wave + (l16 & 7), g.N - 1);
+    wrow = (l16 < 8 ? 0 : g.swiglu_F) + col;
+  } else {
+    wrow = min(16 * NW * tile + 16 * wave + l16, g.N - 1);
+  }
+  const int k0 = SPLIT ? blockIdx.y * g.kslice : 0;
+  const int nch = (SPLIT ? g.kslice : g.K) / SK_KC;
+  const auto a_rsrc = buffer_rsrc(g.A, a_bytes);
+  const auto b_rsrc = buffer_rsrc(g.B, b_bytes);
+  // activation copies: instruction i of this wave fills rows 4 (4 wave + i) ..
+  // + 3; lane l row + l / 16, piece l % 16 holding logical piece
+  // (l % 16) ^ (row % 16)
+  int a_off[CPW];
+#pragma unroll
+  for (int i = 0; i < CPW; ++i) {
+    const int row = 4 * (CPW * wave + i) + (lane >> 4);
+    const int c = (lane & 15) ^ (row & 15);
+    a_off[i] = (min(row, g.M - 1) * (int)g.lda + k0 + c * 8) * 2;
+  }
+  const int b_off = (wrow * (int)g.ldb + k0 + lg * 8) * 2;
+#define SK_COPY(ch_, stage_)                                                                       \
+  _Pragma("unroll") for (int i = 0; i < CPW; ++i)                                                  \
+      copy16_to_lds(a_rsrc, a_off[i], (ch_) * SK_ROWB,                                             \
+                    (lds_void*)(sk_smem + (stage_) * SK_STAGE + (CPW * wave + i) * 1024));
+#define SK_WLOAD(ch_, set_)                                                                        \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q) w[set_][q] = buffer_load16(b_rsrc, b_off + q * 64, (ch_) * SK_ROWB);
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = (f32x4){0, 0, 0, 0};
+  u32x4 w[SK_NSET][4];
+#pragma unroll
+  for (int p = 0; p < SK_NSET - 1; ++p) {
+    SK_COPY(min(p, nch - 1), p);
+    SK_WLOAD(min(p, nch - 1), p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Every load is unconditional (past the end the last chunk is loaded again,
+  // into the idle stage / registers), so every path has the same loads in
+  // flight and the waits stay exact.  Chunk p's 4 copies are followed by its
+  // 4 weight loads; when chunk c starts, chunks c + 1 and c + 2 (16 loads)
+  // were issued after chunk c's, so vmcnt(16) means chunk c has landed.
+  for (int c0 = 0; c0 < nch; c0 += SK_NSET) {
+#pragma unroll
+    for (int j = 0; j < SK_NSET; ++j) {
+      const int c = c0 + j;
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<(CPW + 4) * (SK_NSET - 2)>();
+      lds_barrier();  // chunk c visible; every wave is done with chunk c - 1
+      __builtin_amdgcn_sched_barrier(0);
+      SK_COPY(min(c + SK_NSET - 1, nch - 1), (j + SK_NSET - 1) % SK_NSET);
+      SK_WLOAD(min(c + SK_NSET - 1, nch - 1), (j + SK_NSET - 1) % SK_NSET);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* st = sk_smem + j * SK_STAGE;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x8 bfr[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          bfr[mt] = *reinterpret_cast<const bf16x8*>(st + (16 * mt + l16) * SK_ROWB + (((4 * q + lg) ^ l16) << 4));
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16x16x32(__builtin_bit_cast(bf16x8, w[j][q]), bfr[mt], acc[mt]);
+      }
+    }
+  }
+#undef SK_COPY
+#undef SK_WLOAD
+  wait_vmem();
+
+  // lane holds C^T[row 4 lg + r of the wave][m = 16 mt + l16]
+  if (EPI == LOOP_EPI_SWIGLU) {
+    float up[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) up[mt][r] = __shfl_xor(acc[mt][r], 32, 64);
+    if (lg >= 2) return;
+    uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
+    const int col = 8 * NW * tile + 8 * wave + 4 * lg;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int m = 16 * mt + l16;
+      if (m >= g.M) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (col + r >= g.N) continue;
+        if (SPLIT) {  // gate and up apart: [split][m][2][N]
+          float* P = g.part + (((int64_t)blockIdx.y * g.M + m) * 2) * g.N + col + r;
+          P[0] = acc[mt][r];
+          P[g.N] = up[mt][r];
+        } else {
+          C[(int64_t)m * g.ldc + col + r] = f2bf_bits(siluf_(acc[mt][r]) * up[mt][r]);
+        }
+      }
+    }
+    return;
+  }
+  const int col = 16 * NW * tile + 16 * wave + 4 * lg;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int m = 16 * mt + l16;
+    if (m >= g.M) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (col + r >= g.N) continue;
+      const float v = acc[mt][r];
+      if (SPLIT) {
+        g.part[((int64_t)blockIdx.y * g.M + m) * g.N + col + r] = v;
+      } else {
+        const int64_t o = (int64_t)m * g.ldc + col + r;
+        if (EPI == LOOP_EPI_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = f2bf_bits(v);
+        else if (EPI == LOOP_EPI_F32) reinterpret_cast<float*>(g.C)[o] = v;
+        else reinterpret_cast<float*>(g.C)[o] = g.R[o] + v;
+      }
+    }
+  }
+}
+
+// M <= 64, K range of every workgroup a multiple of SK_NSET chunks, operands
+// within 32-bit buffer offsets.
+template <int EPI, int NW>
+hipError_t launch_skinny_w(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
+  const int per = (EPI == LOOP_EPI_SWIGLU) ? 8 * NW : 16 * NW;  // output columns per workgroup
+  const int tiles = (g.N + per - 1) / per;
+  int splits = 1;
+  while (tiles * splits < 256 && g.K % (SK_KC * SK_NSET * splits * 2) == 0) splits *= 2;
+  const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
+  if (splits > 1 && g.part && need <= ws_bytes) {
+    g.kslice = g.K / splits;
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, NW>), dim3(tiles, splits), dim3(64 * NW), 0, s, g, a_bytes,
+                       b_bytes);
+    const int64_t n_out = (int64_t)g.M * g.N;
+    const int blocks = (int)std::min<int64_t>((n_out + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, splits);
+  } else {
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, false, NW>), dim3(tiles), dim3(64 * NW), 0, s, g, a_bytes, b_bytes);
+  }
+  return hipGetLastError();
+}
+
+template <int EPI>
+hipError_t launch_skinny(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
+  return launch_skinny_w<EPI, SK_WAVES>(g, ws_bytes, a_bytes, b_bytes, s);
+}
+
 // Ring shape: two stages of K = 64 (128 KB of LDS).  Deeper rings of K = 32
 // steps (up to 5 stages, the whole 160 KB) measured slower on every shape.
 constexpr int DB_KB = 64, DB_NS = 2;
@@ -582,6 +758,16 @@ hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
       return launch_db<EPI>(g, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
     }
     return launch_cfg<256, 256, 2, 4, EPI, false>(g, 1, s);
+  }
+  {
+    const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
+    const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
+    // measured on the decode shapes (64 rows): these tiles win where the
+    // output has at most 4096 columns and K at most 4096; the register-staged
+    // 64 x 128 tiles stream the wider and deeper weight matrices faster
+    if (g.M <= 64 && g.N <= 4096 && g.K <= 4096 && g.K % (SK_KC * SK_NSET) == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && a_bytes < (1ll << 31) &&
+        b_bytes < (1ll << 31))
+      return launch_skinny<EPI>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
   }
   return launch_small<EPI>(g, ws_bytes, s);
 }

@@ -77,6 +77,8 @@ int validate_config(const loop_config* c) {
   if (c->max_batch <= 0 || c->max_seq <= 0 || c->max_tokens <= 0)
     return loop_fail(LOOP_ECAPACITY, "max_batch, max_seq and max_tokens must be positive");
   if (c->max_seq % 64) return loop_fail(LOOP_ESHAPE, "max_seq must be a multiple of 64");
+  if (c->max_seq > (int64_t)DEC_SPLIT_KEYS * DEC_MAX_SPLITS)
+    return loop_fail(LOOP_ECAPACITY, "max_seq %d above %d", c->max_seq, DEC_SPLIT_KEYS * DEC_MAX_SPLITS);
   if (!(c->eps > 0.f)) return loop_fail(LOOP_ESHAPE, "eps must be positive");
   return 0;
 }

@@ -78,6 +78,11 @@ struct FlashArgs {
 };
 hipError_t launch_flash_prefill(const FlashArgs& a, int B, hipStream_t s);
 
+// Decode attention splits the keys of a sequence into DEC_SPLIT_KEYS-key
+// pieces (one workgroup each); contexts of up to DEC_SPLIT_KEYS *
+// DEC_MAX_SPLITS positions.
+constexpr int DEC_SPLIT_KEYS = 1024;
+constexpr int DEC_MAX_SPLITS = 1024;
 struct DecodeAttnArgs {
   const uint16_t* q; int Hq, Hkv, D, max_seq;
   const int32_t* pos;  // device [B]: position of the new token (keys 0..pos)

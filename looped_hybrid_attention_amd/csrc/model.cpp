@@ -30,7 +30,7 @@
 namespace {
 
 constexpr size_t ALIGN = 256;
-constexpr int DEC_SPLIT = 512;  // keys per decode-attention split (decode_attn_kernel)
+constexpr int DEC_SPLIT = DEC_SPLIT_KEYS;  // keys per decode-attention split (decode_attn_kernel)
 
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 

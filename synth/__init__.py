@@ -146,8 +146,10 @@ def _c():
 
 
 def normal(seed: int, name: str, shape, std: float, mean: float = 0.0,
-           dtype: str = "f32", chunk: int = 1 << 24, use_c: bool = True) -> np.ndarray:
-    """N(mean, std) tensor of the given shape.
+           dtype: str = "f32", chunk: int = 1 << 24, use_c: bool = True,
+           start: int = 0) -> np.ndarray:
+    """N(mean, std) tensor of the given shape, from draws ``start ..`` of the
+    stream (``start`` > 0 takes a slice of a longer tensor drawn from 0).
 
     ``dtype="f32"`` returns float32; ``dtype="bf16"`` returns the uint16 bf16
     bit patterns (use :func:`bf16_bits_to_f32` for the values).  ``mean`` is
@@ -158,12 +160,12 @@ def normal(seed: int, name: str, shape, std: float, mean: float = 0.0,
     out = np.empty(n, np.uint16 if dtype == "bf16" else np.float32)
     lib = _c() if use_c else None
     if lib is not None:
-        lib.synth_normal(seed & 0xFFFFFFFF, fnv1a32(name), 0, n, float(std), float(mean),
+        lib.synth_normal(seed & 0xFFFFFFFF, fnv1a32(name), int(start), n, float(std), float(mean),
                          1 if dtype == "bf16" else 0, out.ctypes.data)
         return out.reshape(shape)
     for s in range(0, n, chunk):
         m = min(chunk, n - s)
-        v = (normal_f64(seed, name, m, s) * float(std) + float(mean)).astype(np.float32)
+        v = (normal_f64(seed, name, m, start + s) * float(std) + float(mean)).astype(np.float32)
         out[s:s + m] = f32_to_bf16_bits(v) if dtype == "bf16" else v
     return out.reshape(shape)
 

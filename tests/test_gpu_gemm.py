@@ -112,12 +112,15 @@ def test_gemm_real_shapes_sampled(M, N, K, epi):
         assert rel_err(got, gu) < (2 ** -8 if epi == 0 else 1e-5)
 
 
-# The decode projections (64 sequences): split-K with fp32 partials summed in
-# split order, against the float64 product; also bit-identical reruns.  The
+# The decode projections (up to 64 sequences: weight-streaming tiles, split K
+# with fp32 partials summed in split order where the row tiles alone do not
+# fill the chip), against the float64 product; also bit-identical reruns.  The
 # large-M shapes with a narrow column remainder run that strip split-K.
 DECODE = [(64, 10240, 4096, 0), (64, 8224, 4096, 0), (64, 4096, 4096, 2), (64, 4096, 2048, 1),
           (64, 12288, 4096, 3), (64, 4096, 12288, 2), (1, 4096, 12288, 2), (37, 520, 768, 3),
-          (1024, 288, 1024, 0), (1024, 288, 1024, 2), (600, 1032, 512, 1)]
+          (1024, 288, 1024, 0), (1024, 288, 1024, 2), (600, 1032, 512, 1),
+          (17, 1000, 256, 1), (64, 300, 1280, 0), (50, 4100, 1024, 2), (3, 40, 512, 3),
+          (50, 4000, 1024, 2), (17, 1000, 2048, 3)]
 
 
 @pytest.mark.parametrize("M,N,K,epi", DECODE)

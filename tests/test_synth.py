@@ -55,3 +55,12 @@ def test_token_ids_range():
     ids = synth.token_ids(1, "ids", 100000, 1000)
     assert ids.min() >= 0 and ids.max() < 1000
     assert abs(np.bincount(ids, minlength=1000).std() / 100 - 0.1) < 0.05
+
+
+@pytest.mark.parametrize("use_c", [True, False])
+def test_normal_slice_matches_whole(use_c):
+    if use_c and synth._c() is None:
+        synth.build_host_generator()
+    whole = synth.normal(2, "kv", (4099,), 1.0, dtype="bf16", use_c=use_c)
+    part = synth.normal(2, "kv", (1000,), 1.0, dtype="bf16", use_c=use_c, start=1537)
+    assert np.array_equal(whole[1537:2537], part)
