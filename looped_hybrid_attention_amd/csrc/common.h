@@ -85,6 +85,19 @@ DEV void copy16_to_lds(__amdgpu_buffer_rsrc_t src, int voffset, int soffset, lds
 DEV u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voffset, int soffset) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, voffset, soffset, 0);
 }
+// Workgroup barrier after this wave's LDS accesses have completed.  Copies
+// still in flight to other ring stages stay in flight: a fence would make the
+// compiler drain them (it counts them as pending LDS writes).  The memory
+// clobber keeps LDS accesses on their side of the barrier.
+DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// s_waitcnt with vmcnt(N), other counters untouched: at most the N newest
+// vector memory operations of this wave are still outstanding (they complete
+// in issue order).
+template <int N>
+DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 // s_waitcnt vmcnt(0): this wave's vector memory operations (LDS copies
 // included) have completed.
 DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

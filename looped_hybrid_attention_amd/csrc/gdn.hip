@@ -168,9 +168,11 @@ DEV void mma2(f32x4& acc0, f32x4& acc1, const float (&a0)[K / 4], const float (&
 }
 
 // Chunk workspace layout, per (seq b, head h, chunk c), fp32:
-//   W, Ut, Kd, Qp, Up: [CH][DK] each, then gC; S_c (entry state) [DV][DK].
+//   W, Qp, Up: [CH][DK]; UtT = Ut^T [DV][CH] and KdT = Kd^T [DK][CH]
+//   (transposed: the scan reads them along the chunk's tokens); gC;
+//   S_c (entry state) [DV][DK].
 struct ChunkPtr {
-  float *W, *Ut, *Kd, *Qp, *Up, *S;
+  float *W, *UtT, *KdT, *Qp, *Up, *S;
   float* gC;
 };
 DEV ChunkPtr chunk_ptr(const GdnArgs& a, int b, int h, int c, int DK) {
@@ -178,8 +180,8 @@ DEV ChunkPtr chunk_ptr(const GdnArgs& a, int b, int h, int c, int DK) {
   const int64_t mat = (int64_t)CH * DK;
   ChunkPtr p;
   p.W = a.W + cb * mat;
-  p.Ut = a.Ut + cb * mat;
-  p.Kd = a.Kd + cb * mat;
+  p.UtT = a.Ut + cb * mat;
+  p.KdT = a.Kd + cb * mat;
   p.Qp = a.Qg + cb * mat;
   p.Up = a.Mqk + cb * mat;
   p.S = a.Sc + cb * (int64_t)DK * DK;
@@ -306,10 +308,10 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
     }
   }
   __syncthreads();
-  // Kd = exp(G_C - G) k^ (rows >= C are zero because k^ is)
+  // Kd^T = (exp(G_C - G) k^)^T (rows >= C are zero because k^ is)
   for (int idx = tid; idx < CH * DK; idx += NT) {
-    const int r = idx / DK, d = idx % DK;
-    P.Kd[idx] = sEK[r] * sK[r * LD + d];
+    const int d = idx / CH, r = idx % CH;
+    P.KdT[idx] = sEK[r] * sK[r * LD + d];
   }
   // T = (I + A)^-1 (unit lower triangular) into sT2, in 16 x 16 blocks.
   // Diagonal blocks by forward substitution (wave w: block w, lane j < 16
@@ -394,10 +396,13 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
         sK[row * LD + col] = w;
         sV[row * LD + col] = u;
         P.W[row * DK + col] = w;
-        P.Ut[row * DK + col] = u;
       }
   }
   __syncthreads();
+  for (int idx = tid; idx < CH * DV; idx += NT) {  // Ut^T
+    const int d = idx / CH, r = idx % CH;
+    P.UtT[idx] = sV[r * LD + d];
+  }
   // Qp = gamma Q - Mqk W, Up = Mqk Ut
   {
     const int i16 = lane & 15, kk = lane >> 4;
@@ -422,26 +427,52 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
 }
 
 // ------------------------------------------------------- chunk scan
-// One workgroup per (16 rows of S, head, seq): rows j0 .. j0+15 of S,
-// carried over the chunks in order: U = Ut - W S^T, S <- gC S + U^T Kd.
+// One workgroup (eight waves) per (16 rows of S, head, seq): rows j0 .. j0+15
+// of S carried over the chunks in order,
+//   U = Ut - W S^T,   S <- gC S + U^T Kd.
+// Chunk c + 1's W [CH][DK], Kd^T [DK][CH] and the 16 rows of Ut^T go global ->
+// LDS by buffer_load ... lds while chunk c computes (two-stage ring; 16-byte
+// piece p of row r stored at p ^ (r % 16), so that the 128-bit operand reads
+// of 16 consecutive rows hit distinct banks), and chunk c + 2 is pulled into
+// L2 (one 4-byte copy per 128-byte line, into a scratch corner of LDS) so
+// that the copies of the next step hit L2.  Per chunk, two barriers:
+//   U phase: wave w computes the partial product of token tile w % 4 over
+//   the K half w / 4 (16 fp32 MFMAs), stored transposed [j][t];
+//   update: wave w updates S columns 16w .. 16w+15 from U^T (= Ut^T minus the
+//   two partials) and Kd^T (16 MFMAs).
 // The entry state of every chunk is written for the output kernel; the final
 // state to the slot.  All Dv/16 row blocks of a (seq, head) read the same W
 // and Kd, so they are placed on one XCD (workgroups go to XCDs round-robin
 // by linear index): index = x + 8 ((g / 8) Dv/16 + jb) for group g = seq*H + head.
 constexpr int N_XCD = 8;
+constexpr int SCAN_NT = 512;
+constexpr int SCAN_MAX_CHUNKS = 1024;  // chunks per sequence and call (65,536 tokens)
+template <int DK, int SCAN_NT_ = SCAN_NT>
+struct ScanLds {
+  static constexpr int W_B = CH * DK * 4;     // W tile
+  static constexpr int K_B = DK * CH * 4;     // Kd^T tile
+  static constexpr int U_B = 16 * CH * 4;     // 16 rows of Ut^T
+  static constexpr int STAGE = W_B + K_B + U_B;
+  static constexpr int LS = DK + 4;           // S rows (floats)
+  static constexpr int LP = CH + 4;           // partial-product rows (floats)
+  static constexpr int S_OFF = 2 * STAGE;
+  static constexpr int P_OFF = S_OFF + 16 * LS * 4;
+  static constexpr int X_OFF = P_OFF + 2 * 16 * LP * 4;  // L2 warm-up landing (4 bytes per lane)
+  static constexpr int G_OFF = X_OFF + SCAN_NT_ * 4;      // gC of every chunk
+  static constexpr int bytes = G_OFF + SCAN_MAX_CHUNKS * 4;
+};
 template <int DK>
-__global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, int n_groups) {
-  constexpr int LW = DK + 4;    // W rows (nt operand)
-  constexpr int LK = DK + 16;   // Kd rows (tn operand)
-  constexpr int LS = DK + 4;    // S rows (nt operand)
-  constexpr int LU = 16;        // U rows (tn operand)
-  constexpr int PW = CH * DK / (4 * NT);  // 16-byte pieces of W (and of Kd) per thread
-  static_assert(PW * 4 * NT == CH * DK && CH * 16 == 4 * NT, "prefetch split");
-  __shared__ __align__(16) float sW[CH * LW];
-  __shared__ __align__(16) float sKd[CH * LK];
-  __shared__ __align__(16) float sUt[CH * 16];
-  __shared__ __align__(16) float sU[CH * LU];
-  __shared__ __align__(16) float sS[16 * LS];
+__global__ __launch_bounds__(SCAN_NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, int n_groups) {
+  static_assert(DK == 64 || DK == 128, "scan tiling");
+  using L = ScanLds<DK>;
+  constexpr int LS = L::LS, LP = L::LP;
+  constexpr int WI = L::W_B / 1024 / 8;       // W copy instructions per wave
+  constexpr int KI = L::K_B / 1024 / 8;       // Kd^T copy instructions per wave
+  constexpr int WPR = DK / 4;                 // 16-byte pieces per W row
+  constexpr int KQ = DK / 8;                  // k per lane group in the U phase
+  extern __shared__ __align__(16) uint8_t scan_smem[];
+  float* sS = reinterpret_cast<float*>(scan_smem + L::S_OFF);
+  float* sP = reinterpret_cast<float*>(scan_smem + L::P_OFF);   // [2][16][LP]
   constexpr int NJB = DK / 16;
   const int xcd = blockIdx.x % N_XCD, q = blockIdx.x / N_XCD;
   const int g = (q / NJB) * N_XCD + xcd;
@@ -451,126 +482,151 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, int n_
   const int i16 = lane & 15, kk = lane >> 4;
   float* Sg = a.state + ((int64_t)a.seq_slot[b] * a.H + h) * (int64_t)DK * DK;  // [Dv][Dk]
   const bool fresh = a.pos[b] == 0;
-  for (int idx = tid; idx < 16 * DK; idx += NT) {
+  for (int idx = tid; idx < 16 * DK; idx += SCAN_NT) {
     const int j = idx / DK, k = idx % DK;
     sS[j * LS + k] = fresh ? 0.f : Sg[(int64_t)(j0 + j) * DK + k];
   }
-  // prefetch of the next chunk: this thread's 16-byte pieces of W and Kd
-  // (PW each) and of its 16 columns of Ut, one chunk ahead in registers
-  u32x4 pf[2 * PW + 1];
-  float gC_next;
-#define SCAN_LOAD(c_)                                                                        \
-  {                                                                                          \
-    const ChunkPtr P_ = chunk_ptr(a, b, h, (c_), DK);                                        \
-    gC_next = *P_.gC;                                                                        \
-    _Pragma("unroll") for (int i = 0; i < PW; ++i)                                           \
-        pf[i] = *reinterpret_cast<const u32x4*>(P_.W + (tid + i * NT) * 4);                  \
-    _Pragma("unroll") for (int i = 0; i < PW; ++i)                                           \
-        pf[PW + i] = *reinterpret_cast<const u32x4*>(P_.Kd + (tid + i * NT) * 4);            \
-    pf[2 * PW] = *reinterpret_cast<const u32x4*>(P_.Ut + (tid / 4) * DK + j0 + (tid % 4) * 4); \
+  // copy sources (byte offsets within a chunk's tile): W instruction n =
+  // WI wave + i fills rows (64 / WPR) n .., lane l row + l / WPR, piece
+  // l % WPR holding logical piece (l % WPR) ^ (row % 16); Kd^T and Ut^T rows
+  // hold 16 pieces: 4 rows per instruction
+  int w_src[WI], k_src[KI], u_src;
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = (64 / WPR) * (wave * WI + i) + lane / WPR, p = lane % WPR;
+    w_src[i] = (row * DK + ((p ^ (row & 15)) * 4)) * 4;
   }
-#define SCAN_STASH()                                                                         \
-  {                                                                                          \
-    _Pragma("unroll") for (int i = 0; i < PW; ++i) {                                         \
-      const int e = (tid + i * NT) * 4;                                                      \
-      *reinterpret_cast<u32x4*>(sW + (e / DK) * LW + e % DK) = pf[i];                        \
-      *reinterpret_cast<u32x4*>(sKd + (e / DK) * LK + e % DK) = pf[PW + i];                  \
-    }                                                                                        \
-    *reinterpret_cast<u32x4*>(sUt + tid * 4) = pf[2 * PW];                                   \
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int row = 4 * (wave * KI + i) + (lane >> 4), p = lane & 15;
+    k_src[i] = (row * CH + ((p ^ (row & 15)) * 4)) * 4;
   }
-  SCAN_LOAD(0);
+  {
+    const int row = 4 * (wave & 3) + (lane >> 4), p = lane & 15;  // waves 0..3: Ut^T rows
+    u_src = ((j0 + row) * CH + ((p ^ (row & 15)) * 4)) * 4;
+  }
+  const int64_t cb0 = ((int64_t)b * a.H + h) * a.n_chunks;
+  const int64_t mat = (int64_t)CH * DK;
+  const auto w_rsrc = buffer_rsrc(a.W + cb0 * mat, (uint32_t)(a.n_chunks * mat * 4));
+  const auto k_rsrc = buffer_rsrc(a.Kd + cb0 * mat, (uint32_t)(a.n_chunks * mat * 4));
+  const auto u_rsrc = buffer_rsrc(a.Ut + cb0 * mat, (uint32_t)(a.n_chunks * mat * 4));
+  // L2 warm-up source: the workgroup's share of the chunk (1/8 of the head's
+  // W and Kd^T lines, its own 32 lines of Ut^T), one source tensor per wave
+  // (wave-uniform, w % 3; lanes 32..63 repeat 0..31), so that every wave
+  // issues exactly one copy
+  const int xw = __builtin_amdgcn_readfirstlane(wave) % 3, jb = j0 / 16;
+  const __amdgpu_buffer_rsrc_t x_rsrc = xw == 0 ? w_rsrc : (xw == 1 ? k_rsrc : u_rsrc);
+  const int x_src = xw < 2 ? (jb * 32 + (lane & 31)) * 128 : j0 * CH * 4 + (lane & 31) * 128;
+#define SCAN_WARM(c_)                                                                             \
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lds_void*)(scan_smem + L::X_OFF + wave * 256), 4, \
+                                           x_src, (c_) * (int)mat * 4, 0, 0);
+#define SCAN_COPY(c_, st_)                                                                        \
+  {                                                                                               \
+    uint8_t* S_ = scan_smem + (st_) * L::STAGE;                                                   \
+    const int so_ = (c_) * (int)mat * 4;                                                          \
+    _Pragma("unroll") for (int i = 0; i < WI; ++i)                                                \
+        copy16_to_lds(w_rsrc, w_src[i], so_, (lds_void*)(S_ + (wave * WI + i) * 1024));          \
+    _Pragma("unroll") for (int i = 0; i < KI; ++i)                                                \
+        copy16_to_lds(k_rsrc, k_src[i], so_, (lds_void*)(S_ + L::W_B + (wave * KI + i) * 1024)); \
+    if (wave < 4) copy16_to_lds(u_rsrc, u_src, so_, (lds_void*)(S_ + L::W_B + L::K_B + wave * 1024)); \
+  }
+  float* sG = reinterpret_cast<float*>(scan_smem + L::G_OFF);
+  for (int i = tid; i < a.n_chunks; i += SCAN_NT) sG[i] = a.gC[cb0 + i];
+  // Issue order per chunk c: the copies of chunk c + 1, the warm-up of chunk
+  // c + 2, the entry-state store of chunk c (all unconditional, clamped to
+  // the last chunk, so every wave has the same operations in flight): at the
+  // top of chunk c + 1, vmcnt(2) means its copies have landed.
+  SCAN_COPY(0, 0);
+  SCAN_WARM(min(1, a.n_chunks - 1));
+  // U phase operands: token tile tt, K half hh; update: S columns 16 wave ..
+  const int tt = wave & 3, hh = wave >> 2;
   for (int c = 0; c < a.n_chunks; ++c) {
-    __syncthreads();  // previous chunk's LDS reads are done
-    SCAN_STASH();
-    const float gC = gC_next;
-    __syncthreads();
-    if (c + 1 < a.n_chunks) SCAN_LOAD(c + 1);
-    // entry state of chunk c (16-byte pieces; all LDS reads before the stores)
+    // chunk c has landed (this wave's copies) and every wave has finished
+    // chunk c - 1
+    wait_vmcnt<2>();
+    lds_barrier();  // (a fence here would drain the warm-up and the store)
+    const uint8_t* st = scan_smem + (c & 1) * L::STAGE;
+    {
+      const int cn = min(c + 1, a.n_chunks - 1);  // past the end: the idle stage, harmlessly
+      SCAN_COPY(cn, (c + 1) & 1);
+      SCAN_WARM(min(c + 2, a.n_chunks - 1));
+    }
+    const float gC = sG[c];
+    // entry state of chunk c (every lane stores; for Dk = 64 the second half
+    // of the workgroup repeats the first)
     {
       const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
-      constexpr int NE = 16 * DK / 4 / NT;
-      static_assert(NE * 4 * NT == 16 * DK, "entry-state split");
-      f32x4 ev[NE];
-#pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        const int e = (tid + i * NT) * 4;
-        ev[i] = *reinterpret_cast<const f32x4*>(sS + (e / DK) * LS + e % DK);
-      }
-#pragma unroll
-      for (int i = 0; i < NE; ++i) {
-        const int e = (tid + i * NT) * 4;
-        *reinterpret_cast<f32x4*>(P.S + (int64_t)(j0 + e / DK) * DK + e % DK) = ev[i];
-      }
+      const int e = tid % (4 * DK);
+      const int j = e / (DK / 4), k4 = (e % (DK / 4)) * 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sS + j * LS + k4);
+      *reinterpret_cast<f32x4*>(P.S + (int64_t)(j0 + j) * DK + k4) = v;
     }
-    // U = Ut - W S^T ; wave w: rows 16w..16w+15, the 16 columns j.  Lane
-    // group kk contributes k = kk DK/4 + i at MFMA step i (a permutation of
-    // K, the same on both operands), so its operands are contiguous runs
-    // read with 128-bit loads, all before the MFMAs.
+    // U phase: P_hh[j][t] = sum over k in half hh of W[t][k] S[j][k], tokens
+    // t of tile tt.  Lane group kk takes k = DK/2 hh + KQ kk .. + KQ-1 (a
+    // permutation of K applied to both operands): 128-bit reads.
     {
-      constexpr int KQ = DK / 4;
+      const int row = 16 * tt + i16;
+      const float* wr = reinterpret_cast<const float*>(st) + row * DK;
+      const float* sr = sS + i16 * LS + (DK / 2) * hh + KQ * kk;
       float av[KQ], bv[KQ];
-      const float* ar = sW + (wave * 16 + i16) * LW + kk * KQ;
-      const float* br = sS + i16 * LS + kk * KQ;
 #pragma unroll
-      for (int q = 0; q < KQ / 4; ++q) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(ar + 4 * q);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(br + 4 * q);
+      for (int qq = 0; qq < KQ / 4; ++qq) {
+        const int pc = ((DK / 2) * hh + KQ * kk) / 4 + qq;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(wr + 4 * (pc ^ (row & 15)));
+        const f32x4 y = *reinterpret_cast<const f32x4*>(sr + 4 * qq);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { av[4 * q + e] = x[e]; bv[4 * q + e] = y[e]; }
+        for (int e = 0; e < 4; ++e) { av[4 * qq + e] = x[e]; bv[4 * qq + e] = y[e]; }
       }
-      f32x4 acc = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+      f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < KQ; i += 2) {
-        acc = mfma16x16x4f32(av[i], bv[i], acc);
+        acc0 = mfma16x16x4f32(av[i], bv[i], acc0);
         acc1 = mfma16x16x4f32(av[i + 1], bv[i + 1], acc1);
       }
-      acc += acc1;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wave * 16 + 4 * kk + r;
-        sU[row * LU + i16] = sUt[row * 16 + i16] - acc[r];
-      }
+      acc0 += acc1;
+      // lane holds P[t = 16 tt + 4 kk + r][j = i16]
+      *reinterpret_cast<f32x4*>(sP + (hh * 16 + i16) * LP + 16 * tt + 4 * kk) = acc0;
     }
-    __syncthreads();
-    // S = gC S + U^T Kd ; wave w: k-tile w (and w + 4 when Dk = 128)
-    constexpr int TPW = DK / 16 / (NT / 64);
-    static_assert(TPW == 1 || TPW == 2, "k-tiles per wave");
-    if constexpr (TPW == 2) {
-      const int nt0 = wave, nt1 = wave + NT / 64;
+    lds_barrier();  // the next chunk's copies stay in flight
+    // update: S[j][k] = gC S[j][k] + sum_t U[t][j] Kd[t][k] for the columns
+    // k = 16 wave + i16; U^T[j][t] = Ut^T[j][t] - P_0[j][t] - P_1[j][t].
+    // Lane group kk takes t = 16 kk .. + 15.
+    if (wave < DK / 16) {
+      const float* ut = reinterpret_cast<const float*>(st + L::W_B + L::K_B) + i16 * CH;
+      const float* kd = reinterpret_cast<const float*>(st + L::W_B) + (16 * wave + i16) * CH;
+      const float* p0 = sP + i16 * LP + 16 * kk;
+      const float* p1 = sP + (16 + i16) * LP + 16 * kk;
+      float av[16], bv[16];
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int pc = 4 * kk + qq;
+        const f32x4 u = *reinterpret_cast<const f32x4*>(ut + 4 * (pc ^ i16));
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(p0 + 4 * qq);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(p1 + 4 * qq);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(kd + 4 * (pc ^ i16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { av[4 * qq + e] = u[e] - x0[e] - x1[e]; bv[4 * qq + e] = y[e]; }
+      }
       f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-      float ua[CH / 4], k0v[CH / 4], k1v[CH / 4];
 #pragma unroll
-      for (int q = 0; q < CH / 4; ++q) {
-        const int k = kk + 4 * q;
-        ua[q] = sU[k * LU + i16];
-        k0v[q] = sKd[k * LK + nt0 * 16 + i16];
-        k1v[q] = sKd[k * LK + nt1 * 16 + i16];
+      for (int i = 0; i < 16; i += 2) {
+        acc0 = mfma16x16x4f32(av[i], bv[i], acc0);
+        acc1 = mfma16x16x4f32(av[i + 1], bv[i + 1], acc1);
       }
-#pragma unroll
-      for (int q = 0; q < CH / 4; ++q) {
-        acc0 = mfma16x16x4f32(ua[q], k0v[q], acc0);
-        acc1 = mfma16x16x4f32(ua[q], k1v[q], acc1);
-      }
+      acc0 += acc1;
+      // lane holds dS[j = 4 kk + r][k = 16 wave + i16]
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = 4 * kk + r;
-        sS[j * LS + nt0 * 16 + i16] = gC * sS[j * LS + nt0 * 16 + i16] + acc0[r];
-        sS[j * LS + nt1 * 16 + i16] = gC * sS[j * LS + nt1 * 16 + i16] + acc1[r];
-      }
-    } else {
-      f32x4 acc = {0, 0, 0, 0};
-      mm_tn(acc, sU, LU, sKd + wave * 16, LK, CH);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = 4 * kk + r;
-        sS[j * LS + wave * 16 + i16] = gC * sS[j * LS + wave * 16 + i16] + acc[r];
+        float* sp = sS + (4 * kk + r) * LS + 16 * wave + i16;
+        *sp = gC * *sp + acc0[r];
       }
     }
   }
-#undef SCAN_LOAD
-#undef SCAN_STASH
+#undef SCAN_COPY
+#undef SCAN_WARM
+  wait_vmem();
   __syncthreads();
-  for (int idx = tid; idx < 16 * DK; idx += NT) {
+  for (int idx = tid; idx < 16 * DK; idx += SCAN_NT) {
     const int j = idx / DK, k = idx % DK;
     Sg[(int64_t)(j0 + j) * DK + k] = sS[j * LS + k];
   }
@@ -774,18 +830,21 @@ hipError_t set_lds(K k, size_t bytes) {
 
 template <int DK>
 hipError_t prefill_dk(const GdnArgs& a, int B, hipStream_t s) {
+  if (a.n_chunks > SCAN_MAX_CHUNKS) return hipErrorInvalidValue;
   const size_t lds_prep = (3 * CH * (DK + 4) + 3 * CH * (CH + 4) + 4 * CH + 4 * 16 * 20) * sizeof(float);
   const size_t lds_out = (CH * (DK + 4) + DK * (DK + 4)) * sizeof(float);
   static bool attr = false;
   if (!attr) {
     hipError_t e = set_lds(gdn_chunk_prep_kernel<DK>, lds_prep);
     if (e == hipSuccess) e = set_lds(gdn_chunk_out_kernel<DK>, lds_out);
+    if (e == hipSuccess) e = set_lds(gdn_chunk_scan_kernel<DK>, ScanLds<DK>::bytes);
     if (e != hipSuccess) return e;
     attr = true;
   }
   hipLaunchKernelGGL(gdn_chunk_prep_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), lds_prep, s, a);
   const int groups = (a.H * B + N_XCD - 1) / N_XCD * N_XCD;
-  hipLaunchKernelGGL(gdn_chunk_scan_kernel<DK>, dim3(groups * (DK / 16)), dim3(NT), 0, s, a, a.H * B);
+  hipLaunchKernelGGL(gdn_chunk_scan_kernel<DK>, dim3(groups * (DK / 16)), dim3(SCAN_NT), ScanLds<DK>::bytes, s, a,
+                     a.H * B);
   hipLaunchKernelGGL(gdn_chunk_out_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), lds_out, s, a);
   return hipGetLastError();
 }

@@ -305,17 +305,6 @@ struct DbShape {
 constexpr int DB_BM = 256, DB_BN = 256;
 constexpr int db_lds(int kb, int ns) { return ns * 2 * 256 * kb * 2; }
 
-// s_waitcnt with vmcnt(N), other counters untouched
-template <int N>
-DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-// Workgroup barrier after this wave's LDS reads have returned.  Copies still
-// in flight to other ring stages stay in flight: a fence would make the
-// compiler drain them (it counts them as pending LDS writes).  The memory
-// clobber keeps LDS accesses on their side of the barrier.
-DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int EPI, int KB, int NS>
 __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes) {
@@ -713,13 +702,18 @@ hipError_t launch_db(const GemmArgs& g, uint32_t a_bytes, uint32_t b_bytes, hipS
 }
 
 // 64 x 128 tiles; calls with too few tiles to fill the chip split K so that
-// tiles * splits >= ~512 workgroups, if a large enough partial buffer is given.
+// tiles * splits reaches ~256-512 workgroups, if a large enough partial buffer
+// is given.
 template <int EPI>
 hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? 64 : 128;
   const int tiles = ((g.M + 63) / 64) * ((g.N + OUT_BN - 1) / OUT_BN);
+  // fewer splits mean fewer fp32 partials to write and sum; measured on the
+  // decode shapes (64 rows), ~256 workgroups suffice for K <= 4096 without
+  // SwiGLU
+  const int target = (EPI != LOOP_EPI_SWIGLU && g.K <= 4096 && g.M <= 64) ? 256 : 512;
   int splits = 1;
-  while (tiles * splits < 512 && g.K % (64 * splits * 2) == 0 && g.K / (splits * 2) >= 256) splits *= 2;
+  while (tiles * splits < target && g.K % (64 * splits * 2) == 0 && g.K / (splits * 2) >= 256) splits *= 2;
   const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
   if (splits > 1 && g.part && need <= ws_bytes) {
     g.kslice = g.K / splits;

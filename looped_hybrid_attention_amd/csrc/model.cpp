@@ -495,6 +495,7 @@ extern "C" int loop_prefill(loop_model* m, const loop_prefill_args* a, void* str
   const int B = a->batch, T = a->seq_len;
   if (B < 1 || B > c.max_batch) return loop_fail(LOOP_ECAPACITY, "batch %d out of [1, %d]", B, c.max_batch);
   if (T < 1) return loop_fail(LOOP_EINVAL, "seq_len must be >= 1");
+  if (T > 65536) return loop_fail(LOOP_ECAPACITY, "seq_len %d above 65536 tokens per call (chunked prefill: several calls)", T);
   if ((int64_t)B * T > c.max_tokens) return loop_fail(LOOP_ECAPACITY, "batch*seq_len %lld > max_tokens %d", (long long)B * T, c.max_tokens);
   if (int r = check_slots(c, B, a->slots)) return r;
   if (!a->start_pos) return loop_fail(LOOP_EINVAL, "start_pos is NULL");
