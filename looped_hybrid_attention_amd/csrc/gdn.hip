@@ -436,10 +436,10 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
 // of 16 consecutive rows hit distinct banks), and chunk c + 2 is pulled into
 // L2 (one 4-byte copy per 128-byte line, into a scratch corner of LDS) so
 // that the copies of the next step hit L2.  Per chunk, two barriers:
-//   U phase: wave w computes the partial product of token tile w % 4 over
-//   the K half w / 4 (16 fp32 MFMAs), stored transposed [j][t];
-//   update: wave w updates S columns 16w .. 16w+15 from U^T (= Ut^T minus the
-//   two partials) and Kd^T (16 MFMAs).
+//   U phase: waves 0..3 compute U for token tile w (32 fp32 MFMAs over all
+//   of K), stored transposed [j][t] (the next phase reads it along t);
+//   update: wave w updates S columns 16w .. 16w+15 from U^T and Kd^T
+//   (16 MFMAs).
 // The entry state of every chunk is written for the output kernel; the final
 // state to the slot.  All Dv/16 row blocks of a (seq, head) read the same W
 // and Kd, so they are placed on one XCD (workgroups go to XCDs round-robin
@@ -454,10 +454,10 @@ struct ScanLds {
   static constexpr int U_B = 16 * CH * 4;     // 16 rows of Ut^T
   static constexpr int STAGE = W_B + K_B + U_B;
   static constexpr int LS = DK + 4;           // S rows (floats)
-  static constexpr int LP = CH + 4;           // partial-product rows (floats)
+  static constexpr int LP = CH + 4;           // U^T rows (floats)
   static constexpr int S_OFF = 2 * STAGE;
   static constexpr int P_OFF = S_OFF + 16 * LS * 4;
-  static constexpr int X_OFF = P_OFF + 2 * 16 * LP * 4;  // L2 warm-up landing (4 bytes per lane)
+  static constexpr int X_OFF = P_OFF + 16 * LP * 4;  // L2 warm-up landing (4 bytes per lane)
   static constexpr int G_OFF = X_OFF + SCAN_NT_ * 4;      // gC of every chunk
   static constexpr int bytes = G_OFF + SCAN_MAX_CHUNKS * 4;
 };
@@ -469,10 +469,9 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, i
   constexpr int WI = L::W_B / 1024 / 8;       // W copy instructions per wave
   constexpr int KI = L::K_B / 1024 / 8;       // Kd^T copy instructions per wave
   constexpr int WPR = DK / 4;                 // 16-byte pieces per W row
-  constexpr int KQ = DK / 8;                  // k per lane group in the U phase
   extern __shared__ __align__(16) uint8_t scan_smem[];
   float* sS = reinterpret_cast<float*>(scan_smem + L::S_OFF);
-  float* sP = reinterpret_cast<float*>(scan_smem + L::P_OFF);   // [2][16][LP]
+  float* sP = reinterpret_cast<float*>(scan_smem + L::P_OFF);   // U^T [16][LP]
   constexpr int NJB = DK / 16;
   const int xcd = blockIdx.x % N_XCD, q = blockIdx.x / N_XCD;
   const int g = (q / NJB) * N_XCD + xcd;
@@ -538,8 +537,6 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, i
   // top of chunk c + 1, vmcnt(2) means its copies have landed.
   SCAN_COPY(0, 0);
   SCAN_WARM(min(1, a.n_chunks - 1));
-  // U phase operands: token tile tt, K half hh; update: S columns 16 wave ..
-  const int tt = wave & 3, hh = wave >> 2;
   for (int c = 0; c < a.n_chunks; ++c) {
     // chunk c has landed (this wave's copies) and every wave has finished
     // chunk c - 1
@@ -561,17 +558,18 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, i
       const f32x4 v = *reinterpret_cast<const f32x4*>(sS + j * LS + k4);
       *reinterpret_cast<f32x4*>(P.S + (int64_t)(j0 + j) * DK + k4) = v;
     }
-    // U phase: P_hh[j][t] = sum over k in half hh of W[t][k] S[j][k], tokens
-    // t of tile tt.  Lane group kk takes k = DK/2 hh + KQ kk .. + KQ-1 (a
+    // U phase (waves 0..3): U^T[j][t] = Ut^T[j][t] - sum_k W[t][k] S[j][k]
+    // for tokens t of tile wave.  Lane group kk takes k = DK/4 kk .. (a
     // permutation of K applied to both operands): 128-bit reads.
-    {
-      const int row = 16 * tt + i16;
+    if (wave < 4) {
+      constexpr int KQ4 = DK / 4;
+      const int row = 16 * wave + i16;
       const float* wr = reinterpret_cast<const float*>(st) + row * DK;
-      const float* sr = sS + i16 * LS + (DK / 2) * hh + KQ * kk;
-      float av[KQ], bv[KQ];
+      const float* sr = sS + i16 * LS + KQ4 * kk;
+      float av[KQ4], bv[KQ4];
 #pragma unroll
-      for (int qq = 0; qq < KQ / 4; ++qq) {
-        const int pc = ((DK / 2) * hh + KQ * kk) / 4 + qq;
+      for (int qq = 0; qq < KQ4 / 4; ++qq) {
+        const int pc = (KQ4 * kk) / 4 + qq;
         const f32x4 x = *reinterpret_cast<const f32x4*>(wr + 4 * (pc ^ (row & 15)));
         const f32x4 y = *reinterpret_cast<const f32x4*>(sr + 4 * qq);
 #pragma unroll
@@ -579,33 +577,31 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, i
       }
       f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < KQ; i += 2) {
+      for (int i = 0; i < KQ4; i += 2) {
         acc0 = mfma16x16x4f32(av[i], bv[i], acc0);
         acc1 = mfma16x16x4f32(av[i + 1], bv[i + 1], acc1);
       }
       acc0 += acc1;
-      // lane holds P[t = 16 tt + 4 kk + r][j = i16]
-      *reinterpret_cast<f32x4*>(sP + (hh * 16 + i16) * LP + 16 * tt + 4 * kk) = acc0;
+      // lane holds W S^T [t = 16 wave + 4 kk + r][j = i16]
+      const float* ut = reinterpret_cast<const float*>(st + L::W_B + L::K_B) + i16 * CH;
+      const int pc = 4 * wave + kk;  // Ut^T piece of t = 16 wave + 4 kk ..
+      const f32x4 u = *reinterpret_cast<const f32x4*>(ut + 4 * (pc ^ i16));
+      *reinterpret_cast<f32x4*>(sP + i16 * LP + 16 * wave + 4 * kk) = u - acc0;
     }
     lds_barrier();  // the next chunk's copies stay in flight
     // update: S[j][k] = gC S[j][k] + sum_t U[t][j] Kd[t][k] for the columns
-    // k = 16 wave + i16; U^T[j][t] = Ut^T[j][t] - P_0[j][t] - P_1[j][t].
-    // Lane group kk takes t = 16 kk .. + 15.
+    // k = 16 wave + i16.  Lane group kk takes t = 16 kk .. + 15.
     if (wave < DK / 16) {
-      const float* ut = reinterpret_cast<const float*>(st + L::W_B + L::K_B) + i16 * CH;
       const float* kd = reinterpret_cast<const float*>(st + L::W_B) + (16 * wave + i16) * CH;
-      const float* p0 = sP + i16 * LP + 16 * kk;
-      const float* p1 = sP + (16 + i16) * LP + 16 * kk;
+      const float* uu = sP + i16 * LP + 16 * kk;
       float av[16], bv[16];
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) {
         const int pc = 4 * kk + qq;
-        const f32x4 u = *reinterpret_cast<const f32x4*>(ut + 4 * (pc ^ i16));
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(p0 + 4 * qq);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(p1 + 4 * qq);
+        const f32x4 u = *reinterpret_cast<const f32x4*>(uu + 4 * qq);
         const f32x4 y = *reinterpret_cast<const f32x4*>(kd + 4 * (pc ^ i16));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { av[4 * qq + e] = u[e] - x0[e] - x1[e]; bv[4 * qq + e] = y[e]; }
+        for (int e = 0; e < 4; ++e) { av[4 * qq + e] = u[e]; bv[4 * qq + e] = y[e]; }
       }
       f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
 #pragma unroll
