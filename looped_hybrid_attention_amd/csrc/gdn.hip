@@ -190,11 +190,14 @@ DEV ChunkPtr chunk_ptr(const GdnArgs& a, int b, int h, int c, int DK) {
 }
 
 // ------------------------------------------------------- chunk prep
-// grid (chunk, head, seq).  Writes W = T diag(beta gamma) K, Ut = T diag(beta) V,
+// grid (chunk, head, seq), eight waves (two per SIMD, so that one's LDS reads
+// overlap the other's MFMAs).  Writes W = T diag(beta gamma) K, Ut = T diag(beta) V,
 // Kd = exp(G_C - G) K, Qp = gamma Q - Mqk W and Up = Mqk Ut, and gC, where
-// Mqk = tril(exp(G_r - G_i)) * Q K^T and T = (I + A)^-1.
+// Mqk = tril(exp(G_r - G_i)) * Q K^T and T = (I + A)^-1.  In the products
+// wave w takes the 16-row tile w % 4 and half (w / 4) of the column tiles.
+constexpr int PNT = 512;
 template <int DK>
-__global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
+__global__ __launch_bounds__(PNT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   constexpr int DV = DK;
   constexpr int LD = DK + 4;   // [CH][DK] rows
   constexpr int LC = CH + 4;   // [CH][CH] rows
@@ -218,13 +221,13 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   const int64_t row0 = (int64_t)b * a.T + t0;
   const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
 
-  // q, k, v of the chunk's rows: 4 threads per row, DK/4 dims each, every
+  // q, k, v of the chunk's rows: 8 threads per row, DK/8 dims each, every
   // load issued before any is used; q and k L2-normalised per row.
   {
-    static_assert(CH * 4 == NT, "4 threads per row");
-    constexpr int PER = DK / 4;      // dims per thread
+    static_assert(CH * 8 == PNT, "8 threads per row");
+    constexpr int PER = DK / 8;      // dims per thread
     constexpr int NV = PER / 8;      // 16-byte loads per tensor
-    const int r = tid >> 2, part = tid & 3;
+    const int r = tid >> 3, part = tid & 7;
     const bool ok = r < C;
     const uint16_t* pr = a.proj + (row0 + min(r, C - 1)) * a.proj_stride;
     const int d0 = part * PER;
@@ -250,10 +253,11 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
         sq += q * q;
         sk += k * k;
       }
-    sq += __shfl_xor(sq, 1, 64);
-    sq += __shfl_xor(sq, 2, 64);
-    sk += __shfl_xor(sk, 1, 64);
-    sk += __shfl_xor(sk, 2, 64);
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) {
+      sq += __shfl_xor(sq, o, 64);
+      sk += __shfl_xor(sk, o, 64);
+    }
     const float iq = ok ? rsqrtf(sq + a.eps) * a.q_scale : 0.f;
     const float ik = ok ? rsqrtf(sk + a.eps) : 0.f;
 #pragma unroll
@@ -288,19 +292,22 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   }
   if (tid == 0) *P.gC = __expf(GC);
   // A = beta_r exp(G_r - G_i) k_r.k_i (i < r), Mqk = exp(G_r - G_i) q_r.k_i (i <= r)
+  const int rt = wave & 3, ch = wave >> 2;  // row tile, column half of the products
   {
     const int i16 = lane & 15, kk = lane >> 4;
     float aK[DK / 4], aQ[DK / 4];
-    row_quarter<DK>(aK, sK + wave * 16 * LD, LD);
-    row_quarter<DK>(aQ, sQ + wave * 16 * LD, LD);
-    for (int nt = 0; nt < CH / 16; ++nt) {
+    row_quarter<DK>(aK, sK + rt * 16 * LD, LD);
+    row_quarter<DK>(aQ, sQ + rt * 16 * LD, LD);
+#pragma unroll
+    for (int n2 = 0; n2 < CH / 32; ++n2) {
+      const int nt = ch * (CH / 32) + n2;
       f32x4 kk_acc = {0, 0, 0, 0}, qk_acc = {0, 0, 0, 0};
       float bK[DK / 4];
       row_quarter<DK>(bK, sK + nt * 16 * LD, LD);
       mma2<DK>(kk_acc, qk_acc, aK, bK, aQ, bK);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
+        const int row = rt * 16 + 4 * kk + r, col = nt * 16 + i16;
         const float dec = col <= row ? __expf(sG[row] - sG[col]) : 0.f;
         sA[row * LC + col] = col < row ? sB[row] * dec * kk_acc[r] : 0.f;
         sM[row * LC + col] = col <= row ? dec * qk_acc[r] : 0.f;
@@ -309,15 +316,15 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   }
   __syncthreads();
   // Kd^T = (exp(G_C - G) k^)^T (rows >= C are zero because k^ is)
-  for (int idx = tid; idx < CH * DK; idx += NT) {
+  for (int idx = tid; idx < CH * DK; idx += PNT) {
     const int d = idx / CH, r = idx % CH;
     P.KdT[idx] = sEK[r] * sK[r * LD + d];
   }
   // T = (I + A)^-1 (unit lower triangular) into sT2, in 16 x 16 blocks.
-  // Diagonal blocks by forward substitution (wave w: block w, lane j < 16
-  // owns column j); then, by block diagonal d = I - J = 1, 2, 3 (one block
+  // Diagonal blocks by forward substitution (wave w < 4: block w, lane j <
+  // 16 owns column j); then, by block diagonal d = I - J = 1, 2, 3 (one block
   // per wave), T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ on the MFMA.
-  {
+  if (wave < CH / 16) {
     const int I = wave, j = lane & 15;
     const float* Ab = sA + (16 * I) * LC + 16 * I;
     float t[16];
@@ -334,7 +341,9 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sT2[(16 * I + i) * LC + 16 * I + j] = t[i];
     }
-    for (int idx = tid; idx < CH * CH; idx += NT) {  // blocks above the diagonal
+  }
+  {
+    for (int idx = tid; idx < CH * CH; idx += PNT) {  // blocks above the diagonal
       const int r = idx / CH, cc = idx % CH;
       if ((cc >> 4) > (r >> 4)) sT2[r * LC + cc] = 0.f;
     }
@@ -359,47 +368,49 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
     }
   }
   // T diag(beta gamma) -> sA (A is no longer needed), T diag(beta) -> sT2
-  for (int idx = tid; idx < CH * CH; idx += NT) {
+  for (int idx = tid; idx < CH * CH; idx += PNT) {
     const int r = idx / CH, cc = idx % CH;
     const float tv = sT2[r * LC + cc];
     sA[r * LC + cc] = tv * sB[cc] * sEG[cc];
     sT2[r * LC + cc] = tv * sB[cc];
   }
   __syncthreads();
-  // W = (T diag(beta gamma)) K^, Ut = (T diag(beta)) V; wave w: rows 16w..16w+15
-  constexpr int NTILE = DK / 16;
+  // W = (T diag(beta gamma)) K^, Ut = (T diag(beta)) V; wave w: rows of tile
+  // w % 4, column tiles of half w / 4
+  constexpr int NTILE = DK / 16 / 2;
   f32x4 wacc[NTILE], uacc[NTILE];
   {
     float a0[CH / 4], a1[CH / 4];
-    row_quarter<CH>(a0, sA + wave * 16 * LC, LC);
-    row_quarter<CH>(a1, sT2 + wave * 16 * LC, LC);
+    row_quarter<CH>(a0, sA + rt * 16 * LC, LC);
+    row_quarter<CH>(a1, sT2 + rt * 16 * LC, LC);
 #pragma unroll
-    for (int nt = 0; nt < NTILE; ++nt) {
-      wacc[nt] = (f32x4){0, 0, 0, 0};
-      uacc[nt] = (f32x4){0, 0, 0, 0};
+    for (int n = 0; n < NTILE; ++n) {
+      const int nt = ch * NTILE + n;
+      wacc[n] = (f32x4){0, 0, 0, 0};
+      uacc[n] = (f32x4){0, 0, 0, 0};
       float b0[CH / 4], b1[CH / 4];
       col_quarter<CH>(b0, sK + nt * 16, LD);
       col_quarter<CH>(b1, sV + nt * 16, LD);
-      mma2<CH>(wacc[nt], uacc[nt], a0, b0, a1, b1);
+      mma2<CH>(wacc[n], uacc[n], a0, b0, a1, b1);
     }
   }
   __syncthreads();  // sK, sV fully read: reuse them for W and Ut
   {
     const int i16 = lane & 15, kk = lane >> 4;
 #pragma unroll
-    for (int nt = 0; nt < NTILE; ++nt)
+    for (int n = 0; n < NTILE; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
+        const int row = rt * 16 + 4 * kk + r, col = (ch * NTILE + n) * 16 + i16;
         const bool ok = row < C;
-        const float w = ok ? wacc[nt][r] : 0.f, u = ok ? uacc[nt][r] : 0.f;
+        const float w = ok ? wacc[n][r] : 0.f, u = ok ? uacc[n][r] : 0.f;
         sK[row * LD + col] = w;
         sV[row * LD + col] = u;
         P.W[row * DK + col] = w;
       }
   }
   __syncthreads();
-  for (int idx = tid; idx < CH * DV; idx += NT) {  // Ut^T
+  for (int idx = tid; idx < CH * DV; idx += PNT) {  // Ut^T
     const int d = idx / CH, r = idx % CH;
     P.UtT[idx] = sV[r * LD + d];
   }
@@ -407,9 +418,10 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
   {
     const int i16 = lane & 15, kk = lane >> 4;
     float am[CH / 4];
-    row_quarter<CH>(am, sM + wave * 16 * LC, LC);
+    row_quarter<CH>(am, sM + rt * 16 * LC, LC);
 #pragma unroll
-    for (int nt = 0; nt < NTILE; ++nt) {
+    for (int n = 0; n < NTILE; ++n) {
+      const int nt = ch * NTILE + n;
       f32x4 mw = {0, 0, 0, 0}, mu = {0, 0, 0, 0};
       float b0[CH / 4], b1[CH / 4];
       col_quarter<CH>(b0, sK + nt * 16, LD);
@@ -417,7 +429,7 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
       mma2<CH>(mw, mu, am, b0, am, b1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wave * 16 + 4 * kk + r, col = nt * 16 + i16;
+        const int row = rt * 16 + 4 * kk + r, col = nt * 16 + i16;
         const bool ok = row < C;
         P.Qp[row * DK + col] = ok ? sEG[row] * sQ[row * LD + col] - mw[r] : 0.f;
         P.Up[row * DK + col] = ok ? mu[r] : 0.f;
@@ -837,7 +849,7 @@ hipError_t prefill_dk(const GdnArgs& a, int B, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(gdn_chunk_prep_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), lds_prep, s, a);
+  hipLaunchKernelGGL(gdn_chunk_prep_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(PNT), lds_prep, s, a);
   const int groups = (a.H * B + N_XCD - 1) / N_XCD * N_XCD;
   hipLaunchKernelGGL(gdn_chunk_scan_kernel<DK>, dim3(groups * (DK / 16)), dim3(SCAN_NT), ScanLds<DK>::bytes, s, a,
                      a.H * B);
