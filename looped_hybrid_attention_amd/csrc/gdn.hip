@@ -24,7 +24,6 @@
 namespace {
 
 constexpr int CH = 64;   // chunk length
-constexpr int NT = 256;
 
 DEV float softplusf_(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 
@@ -641,16 +640,17 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, i
 }
 
 // ------------------------------------------------------- chunk output
-// grid (chunk, head, seq): O = Qp S_c^T + Up, then per token and head
-// y = RMSNorm(o; g_o) * SiLU(z) -> bf16.
+// grid (chunk, head, seq), eight waves: O = Qp S_c^T + Up, then per token
+// and head y = RMSNorm(o; g_o) * SiLU(z) -> bf16.
+constexpr int ONT = 512;
 template <int DK>
-__global__ __launch_bounds__(NT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
+__global__ __launch_bounds__(ONT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
   constexpr int DV = DK;
   constexpr int LD = DK + 4;
-  constexpr int NQ = CH * DK / 4 / NT;   // 16-byte pieces of Qp per thread
-  constexpr int NS = DV * DK / 4 / NT;   // of S_c
-  constexpr int PER = DV / 4;            // output dims per thread (4 threads per row)
-  static_assert(NQ * 4 * NT == CH * DK && NS * 4 * NT == DV * DK && CH * 4 == NT, "thread split");
+  constexpr int NQ = CH * DK / 4 / ONT;  // 16-byte pieces of Qp per thread
+  constexpr int NS = DV * DK / 4 / ONT;  // of S_c
+  constexpr int PER = DV / 8;            // output dims per thread (8 threads per row)
+  static_assert(NQ * 4 * ONT == CH * DK && NS * 4 * ONT == DV * DK && CH * 8 == ONT, "thread split");
   extern __shared__ __align__(16) float gsm[];
   float* sQ = gsm;             // Qp [CH][LD], later O
   float* sS = sQ + CH * LD;    // S_c [DV][LD]
@@ -660,13 +660,13 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
   const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
   // every global read first: Qp and S_c (for LDS), this thread's row piece
   // of Up and of the gate z
-  const int r = tid >> 2, d0 = (tid & 3) * PER;
+  const int r = tid >> 3, d0 = (tid & 7) * PER;
   const int64_t m = (int64_t)b * a.T + c * CH + min(r, C - 1);
   u32x4 rq[NQ], rs[NS], ru[PER / 4], rz[PER / 8];
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) rq[i] = *reinterpret_cast<const u32x4*>(P.Qp + (tid + i * NT) * 4);
+  for (int i = 0; i < NQ; ++i) rq[i] = *reinterpret_cast<const u32x4*>(P.Qp + (tid + i * ONT) * 4);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) rs[i] = *reinterpret_cast<const u32x4*>(P.S + (tid + i * NT) * 4);
+  for (int i = 0; i < NS; ++i) rs[i] = *reinterpret_cast<const u32x4*>(P.S + (tid + i * ONT) * 4);
 #pragma unroll
   for (int i = 0; i < PER / 4; ++i) ru[i] = *reinterpret_cast<const u32x4*>(P.Up + r * DK + d0 + 4 * i);
   const uint16_t* z = a.proj + m * a.proj_stride + a.off_z + h * DV + d0;
@@ -674,31 +674,34 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
   for (int i = 0; i < PER / 8; ++i) rz[i] = *reinterpret_cast<const u32x4*>(z + 8 * i);
 #pragma unroll
   for (int i = 0; i < NQ; ++i) {
-    const int e = (tid + i * NT) * 4;
+    const int e = (tid + i * ONT) * 4;
     *reinterpret_cast<u32x4*>(sQ + (e / DK) * LD + e % DK) = rq[i];
   }
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    const int e = (tid + i * NT) * 4;
+    const int e = (tid + i * ONT) * 4;
     *reinterpret_cast<u32x4*>(sS + (e / DK) * LD + e % DK) = rs[i];
   }
   __syncthreads();
-  // O = Qp S_c^T (+ Up below); wave w: rows 16w .. 16w+15, tiles in pairs
-  constexpr int NTILE = DV / 16;
+  // O = Qp S_c^T (+ Up below); wave w: rows of tile w % 4, the column
+  // tiles of half w / 4, in pairs
+  constexpr int NTILE = DV / 16 / 2;
   static_assert(NTILE % 2 == 0, "tile pairs");
+  const int rt = wave & 3, ch = wave >> 2;
   f32x4 acc[NTILE];
   const int i16 = lane & 15, kk = lane >> 4;
 #pragma unroll
-  for (int nt = 0; nt < NTILE; nt += 2) {
-    acc[nt] = (f32x4){0, 0, 0, 0};
-    acc[nt + 1] = (f32x4){0, 0, 0, 0};
-    mm_nt2s(acc[nt], acc[nt + 1], sQ + wave * 16 * LD, LD, sS + nt * 16 * LD, sS + (nt + 1) * 16 * LD, LD, DK);
+  for (int n = 0; n < NTILE; n += 2) {
+    const int nt = ch * NTILE + n;
+    acc[n] = (f32x4){0, 0, 0, 0};
+    acc[n + 1] = (f32x4){0, 0, 0, 0};
+    mm_nt2s(acc[n], acc[n + 1], sQ + rt * 16 * LD, LD, sS + nt * 16 * LD, sS + (nt + 1) * 16 * LD, LD, DK);
   }
   __syncthreads();  // sQ fully read: reuse it for O
 #pragma unroll
-  for (int nt = 0; nt < NTILE; ++nt)
+  for (int n = 0; n < NTILE; ++n)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sQ[(wave * 16 + 4 * kk + q) * LD + nt * 16 + i16] = acc[nt][q];
+    for (int q = 0; q < 4; ++q) sQ[(rt * 16 + 4 * kk + q) * LD + (ch * NTILE + n) * 16 + i16] = acc[n][q];
   __syncthreads();
   // per token and head: y = RMSNorm(O + Up; g_o) * SiLU(z) -> bf16
   float v[PER];
@@ -710,8 +713,8 @@ __global__ __launch_bounds__(NT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
       v[4 * i + e] = sQ[r * LD + d0 + 4 * i + e] + __uint_as_float(ru[i][e]);
       ss += v[4 * i + e] * v[4 * i + e];
     }
-  ss += __shfl_xor(ss, 1, 64);
-  ss += __shfl_xor(ss, 2, 64);
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) ss += __shfl_xor(ss, o, 64);
   const float inv = rsqrtf(ss / DV + a.eps);
   if (r < C) {
     uint16_t* y = a.out + m * a.out_stride + h * DV + d0;
@@ -853,7 +856,7 @@ hipError_t prefill_dk(const GdnArgs& a, int B, hipStream_t s) {
   const int groups = (a.H * B + N_XCD - 1) / N_XCD * N_XCD;
   hipLaunchKernelGGL(gdn_chunk_scan_kernel<DK>, dim3(groups * (DK / 16)), dim3(SCAN_NT), ScanLds<DK>::bytes, s, a,
                      a.H * B);
-  hipLaunchKernelGGL(gdn_chunk_out_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(NT), lds_out, s, a);
+  hipLaunchKernelGGL(gdn_chunk_out_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(ONT), lds_out, s, a);
   return hipGetLastError();
 }
 
