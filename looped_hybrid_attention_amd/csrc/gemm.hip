@@ -15,6 +15,7 @@
 #include "launch.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace {
 
@@ -256,6 +257,54 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, int spli
       else if (EPI == LOOP_EPI_F32) reinterpret_cast<float*>(g.C)[o] = v;
       else reinterpret_cast<float*>(g.C)[o] = g.R[o] + v;
     }
+  }
+}
+
+// Split-K sum fused with the next pre-norm (rows of a decode call): per row
+// m, C = sum of the partials in split order (+ R), then
+// hn = bf16(RMSNorm(C + X2; gain)) with X2 the loop input x, or none.
+// One row per workgroup of 1024 threads, PER columns (4 apart by 1024) per
+// thread; the split partials are summed in split order (SPL splits).
+template <int EPI, int PER, int SPL>
+__global__ __launch_bounds__(1024) void splitk_reduce_norm_kernel(GemmArgs g, const float* X2, const uint16_t* gain,
+                                                                  uint16_t* hn, float eps) {
+  static_assert(EPI == LOOP_EPI_F32 || EPI == LOOP_EPI_F32_RES, "fp32 output");
+  __shared__ float red[16];
+  const int64_t m = blockIdx.x;
+  float pv[PER][SPL], rx[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = min((int)threadIdx.x + 1024 * i, g.N - 1);
+#pragma unroll
+    for (int sp = 0; sp < SPL; ++sp) pv[i][sp] = g.part[((int64_t)sp * g.M + m) * g.N + c];
+    const int64_t o = m * g.ldc + c;
+    rx[i] = (EPI == LOOP_EPI_F32_RES ? g.R[o] : 0.f) + (X2 ? X2[o] : 0.f);
+  }
+  float y[PER];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = threadIdx.x + 1024 * i;
+    float v = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < SPL; ++sp) v += pv[i][sp];
+    const int64_t o = m * g.ldc + c;
+    float yv = 0.f;
+    if (c < g.N) {
+      // plain: C = R + v (and the norm input is C); loop: C = v, input C + X2
+      const float cv = EPI == LOOP_EPI_F32_RES ? g.R[o] + v : v;
+      reinterpret_cast<float*>(g.C)[o] = cv;
+      yv = EPI == LOOP_EPI_F32_RES ? cv : v + rx[i];
+    }
+    y[i] = yv;
+    ss += yv * yv;
+  }
+  ss = block_sum<1024>(ss, red);
+  const float inv = rsqrtf(ss / g.N + eps);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = threadIdx.x + 1024 * i;
+    if (c < g.N) hn[m * g.N + c] = f2bf_bits(y[i] * inv * bf2f(gain[c]));
   }
 }
 
@@ -779,4 +828,42 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, v
     case LOOP_EPI_SWIGLU: return launch_epi<LOOP_EPI_SWIGLU>(g, ws_bytes, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_norm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
+                            const float* R, const float* X2, const void* gain, void* hn, float eps, int M, int N,
+                            int K, hipStream_t s, float* ws, size_t ws_bytes) {
+  GemmArgs g{(const uint16_t*)A, lda, (const uint16_t*)B, ldb, C, ldc, R, M, N, K, N, ws, K};
+  const int64_t a_bytes = (int64_t)M * lda * 2, b_bytes = (int64_t)N * ldb * 2;
+  // the decode shape of the projection feeding the FFN norm: weight-streaming
+  // tiles with split K, the split sum and the norm in one row pass
+  if (M <= 64 && N <= 4096 && K <= 4096 && K % (SK_KC * SK_NSET) == 0 && lda % 8 == 0 &&
+      ldb % 8 == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31)) {
+    const int tiles = (N + 16 * SK_WAVES - 1) / (16 * SK_WAVES);
+    int splits = 1;
+    while (tiles * splits < 256 && splits < 8 && K % (SK_KC * SK_NSET * splits * 2) == 0) splits *= 2;
+    if (splits > 1 && ws && (size_t)splits * M * N * sizeof(float) <= ws_bytes) {
+      g.kslice = K / splits;
+      auto launch = [&](auto epi_tag) {
+        constexpr int EPI = decltype(epi_tag)::value;
+        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, SK_WAVES>), dim3(tiles, splits), dim3(64 * SK_WAVES), 0, s,
+                           g, (uint32_t)a_bytes, (uint32_t)b_bytes);
+        if (splits == 4)
+          hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 4>), dim3(M), dim3(1024), 0, s, g, X2,
+                             (const uint16_t*)gain, (uint16_t*)hn, eps);
+        else if (splits == 2)
+          hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 2>), dim3(M), dim3(1024), 0, s, g, X2,
+                             (const uint16_t*)gain, (uint16_t*)hn, eps);
+        else
+          hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 8>), dim3(M), dim3(1024), 0, s, g, X2,
+                             (const uint16_t*)gain, (uint16_t*)hn, eps);
+      };
+      if (R) launch(std::integral_constant<int, LOOP_EPI_F32_RES>());
+      else launch(std::integral_constant<int, LOOP_EPI_F32>());
+      return hipGetLastError();
+    }
+  }
+  hipError_t e = launch_gemm(A, lda, B, ldb, C, ldc, R, M, N, K, R ? LOOP_EPI_F32_RES : LOOP_EPI_F32, s, ws, ws_bytes);
+  if (e != hipSuccess) return e;
+  return launch_rmsnorm(C, X2, nullptr, ldc, gain, hn, M, N, eps, s);
 }

@@ -12,6 +12,13 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, v
                        const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws = nullptr,
                        size_t ws_bytes = 0);
 
+// C = A . B^T (+ R) as launch_gemm (fp32 output), then
+// hn[m] = bf16(RMSNorm(C[m] + X2[m]; gain)) (X2 may be NULL; rows of C and
+// X2 share the stride ldc; hn rows are N apart).
+hipError_t launch_gemm_norm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,
+                            const float* R, const float* X2, const void* gain, void* hn, float eps, int M, int N,
+                            int K, hipStream_t s, float* ws, size_t ws_bytes);
+
 hipError_t launch_synth_normal(void* dst, int64_t n, int dtype, uint32_t seed, uint32_t key,
                                int64_t start, double std, double mean, hipStream_t s);
 hipError_t launch_synth_token_ids(int32_t* dst, int64_t n, uint32_t vocab, uint32_t seed,

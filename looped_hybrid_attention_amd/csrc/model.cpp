@@ -342,16 +342,15 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   uint16_t* hn = at<uint16_t>(m, L.hn);
   uint16_t* act = at<uint16_t>(m, L.act);
   {
+    // O-projection and the FFN pre-norm: plain hmid = h + o W_o^T, hn =
+    // RMSNorm(hmid); loop a = o W_o^T, hn = RMSNorm(x + a)
     Prof p(m, LOOP_K_GEMM_O, s);
     if (!d.loop)
-      HIP_TRY(launch_gemm(obuf, mix_width, w.w_o, mix_width, hmid, dm, h, M, dm, mix_width, LOOP_EPI_F32_RES, s, SK));
+      HIP_TRY(launch_gemm_norm(obuf, mix_width, w.w_o, mix_width, hmid, dm, h, nullptr, w.ffn_norm, hn, c.eps, M, dm,
+                               mix_width, s, SK));
     else
-      HIP_TRY(launch_gemm(obuf, mix_width, w.w_o, mix_width, a, dm, nullptr, M, dm, mix_width, LOOP_EPI_F32, s, SK));
-  }
-  {
-    Prof p(m, LOOP_K_ROWS, s);
-    if (!d.loop) HIP_TRY(launch_rmsnorm(hmid, nullptr, nullptr, dm, w.ffn_norm, hn, M, dm, c.eps, s));
-    else HIP_TRY(launch_rmsnorm(x, a, nullptr, dm, w.ffn_norm, hn, M, dm, c.eps, s));
+      HIP_TRY(launch_gemm_norm(obuf, mix_width, w.w_o, mix_width, a, dm, nullptr, x, w.ffn_norm, hn, c.eps, M, dm,
+                               mix_width, s, SK));
   }
   {
     Prof p(m, LOOP_K_GEMM_GATEUP, s);

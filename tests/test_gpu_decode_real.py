@@ -1,12 +1,14 @@
 """Decode at real width and full context, in the launch configuration of the
-decode benchmark: one 4-layer group (GDN, GDN, GDN, full attention; d 4096,
-FFN 12288, 16 Q / 4 KV heads x 256, GDN 16 x 128) run as a loop block with a
-1024-token vocabulary, batch 64, every sequence at position 32,768 over a
-pre-filled cache (K and V N(0, 1) bf16 at positions 0..32767 of the
-full-attention slot, GDN states N(0, 0.1) fp32), as the decode workload fills
-its 14 KV and 42 GDN slots.  This runs the kernels the benchmark times: the
-split decode attention over 32,769 keys with its combine, the Gated-DeltaNet
-single-token recurrence, the batch-64 projections.
+decode benchmark: two 4-layer groups (GDN, GDN, GDN, full attention; d 4096,
+FFN 12288, 16 Q / 4 KV heads x 256, GDN 16 x 128), the first run as plain
+residual layers and the second as a one-pass loop block (fork, mHC, merge),
+with a 1024-token vocabulary, batch 64, every sequence at position 32,768
+over pre-filled caches (K and V N(0, 1) bf16 at positions 0..32767 of both
+full-attention slots, GDN states N(0, 0.1) fp32), as the decode workload
+fills its 14 KV and 42 GDN slots.  This runs the kernels the benchmark
+times: the split decode attention over 32,769 keys with its combine, the
+Gated-DeltaNet single-token recurrence, the batch-64 projections (plain and
+loop epilogues, the split sum fused with the FFN pre-norm).
 
 Sampled: the oracle decodes 3 of the 64 sequences (every step of the path is
 independent across sequences: the projections are row-wise, attention and
@@ -37,7 +39,7 @@ SAMPLE = (0, 37, 63)
 
 def test_decode_b64_ctx32768_group():
     torch = torch_cuda()
-    dims = synth.preset("group", vocab=V)
+    dims = synth.preset("group", vocab=V, n_layers=8, loop_start=4, loop_end=8)
     d = dims["d_model"]
     Hkv, D = dims["n_kv_heads"], dims["head_dim"]
     H, Dk, Dv = dims["gdn_heads"], dims["gdn_dk"], dims["gdn_dv"]
@@ -48,11 +50,12 @@ def test_decode_b64_ctx32768_group():
         rows = L.loop_schedule(cfg)
         n_full = sum(r[1] for r in rows)
         n_gdn = len(rows) - n_full
-        assert n_full == 1 and n_gdn == 3
+        assert n_full == 2 and n_gdn == 6
         kv_n = B * Hkv * max_seq * D
-        for which, name in ((0, "test.decode.k"), (1, "test.decode.v")):
-            L.loop_synth_normal(g.arena.data_ptr() + L.loop_cache_offset(cfg, which, 0, 0), kv_n, 1,
-                                synth.SEED_C, synth.fnv1a32(name), 0, 1.0, 0.0, s)
+        for f in range(n_full):
+            for which, name in ((0, f"test.decode.k.{f}"), (1, f"test.decode.v.{f}")):
+                L.loop_synth_normal(g.arena.data_ptr() + L.loop_cache_offset(cfg, which, f, 0), kv_n, 1,
+                                    synth.SEED_C, synth.fnv1a32(name), 0, 1.0, 0.0, s)
         st_n = B * H * Dv * Dk
         for j in range(n_gdn):
             L.loop_synth_normal(g.arena.data_ptr() + L.loop_cache_offset(cfg, 2, j, 0), st_n, 0,
@@ -68,7 +71,7 @@ def test_decode_b64_ctx32768_group():
         torch.cuda.synchronize()
         got_l, got_h, got_n = host(logits), host(hid), host(nxt)
         assert np.isfinite(got_l).all() and np.isfinite(got_h).all()
-        k0 = L.loop_cache_offset(cfg, 0, 0, 0)
+        k0 = L.loop_cache_offset(cfg, 0, n_full - 1, 0)
         k_new = host(g.arena[k0:k0 + kv_n * 2].view(torch.bfloat16).view(B, Hkv, max_seq, D)[:, :, CTX]
                      .contiguous())
 
@@ -79,12 +82,13 @@ def test_decode_b64_ctx32768_group():
         def state_of(b, dtype):
             st = om.SeqState(ocfg, dtype)
             per = Hkv * max_seq * D
-            kb = synth.normal(synth.SEED_C, "test.decode.k", (per,), 1.0, dtype="bf16", start=b * per)
-            vb = synth.normal(synth.SEED_C, "test.decode.v", (per,), 1.0, dtype="bf16", start=b * per)
-            K = synth.bf16_bits_to_f32(kb).reshape(Hkv, max_seq, D)[:, :CTX]
-            Vt = synth.bf16_bits_to_f32(vb).reshape(Hkv, D, max_seq)[:, :, :CTX]
-            st.kv[0].k = np.ascontiguousarray(K, dtype)
-            st.kv[0].v = np.ascontiguousarray(Vt.transpose(0, 2, 1), dtype)
+            for f in range(n_full):
+                kb = synth.normal(synth.SEED_C, f"test.decode.k.{f}", (per,), 1.0, dtype="bf16", start=b * per)
+                vb = synth.normal(synth.SEED_C, f"test.decode.v.{f}", (per,), 1.0, dtype="bf16", start=b * per)
+                K = synth.bf16_bits_to_f32(kb).reshape(Hkv, max_seq, D)[:, :CTX]
+                Vt = synth.bf16_bits_to_f32(vb).reshape(Hkv, D, max_seq)[:, :, :CTX]
+                st.kv[f].k = np.ascontiguousarray(K, dtype)
+                st.kv[f].v = np.ascontiguousarray(Vt.transpose(0, 2, 1), dtype)
             for j in range(n_gdn):
                 per_s = H * Dv * Dk
                 S = synth.normal(synth.SEED_C, f"test.decode.state.{j}", (per_s,), 0.1, start=b * per_s)
@@ -98,7 +102,7 @@ def test_decode_b64_ctx32768_group():
             for W, dt in ((W32, np.float32), (W64, np.float64)):
                 st = state_of(b, dt)
                 lg, nx, h = om.decode_step(ocfg, W, [st], [int(ids[b])], bf16=True)
-                evals.append((lg[0], h[0], st.kv[0].k[:, CTX]))
+                evals.append((lg[0], h[0], st.kv[n_full - 1].k[:, CTX]))
             tol_l = parity_bar([e[0] for e in evals])
             tol_h = parity_bar([e[1] for e in evals])
             el = rel_err(got_l[b], evals[0][0])
