@@ -120,8 +120,10 @@ int64_t loop_workspace_bytes(const loop_config* cfg, int32_t max_tokens);
 
 /* Cache layout inside the arena (byte offsets from the arena base):
  *   K of (kv slot s, sequence slot b): bf16 [n_kv_heads][max_seq][head_dim]
- *   V of (s, b):                       bf16 [n_kv_heads][head_dim][max_seq]
- *                                      (transposed: positions contiguous)
+ *   V of (s, b):                       bf16 [n_kv_heads][max_seq/32][head_dim][32]
+ *                                      (transposed in blocks of 32 positions:
+ *                                      block j holds positions 32j .. 32j+31,
+ *                                      dim d of them contiguous at d * 32)
  *   per kv slot s the K blocks of sequence slots 0..max_batch-1 follow each
  *   other, then the V blocks; the GDN states follow all KV slots.
  *   GDN state of (gdn slot g, b):      fp32 [gdn_heads][gdn_dv][gdn_dk]

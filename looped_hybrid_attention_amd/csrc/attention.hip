@@ -12,12 +12,16 @@
 // of the gate projection, applied before W_o.
 //
 // Cache layout per (execution slot, sequence slot): K [Hkv][max_seq][D] and
-// V transposed [Hkv][D][max_seq], so that both the K.Q^T and the V^T.P^T
+// V transposed in blocks of VB = 32 positions, [Hkv][max_seq/32][D][32], so
+// that a block of keys is one contiguous run for both matrices and both the
+// K.Q^T and the V^T.P^T
 // products of the prefill read 16-byte runs from LDS.
 #include "common.h"
 #include "launch.h"
 
 namespace {
+
+constexpr int VB = 32;  // positions per block of the transposed V cache
 
 // ---------------------------------------------------------------- prep
 // One workgroup per token: the rotary cos / sin of the token's position are
@@ -120,9 +124,10 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(AttnPrepArgs a) {
   __syncthreads();
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t slot_b = a.seq_slot[b];
-  uint16_t* vt = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq + a.pos[b] + t0;
+  const int p = a.pos[b] + t0 + lane;  // position of this lane's token
+  uint16_t* vt = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq + (int64_t)(p / VB) * D * VB + p % VB;
   if (lane < nt)
-    for (int d = wave; d < D; d += 4) vt[(int64_t)d * a.max_seq + lane] = tile[lane * LS + d];
+    for (int d = wave; d < D; d += 4) vt[d * VB] = tile[lane * LS + d];
 }
 
 // ------------------------------------------------------- flash prefill
@@ -243,7 +248,8 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
   for (int i = 0; i < VI; ++i) {
     const int n = wave * VI + i;
     const int d = (n * 64 + lane) / 8, p = (n * 64 + lane) % 8;
-    v_src[i] = d * a.max_seq + (p ^ v_swz(d)) * 8;
+    const int lp = p ^ v_swz(d);  // keys 8 lp .. of the tile: block lp / 4 of its two
+    v_src[i] = (lp / 4) * D * VB + d * VB + (lp % 4) * 8;
   }
   // Buffer resources over this (sequence, KV head)'s K and V^T blocks.  The
   // MUBUF form of the LDS copy keeps the compiler's LDS-read waits counted
@@ -256,7 +262,7 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
     _Pragma("unroll") for (int i = 0; i < KI; ++i)                                            \
         copy16_to_lds(k_rsrc, ((k0_) * D + k_src[i]) * 2, 0, (lds_void*)(S_ + (wave * KI + i) * 1024)); \
     _Pragma("unroll") for (int i = 0; i < VI; ++i)                                            \
-        copy16_to_lds(v_rsrc, ((k0_) + v_src[i]) * 2, 0,                                      \
+        copy16_to_lds(v_rsrc, ((k0_) / VB * D * VB + v_src[i]) * 2, 0,                       \
                       (lds_void*)(S_ + KT * L::KROW + (wave * VI + i) * 1024));               \
   }
   // V^T keys at or past L_valid may hold anything; P is 0 there but 0 * NaN
@@ -445,7 +451,7 @@ __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a
   const int nk = k_end - k_begin;
   const int64_t slot_b = a.seq_slot[b];
   const uint16_t* Kc = a.k_cache + ((slot_b * a.Hkv + kvh) * (int64_t)a.max_seq + k_begin) * D;
-  const uint16_t* Vc = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq + k_begin;
+  const uint16_t* Vc = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
 
@@ -462,11 +468,12 @@ __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a
   // range ends at key nk, so K rows past it read as zero (and are masked).
   const int krow = 8 * (l16 >> 2) + (l16 & 3);  // key of this A-operand row in pass 0 (pass 1: + 4)
   const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kc, (uint32_t)nk * D * 2);
-  // V^T range: to the end of this (sequence, head) block
-  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vc, (uint32_t)((int64_t)D * a.max_seq - k_begin) * 2);
+  // V^T range: this (sequence, head)'s blocks
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vc, (uint32_t)((int64_t)D * a.max_seq * 2));
   const int kvo = (krow * D + lg * 8) * 2;
-  const int vvo = (l16 * a.max_seq + lg * 8) * 2;
-  const int vtile = 16 * a.max_seq * 2;  // bytes between 16-dim tiles of V^T
+  // V^T of the step's 32 keys is one block [D][32]: lane (l16, lg) reads dim
+  // row 16 dt + l16, keys 8 lg ..
+  const int vvo = (l16 * VB + lg * 8) * 2;
 
   float m = -1e30f, l = 0.f;  // running max (log2 units) and this lane's partial sum
   f32x4 o[NDT];
@@ -480,7 +487,7 @@ __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) kv[u][ks] = buffer_load16(krs, kvo + (kb * D + u * 4 * D + ks * 32) * 2, 0);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) vv[dt] = buffer_load16(vrs, vvo + kb * 2, dt * vtile);
+    for (int dt = 0; dt < NDT; ++dt) vv[dt] = buffer_load16(vrs, vvo + (k_begin + kb) / VB * (D * VB * 2), dt * 16 * VB * 2);
     if (kb + 32 > nk) {
       // ragged last step: V^T entries of keys at or past nk are zeroed (their
       // probabilities are zero, but the cache there may hold anything)

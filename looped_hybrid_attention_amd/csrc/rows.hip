@@ -352,6 +352,8 @@ hipError_t launch_transition(TransitionArgs t, hipStream_t s) {
   t.rows_per_block = 1;
   if (t.d <= 256) hipLaunchKernelGGL((transition_kernel<256, 1>), dim3(t.M), dim3(256), 0, s, t);
   else if (t.d <= 1024) hipLaunchKernelGGL((transition_kernel<256, 4>), dim3(t.M), dim3(256), 0, s, t);
+  // few rows (decode): more threads per row, so that more loads are in flight
+  else if (t.d <= 4096 && t.M <= 256) hipLaunchKernelGGL((transition_kernel<1024, 4>), dim3(t.M), dim3(1024), 0, s, t);
   else if (t.d <= 4096) hipLaunchKernelGGL((transition_kernel<512, 8>), dim3(t.M), dim3(512), 0, s, t);
   else if (t.d <= 8192) hipLaunchKernelGGL((transition_kernel<1024, 8>), dim3(t.M), dim3(1024), 0, s, t);
   else return hipErrorInvalidValue;

@@ -13,7 +13,8 @@ loop epilogues, the split sum fused with the FFN pre-norm).
 Sampled: the oracle decodes 3 of the 64 sequences (every step of the path is
 independent across sequences: the projections are row-wise, attention and
 the recurrence are per sequence).  The cache contents are drawn on the device
-by the seeded generator in the documented arena layout (V transposed) and
+by the seeded generator in the documented arena layout (V transposed in
+blocks of 32 positions) and
 regenerated on the host for the sampled sequences from the same counter
 streams.  Metric max |gpu - oracle| / max |oracle| per tensor (logits and
 final hidden state of each sampled sequence); bar ``parity.bar`` over the
@@ -86,9 +87,11 @@ def test_decode_b64_ctx32768_group():
                 kb = synth.normal(synth.SEED_C, f"test.decode.k.{f}", (per,), 1.0, dtype="bf16", start=b * per)
                 vb = synth.normal(synth.SEED_C, f"test.decode.v.{f}", (per,), 1.0, dtype="bf16", start=b * per)
                 K = synth.bf16_bits_to_f32(kb).reshape(Hkv, max_seq, D)[:, :CTX]
-                Vt = synth.bf16_bits_to_f32(vb).reshape(Hkv, D, max_seq)[:, :, :CTX]
+                # V cache: [Hkv][max_seq / 32][D][32] (blocks of 32 positions, transposed)
+                Vb = synth.bf16_bits_to_f32(vb).reshape(Hkv, max_seq // 32, D, 32)
+                Vp = Vb.transpose(0, 1, 3, 2).reshape(Hkv, max_seq, D)[:, :CTX]
                 st.kv[f].k = np.ascontiguousarray(K, dtype)
-                st.kv[f].v = np.ascontiguousarray(Vt.transpose(0, 2, 1), dtype)
+                st.kv[f].v = np.ascontiguousarray(Vp, dtype)
             for j in range(n_gdn):
                 per_s = H * Dv * Dk
                 S = synth.normal(synth.SEED_C, f"test.decode.state.{j}", (per_s,), 0.1, start=b * per_s)
