@@ -86,30 +86,63 @@ __global__ __launch_bounds__(NT) void embed_kernel(const int32_t* ids, const uin
 }
 
 // y = bf16(rmsnorm(x [+ x2]) * g) for row blockIdx.x (or rows[blockIdx.x]).
+// With PER a multiple of 4 each thread takes groups of four contiguous
+// columns, 4 (tid + q NT) .. (16-byte loads, all issued before the sums).
 template <int PER>
 __global__ __launch_bounds__(NT) void rmsnorm_kernel(const float* x, const float* x2, const int32_t* rows,
                                                      int64_t x_stride, const uint16_t* g, uint16_t* y,
                                                      int d, float eps) {
+  constexpr bool VEC = PER % 4 == 0;
   __shared__ float red[2 * NT / 64];
   const int64_t m = rows ? rows[blockIdx.x] : blockIdx.x;
   const float* xr = x + m * x_stride;
   const float* x2r = x2 ? x2 + m * x_stride : nullptr;
+  auto col = [](int i) { return VEC ? 4 * ((int)threadIdx.x + (i / 4) * NT) + (i & 3) : (int)threadIdx.x + i * NT; };
   float v[PER];
+  if (VEC) {
+    f32x4 a[VEC ? PER / 4 : 1], b[VEC ? PER / 4 : 1];
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      const int c = col(4 * q);
+      a[q] = c < d ? *reinterpret_cast<const f32x4*>(xr + c) : (f32x4){0, 0, 0, 0};
+      b[q] = (x2r && c < d) ? *reinterpret_cast<const f32x4*>(x2r + c) : (f32x4){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = a[q][e] + b[q][e];
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = col(i);
+      v[i] = c < d ? xr[c] + (x2r ? x2r[c] : 0.f) : 0.f;
+    }
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    int c = threadIdx.x + i * NT;
-    v[i] = c < d ? xr[c] + (x2r ? x2r[c] : 0.f) : 0.f;
-    ss += v[i] * v[i];
-  }
+  for (int i = 0; i < PER; ++i) ss += v[i] * v[i];
   float dummy = 0.f;
   block_sum2(ss, dummy, red);
   const float inv = rsqrtf(ss / d + eps);
   uint16_t* yr = y + (int64_t)blockIdx.x * d;
+  if (VEC) {
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    int c = threadIdx.x + i * NT;
-    if (c < d) yr[c] = f2bf_bits(v[i] * inv * bf2f(g[c]));
+    for (int q = 0; q < PER / 4; ++q) {
+      const int c = col(4 * q);
+      if (c >= d) continue;
+      const uint2 gv = *reinterpret_cast<const uint2*>(g + c);
+      const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
+      uint16_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f2bf_bits(v[4 * q + e] * inv * bf2f(ge[e]));
+      *reinterpret_cast<uint2*>(yr + c) = *reinterpret_cast<const uint2*>(o);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = col(i);
+      if (c < d) yr[c] = f2bf_bits(v[i] * inv * bf2f(g[c]));
+    }
   }
 }
 
