@@ -762,7 +762,14 @@ hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
   // SwiGLU
   const int target = (EPI != LOOP_EPI_SWIGLU && g.K <= 4096 && g.M <= 64) ? 256 : 512;
   int splits = 1;
-  while (tiles * splits < target && g.K % (64 * splits * 2) == 0 && g.K / (splits * 2) >= 256) splits *= 2;
+  if (g.M >= 512) {
+    // many rows (the narrow column strip of a prefill projection): a split
+    // count that does not depend on M, so that a row's result does not
+    // depend on how many rows share the call (chunked prefill = whole)
+    if (g.K % 256 == 0 && g.K >= 1024) splits = 4;
+  } else {
+    while (tiles * splits < target && g.K % (64 * splits * 2) == 0 && g.K / (splits * 2) >= 256) splits *= 2;
+  }
   const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
   if (splits > 1 && g.part && need <= ws_bytes) {
     g.kslice = g.K / splits;

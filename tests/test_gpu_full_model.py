@@ -1,0 +1,138 @@
+"""The full looped stack at its real size -- 32 weight layers run 4 + 24x2 + 4
+= 56 executions (14 full attention, 42 Gated-DeltaNet), d 4096, FFN 12288,
+vocabulary 248,320, bf16 weights N(0, 0.02) drawn on the device by the seeded
+generator -- in the launch configurations the benchmark times: prefill of
+8192 tokens and decode at 32,768 tokens of context.
+
+The oracle cannot evaluate this stack within a test, so these are properties
+that hold at any size (the values themselves are pinned at real width by the
+one-group and decode tests, which share every kernel with this stack):
+- prefill: finite logits; a rerun is bit-identical (fixed reduction orders);
+  the same 8192 tokens prefilled as two calls of 4096 into another sequence
+  slot (the second call attends to the cached keys of the first and starts
+  from its Gated-DeltaNet states) give bit-identical final hidden states and
+  logits (every kernel's per-row arithmetic is independent of the number of
+  rows in the call);
+- decode at position 32,768 over pre-filled caches (K, V N(0, 1) bf16, GDN
+  states N(0, 0.1), as in the decode benchmark): a sequence's logits do not
+  depend on the batch it is decoded in (batch 4 against batch 1 on a copy of
+  one sequence's caches): bit-identical.
+"""
+import numpy as np
+import pytest
+
+import synth
+from synth.presets import weight_specs
+from gpu_util import torch_cuda, host, say, rel_err
+
+pytestmark = pytest.mark.gpu
+
+T = 8192
+CTX = 32768
+NSEQ = 5   # sequence slots: 0, 1 prefill; 0..3 and 4 (copy of 2) decode
+
+
+@pytest.fixture(scope="module")
+def full():
+    torch = torch_cuda()
+    import looped_hybrid_attention_amd as L
+    dims = synth.preset("full")
+    max_seq = CTX + 64
+    cfg = L.make_config(dims, max_batch=NSEQ, max_seq=max_seq, max_tokens=T)
+    sched = L.loop_schedule(cfg)
+    kinds_layer = {}
+    for layer, is_full, *_ in sched:
+        kinds_layer[layer] = "full" if is_full else "gdn"
+    kinds = [kinds_layer[l] for l in range(dims["n_layers"])]
+    s = torch.cuda.current_stream().cuda_stream
+    say("full model weights")
+    tensors, ptrs = {}, {}
+    for name, shape, dt, std, mean in weight_specs(dims, kinds):
+        t = torch.empty(shape, dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device="cuda")
+        L.loop_synth_normal(t.data_ptr(), t.numel(), 1 if dt == "bf16" else 0, synth.SEED_W,
+                            synth.fnv1a32(name), 0, std, mean, s)
+        tensors[name] = t
+        ptrs[name] = t.data_ptr()
+    wstruct = L.make_weights_struct(dims["n_layers"], ptrs)
+    ab, wb = L.loop_arena_bytes(cfg), L.loop_workspace_bytes(cfg, T)
+    arena = torch.zeros(ab, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(wb, dtype=torch.uint8, device="cuda")
+    handle = L.loop_model_create(cfg, wstruct, arena.data_ptr(), ab, ws.data_ptr(), wb)
+    torch.cuda.synchronize()
+    yield torch, L, dims, cfg, sched, handle, arena, s
+    L.loop_model_destroy(handle)
+
+
+def test_prefill_8192_rerun_and_chunked(full):
+    torch, L, dims, cfg, sched, handle, arena, s = full
+    V, d = dims["vocab"], dims["d_model"]
+    ids = torch.empty(T, dtype=torch.int32, device="cuda")
+    L.loop_synth_token_ids(ids.data_ptr(), T, V, synth.SEED_X, synth.fnv1a32("test.full.ids"), s)
+    logits = [torch.zeros((1, V), dtype=torch.float32, device="cuda") for _ in range(2)]
+    hid = [torch.zeros((T, d), dtype=torch.float32, device="cuda") for _ in range(2)]
+    for r in range(2):
+        say("full prefill 8192, run", r)
+        L.loop_prefill(handle, 1, T, [0], [0], d_tokens=ids.data_ptr(), d_logits=logits[r].data_ptr(),
+                       d_hidden_out=hid[r].data_ptr(), stream=s)
+    torch.cuda.synchronize()
+    lg = host(logits[0])
+    assert np.isfinite(lg).all() and np.isfinite(host(hid[0])).all()
+    assert torch.equal(logits[0], logits[1]) and torch.equal(hid[0], hid[1])
+    # the same tokens as two calls of 4096 into slot 1
+    say("full prefill 2 x 4096")
+    hc = torch.zeros((T // 2, d), dtype=torch.float32, device="cuda")
+    lc = torch.zeros((1, V), dtype=torch.float32, device="cuda")
+    L.loop_prefill(handle, 1, T // 2, [1], [0], d_tokens=ids.data_ptr(), stream=s)
+    L.loop_prefill(handle, 1, T // 2, [1], [T // 2], d_tokens=ids[T // 2:].data_ptr(), d_logits=lc.data_ptr(),
+                   d_hidden_out=hc.data_ptr(), stream=s)
+    torch.cuda.synchronize()
+    eh = rel_err(host(hc), host(hid[0])[T // 2:])
+    el = rel_err(host(lc), lg)
+    print("full prefill: chunked vs whole hidden %.2e, logits %.2e" % (eh, el))
+    assert torch.equal(hc, hid[0][T // 2:]) and torch.equal(lc, logits[0])
+
+
+def test_decode_ctx32768_batch_independent(full):
+    torch, L, dims, cfg, sched, handle, arena, s = full
+    V = dims["vocab"]
+    Hkv, D = dims["n_kv_heads"], dims["head_dim"]
+    H, Dk, Dv = dims["gdn_heads"], dims["gdn_dk"], dims["gdn_dv"]
+    n_full = sum(r[1] for r in sched)
+    n_gdn = len(sched) - n_full
+    max_seq = cfg.max_seq
+    say("full decode caches")
+    kv_n = NSEQ * Hkv * max_seq * D
+    for f in range(n_full):
+        for which in (0, 1):
+            L.loop_synth_normal(arena.data_ptr() + L.loop_cache_offset(cfg, which, f, 0), kv_n, 1, synth.SEED_C,
+                                synth.fnv1a32(f"test.full.kv{which}.{f}"), 0, 1.0, 0.0, s)
+    st_n = NSEQ * H * Dv * Dk
+    for j in range(n_gdn):
+        L.loop_synth_normal(arena.data_ptr() + L.loop_cache_offset(cfg, 2, j, 0), st_n, 0, synth.SEED_C,
+                            synth.fnv1a32(f"test.full.state.{j}"), 0, 0.1, 0.0, s)
+    # slot 4 = copy of slot 2 (every KV block and GDN state)
+    kv_b = Hkv * max_seq * D * 2
+    st_b = H * Dv * Dk * 4
+    for which, n, nb in ((0, n_full, kv_b), (1, n_full, kv_b), (2, n_gdn, st_b)):
+        for f in range(n):
+            src = L.loop_cache_offset(cfg, which, f, 2)
+            dst = L.loop_cache_offset(cfg, which, f, 4)
+            arena[dst:dst + nb].copy_(arena[src:src + nb])
+    tok = torch.empty(4, dtype=torch.int32, device="cuda")
+    L.loop_synth_token_ids(tok.data_ptr(), 4, V, synth.SEED_X, synth.fnv1a32("test.full.decode.ids"), s)
+    l4 = torch.zeros((4, V), dtype=torch.float32, device="cuda")
+    l1 = torch.zeros((1, V), dtype=torch.float32, device="cuda")
+    n4 = torch.zeros(4, dtype=torch.int32, device="cuda")
+    n1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    say("full decode batch 4")
+    L.loop_decode_step(handle, 4, [0, 1, 2, 3], [CTX] * 4, tok.data_ptr(), d_logits=l4.data_ptr(),
+                       d_next=n4.data_ptr(), stream=s)
+    say("full decode batch 1")
+    L.loop_decode_step(handle, 1, [4], [CTX], tok[2:3].data_ptr(), d_logits=l1.data_ptr(), d_next=n1.data_ptr(),
+                       stream=s)
+    torch.cuda.synchronize()
+    a, b = host(l4)[2], host(l1)[0]
+    assert np.isfinite(host(l4)).all()
+    print("full decode: batch-4 vs batch-1 logits max |diff| %.3e" % float(np.max(np.abs(a - b))))
+    assert np.array_equal(a, b)
+    assert int(host(n4)[2]) == int(host(n1)[0]) == int(np.argmax(a))
