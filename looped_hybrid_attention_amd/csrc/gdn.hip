@@ -41,6 +41,23 @@ DEV void mm_nt(f32x4& acc, const float* A, int lda, const float* B, int ldb, int
 #pragma unroll
   for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k], b[k], acc);
 }
+// The same MFMA with its result kept apart from its C operand: C stays live
+// until the result exists, so the registers cannot partially overlap (the
+// compiler otherwise may place a chain's result one register pair off its C
+// operand, which the hardware does not compute correctly).
+DEV f32x4 mfma16x16x4f32_apart(float a, float b, f32x4 c) {
+  const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  asm volatile("" ::"v"(c), "v"(d));
+  return d;
+}
+// acc += A[0:16, 0:16] . B[0:16, 0:16] with every result apart from its C
+DEV void mm_nn16_apart(f32x4& acc, const float* A, int lda, const float* B, int ldb) {
+  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
+  const float* a = A + i * lda + kk;
+  const float* b = B + kk * ldb + i;
+#pragma unroll
+  for (int k = 0; k < 16; k += 4) acc = mfma16x16x4f32_apart(a[k], b[k * ldb], acc);
+}
 // acc += A[0:16, 0:K] . B[0:K, 0:16]
 DEV void mm_nn(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
   const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
@@ -355,11 +372,11 @@ __global__ __launch_bounds__(PNT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
       if (wave < CH / 16 - d) {
         const int J = wave, I = wave + d;
         f32x4 x = {0, 0, 0, 0};
-        for (int K = J; K < I; ++K) mm_nn(x, sA + 16 * I * LC + 16 * K, LC, sT2 + 16 * K * LC + 16 * J, LC, 16);
+        for (int K = J; K < I; ++K) mm_nn16_apart(x, sA + 16 * I * LC + 16 * K, LC, sT2 + 16 * K * LC + 16 * J, LC);
 #pragma unroll
         for (int r = 0; r < 4; ++r) X[(4 * kk + r) * XS + i16] = x[r];
         f32x4 y = {0, 0, 0, 0};
-        mm_nn(y, sT2 + 16 * I * LC + 16 * I, LC, X, XS, 16);
+        mm_nn16_apart(y, sT2 + 16 * I * LC + 16 * I, LC, X, XS);
 #pragma unroll
         for (int r = 0; r < 4; ++r) sT2[(16 * I + 4 * kk + r) * LC + 16 * J + i16] = -y[r];
       }
