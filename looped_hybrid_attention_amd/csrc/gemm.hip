@@ -331,78 +331,101 @@ hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t s) {
 
 
 // ------------------------------------------------- large-M tiles, LDS copy
-// 256 x 256 output tile, K in steps of KB, four waves (one per SIMD), each
+// 256 x 256 output tiles, K in steps of KB, four waves (one per SIMD), each
 // computing 128 x 128 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with the
-// accumulators in AGPRs.  A and B tiles go global -> LDS with buffer_load
-// ... lds through an NS-stage ring: the copies of step t + NS - 1 are issued
-// at the top of step t, so NS - 1 steps of copies are in flight while a step
-// computes.  The barrier that publishes step t + 1 sits before the MFMAs of
-// step t's last 16-deep slice, so the next step's first operand reads overlap
-// them.  Operand reads run one 16-deep slice ahead of the MFMAs.  Rows are
-// unpadded (KB * 2 bytes); 16-byte chunk c of row r sits at c ^ swz(r), which
-// puts the 128-bit operand reads of 16 consecutive rows on distinct banks.
-template <int KB>
+// accumulators in AGPRs.  The grid is persistent (one workgroup per CU, tiles
+// blockIdx.x, + gridDim.x, ...) and the copy pipeline runs on across tiles:
+// A and B go global -> LDS with buffer_load ... lds through two stages, the
+// copies of step t + 1 issued at the top of step t, and the last step of a
+// tile copies the first step of the workgroup's next tile, so that copy is in
+// flight while the epilogue stores.  The barrier that publishes step t + 1
+// sits before the MFMAs of step t's last 16-deep slice, so the next step's
+// first operand reads overlap them.  Operand reads run one 16-deep slice
+// ahead of the MFMAs.  Rows are unpadded (KB * 2 bytes); 16-byte chunk c of
+// row r sits at c ^ swz(r), which puts the 128-bit operand reads of 16
+// consecutive rows on distinct banks.
+//
+// The MFMA takes the B rows (output columns) as its first operand, so lane
+// (lr, h) of a 32 x 32 tile holds output row lr and, for each q = 0..3, the
+// four consecutive columns 8 q + 4 h .. + 3: the epilogue stores (and, for
+// the residual, loads) 8 or 16 bytes per lane.
+template <int KB, int NW>
 struct DbShape {
   static constexpr int ROW = KB * 2;               // bytes of one operand row
   static constexpr int CPR = ROW / 16;             // 16-byte chunks per row
   static constexpr int RPI = 1024 / ROW;           // rows per 1 KB copy instruction
-  static constexpr int CPW = 256 / RPI / 4;        // copy instructions per wave per operand
+  static constexpr int CPW = 256 / RPI / NW;       // copy instructions per wave per operand
   static constexpr int TILE = 256 * ROW;           // bytes of one operand tile
   static constexpr int STAGE = 2 * TILE;           // A then B
   static DEV int swz(int row) { return (row / (16 / CPR)) % CPR; }
 };
 constexpr int DB_BM = 256, DB_BN = 256;
-constexpr int db_lds(int kb, int ns) { return ns * 2 * 256 * kb * 2; }
+constexpr int db_lds(int kb) { return 2 * 2 * 256 * kb * 2; }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-template <int EPI, int KB, int NS>
-__global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes) {
-  using S = DbShape<KB>;
-  static_assert(NS >= 2 && KB % 32 == 0 && S::CPW * 2 * (NS - 2) < 64, "ring shape");
-  constexpr int TM = 4, TN = 4, KS = KB / 16;
-  extern __shared__ __align__(16) uint8_t db_smem[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = (g.M + DB_BM - 1) / DB_BM;
-  const int m0 = (blockIdx.x % tiles_m) * DB_BM;
-  const int tn = blockIdx.x / tiles_m;
+// four fp32 -> four bf16 (round to nearest even) as 8 bytes
+DEV u32x2 pack_bf16x4(float a, float b, float c, float d) {
+  const bf16x2 lo = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2){c, d}, bf16x2);
+  return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+}
+
+template <int EPI, int KB, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes, int n_tiles) {
+  using S = DbShape<KB, NW>;
+  static_assert(KB % 32 == 0 && (NW == 4 || NW == 8), "ring shape");
+  // waves: 2 along M (128 rows each) x NW / 2 along N (256 / (NW / 2) B rows)
+  constexpr int WN = NW / 2, TM = 4, TN = 8 / WN, KS = KB / 16;
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? DB_BN / 2 : DB_BN;
-  const int n0 = tn * OUT_BN;
+  extern __shared__ __align__(16) uint8_t db_smem[];
+  // the wave index is uniform: kept in an SGPR, LDS copy targets are scalar
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_m = (g.M + DB_BM - 1) / DB_BM;
 
-  // Byte offsets (k = 0) of this lane's 16-byte piece in each of the wave's
+  // Only whole tiles (M and N multiples of 256 and OUT_BN, ldc a multiple
+  // of 4, C and R 16-byte aligned): the launcher sends ragged edges to the
+  // small tiles.  A tile's origin is then a scalar byte offset and the
+  // per-lane offsets below do not depend on the tile.
+  //
+  // Per-lane byte offsets of this lane's 16-byte piece in each of the wave's
   // copy instructions per operand tile: instruction n fills rows RPI n ..
   // RPI n + RPI - 1, lane l row RPI n + l / CPR at chunk l % CPR (holding
-  // logical chunk (l % CPR) ^ swz).  Rows past M (N) are clamped: they feed
-  // outputs that are never stored.
+  // logical chunk (l % CPR) ^ swz).  SwiGLU tiles alternate 32 gate rows and
+  // the 32 matching up rows (F rows further on).
   int a_off[S::CPW], b_off[S::CPW];
 #pragma unroll
   for (int i = 0; i < S::CPW; ++i) {
     const int row = (wave * S::CPW + i) * S::RPI + lane / S::CPR;
     const int c = (lane % S::CPR) ^ S::swz(row);
-    a_off[i] = (min(m0 + row, g.M - 1) * (int)g.lda + c * 8) * 2;
-    int gn;
+    a_off[i] = (row * (int)g.lda + c * 8) * 2;
+    int gn = row;
     if (EPI == LOOP_EPI_SWIGLU) {
-      const int blk = row / 32, part = blk & 1, col = min(n0 + (blk >> 1) * 32 + (row & 31), g.N - 1);
-      gn = part * g.swiglu_F + col;
-    } else {
-      gn = min(n0 + row, g.N - 1);
+      const int blk = row / 32;
+      gn = (blk & 1) * g.swiglu_F + (blk >> 1) * 32 + (row & 31);
     }
     b_off[i] = (gn * (int)g.ldb + c * 8) * 2;
   }
+  auto tile_m0 = [&](int tile) { return (tile % tiles_m) * DB_BM; };
+  auto tile_n0 = [&](int tile) { return (tile / tiles_m) * OUT_BN; };
+  auto a_base = [&](int tile) { return tile_m0(tile) * (int)g.lda * 2; };
+  auto b_base = [&](int tile) { return tile_n0(tile) * (int)g.ldb * 2; };
   const auto a_rsrc = buffer_rsrc(g.A, a_bytes);
   const auto b_rsrc = buffer_rsrc(g.B, b_bytes);
-#define DB_COPY(k0_, stage_)                                                                       \
+#define DB_COPY(sa_, sb_, stage_)                                                                  \
   {                                                                                                \
     uint8_t* S_ = db_smem + (stage_) * S::STAGE;                                                   \
     _Pragma("unroll") for (int i = 0; i < S::CPW; ++i)                                             \
-        copy16_to_lds(a_rsrc, a_off[i], (k0_) * 2, (lds_void*)(S_ + (wave * S::CPW + i) * 1024));  \
+        copy16_to_lds(a_rsrc, a_off[i], (sa_), (lds_void*)(S_ + (wave * S::CPW + i) * 1024));      \
     _Pragma("unroll") for (int i = 0; i < S::CPW; ++i)                                             \
-        copy16_to_lds(b_rsrc, b_off[i], (k0_) * 2,                                                 \
-                      (lds_void*)(S_ + S::TILE + (wave * S::CPW + i) * 1024));                     \
+        copy16_to_lds(b_rsrc, b_off[i], (sb_), (lds_void*)(S_ + S::TILE + (wave * S::CPW + i) * 1024)); \
   }
   // operand reads: lane (lr, half) row lr of each 32-row tile, chunk 2 ks + half
   const int lr = lane & 31, half = lane >> 5, sw = S::swz(lr);
-  const int a_row = (wm * 128 + lr) * S::ROW, b_row = S::TILE + (wn * 128 + lr) * S::ROW;
+  const int a_row = (wm * 128 + lr) * S::ROW, b_row = S::TILE + (wn * 32 * TN + lr) * S::ROW;
   bf16x8 fa[2][TM], fb[2][TN];
 #define DB_READ(stage_, ks_, buf_)                                                                 \
   {                                                                                                \
@@ -415,144 +438,124 @@ __global__ __launch_bounds__(256, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_
 #define DB_MFMA(buf_)                                                                              \
   _Pragma("unroll") for (int i = 0; i < TM; ++i)                                                   \
       _Pragma("unroll") for (int j = 0; j < TN; ++j)                                               \
-          acc[i][j] = mfma32x32x16(fa[buf_][i], fb[buf_][j], acc[i][j]);
-// interleave: the 8 reads of the next slice spread over the 16 MFMAs
+          acc[i][j] = mfma32x32x16(fb[buf_][j], fa[buf_][i], acc[i][j]);
+// interleave: the TM + TN reads of the next slice spread over its TM x TN MFMAs
+  constexpr int MPR = TM * TN / (TM + TN);
 #define DB_SCHED()                                                                                 \
   _Pragma("unroll") for (int q = 0; q < TM + TN; ++q) {                                            \
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                             \
+    __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);                                           \
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
-  }
+  }                                                                                                \
+  if (TM * TN > MPR * (TM + TN)) __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - MPR * (TM + TN), 0);
 
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
-
-  // Copies complete in issue order, so "at most CPW*2*(NS-2) outstanding"
-  // means every stage but the NS-2 newest has landed.  Steps past the end
-  // re-copy the last step into an idle stage, harmlessly: nothing reads it.
-  constexpr int IN_FLIGHT = S::CPW * 2 * (NS - 2);
   const int nk = g.K / KB;
-#pragma unroll
-  for (int p = 0; p < NS - 1; ++p) DB_COPY(min(p, nk - 1) * KB, p);
-  wait_vmcnt<IN_FLIGHT>();
+  int tile = blockIdx.x;
+  DB_COPY(a_base(tile), b_base(tile), 0);
+  wait_vmcnt<0>();
   lds_barrier();
-  DB_READ(0, 0, 0);
-  int s = 0, s_fill = NS - 1;
-  for (int t = 0; t < nk; ++t) {
-    // the stage refilled here was last read before the previous barrier
-    DB_READ(s, 1, 1);
-    DB_COPY(min(t + NS - 1, nk - 1) * KB, s_fill);
-    DB_MFMA(0);
-    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
-    _Pragma("unroll") for (int q = 0; q < TM * TN; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2 * S::CPW / (TM * TN), 0);
-    }
+  int s = 0;
+  for (; tile < n_tiles; tile += gridDim.x) {
+    const int m0 = tile_m0(tile), n0 = tile_n0(tile);
+    const int ab = a_base(tile), bb = b_base(tile);
+    // the last step copies the next tile's first (the last tile its own
+    // first again, into a stage nothing reads)
+    const int nxt = tile + (int)gridDim.x < n_tiles ? tile + (int)gridDim.x : tile;
+    const int ab_next = a_base(nxt), bb_next = b_base(nxt);
+    f32x16 acc[TM][TN];
 #pragma unroll
-    for (int ks = 2; ks < KS; ++ks) {
-      DB_READ(s, ks, ks & 1);
-      DB_MFMA((ks - 1) & 1);
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
+    // The MFMAs of a step's last slice run after the barrier that ends the
+    // step, under the next step's first operand reads; at a tile's first
+    // step they multiply zero operands.
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[1][i] = (bf16x8){};
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[1][j] = (bf16x8){};
+    // One K step on stage s, copying the next step into the other stage.
+    // Copies complete in issue order; the wait before the barrier leaves
+    // nothing outstanding, so past it the other stage has landed for every
+    // wave and every wave is done reading stage s.
+    for (int t = 0; t < nk; ++t) {
+      int left = nk - 1 - t;
+      asm volatile("" : "+s"(left));  // keeps the loop whole (no peeled last step)
+      const int sa = left == 0 ? ab_next : ab + (t + 1) * KB * 2;
+      const int sb = left == 0 ? bb_next : bb + (t + 1) * KB * 2;
+      DB_READ(s, 0, 0);
+      DB_MFMA((KS - 1) & 1);
       DB_SCHED();
+      DB_READ(s, 1, 1);
+      DB_COPY(sa, sb, s ^ 1);
+      DB_MFMA(0);
+      __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);
+#pragma unroll
+      for (int q = 0; q < TM * TN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * S::CPW / (TM * TN), 0);
+      }
+#pragma unroll
+      for (int ks = 2; ks < KS; ++ks) {
+        DB_READ(s, ks, ks & 1);
+        DB_MFMA((ks - 1) & 1);
+        DB_SCHED();
+      }
+      wait_vmcnt<0>();
+      lds_barrier();
+      s ^= 1;
     }
-    // step t + 1 has landed and every wave is done reading step t - 1 past
-    // this barrier
-    wait_vmcnt<IN_FLIGHT>();
-    lds_barrier();
-    s = (s + 1 == NS) ? 0 : s + 1;
-    s_fill = (s_fill + 1 == NS) ? 0 : s_fill + 1;
-    DB_READ(s, 0, 0);
     DB_MFMA((KS - 1) & 1);
-    DB_SCHED();
+
+    // Epilogue: lane (lr, half) holds row r0 + 32 i and, for r = 4 q + e,
+    // column c0 + 32 j + 8 q + e of the wave's 128 x 128 block.  One row
+    // block at a time (sched_barrier), so that only its values are live.
+    const int r0 = m0 + wm * 128 + lr;
+    const int c0 = n0 + wn * (OUT_BN / WN) + 4 * half;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int64_t o0 = (int64_t)(r0 + i * 32) * g.ldc + c0;
+      if (EPI == LOOP_EPI_SWIGLU) {
+        uint16_t* Cr = reinterpret_cast<uint16_t*>(g.C) + o0;
+#pragma unroll
+        for (int j = 0; j < TN; j += 2)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = siluf_(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e];
+            *reinterpret_cast<u32x2*>(Cr + (j / 2) * 32 + 8 * q) = pack_bf16x4(o[0], o[1], o[2], o[3]);
+          }
+      } else {
+        f32x4 rv[TN][4];
+        if (EPI == LOOP_EPI_F32_RES) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rv[j][q] = *reinterpret_cast<const f32x4*>(g.R + o0 + j * 32 + 8 * q);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t o = o0 + j * 32 + 8 * q;
+            f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            if (EPI == LOOP_EPI_BF16) {
+              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(g.C) + o) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+            } else {
+              if (EPI == LOOP_EPI_F32_RES) v += rv[j][q];
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + o) = v;
+            }
+          }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
+  // nothing may still be writing LDS when the workgroup ends
   wait_vmem();
 #undef DB_COPY
 #undef DB_READ
 #undef DB_MFMA
 #undef DB_SCHED
-
-  // Epilogue.  Lane holds column lr of each 32x32 tile and rows
-  // 8*(r/4) + 4*(lane/32) + r%4.  Tiles wholly inside the output take a
-  // branch-free path whose loads (residual) are issued a row block at a time.
-  const int row_base = m0 + wm * 128 + 4 * half;
-  const bool full = m0 + DB_BM <= g.M && n0 + OUT_BN <= g.N;
-  if (EPI == LOOP_EPI_SWIGLU) {
-    uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
-    if (full) {
-#pragma unroll
-      for (int j = 0; j < TN; j += 2) {
-        const int col = n0 + wn * 64 + (j / 2) * 32 + lr;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          uint16_t o[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[r] = f2bf_bits(siluf_(acc[i][j][r]) * acc[i][j + 1][r]);
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            C[(int64_t)(row_base + i * 32 + 8 * (r >> 2) + (r & 3)) * g.ldc + col] = o[r];
-        }
-      }
-      return;
-    }
-#pragma unroll
-    for (int j = 0; j < TN; j += 2) {
-      const int col = n0 + wn * 64 + (j / 2) * 32 + lr;
-      if (col >= g.N) continue;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-          if (row < g.M) C[(int64_t)row * g.ldc + col] = f2bf_bits(siluf_(acc[i][j][r]) * acc[i][j + 1][r]);
-        }
-    }
-    return;
-  }
-  if (full) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      float rv[TN][16];
-      if (EPI == LOOP_EPI_F32_RES) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-            rv[j][r] = g.R[(int64_t)row * g.ldc + n0 + wn * 128 + j * 32 + lr];
-          }
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-          const int64_t o = (int64_t)row * g.ldc + n0 + wn * 128 + j * 32 + lr;
-          const float v = acc[i][j][r];
-          if (EPI == LOOP_EPI_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = f2bf_bits(v);
-          else if (EPI == LOOP_EPI_F32) reinterpret_cast<float*>(g.C)[o] = v;
-          else reinterpret_cast<float*>(g.C)[o] = rv[j][r] + v;
-        }
-    }
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int col = n0 + wn * 128 + j * 32 + lr;
-    if (col >= g.N) continue;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row >= g.M) continue;
-        const int64_t o = (int64_t)row * g.ldc + col;
-        const float v = acc[i][j][r];
-        if (EPI == LOOP_EPI_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = f2bf_bits(v);
-        else if (EPI == LOOP_EPI_F32) reinterpret_cast<float*>(g.C)[o] = v;
-        else reinterpret_cast<float*>(g.C)[o] = g.R[o] + v;
-      }
-  }
 }
 
 // ------------------------------------------------------- decode (M <= 64)
@@ -731,22 +734,26 @@ hipError_t launch_skinny(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t
   return launch_skinny_w<EPI, SK_WAVES>(g, ws_bytes, a_bytes, b_bytes, s);
 }
 
-// Ring shape: two stages of K = 64 (128 KB of LDS).  Deeper rings of K = 32
-// steps (up to 5 stages, the whole 160 KB) measured slower on every shape.
-constexpr int DB_KB = 64, DB_NS = 2;
+// Two stages of K = 64 (128 KB of LDS).  Deeper rings of K = 32 steps (up to
+// 5 stages, the whole 160 KB) measured slower on every shape.
+constexpr int DB_KB = 64, DB_NW = 4;
 template <int EPI>
 hipError_t launch_db(const GemmArgs& g, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? DB_BN / 2 : DB_BN;
-  constexpr int lds = db_lds(DB_KB, DB_NS);
+  constexpr int lds = db_lds(DB_KB);
   const int tiles = ((g.M + DB_BM - 1) / DB_BM) * ((g.N + OUT_BN - 1) / OUT_BN);
-  auto k = gemm_db_kernel<EPI, DB_KB, DB_NS>;
-  static bool attr_set = false;
-  if (!attr_set) {
+  auto k = gemm_db_kernel<EPI, DB_KB, DB_NW>;
+  static int n_cu = 0;
+  if (!n_cu) {
     hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k, dim3(tiles), dim3(256), lds, s, g, a_bytes, b_bytes);
+  // one workgroup per CU (the LDS ring admits no second one)
+  hipLaunchKernelGGL(k, dim3(std::min(tiles, n_cu)), dim3(64 * DB_NW), lds, s, g, a_bytes, b_bytes, tiles);
   return hipGetLastError();
 }
 
@@ -781,31 +788,46 @@ hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
 // Large M: 256 x 256 tiles; small M (decode): 64 x 128 tiles, split K.
 template <int EPI>
 hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
-  // Large M: 256 x 256 tiles fed by LDS copies; operands whose byte range
-  // does not fit the 32-bit buffer offsets use the register-staged kernel
-  // (eight waves, two per SIMD).
+  // Large M: whole 256 x 256 tiles fed by LDS copies on the persistent
+  // kernel; the ragged edges (fewer than 256 rows, or fewer than one tile
+  // of columns) on 64 x 128 tiles, split K (e.g. 8224 columns: 1024 whole
+  // tiles, and the last 32 columns in a fraction of another round of big
+  // tiles).  Operands whose byte range does not fit the 32-bit buffer
+  // offsets, or unaligned outputs, use the register-staged kernel (eight
+  // waves, two per SIMD).
   if (g.M >= 512) {
-    const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
+    constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? DB_BN / 2 : DB_BN;
+    const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? (int64_t)g.swiglu_F + g.N : g.N;
     const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
-    if (g.K % DB_KB == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31)) {
-      // A strip of at most 128 columns past the last whole 256-column tile
-      // would cost a full extra round of 256 x 256 tiles (e.g. 8224 columns:
-      // 1024 whole tiles, then 32 more on an otherwise idle chip); 64 x 128
-      // tiles with split K cover it in a fraction of that.
-      const int rem = g.N % DB_BN;
-      if (EPI != LOOP_EPI_SWIGLU && rem != 0 && rem <= 128 && g.N > DB_BN) {
-        const int nm = g.N - rem;
-        GemmArgs main = g, tail = g;
-        main.N = main.swiglu_F = nm;
-        hipError_t e = launch_db<EPI>(main, (uint32_t)a_bytes, (uint32_t)((int64_t)nm * g.ldb * 2), s);
-        if (e != hipSuccess) return e;
+    const int mm = g.M / DB_BM * DB_BM, nm = g.N / OUT_BN * OUT_BN;
+    const bool aligned = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(g.R) & 15) == 0 && (g.lda & 7) == 0 && (g.ldb & 7) == 0;
+    if (g.K % DB_KB == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31) && aligned && nm > 0) {
+      const size_t esz = (EPI == LOOP_EPI_BF16 || EPI == LOOP_EPI_SWIGLU) ? 2 : 4;
+      GemmArgs main = g;
+      main.M = mm;
+      main.N = nm;
+      hipError_t e = launch_db<EPI>(main, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+      if (e != hipSuccess) return e;
+      if (nm < g.N) {  // all rows, columns nm .. N - 1 (SwiGLU: up rows stay swiglu_F further on)
+        GemmArgs tail = g;
         tail.B = g.B + (int64_t)nm * g.ldb;
-        tail.C = (uint8_t*)g.C + (int64_t)nm * (EPI == LOOP_EPI_BF16 ? 2 : 4);
+        tail.C = (uint8_t*)g.C + (int64_t)nm * esz;
         tail.R = g.R ? g.R + nm : nullptr;
-        tail.N = tail.swiglu_F = rem;
-        return launch_small<EPI>(tail, ws_bytes, s);
+        tail.N = g.N - nm;
+        e = launch_small<EPI>(tail, ws_bytes, s);
+        if (e != hipSuccess) return e;
       }
-      return launch_db<EPI>(g, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+      if (mm < g.M) {  // rows mm .. M - 1, columns 0 .. nm - 1
+        GemmArgs tail = g;
+        tail.A = g.A + (int64_t)mm * g.lda;
+        tail.C = (uint8_t*)g.C + (int64_t)mm * g.ldc * esz;
+        tail.R = g.R ? g.R + (int64_t)mm * g.ldc : nullptr;
+        tail.M = g.M - mm;
+        tail.N = nm;
+        e = launch_small<EPI>(tail, ws_bytes, s);
+      }
+      return e;
     }
     return launch_cfg<256, 256, 2, 4, EPI, false>(g, 1, s);
   }
