@@ -45,3 +45,17 @@ class GpuModel:
 
     def stream(self):
         return self.torch.cuda.current_stream().cuda_stream
+
+
+def device_full_weights(torch, L, dims, kinds, stream):
+    """The full model's weights drawn on the device by the seeded generator
+    (same stream names and recipe as the host draw): (tensors, weights struct)."""
+    from synth.presets import weight_specs
+    tensors, ptrs = {}, {}
+    for name, shape, dt, std, mean in weight_specs(dims, kinds):
+        t = torch.empty(shape, dtype=torch.bfloat16 if dt == "bf16" else torch.float32, device="cuda")
+        L.loop_synth_normal(t.data_ptr(), t.numel(), 1 if dt == "bf16" else 0, synth.SEED_W,
+                            synth.fnv1a32(name), 0, std, mean, stream)
+        tensors[name] = t
+        ptrs[name] = t.data_ptr()
+    return tensors, L.make_weights_struct(dims["n_layers"], ptrs)
