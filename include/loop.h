@@ -165,8 +165,17 @@ void loop_model_destroy(loop_model* m);
  *   n_taps / tap_exec (host) / d_taps device fp32 [n_taps, batch, d_model]:
  *              hidden state after the listed executions at the last position
  *              (mean of the streams inside the loop), or 0 / NULL.
+ *   loop_passes number of times the shared block runs in this call: 0 = the
+ *              configuration's loop_passes, else 1 .. loop_passes.  A p-pass
+ *              call runs the head layers, the block's first p passes (each
+ *              execution on the cache slot it has in the full schedule) and
+ *              the tail ([P1 section 2]: the pass count is a property of the
+ *              forward pass, fixed per sequence); tap_exec then indexes the
+ *              p-pass execution list.  A sequence keeps the count of the call
+ *              that prefilled it from position 0: later calls on its slot
+ *              with another count are rejected (LOOP_EINVAL).
  * Requires batch*seq_len <= max_tokens, start_pos+seq_len <= max_seq,
- * slot < max_batch. */
+ * slot < max_batch.  Zero-initialise the struct: fields may be appended. */
 typedef struct loop_prefill_args {
   int32_t batch, seq_len;
   const int32_t* slots;
@@ -178,6 +187,7 @@ typedef struct loop_prefill_args {
   int32_t n_taps;
   const int32_t* tap_exec;
   float* d_taps;
+  int32_t loop_passes;
 } loop_prefill_args;
 int loop_prefill(loop_model* m, const loop_prefill_args* a, void* stream);
 
@@ -187,7 +197,9 @@ int loop_prefill(loop_model* m, const loop_prefill_args* a, void* stream);
  *   d_tokens    device int32 [batch]
  *   d_logits    device fp32 [batch, vocab] or NULL
  *   d_next      device int32 [batch] or NULL
- *   d_hidden_out device fp32 [batch, d_model] (h before the final norm) or NULL */
+ *   d_hidden_out device fp32 [batch, d_model] (h before the final norm) or NULL
+ *   loop_passes 0 = the configuration's, else 1 .. loop_passes; must equal
+ *               the count each sequence was prefilled with (LOOP_EINVAL). */
 typedef struct loop_decode_args {
   int32_t batch;
   const int32_t* slots;
@@ -196,6 +208,7 @@ typedef struct loop_decode_args {
   float* d_logits;
   int32_t* d_next;
   float* d_hidden_out;
+  int32_t loop_passes;
 } loop_decode_args;
 int loop_decode_step(loop_model* m, const loop_decode_args* a, void* stream);
 

@@ -51,12 +51,13 @@ class loop_prefill_args(ctypes.Structure):
     _fields_ = [("batch", _i32), ("seq_len", _i32), ("slots", ctypes.POINTER(_i32)),
                 ("start_pos", ctypes.POINTER(_i32)), ("d_tokens", _vp), ("d_hidden_in", _vp),
                 ("d_logits", _vp), ("d_hidden_out", _vp), ("n_taps", _i32),
-                ("tap_exec", ctypes.POINTER(_i32)), ("d_taps", _vp)]
+                ("tap_exec", ctypes.POINTER(_i32)), ("d_taps", _vp), ("loop_passes", _i32)]
 
 
 class loop_decode_args(ctypes.Structure):
     _fields_ = [("batch", _i32), ("slots", ctypes.POINTER(_i32)), ("pos", ctypes.POINTER(_i32)),
-                ("d_tokens", _vp), ("d_logits", _vp), ("d_next", _vp), ("d_hidden_out", _vp)]
+                ("d_tokens", _vp), ("d_logits", _vp), ("d_next", _vp), ("d_hidden_out", _vp),
+                ("loop_passes", _i32)]
 
 
 def _load():
@@ -217,8 +218,9 @@ def _i32arr(xs):
 
 def loop_prefill(model: int, batch: int, seq_len: int, slots, start_pos, d_tokens: int = 0,
                  d_hidden_in: int = 0, d_logits: int = 0, d_hidden_out: int = 0, tap_exec=(),
-                 d_taps: int = 0, stream: int = 0) -> None:
+                 d_taps: int = 0, stream: int = 0, loop_passes: int = 0) -> None:
     a = loop_prefill_args()
+    a.loop_passes = loop_passes
     a.batch, a.seq_len = batch, seq_len
     sl, sp, te = _i32arr(slots), _i32arr(start_pos), _i32arr(tap_exec)
     a.slots, a.start_pos = sl, sp
@@ -231,8 +233,9 @@ def loop_prefill(model: int, batch: int, seq_len: int, slots, start_pos, d_token
 
 
 def loop_decode_step(model: int, batch: int, slots, pos, d_tokens: int, d_logits: int = 0,
-                     d_next: int = 0, d_hidden_out: int = 0, stream: int = 0) -> None:
+                     d_next: int = 0, d_hidden_out: int = 0, stream: int = 0, loop_passes: int = 0) -> None:
     a = loop_decode_args()
+    a.loop_passes = loop_passes
     a.batch = batch
     sl, ps = _i32arr(slots), _i32arr(pos)
     a.slots, a.pos = sl, ps

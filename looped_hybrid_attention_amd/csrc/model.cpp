@@ -108,6 +108,12 @@ struct loop_model {
   size_t ws_bytes;
   Layout L;
   std::vector<ExecDesc> sched;
+  // sched_p[p - 1]: the executions of a call that runs the block p times
+  // (p = 1 .. loop_passes); each keeps its slot of the full schedule
+  std::vector<std::vector<ExecDesc>> sched_p;
+  // pass count each sequence slot was started with (0: not started by a
+  // prefill from position 0 here)
+  std::vector<int32_t> slot_passes;
   std::vector<int32_t> meta_host;
   // kernel-class timing
   int prof_class = -1;
@@ -176,6 +182,21 @@ extern "C" int loop_model_create(const loop_config* cfg, const loop_weights* w, 
   m->ws_bytes = ws_bytes;
   m->L = L;
   m->sched = sched;
+  // Executions of a p-pass call: the head, the block's first p passes, the
+  // tail, in schedule order, with the merge moved to the end of pass p.
+  const int blk = cfg->loop_end - cfg->loop_start;
+  for (int p = 1; p <= cfg->loop_passes; ++p) {
+    std::vector<ExecDesc> sp;
+    for (int e = 0; e < (int)sched.size(); ++e) {
+      const bool in_block = e >= cfg->loop_start && e < cfg->loop_start + blk * cfg->loop_passes;
+      if (in_block && (e - cfg->loop_start) / blk >= p) continue;
+      ExecDesc d = sched[e];
+      if (blk > 0 && in_block) d.merge = e == cfg->loop_start + blk * p - 1;
+      sp.push_back(d);
+    }
+    m->sched_p.push_back(sp);
+  }
+  m->slot_passes.assign(cfg->max_batch, 0);
   *out = m;
   return 0;
 }
@@ -245,6 +266,7 @@ struct Call {
   const int32_t* d_pos;
   const int32_t* d_slot;
   const int32_t* d_last;
+  const std::vector<ExecDesc>* sched;  // this call's executions
 };
 
 #define HIP_TRY(x)                                              \
@@ -259,7 +281,8 @@ T* at(loop_model* m, size_t off) { return reinterpret_cast<T*>(m->ws + off); }
 int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   const loop_config& c = m->cfg;
   const Layout& L = m->L;
-  const ExecDesc& d = m->sched[e];
+  const std::vector<ExecDesc>& sched = *k.sched;
+  const ExecDesc& d = sched[e];
   const loop_layer_weights& w = m->lw[d.layer];
   const int M = k.M, dm = c.d_model;
   uint16_t* xn = at<uint16_t>(m, L.xn);
@@ -377,7 +400,7 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   } else {
     t.in_mode = TR_IN_H;
   }
-  const bool last = e + 1 == (int)m->sched.size();
+  const bool last = e + 1 == (int)sched.size();
   if (last) {
     if (d.loop) {
       t.out_mode = TR_OUT_NONE;
@@ -385,7 +408,7 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
     }
     return 0;
   }
-  const ExecDesc& nd = m->sched[e + 1];
+  const ExecDesc& nd = sched[e + 1];
   const loop_layer_weights& nw = m->lw[nd.layer];
   t.norm_g = (const uint16_t*)nw.attn_norm;
   if (nd.loop && !nd.fork) {  // stay inside the loop
@@ -409,7 +432,7 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
 int run_entry(loop_model* m, const Call& k, hipStream_t s) {
   const loop_config& c = m->cfg;
   const Layout& L = m->L;
-  const ExecDesc& d = m->sched[0];
+  const ExecDesc& d = (*k.sched)[0];
   const loop_layer_weights& w = m->lw[d.layer];
   float* h = at<float>(m, L.h);
   if (!d.loop) {
@@ -439,11 +462,11 @@ int run_forward(loop_model* m, const Call& k, const int32_t* taps, int n_taps, f
     HIP_TRY(launch_sinkhorn_layers(sb, s));
   }
   if (int r = run_entry(m, k, s)) return r;
-  for (int e = 0; e < (int)m->sched.size(); ++e) {
+  for (int e = 0; e < (int)k.sched->size(); ++e) {
     if (int r = run_exec(m, k, e, s)) return r;
     for (int i = 0; i < n_taps; ++i) {
       if (taps[i] != e) continue;
-      const ExecDesc& d = m->sched[e];
+      const ExecDesc& d = (*k.sched)[e];
       const bool streams = d.loop && !d.merge;
       HIP_TRY(launch_tap(at<float>(m, L.h), streams ? at<float>(m, L.s0) : nullptr,
                          streams ? at<float>(m, L.s1) : nullptr, d_taps + (int64_t)i * k.B * c.d_model,
@@ -473,6 +496,22 @@ int head_logits(loop_model* m, const Call& k, float* logits, hipStream_t s) {
   HIP_TRY(launch_rmsnorm(at<float>(m, L.h), nullptr, k.d_last, c.d_model, m->final_norm, xf, k.B, c.d_model, c.eps, s));
   HIP_TRY(launch_gemm(xf, c.d_model, m->head, c.d_model, logits, c.vocab, nullptr, k.B, c.vocab, c.d_model,
                       LOOP_EPI_F32, s, at<float>(m, L.splitk), L.splitk_bytes));
+  return 0;
+}
+
+// The call's block pass count (0 = the configuration's), checked against the
+// count each sequence was started with.
+int call_passes(loop_model* m, int32_t req, int B, const int32_t* slots, const int32_t* start, int* out) {
+  const int p = req == 0 ? m->cfg.loop_passes : req;
+  if (p < 1 || p > m->cfg.loop_passes)
+    return loop_fail(LOOP_EINVAL, "loop_passes %d out of [1, %d]", req, m->cfg.loop_passes);
+  for (int b = 0; b < B; ++b) {
+    const int rec = m->slot_passes[slots[b]];
+    const bool fresh = start && start[b] == 0;
+    if (!fresh && rec != 0 && rec != p)
+      return loop_fail(LOOP_EINVAL, "slot %d was started with %d loop passes, this call asks for %d", slots[b], rec, p);
+  }
+  *out = p;
   return 0;
 }
 
@@ -506,10 +545,13 @@ extern "C" int loop_prefill(loop_model* m, const loop_prefill_args* a, void* str
   if (a->d_tokens && c.vocab == 0) return loop_fail(LOOP_EINVAL, "token input needs vocab > 0");
   if (a->d_logits && c.vocab == 0) return loop_fail(LOOP_EINVAL, "logits need vocab > 0");
   if (a->n_taps < 0 || (a->n_taps > 0 && (!a->tap_exec || !a->d_taps))) return loop_fail(LOOP_EINVAL, "bad taps");
+  int passes = 0;
+  if (int r = call_passes(m, a->loop_passes, B, a->slots, a->start_pos, &passes)) return r;
+  const std::vector<ExecDesc>& sched = m->sched_p[passes - 1];
   for (int i = 0; i < a->n_taps; ++i)
-    if (a->tap_exec[i] < 0 || a->tap_exec[i] >= (int)m->sched.size()) return loop_fail(LOOP_EINVAL, "tap %d out of range", a->tap_exec[i]);
+    if (a->tap_exec[i] < 0 || a->tap_exec[i] >= (int)sched.size()) return loop_fail(LOOP_EINVAL, "tap %d out of range", a->tap_exec[i]);
   hipStream_t s = (hipStream_t)stream;
-  Call k{B, T, B * T, false, nullptr, nullptr, nullptr};
+  Call k{B, T, B * T, false, nullptr, nullptr, nullptr, &sched};
   const int32_t* meta = at<int32_t>(m, m->L.meta);
   k.d_pos = meta;
   k.d_slot = meta + c.max_batch;
@@ -519,6 +561,8 @@ extern "C" int loop_prefill(loop_model* m, const loop_prefill_args* a, void* str
   if (a->d_tokens) HIP_TRY(launch_embed(a->d_tokens, m->embed, h, k.M, c.d_model, c.vocab, s));
   else HIP_TRY(hipMemcpyAsync(h, a->d_hidden_in, (size_t)k.M * c.d_model * 4, hipMemcpyDeviceToDevice, s));
   if (int r = run_forward(m, k, a->tap_exec, a->n_taps, a->d_taps, s)) return r;
+  for (int b = 0; b < B; ++b)
+    if (a->start_pos[b] == 0) m->slot_passes[a->slots[b]] = passes;
   if (a->d_hidden_out)
     HIP_TRY(hipMemcpyAsync(a->d_hidden_out, h, (size_t)k.M * c.d_model * 4, hipMemcpyDeviceToDevice, s));
   if (a->d_logits)
@@ -536,8 +580,10 @@ extern "C" int loop_decode_step(loop_model* m, const loop_decode_args* a, void* 
   if (int r = check_slots(c, B, a->slots)) return r;
   for (int b = 0; b < B; ++b)
     if (a->pos[b] < 0 || a->pos[b] >= c.max_seq) return loop_fail(LOOP_ECAPACITY, "pos %d out of [0, %d)", a->pos[b], c.max_seq);
+  int passes = 0;
+  if (int r = call_passes(m, a->loop_passes, B, a->slots, nullptr, &passes)) return r;
   hipStream_t s = (hipStream_t)stream;
-  Call k{B, 1, B, true, nullptr, nullptr, nullptr};
+  Call k{B, 1, B, true, nullptr, nullptr, nullptr, &m->sched_p[passes - 1]};
   const int32_t* meta = at<int32_t>(m, m->L.meta);
   k.d_pos = meta;
   k.d_slot = meta + c.max_batch;
