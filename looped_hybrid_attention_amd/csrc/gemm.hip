@@ -373,6 +373,53 @@ DEV u32x2 pack_bf16x4(float a, float b, float c, float d) {
   return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
+// Epilogue of a wave's 128 x (32 TN) block: lane (lr, half) holds row r0 + 32 i
+// and, for r = 4 q + e, column c0 + 32 j + 8 q + e (c0 includes 4 half);
+// SwiGLU pairs tiles j (gate) and j + 1 (up) into output columns c0 + 32 (j /
+// 2) + 8 q + e.  One row block at a time (sched_barrier), so that only its
+// values are live.
+template <int EPI, int TM, int TN, int WCOLS>
+DEV void db_epilogue(const GemmArgs& g, f32x16 (&acc)[TM][TN], int r0, int c0) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t o0 = (int64_t)(r0 + i * 32) * g.ldc + c0;
+    if (EPI == LOOP_EPI_SWIGLU) {
+      uint16_t* Cr = reinterpret_cast<uint16_t*>(g.C) + o0;
+#pragma unroll
+      for (int j = 0; j < TN; j += 2)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = siluf_(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e];
+          *reinterpret_cast<u32x2*>(Cr + (j / 2) * 32 + 8 * q) = pack_bf16x4(o[0], o[1], o[2], o[3]);
+        }
+    } else {
+      f32x4 rv[TN][4];
+      if (EPI == LOOP_EPI_F32_RES) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rv[j][q] = *reinterpret_cast<const f32x4*>(g.R + o0 + j * 32 + 8 * q);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t o = o0 + j * 32 + 8 * q;
+          f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (EPI == LOOP_EPI_BF16) {
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(g.C) + o) = pack_bf16x4(v[0], v[1], v[2], v[3]);
+          } else {
+            if (EPI == LOOP_EPI_F32_RES) v += rv[j][q];
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + o) = v;
+          }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int EPI, int KB, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void gemm_db_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes, int n_tiles) {
   using S = DbShape<KB, NW>;
@@ -506,49 +553,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_db_kernel(GemmArgs g, uint32_
     }
     DB_MFMA((KS - 1) & 1);
 
-    // Epilogue: lane (lr, half) holds row r0 + 32 i and, for r = 4 q + e,
-    // column c0 + 32 j + 8 q + e of the wave's 128 x 128 block.  One row
-    // block at a time (sched_barrier), so that only its values are live.
-    const int r0 = m0 + wm * 128 + lr;
-    const int c0 = n0 + wn * (OUT_BN / WN) + 4 * half;
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int64_t o0 = (int64_t)(r0 + i * 32) * g.ldc + c0;
-      if (EPI == LOOP_EPI_SWIGLU) {
-        uint16_t* Cr = reinterpret_cast<uint16_t*>(g.C) + o0;
-#pragma unroll
-        for (int j = 0; j < TN; j += 2)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = siluf_(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e];
-            *reinterpret_cast<u32x2*>(Cr + (j / 2) * 32 + 8 * q) = pack_bf16x4(o[0], o[1], o[2], o[3]);
-          }
-      } else {
-        f32x4 rv[TN][4];
-        if (EPI == LOOP_EPI_F32_RES) {
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) rv[j][q] = *reinterpret_cast<const f32x4*>(g.R + o0 + j * 32 + 8 * q);
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t o = o0 + j * 32 + 8 * q;
-            f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            if (EPI == LOOP_EPI_BF16) {
-              *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(g.C) + o) = pack_bf16x4(v[0], v[1], v[2], v[3]);
-            } else {
-              if (EPI == LOOP_EPI_F32_RES) v += rv[j][q];
-              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + o) = v;
-            }
-          }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    db_epilogue<EPI, TM, TN, OUT_BN / WN>(g, acc, m0 + wm * 128 + lr, n0 + wn * (OUT_BN / WN) + 4 * half);
   }
   // nothing may still be writing LDS when the workgroup ends
   wait_vmem();
@@ -734,8 +739,12 @@ hipError_t launch_skinny(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t
   return launch_skinny_w<EPI, SK_WAVES>(g, ws_bytes, a_bytes, b_bytes, s);
 }
 
-// Two stages of K = 64 (128 KB of LDS).  Deeper rings of K = 32 steps (up to
-// 5 stages, the whole 160 KB) measured slower on every shape.
+// Two stages of K = 64 (128 KB of LDS).  Measured slower on every shape:
+// deeper rings of K = 32 steps (up to 5 stages, the whole 160 KB; 64-byte
+// row pieces double the L2 requests), a five-slot ring of 64-deep operand
+// pieces (the 160 KB; each B piece one step ahead, each A piece two), eight
+// waves (two per SIMD, 128 x 64 each), an L2 warm-up of the step after next,
+// K start staggered by column tile, and other tile orders.
 constexpr int DB_KB = 64, DB_NW = 4;
 template <int EPI>
 hipError_t launch_db(const GemmArgs& g, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
