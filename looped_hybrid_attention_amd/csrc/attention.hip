@@ -326,21 +326,23 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
       const int k0 = j * KT;
       if (j + 1 < nkt) FLASH_COPY(k0 + KT, (j + 1) & 1);
 
-      // S^T for the two 32-key halves: 2 NKS MFMAs, the K fragment reads
-      // kept FD steps ahead of them
+      // S^T for the two 32-key halves: 2 NKS MFMAs alternating between the
+      // halves (two independent accumulation chains keep the MFMA pipe full;
+      // one chain issues at ~60 % of the rate), the K fragment reads kept FD
+      // steps ahead of them
       s[0] = (f32x16){};
       s[1] = (f32x16){};
       {
         const uint8_t* kr = sK + ql * L::KROW;
         bf16x8 kf[2 * NKS];
 #define FLASH_KREAD(g_) \
-  kf[g_] = *reinterpret_cast<const bf16x8*>(kr + ((g_) / NKS) * 32 * L::KROW + (((2 * ((g_) % NKS) + h) ^ ksw) << 4))
+  kf[g_] = *reinterpret_cast<const bf16x8*>(kr + ((g_) & 1) * 32 * L::KROW + (((2 * ((g_) >> 1) + h) ^ ksw) << 4))
 #pragma unroll
         for (int g = 0; g < FD; ++g) FLASH_KREAD(g);
 #pragma unroll
         for (int g = 0; g < 2 * NKS; ++g) {
           if (g + FD < 2 * NKS) FLASH_KREAD(g + FD);
-          s[g / NKS] = mfma32x32x16(kf[g], qf[g % NKS], s[g / NKS]);
+          s[g & 1] = mfma32x32x16(kf[g], qf[g >> 1], s[g & 1]);
         }
 #undef FLASH_KREAD
         __builtin_amdgcn_sched_group_barrier(0x100, FD, 0);
@@ -502,15 +504,14 @@ __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a
           vv[dt][j] = w;
         }
     }
-    f32x4 sacc[2];
+    // the two key groups' accumulations interleaved: two independent chains
+    f32x4 sacc[2] = {(f32x4){0, 0, 0, 0}, (f32x4){0, 0, 0, 0}};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      sacc[u] = (f32x4){0, 0, 0, 0};
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+      for (int u = 0; u < 2; ++u)
         sacc[u] = mfma16x16x32(__builtin_bit_cast(bf16x8, kv[u][ks]),
                                __builtin_bit_cast(bf16x8, sq[l16 * (D / 8) + ks * 4 + lg]), sacc[u]);
-    }
     // lane holds keys kb + 8 lg + 4 u + r of head l16
     float sv[8];
     float mx = -1e30f;
