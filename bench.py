@@ -29,6 +29,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 LONG_T = 131072
+VERIFY_K, VERIFY_STEPS = 4, 8
 PREFILL_T = 8192
 DECODE_B, DECODE_CTX = 64, 32768
 
@@ -77,6 +78,7 @@ def parse():
                    help="first run one plain 1 GiB device-to-device copy (scale for HBM byte counters)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-long", action="store_true", help="skip the 131,072-token chunked prefill")
+    p.add_argument("--no-verify", action="store_true", help="skip the multi-token verify step")
     p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return p.parse_args()
 
@@ -129,7 +131,7 @@ def main():
     from synth.presets import weight_specs
 
     dims = synth.preset("full")
-    max_seq = ((DECODE_CTX + args.decode_warmup + args.decode_steps + 1 + 63) // 64) * 64
+    max_seq = ((DECODE_CTX + args.decode_warmup + args.decode_steps + 1 + VERIFY_K * (VERIFY_STEPS + 1) + 63) // 64) * 64
     cfg = L.make_config(dims, max_batch=DECODE_B, max_seq=max_seq, max_tokens=PREFILL_T)
     sched = L.loop_schedule(cfg)
     kinds_layer = {}
@@ -266,6 +268,36 @@ def main():
                                "kernel": "decode_attn_kernel<256,4> + combine (split-L attention)",
                                "launch_ms": round(a_avg, 4), "launches": a_n,
                                "algorithmic_bytes_per_launch": kv_launch}}
+
+        # multi-token verify: VERIFY_K drafted tokens per sequence checked in
+        # one call (logits and greedy token at every position), continuing
+        # the decode batch's caches
+        if not args.no_verify:
+            vt = torch.empty(DECODE_B * VERIFY_K, dtype=torch.int32, device="cuda")
+            L.loop_synth_token_ids(vt.data_ptr(), vt.numel(), dims["vocab"], synth.SEED_X,
+                                   synth.fnv1a32("bench.verify.ids"), stream)
+            vlog = torch.empty((DECODE_B * VERIFY_K, dims["vocab"]), dtype=torch.float32, device="cuda")
+            vnx = torch.empty(DECODE_B * VERIFY_K, dtype=torch.int32, device="cuda")
+
+            def verify_step(p):
+                L.loop_verify_step(model, DECODE_B, VERIFY_K, slots, [p] * DECODE_B, vt.data_ptr(),
+                                   d_logits=vlog.data_ptr(), d_next=vnx.data_ptr(), stream=stream)
+
+            verify_step(pos)  # warm-up
+            pos += VERIFY_K
+            torch.cuda.synchronize()
+            v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            v0.record()
+            for _ in range(VERIFY_STEPS):
+                verify_step(pos)
+                pos += VERIFY_K
+            v1.record()
+            torch.cuda.synchronize()
+            vms = v0.elapsed_time(v1) / VERIFY_STEPS
+            assert torch.isfinite(vlog).all().item(), "non-finite verify logits"
+            decode["verify"] = {"metric": "verified tok/s", "value": round(DECODE_B * VERIFY_K / (vms / 1e3), 1),
+                                "unit": "tok/s", "k": VERIFY_K, "batch": DECODE_B, "ms_per_step": round(vms, 3),
+                                "steps": VERIFY_STEPS, "context": DECODE_CTX}
 
     L.loop_model_destroy(model)
 

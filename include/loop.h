@@ -212,6 +212,44 @@ typedef struct loop_decode_args {
 } loop_decode_args;
 int loop_decode_step(loop_model* m, const loop_decode_args* a, void* stream);
 
+/* Verify step: k tokens per sequence (k <= LOOP_VERIFY_MAX) appended at
+ * positions pos[b] .. pos[b]+k-1 -- a prefill of k tokens -- with the logits
+ * (and greedy next tokens, and taps) of every position, as speculative
+ * decoding checks k drafted tokens in one pass ([P4 section 03]: a small
+ * draft model proposes several tokens that the full model then checks).  The
+ * caches advance through all k tokens: after accepting j < k of them, a
+ * caller continues at position pos+j (KV entries past it are overwritten by
+ * later calls) but must first restore the GDN states it saved (they are the
+ * arena's state blocks, loop_cache_offset(cfg, 2, slot, b)) and feed the j
+ * accepted tokens again, or re-verify from the restored state.  The taps
+ * are what a drafter reads ([P4 section 03]: the draft model looks at the
+ * hidden states after executions 3, 27, 51, 53 and 54).
+ *   slots, pos  host [batch]
+ *   d_tokens    device int32 [batch*k], sequence-major
+ *   d_logits    device fp32 [batch*k, vocab] or NULL
+ *   d_next      device int32 [batch*k] greedy argmax of every position (needs
+ *               d_logits) or NULL
+ *   d_hidden_out device fp32 [batch*k, d_model] or NULL
+ *   n_taps / tap_exec (host) / d_taps device fp32 [n_taps, batch*k, d_model]:
+ *               hidden state after the listed executions at every position
+ *   loop_passes as for decode.
+ * Requires batch*k <= max_tokens. */
+#define LOOP_VERIFY_MAX 16
+typedef struct loop_verify_args {
+  int32_t batch, k;
+  const int32_t* slots;
+  const int32_t* pos;
+  const int32_t* d_tokens;
+  float* d_logits;
+  int32_t* d_next;
+  float* d_hidden_out;
+  int32_t n_taps;
+  const int32_t* tap_exec;
+  float* d_taps;
+  int32_t loop_passes;
+} loop_verify_args;
+int loop_verify_step(loop_model* m, const loop_verify_args* a, void* stream);
+
 /* Sinkhorn-normalised stream-mix matrices of every loop layer as the device
  * computes them ([P1 section 5]): fp32 [loop_end-loop_start, 2, 2] into
  * device d_out. */

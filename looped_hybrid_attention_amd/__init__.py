@@ -60,6 +60,15 @@ class loop_decode_args(ctypes.Structure):
                 ("loop_passes", _i32)]
 
 
+class loop_verify_args(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("k", _i32), ("slots", ctypes.POINTER(_i32)), ("pos", ctypes.POINTER(_i32)),
+                ("d_tokens", _vp), ("d_logits", _vp), ("d_next", _vp), ("d_hidden_out", _vp),
+                ("n_taps", _i32), ("tap_exec", ctypes.POINTER(_i32)), ("d_taps", _vp), ("loop_passes", _i32)]
+
+
+LOOP_VERIFY_MAX = 16
+
+
 def _load():
     # The library links the HIP runtime that PyTorch-ROCm loads; importing
     # torch first makes that runtime the process's only one.
@@ -83,6 +92,7 @@ def _load():
         "loop_model_destroy": (None, [_vp]),
         "loop_prefill": (ctypes.c_int, [_vp, P(loop_prefill_args), _vp]),
         "loop_decode_step": (ctypes.c_int, [_vp, P(loop_decode_args), _vp]),
+        "loop_verify_step": (ctypes.c_int, [_vp, P(loop_verify_args), _vp]),
         "loop_debug_mhc": (ctypes.c_int, [_vp, _vp, _vp]),
         "loop_last_error": (ctypes.c_char_p, []),
         "loop_profile": (ctypes.c_int, [_vp, _i32]),
@@ -102,7 +112,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("loop_kv_bytes", "loop_state_bytes", "loop_arena_bytes", "loop_workspace_bytes",
             "loop_cache_offset", "loop_schedule", "loop_model_create", "loop_model_destroy",
-            "loop_prefill", "loop_decode_step", "loop_debug_mhc", "loop_last_error",
+            "loop_prefill", "loop_decode_step", "loop_verify_step", "loop_debug_mhc", "loop_last_error",
             "loop_profile", "loop_profile_read", "loop_op_gemm", "loop_synth_normal",
             "loop_synth_token_ids")
 LOOP_K = dict(gemm_gateup=0, gemm_down=1, gemm_in=2, gemm_o=3, attn_prep=4, flash=5, gdn=6,
@@ -242,6 +252,21 @@ def loop_decode_step(model: int, batch: int, slots, pos, d_tokens: int, d_logits
     a.d_tokens = d_tokens
     a.d_logits, a.d_next, a.d_hidden_out = d_logits or None, d_next or None, d_hidden_out or None
     _check(_lib.loop_decode_step(model, ctypes.byref(a), stream or None))
+
+
+def loop_verify_step(model: int, batch: int, k: int, slots, pos, d_tokens: int, d_logits: int = 0,
+                     d_next: int = 0, d_hidden_out: int = 0, tap_exec=(), d_taps: int = 0, stream: int = 0,
+                     loop_passes: int = 0) -> None:
+    a = loop_verify_args()
+    a.batch, a.k, a.loop_passes = batch, k, loop_passes
+    sl, ps, te = _i32arr(slots), _i32arr(pos), _i32arr(tap_exec)
+    a.slots, a.pos = sl, ps
+    a.d_tokens = d_tokens
+    a.d_logits, a.d_next, a.d_hidden_out = d_logits or None, d_next or None, d_hidden_out or None
+    a.n_taps = len(tap_exec)
+    a.tap_exec = te if len(tap_exec) else None
+    a.d_taps = d_taps or None
+    _check(_lib.loop_verify_step(model, ctypes.byref(a), stream or None))
 
 
 def loop_debug_mhc(model: int, d_out: int, stream: int = 0) -> None:

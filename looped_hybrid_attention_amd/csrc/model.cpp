@@ -46,6 +46,10 @@ struct Layout {
 int n_in_full(const loop_config& c) { return 2 * c.n_q_heads * c.head_dim + 2 * c.n_kv_heads * c.head_dim; }
 int n_in_gdn(const loop_config& c) { return 2 * c.gdn_heads * c.gdn_dk + 2 * c.gdn_heads * c.gdn_dv + 2 * c.gdn_heads; }
 
+int64_t head_rows(const loop_config& c, int64_t M) {
+  return std::max<int64_t>(c.max_batch, std::min<int64_t>(M, (int64_t)LOOP_VERIFY_MAX * c.max_batch));
+}
+
 Layout layout(const loop_config& c, int64_t M) {
   Layout L{};
   const int64_t d = c.d_model, B = c.max_batch;
@@ -77,10 +81,13 @@ Layout layout(const loop_config& c, int64_t M) {
   L.gM = take(cs * 64 * c.gdn_dv * 4);
   L.gC = take(cs * 4);
   L.gS = take(cs * (int64_t)c.gdn_dv * c.gdn_dk * 4);
-  L.xf = take(B * d * 2);
+  // final-norm rows and argmax partials: one per sequence, or up to
+  // LOOP_VERIFY_MAX per sequence for a verify step
+  const int64_t HR = head_rows(c, M);
+  L.xf = take(HR * d * 2);
   L.logits = take(B * (int64_t)std::max(c.vocab, 1) * 4);
-  L.am_v = take(B * (int64_t)argmax_chunks(std::max(c.vocab, 1)) * 4);
-  L.am_i = take(B * (int64_t)argmax_chunks(std::max(c.vocab, 1)) * 4);
+  L.am_v = take(HR * (int64_t)argmax_chunks(std::max(c.vocab, 1)) * 4);
+  L.am_i = take(HR * (int64_t)argmax_chunks(std::max(c.vocab, 1)) * 4);
   L.n_split_max = (c.max_seq + DEC_SPLIT - 1) / DEC_SPLIT;
   L.dec_part = take(B * (int64_t)c.n_q_heads * L.n_split_max * (c.head_dim + 2) * 4);
   L.mhc = take(std::max(c.loop_end - c.loop_start, 1) * 4 * 4);
@@ -267,6 +274,7 @@ struct Call {
   const int32_t* d_slot;
   const int32_t* d_last;
   const std::vector<ExecDesc>* sched;  // this call's executions
+  bool taps_all = false;               // taps at every position (verify), not the last
 };
 
 #define HIP_TRY(x)                                              \
@@ -468,9 +476,11 @@ int run_forward(loop_model* m, const Call& k, const int32_t* taps, int n_taps, f
       if (taps[i] != e) continue;
       const ExecDesc& d = (*k.sched)[e];
       const bool streams = d.loop && !d.merge;
+      // every position: M "sequences" of length 1
+      const int tb = k.taps_all ? k.M : k.B, tt = k.taps_all ? 1 : k.T;
       HIP_TRY(launch_tap(at<float>(m, L.h), streams ? at<float>(m, L.s0) : nullptr,
-                         streams ? at<float>(m, L.s1) : nullptr, d_taps + (int64_t)i * k.B * c.d_model,
-                         k.B, k.T, c.d_model, s));
+                         streams ? at<float>(m, L.s1) : nullptr, d_taps + (int64_t)i * tb * c.d_model,
+                         tb, tt, c.d_model, s));
     }
   }
   return 0;
@@ -598,6 +608,52 @@ extern "C" int loop_decode_step(loop_model* m, const loop_decode_args* a, void* 
     if (int r = head_logits(m, k, logits, s)) return r;
     if (a->d_next)
       HIP_TRY(launch_argmax(logits, B, c.vocab, at<float>(m, m->L.am_v), at<int>(m, m->L.am_i), a->d_next, s));
+  }
+  return 0;
+}
+
+extern "C" int loop_verify_step(loop_model* m, const loop_verify_args* a, void* stream) {
+  if (!m || !a) return loop_fail(LOOP_EINVAL, "model or args NULL");
+  const loop_config& c = m->cfg;
+  const int B = a->batch, K = a->k;
+  if (B < 1 || B > c.max_batch) return loop_fail(LOOP_ECAPACITY, "batch %d out of [1, %d]", B, c.max_batch);
+  if (K < 1 || K > LOOP_VERIFY_MAX) return loop_fail(LOOP_EINVAL, "k %d out of [1, %d]", K, LOOP_VERIFY_MAX);
+  if ((int64_t)B * K > c.max_tokens) return loop_fail(LOOP_ECAPACITY, "batch*k %d > max_tokens %d", B * K, c.max_tokens);
+  if (c.vocab == 0) return loop_fail(LOOP_EINVAL, "verify needs vocab > 0");
+  if (!a->d_tokens || !a->pos) return loop_fail(LOOP_EINVAL, "d_tokens and pos are required");
+  if (int r = check_slots(c, B, a->slots)) return r;
+  for (int b = 0; b < B; ++b)
+    if (a->pos[b] < 0 || (int64_t)a->pos[b] + K > c.max_seq)
+      return loop_fail(LOOP_ECAPACITY, "pos %d + k %d exceeds max_seq %d", a->pos[b], K, c.max_seq);
+  if (a->n_taps < 0 || (a->n_taps > 0 && (!a->tap_exec || !a->d_taps))) return loop_fail(LOOP_EINVAL, "bad taps");
+  int passes = 0;
+  if (int r = call_passes(m, a->loop_passes, B, a->slots, a->pos, &passes)) return r;
+  const std::vector<ExecDesc>& sched = m->sched_p[passes - 1];
+  for (int i = 0; i < a->n_taps; ++i)
+    if (a->tap_exec[i] < 0 || a->tap_exec[i] >= (int)sched.size()) return loop_fail(LOOP_EINVAL, "tap %d out of range", a->tap_exec[i]);
+  hipStream_t s = (hipStream_t)stream;
+  Call k{B, K, B * K, false, nullptr, nullptr, nullptr, &sched};
+  k.taps_all = true;
+  const int32_t* meta = at<int32_t>(m, m->L.meta);
+  k.d_pos = meta;
+  k.d_slot = meta + c.max_batch;
+  k.d_last = meta + 2 * c.max_batch;
+  if (int r = upload_meta(m, B, K, a->pos, a->slots, s)) return r;
+  float* h = at<float>(m, m->L.h);
+  HIP_TRY(launch_embed(a->d_tokens, m->embed, h, k.M, c.d_model, c.vocab, s));
+  if (int r = run_forward(m, k, a->tap_exec, a->n_taps, a->d_taps, s)) return r;
+  for (int b = 0; b < B; ++b)
+    if (a->pos[b] == 0) m->slot_passes[a->slots[b]] = passes;
+  if (a->d_hidden_out) HIP_TRY(hipMemcpyAsync(a->d_hidden_out, h, (size_t)k.M * c.d_model * 4, hipMemcpyDeviceToDevice, s));
+  if (a->d_logits || a->d_next) {
+    if (!a->d_logits) return loop_fail(LOOP_EINVAL, "d_next needs d_logits (logits of every position)");
+    // final norm and head over every position
+    uint16_t* xf = at<uint16_t>(m, m->L.xf);
+    HIP_TRY(launch_rmsnorm(h, nullptr, nullptr, c.d_model, m->final_norm, xf, k.M, c.d_model, c.eps, s));
+    HIP_TRY(launch_gemm(xf, c.d_model, m->head, c.d_model, a->d_logits, c.vocab, nullptr, k.M, c.vocab, c.d_model,
+                        LOOP_EPI_F32, s, at<float>(m, m->L.splitk), m->L.splitk_bytes));
+    if (a->d_next)
+      HIP_TRY(launch_argmax(a->d_logits, k.M, c.vocab, at<float>(m, m->L.am_v), at<int>(m, m->L.am_i), a->d_next, s));
   }
   return 0;
 }
