@@ -78,6 +78,8 @@ def parse():
                    help="first run one plain 1 GiB device-to-device copy (scale for HBM byte counters)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-long", action="store_true", help="skip the 131,072-token chunked prefill")
+    p.add_argument("--long-tokens", type=int, default=LONG_T,
+                   help="length of the chunked long prefill (a multiple of 8192; 262144 = the trained length)")
     p.add_argument("--no-verify", action="store_true", help="skip the multi-token verify step")
     p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return p.parse_args()
@@ -308,18 +310,20 @@ def main():
     if not args.no_long:
         del arena, ws
         torch.cuda.empty_cache()
-        cfg_l = L.make_config(dims, max_batch=1, max_seq=LONG_T + 64, max_tokens=PREFILL_T)
+        n_long = args.long_tokens
+        assert n_long % PREFILL_T == 0 and n_long > 0, "--long-tokens must be a multiple of 8192"
+        cfg_l = L.make_config(dims, max_batch=1, max_seq=n_long + 64, max_tokens=PREFILL_T)
         ab_l, wb_l = L.loop_arena_bytes(cfg_l), L.loop_workspace_bytes(cfg_l, PREFILL_T)
         arena_l = torch.empty(ab_l, dtype=torch.uint8, device="cuda")
         ws_l = torch.empty(wb_l, dtype=torch.uint8, device="cuda")
         model_l = L.loop_model_create(cfg_l, wstruct, arena_l.data_ptr(), ab_l, ws_l.data_ptr(), wb_l)
-        ids_l = torch.empty(LONG_T, dtype=torch.int32, device="cuda")
-        L.loop_synth_token_ids(ids_l.data_ptr(), LONG_T, dims["vocab"], synth.SEED_X,
+        ids_l = torch.empty(n_long, dtype=torch.int32, device="cuda")
+        L.loop_synth_token_ids(ids_l.data_ptr(), n_long, dims["vocab"], synth.SEED_X,
                                synth.fnv1a32("bench.long.ids"), stream)
 
         def long_pass(n_calls):
             for c in range(n_calls):
-                last = c == LONG_T // PREFILL_T - 1
+                last = c == n_long // PREFILL_T - 1
                 L.loop_prefill(model_l, 1, PREFILL_T, [0], [c * PREFILL_T], d_tokens=ids_l[c * PREFILL_T:].data_ptr(),
                                d_logits=logits.data_ptr() if last else 0, stream=stream)
 
@@ -327,18 +331,18 @@ def main():
         torch.cuda.synchronize()
         l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         l0.record()
-        long_pass(LONG_T // PREFILL_T)
+        long_pass(n_long // PREFILL_T)
         l1.record()
         torch.cuda.synchronize()
         lms = l0.elapsed_time(l1)
         assert torch.isfinite(logits).all().item(), "non-finite logits (long prefill)"
-        fl_l = prefill_flops(dims, kinds_exec, LONG_T)
-        long = {"metric": "long prefill tok/s", "value": round(LONG_T / (lms / 1e3), 1), "unit": "tok/s",
-                "tokens": LONG_T, "calls": LONG_T // PREFILL_T, "tokens_per_call": PREFILL_T,
+        fl_l = prefill_flops(dims, kinds_exec, n_long)
+        long = {"metric": "long prefill tok/s", "value": round(n_long / (lms / 1e3), 1), "unit": "tok/s",
+                "tokens": n_long, "calls": n_long // PREFILL_T, "tokens_per_call": PREFILL_T,
                 "ms_total": round(lms, 1),
                 "mfma_frac": round(fl_l["total"] / (lms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                 "algorithmic_flop": fl_l["total"],
-                "kv_bytes": L.loop_kv_bytes(cfg_l, 1, LONG_T), "gdn_state_bytes": L.loop_state_bytes(cfg_l, 1)}
+                "kv_bytes": L.loop_kv_bytes(cfg_l, 1, n_long), "gdn_state_bytes": L.loop_state_bytes(cfg_l, 1)}
         L.loop_model_destroy(model_l)
 
     # --------------------------------------------------------- CPU baseline
