@@ -38,4 +38,4 @@ prefill-then-decode vs longer prefill, single-stream reduction).
 """
 
 from .config import Config, ExecRow, schedule, layer_kind  # noqa: F401
-from . import accounting, ops, attention, gdn, mhc, model  # noqa: F401
+from . import accounting, ops, attention, gdn, mhc, model, quant  # noqa: F401

@@ -612,3 +612,43 @@ def test_bf16_policy_keeps_structural_invariants():
     ucfg, UW = model.unrolled(cfg, W)
     h2, l2, _ = model.prefill(ucfg, UW, [model.SeqState(ucfg)], ids=ids, bf16=True)
     assert np.array_equal(h1, h2) and np.array_equal(l1, l2)
+
+
+# ----------------------------------------------------------- int8 decode weights
+
+def test_int8_codes_definition():
+    """Per-row symmetric int8: the largest magnitude of every row maps to
+    +-127 exactly, every code is the nearest integer to w / s (ties to even),
+    dequantization is within s / 2 of w, a zero row stays zero."""
+    from oracle.quant import quantize_rows_int8, dequantize_rows
+    rng = np.random.default_rng(7)
+    w = rng.normal(0, 0.02, (37, 300)).astype(np.float32)
+    w[5] = 0.0
+    w[6, 17] = -0.5          # a row whose extreme is negative
+    q, s = quantize_rows_int8(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert s[5] == 0 and not q[5].any()
+    assert q[6, 17] == -127
+    for n in range(w.shape[0]):
+        if s[n] == 0:
+            continue
+        assert np.abs(q[n]).max() == 127
+        assert s[n] == np.float32(np.abs(w[n]).max()) / np.float32(127)
+    err = np.abs(dequantize_rows(q, s) - w)
+    assert np.all(err <= s[:, None] * 0.5 * (1 + 1e-6))
+    # values on the grid come back exactly; a half-way value rounds to even
+    g = np.array([[127.0, 3.0, -2.5, 2.5, 1.5]], dtype=np.float32) * np.float32(0.25)
+    qg, sg = quantize_rows_int8(g)
+    assert sg[0] == np.float32(0.25) and list(qg[0]) == [127, 3, -2, 2, 2]
+
+
+def test_int8_decode_weights_only_projections(tiny64):
+    from oracle.quant import int8_decode_weights, PROJECTIONS
+    cfg, W = tiny64[0], tiny64[1]
+    Wq = int8_decode_weights(W, cfg.n_layers)
+    for k, v in W.items():
+        name = k.split(".", 1)[-1]
+        if k.startswith("L") and name in PROJECTIONS:
+            assert not np.array_equal(Wq[k], v) and np.abs(Wq[k] - v).max() <= np.abs(v).max() / 254 * 1.0001
+        else:
+            assert Wq[k] is v
