@@ -30,6 +30,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 LONG_T = 131072
 VERIFY_K, VERIFY_STEPS = 4, 8
+INT8_STEPS, INT8_WARMUP = 32, 2
 PREFILL_T = 8192
 DECODE_B, DECODE_CTX = 64, 32768
 
@@ -81,6 +82,7 @@ def parse():
     p.add_argument("--long-tokens", type=int, default=LONG_T,
                    help="length of the chunked long prefill (a multiple of 8192; 262144 = the trained length)")
     p.add_argument("--no-verify", action="store_true", help="skip the multi-token verify step")
+    p.add_argument("--no-int8", action="store_true", help="skip the weight-only int8 decode")
     p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return p.parse_args()
 
@@ -92,6 +94,12 @@ def layer_matrix_params(d, F, kind, Hq=16, Hkv=4, D=256, H=16, Dk=128, Dv=128):
     if kind == "full":
         return ffn + (2 * Hq * D + 2 * Hkv * D) * d + d * Hq * D
     return ffn + (2 * H * Dk + 2 * H * Dv + 2 * H) * d + d * H * Dv
+
+
+def layer_matrix_rows(d, F, kind, Hq=16, Hkv=4, D=256, H=16, Dk=128, Dv=128):
+    """Output rows of a layer's four projection matrices (one scale each in int8)."""
+    n_in = 2 * Hq * D + 2 * Hkv * D if kind == "full" else 2 * H * Dk + 2 * H * Dv + 2 * H
+    return n_in + d + 2 * F + d
 
 
 def prefill_flops(dims, kinds_exec, T):
@@ -106,11 +114,16 @@ def prefill_flops(dims, kinds_exec, T):
     return dict(gemm=gemm, attn=attn, gdn=gdn, head=head, total=gemm + attn + gdn + head)
 
 
-def decode_bytes(dims, kinds_exec, B, L):
-    """Per step: each executed layer's weights once (bf16), the LM head, all
-    K/V read (L keys) + the appended K/V, GDN state read + write."""
+def decode_bytes(dims, kinds_exec, B, L, int8=False):
+    """Per step: each executed layer's weights once (bf16; with int8, one
+    byte per element plus a 4-byte scale per matrix row), the LM head (bf16),
+    all K/V read (L keys) + the appended K/V, GDN state read + write."""
     d, F = dims["d_model"], dims["d_ff"]
-    weights = sum(2 * layer_matrix_params(d, F, k) for k in kinds_exec) + 2 * d * dims["vocab"]
+    if int8:
+        weights = sum(layer_matrix_params(d, F, k) + 4 * layer_matrix_rows(d, F, k) for k in kinds_exec)
+    else:
+        weights = sum(2 * layer_matrix_params(d, F, k) for k in kinds_exec)
+    weights += 2 * d * dims["vocab"]
     n_full = sum(k == "full" for k in kinds_exec)
     kv_tok = dims["n_kv_heads"] * dims["head_dim"] * 2 * 2
     kv = n_full * B * kv_tok * (L + 1)
@@ -133,7 +146,8 @@ def main():
     from synth.presets import weight_specs
 
     dims = synth.preset("full")
-    max_seq = ((DECODE_CTX + args.decode_warmup + args.decode_steps + 1 + VERIFY_K * (VERIFY_STEPS + 1) + 63) // 64) * 64
+    max_seq = ((DECODE_CTX + args.decode_warmup + args.decode_steps + 1 + VERIFY_K * (VERIFY_STEPS + 1)
+                + INT8_STEPS + INT8_WARMUP + 63) // 64) * 64
     cfg = L.make_config(dims, max_batch=DECODE_B, max_seq=max_seq, max_tokens=PREFILL_T)
     sched = L.loop_schedule(cfg)
     kinds_layer = {}
@@ -270,6 +284,45 @@ def main():
                                "kernel": "decode_attn_kernel<256,4> + combine (split-L attention)",
                                "launch_ms": round(a_avg, 4), "launches": a_n,
                                "algorithmic_bytes_per_launch": kv_launch}}
+
+        # weight-only int8 decode: codes of every layer's four projections,
+        # quantized on the device, then the same decode batch continues
+        if not args.no_int8:
+            q_keep, q_layers = [], []
+            short = {"w_in": "in", "w_o": "o", "w_gateup": "gateup", "w_down": "down"}
+            for l in range(dims["n_layers"]):
+                dq = {}
+                for nm in ("w_in", "w_o", "w_gateup", "w_down"):
+                    w = tensors[f"L{l}.{nm}"]
+                    N, K = w.shape
+                    q = torch.empty((N, K), dtype=torch.int8, device="cuda")
+                    sc = torch.empty(N, dtype=torch.float32, device="cuda")
+                    L.loop_quantize_int8(w.data_ptr(), N, K, K, q.data_ptr(), sc.data_ptr(), stream)
+                    q_keep += [q, sc]
+                    dq["w_" + short[nm]], dq["s_" + short[nm]] = q.data_ptr(), sc.data_ptr()
+                q_layers.append(dq)
+            L.loop_model_set_int8(model, q_layers)
+            for _ in range(INT8_WARMUP):
+                decode_step(pos)
+                pos += 1
+            torch.cuda.synchronize()
+            i0, i1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            i_start = pos
+            i0.record()
+            for _ in range(INT8_STEPS):
+                decode_step(pos)
+                pos += 1
+            i1.record()
+            torch.cuda.synchronize()
+            L.loop_model_set_int8(model, None)
+            del q_keep
+            ims = i0.elapsed_time(i1) / INT8_STEPS
+            by8 = decode_bytes(dims, kinds_exec, DECODE_B, (i_start + pos) // 2, int8=True)
+            decode["int8"] = {"metric": "decode tok/s (weight-only int8 projections)",
+                              "value": round(DECODE_B / (ims / 1e3), 1), "unit": "tok/s",
+                              "ms_per_step": round(ims, 3), "steps": INT8_STEPS, "warmup": INT8_WARMUP,
+                              "hbm_frac_step": round(by8["total"] / (ims / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                              "algorithmic_bytes_per_step": by8["total"], "weight_bytes_per_step": by8["weights"]}
 
         # multi-token verify: VERIFY_K drafted tokens per sequence checked in
         # one call (logits and greedy token at every position), continuing

@@ -255,6 +255,39 @@ int loop_verify_step(loop_model* m, const loop_verify_args* a, void* stream);
  * device d_out. */
 int loop_debug_mhc(loop_model* m, float* d_out, void* stream);
 
+/* ------------------------------------------------------------ int8 decode
+ * Weight-only INT8 for the decode projections ([P1 section 7] estimates the
+ * bf16 weights at about 18 GB, about 9 GB in INT8).  Per output row n of a
+ * [N][K] matrix: scale s_n = max_k |w_nk| / 127 (fp32) and codes q_nk = the
+ * nearest integer to w_nk / s_n (ties to even; fp32, correctly rounded
+ * division), in [-127, 127]; a zero row has s_n = 0 and q = 0.  The decode
+ * projections compute with s_n * q_nk.
+ * loop_quantize_int8: codes and scales of one bf16 matrix, on the device.
+ *   d_w bf16 [N][ldw] (device), d_q int8 [N][K] (device, row stride K),
+ *   d_scale fp32 [N] (device).  LOOP_EINVAL for N < 1, K < 1, ldw < K or
+ *   NULL buffers.
+ * loop_model_set_int8: from now on decode steps (loop_decode_step) use the
+ * codes of every layer's in / O / gate-up / down projection instead of its
+ * bf16 matrix; prefill, verify and the head keep bf16.  layers: host
+ * [n_layers] (copied); each matrix's codes (int8, the bf16 matrix's shape,
+ * row stride = its K) and scales (fp32 [rows]) are device buffers borrowed
+ * until the model is destroyed or int8 is turned off.  NULL turns it off.
+ * Requires every K (d_model, the mixer widths, d_ff) to be a multiple of 128;
+ * decode calls then take at most 64 sequences. */
+typedef struct loop_q8_layer {
+  const int8_t* w_in;
+  const float* s_in;
+  const int8_t* w_o;
+  const float* s_o;
+  const int8_t* w_gateup;
+  const float* s_gateup;
+  const int8_t* w_down;
+  const float* s_down;
+} loop_q8_layer;
+int loop_quantize_int8(const void* d_w, int64_t N, int64_t K, int64_t ldw, int8_t* d_q, float* d_scale,
+                       void* stream);
+int loop_model_set_int8(loop_model* m, const loop_q8_layer* layers);
+
 const char* loop_last_error(void);
 
 /* Kernel timing of one kernel class inside the model calls: with class c
@@ -284,9 +317,10 @@ int loop_profile_read(loop_model* m, double* total_ms, int64_t* launches);
  *                     silu(A.gate^T) * (A.up^T)
  * Requires K % 64 == 0, lda and ldb multiples of 8, A and B 16-byte aligned.
  * d_ws / ws_bytes (device, optional): fp32 scratch for split-K partials,
- * used when M is small (< 512), or for the last N % 256 columns (at most 128)
- * of a large-M call, and the buffer is large enough; the partials are summed
- * in split order (deterministic).  NULL = no split. */
+ * used when M is small (< 512), or for the ragged edges of a large-M call
+ * (rows past the last multiple of 256, columns past the last whole 256-wide
+ * tile), and the buffer is large enough; the partials are summed in split
+ * order (deterministic).  NULL = no split. */
 enum { LOOP_EPI_BF16 = 0, LOOP_EPI_F32 = 1, LOOP_EPI_F32_RES = 2, LOOP_EPI_SWIGLU = 3 };
 int loop_op_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
                  const float* R, int32_t M, int32_t N, int32_t K, int32_t epi, float* d_ws,

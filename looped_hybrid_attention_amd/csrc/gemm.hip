@@ -31,6 +31,7 @@ struct GemmArgs {
   int swiglu_F;  // SwiGLU: offset of the up rows in B (= N)
   float* part;   // split-K: fp32 partials [splits][M][N] ([splits][M][2][N] for SwiGLU)
   int kslice;    // split-K: K per split (blockIdx.y)
+  const float* scale = nullptr;  // int8 weights: per-row scale (B is int8 [rows][ldb])
 };
 
 template <int BM, int BN, int WM, int WN, int EPI, bool SPLIT>
@@ -583,10 +584,34 @@ constexpr int SK_STAGE = 64 * SK_ROWB;        // 16 KB
 constexpr int SK_NSET = 4;                    // ring stages / weight register sets (3 chunks ahead)
 constexpr int SK_WAVES = 4;                   // waves (16 weight rows each) per workgroup
 
-template <int EPI, bool SPLIT, int NW>
+// int8 weight rows -> bf16 MFMA operand: bytes 8 h .. 8 h + 7 of a 16-byte
+// load (the codes are integers in [-127, 127]: exact in bf16)
+template <int H>
+DEV bf16x8 i8x8_to_bf16(const u32x4& v) {
+  const uint32_t lo = v[2 * H], hi = v[2 * H + 1];
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)(float)(int8_t)(lo >> (8 * e));
+    r[4 + e] = (bf16)(float)(int8_t)(hi >> (8 * e));
+  }
+  return r;
+}
+
+// Q8: int8 weight rows with a per-row scale ([P1 section 7]'s weight-only
+// INT8; codes and scales as the oracle defines them).  Lane group lg then
+// loads bytes 32 lg .. 32 lg + 31 of its row's 128-deep chunk (two 16-byte
+// loads, half the bytes of bf16) and MFMA step q takes the 8 of them at
+// 32 lg + 8 q; the activation operand reads the same k (the reduction order
+// within a chunk is permuted, identically on both operands).  The scale
+// multiplies the row's dot products before the epilogue.  The chunk count
+// needs not be a multiple of the ring depth (chunks past the end are loaded,
+// not multiplied).
+template <int EPI, bool SPLIT, int NW, bool Q8 = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes) {
   static_assert(NW == 4 || NW == 8, "waves per workgroup");
   constexpr int CPW = 16 / NW;  // activation copies per wave per chunk
+  constexpr int WL = Q8 ? 2 : 4;  // weight loads per lane per chunk
   __shared__ __align__(16) uint8_t sk_smem[SK_NSET * SK_STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -613,18 +638,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
     const int c = (lane & 15) ^ (row & 15);
     a_off[i] = (min(row, g.M - 1) * (int)g.lda + k0 + c * 8) * 2;
   }
-  const int b_off = (wrow * (int)g.ldb + k0 + lg * 8) * 2;
+  const int b_off = Q8 ? wrow * (int)g.ldb + k0 + lg * 32 : (wrow * (int)g.ldb + k0 + lg * 8) * 2;
 #define SK_COPY(ch_, stage_)                                                                       \
   _Pragma("unroll") for (int i = 0; i < CPW; ++i)                                                  \
       copy16_to_lds(a_rsrc, a_off[i], (ch_) * SK_ROWB,                                             \
                     (lds_void*)(sk_smem + (stage_) * SK_STAGE + (CPW * wave + i) * 1024));
 #define SK_WLOAD(ch_, set_)                                                                        \
-  _Pragma("unroll") for (int q = 0; q < 4; ++q) w[set_][q] = buffer_load16(b_rsrc, b_off + q * 64, (ch_) * SK_ROWB);
+  _Pragma("unroll") for (int q = 0; q < WL; ++q) w[set_][q] =                                      \
+      Q8 ? buffer_load16(b_rsrc, b_off + q * 16, (ch_) * SK_KC) : buffer_load16(b_rsrc, b_off + q * 64, (ch_) * SK_ROWB);
 
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = (f32x4){0, 0, 0, 0};
-  u32x4 w[SK_NSET][4];
+  u32x4 w[SK_NSET][WL];
 #pragma unroll
   for (int p = 0; p < SK_NSET - 1; ++p) {
     SK_COPY(min(p, nch - 1), p);
@@ -641,27 +667,49 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
     for (int j = 0; j < SK_NSET; ++j) {
       const int c = c0 + j;
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<(CPW + 4) * (SK_NSET - 2)>();
+      wait_vmcnt<(CPW + WL) * (SK_NSET - 2)>();
       lds_barrier();  // chunk c visible; every wave is done with chunk c - 1
       __builtin_amdgcn_sched_barrier(0);
       SK_COPY(min(c + SK_NSET - 1, nch - 1), (j + SK_NSET - 1) % SK_NSET);
       SK_WLOAD(min(c + SK_NSET - 1, nch - 1), (j + SK_NSET - 1) % SK_NSET);
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* st = sk_smem + j * SK_STAGE;
+      if (!Q8 || c < nch) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x8 bfr[4];
+        for (int q = 0; q < 4; ++q) {
+          bf16x8 bfr[4];
+          const int piece = Q8 ? 4 * lg + q : 4 * q + lg;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-          bfr[mt] = *reinterpret_cast<const bf16x8*>(st + (16 * mt + l16) * SK_ROWB + (((4 * q + lg) ^ l16) << 4));
+          for (int mt = 0; mt < 4; ++mt)
+            bfr[mt] = *reinterpret_cast<const bf16x8*>(st + (16 * mt + l16) * SK_ROWB + ((piece ^ l16) << 4));
+          bf16x8 wa;
+          if (Q8) wa = (q & 1) ? i8x8_to_bf16<1>(w[j][q >> 1]) : i8x8_to_bf16<0>(w[j][q >> 1]);
+          else wa = __builtin_bit_cast(bf16x8, w[j][q]);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16x16x32(__builtin_bit_cast(bf16x8, w[j][q]), bfr[mt], acc[mt]);
+          for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16x16x32(wa, bfr[mt], acc[mt]);
+        }
       }
     }
   }
 #undef SK_COPY
 #undef SK_WLOAD
   wait_vmem();
+  if (Q8) {  // row scales (A-operand row 4 lg + r of the wave)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * lg + r;
+      int row;
+      if (EPI == LOOP_EPI_SWIGLU) {
+        const int col = min(8 * NW * tile + 8 * wave + (i & 7), g.N - 1);
+        row = (i < 8 ? 0 : g.swiglu_F) + col;
+      } else {
+        row = min(16 * NW * tile + 16 * wave + i, g.N - 1);
+      }
+      const float sc = g.scale[row];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][r] *= sc;
+    }
+  }
 
   // lane holds C^T[row 4 lg + r of the wave][m = 16 mt + l16]
   if (EPI == LOOP_EPI_SWIGLU) {
@@ -853,6 +901,53 @@ hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
   return launch_small<EPI>(g, ws_bytes, s);
 }
 
+// Weight-only int8 (decode, M <= 64): the skinny tiles over int8 rows.
+// Splits as for bf16 (K in 128-deep chunks, any count per split).
+template <int EPI>
+hipError_t launch_q8(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
+  constexpr int NW = SK_WAVES;
+  const int per = (EPI == LOOP_EPI_SWIGLU) ? 8 * NW : 16 * NW;
+  const int tiles = (g.N + per - 1) / per;
+  int splits = 1;
+  while (tiles * splits < 256 && g.K % (SK_KC * splits * 2) == 0 && g.K / (splits * 2) >= 512) splits *= 2;
+  const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
+  if (splits > 1 && g.part && need <= ws_bytes) {
+    g.kslice = g.K / splits;
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, NW, true>), dim3(tiles, splits), dim3(64 * NW), 0, s, g, a_bytes,
+                       b_bytes);
+    const int64_t n_out = (int64_t)g.M * g.N;
+    const int blocks = (int)std::min<int64_t>((n_out + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, splits);
+  } else {
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, false, NW, true>), dim3(tiles), dim3(64 * NW), 0, s, g, a_bytes,
+                       b_bytes);
+  }
+  return hipGetLastError();
+}
+
+// per row of an int8 code matrix: scale = max |w| / 127, code = nearest
+// integer to w / scale (ties to even), both in fp32 with correctly rounded
+// division (the oracle takes the same decisions)
+__global__ __launch_bounds__(256) void quantize_int8_kernel(const uint16_t* w, int64_t ldw, int K, int8_t* q,
+                                                            int64_t ldq, float* scale) {
+  __shared__ float red[4];
+  const int64_t n = blockIdx.x;
+  const uint16_t* wr = w + n * ldw;
+  float mx = 0.f;
+  for (int k = threadIdx.x; k < K; k += 256) mx = fmaxf(mx, fabsf(bf2f(wr[k])));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = __fdiv_rn(mx, 127.0f);
+  if (threadIdx.x == 0) scale[n] = sc;
+  for (int k = threadIdx.x; k < K; k += 256) {
+    const float v = sc > 0.f ? rintf(__fdiv_rn(bf2f(wr[k]), sc)) : 0.f;
+    q[n * ldq + k] = (int8_t)fminf(fmaxf(v, -127.f), 127.f);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
@@ -904,4 +999,65 @@ hipError_t launch_gemm_norm(const void* A, int64_t lda, const void* B, int64_t l
   hipError_t e = launch_gemm(A, lda, B, ldb, C, ldc, R, M, N, K, R ? LOOP_EPI_F32_RES : LOOP_EPI_F32, s, ws, ws_bytes);
   if (e != hipSuccess) return e;
   return launch_rmsnorm(C, X2, nullptr, ldc, gain, hn, M, N, eps, s);
+}
+
+hipError_t launch_gemm_q8(const void* A, int64_t lda, const int8_t* Bq, int64_t ldb, const float* scale, void* C,
+                          int64_t ldc, const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws,
+                          size_t ws_bytes) {
+  if (M < 1 || M > 64 || K % SK_KC || lda % 8 || ldb % 16 || !scale) return hipErrorInvalidValue;
+  GemmArgs g{(const uint16_t*)A, lda, (const uint16_t*)Bq, ldb, C, ldc, R, M, N, K, N, ws, K, scale};
+  const int64_t rows_b = (epi == LOOP_EPI_SWIGLU) ? 2 * (int64_t)N : N;
+  const int64_t a_bytes = (int64_t)M * lda * 2, b_bytes = rows_b * ldb;
+  if (a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31)) return hipErrorInvalidValue;
+  switch (epi) {
+    case LOOP_EPI_BF16: return launch_q8<LOOP_EPI_BF16>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+    case LOOP_EPI_F32: return launch_q8<LOOP_EPI_F32>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+    case LOOP_EPI_F32_RES: return launch_q8<LOOP_EPI_F32_RES>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+    case LOOP_EPI_SWIGLU: return launch_q8<LOOP_EPI_SWIGLU>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_norm_q8(const void* A, int64_t lda, const int8_t* Bq, int64_t ldb, const float* scale,
+                               float* C, int64_t ldc, const float* R, const float* X2, const void* gain, void* hn,
+                               float eps, int M, int N, int K, hipStream_t s, float* ws, size_t ws_bytes) {
+  if (M < 1 || M > 64 || K % SK_KC || lda % 8 || ldb % 16 || !scale) return hipErrorInvalidValue;
+  GemmArgs g{(const uint16_t*)A, lda, (const uint16_t*)Bq, ldb, C, ldc, R, M, N, K, N, ws, K, scale};
+  const int64_t a_bytes = (int64_t)M * lda * 2, b_bytes = (int64_t)N * ldb;
+  if (a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31)) return hipErrorInvalidValue;
+  const int tiles = (N + 16 * SK_WAVES - 1) / (16 * SK_WAVES);
+  int splits = 1;
+  while (tiles * splits < 256 && splits < 8 && K % (SK_KC * splits * 2) == 0 && K / (splits * 2) >= 512) splits *= 2;
+  if (N <= 4096 && splits > 1 && ws && (size_t)splits * M * N * sizeof(float) <= ws_bytes) {
+    g.kslice = K / splits;
+    auto launch = [&](auto epi_tag) {
+      constexpr int EPI = decltype(epi_tag)::value;
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, SK_WAVES, true>), dim3(tiles, splits), dim3(64 * SK_WAVES), 0,
+                         s, g, (uint32_t)a_bytes, (uint32_t)b_bytes);
+      if (splits == 4)
+        hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 4>), dim3(M), dim3(1024), 0, s, g, X2,
+                           (const uint16_t*)gain, (uint16_t*)hn, eps);
+      else if (splits == 2)
+        hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 2>), dim3(M), dim3(1024), 0, s, g, X2,
+                           (const uint16_t*)gain, (uint16_t*)hn, eps);
+      else
+        hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 8>), dim3(M), dim3(1024), 0, s, g, X2,
+                           (const uint16_t*)gain, (uint16_t*)hn, eps);
+    };
+    if (R) launch(std::integral_constant<int, LOOP_EPI_F32_RES>());
+    else launch(std::integral_constant<int, LOOP_EPI_F32>());
+    return hipGetLastError();
+  }
+  hipError_t e = launch_gemm_q8(A, lda, Bq, ldb, scale, C, ldc, R, M, N, K, R ? LOOP_EPI_F32_RES : LOOP_EPI_F32, s, ws,
+                                ws_bytes);
+  if (e != hipSuccess) return e;
+  return launch_rmsnorm(C, X2, nullptr, ldc, gain, hn, M, N, eps, s);
+}
+
+hipError_t launch_quantize_int8(const void* w, int64_t ldw, int64_t N, int K, int8_t* q, int64_t ldq, float* scale,
+                                hipStream_t s) {
+  if (N <= 0 || K <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_int8_kernel, dim3((unsigned)N), dim3(256), 0, s, (const uint16_t*)w, ldw, K, q, ldq,
+                     scale);
+  return hipGetLastError();
 }

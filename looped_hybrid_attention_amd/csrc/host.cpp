@@ -173,6 +173,15 @@ extern "C" int loop_synth_normal(void* dst, int64_t n, int32_t dtype, uint32_t s
   return e == hipSuccess ? 0 : loop_hip_fail(e, "synth launch");
 }
 
+extern "C" int loop_quantize_int8(const void* d_w, int64_t N, int64_t K, int64_t ldw, int8_t* d_q, float* d_scale,
+                                  void* stream) {
+  if (!d_w || !d_q || !d_scale) return loop_fail(LOOP_EINVAL, "quantize: NULL buffer");
+  if (N < 1 || K < 1 || ldw < K || K > (1 << 30) || N > (1ll << 31))
+    return loop_fail(LOOP_EINVAL, "quantize: bad shape N %lld K %lld ldw %lld", (long long)N, (long long)K, (long long)ldw);
+  hipError_t e = launch_quantize_int8(d_w, ldw, N, (int)K, d_q, K, d_scale, (hipStream_t)stream);
+  return e == hipSuccess ? 0 : loop_hip_fail(e, "quantize_int8");
+}
+
 extern "C" int loop_synth_token_ids(int32_t* dst, int64_t n, uint32_t vocab, uint32_t seed,
                                     uint32_t key, void* stream) {
   if (!dst && n > 0) return loop_fail(LOOP_EINVAL, "synth: null destination");
