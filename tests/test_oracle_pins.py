@@ -652,3 +652,83 @@ def test_int8_decode_weights_only_projections(tiny64):
             assert not np.array_equal(Wq[k], v) and np.abs(Wq[k] - v).max() <= np.abs(v).max() / 254 * 1.0001
         else:
             assert Wq[k] is v
+
+
+# ----------------------------------------------------------- int4 decode weights
+
+def test_int4_codes_definition():
+    """Group-wise symmetric int4 (groups of 128 k): the largest magnitude of
+    every group maps to +-7 exactly, codes are the nearest integers to
+    w / s (ties to even), the bf16 dequantization is within s / 2 plus one
+    bf16 rounding of w, and a zero group stays zero."""
+    from oracle.quant import quantize_groups_int4, dequantize_groups_int4
+    rng = np.random.default_rng(11)
+    w = rng.normal(0, 0.02, (9, 384)).astype(np.float32)
+    w[2, 128:256] = 0.0         # one zero group
+    w[4, 300] = -0.5            # a group whose extreme is negative
+    q, s = quantize_groups_int4(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32 and s.shape == (9, 3)
+    assert s[2, 1] == 0 and not q[2, 128:256].any()
+    assert q[4, 300] == -7
+    for n in range(9):
+        for g in range(3):
+            blk = w[n, 128 * g:128 * (g + 1)]
+            if s[n, g] == 0:
+                continue
+            assert np.abs(q[n, 128 * g:128 * (g + 1)]).max() == 7
+            assert s[n, g] == np.float32(np.abs(blk).max()) / np.float32(7)
+    d = dequantize_groups_int4(q, s)
+    srep = np.repeat(s, 128, axis=1)
+    assert np.all(np.abs(d - w) <= srep * 0.5 * (1 + 1e-6) + np.abs(w) * 2.0 ** -8 + 1e-30)
+    # values on the grid come back exactly; half-way values round to even
+    g = np.zeros((1, 128), dtype=np.float32)
+    g[0, :6] = np.array([7.0, 3.0, -2.5, 2.5, 1.5, -7.0], dtype=np.float32) * np.float32(0.25)
+    qg, sg = quantize_groups_int4(g)
+    assert sg[0, 0] == np.float32(0.25) and list(qg[0, :6]) == [7, 3, -2, 2, 2, -7]
+    assert np.array_equal(dequantize_groups_int4(qg, sg)[0, :6], np.array([1.75, 0.75, -0.5, 0.5, 0.5, -1.75],
+                                                                          dtype=np.float32))
+
+
+def test_int4_dequant_rounds_product_to_bf16():
+    """A code times a scale that is not a bf16 value: the dequantized
+    weight is the bf16 value nearest the float32 product (here 3 * s with
+    s = 1 + 2^-9 + 2^-20: the float32 product 3.0059 lies between the bf16
+    values 3 and 3 + 2^-6 and rounds to 3)."""
+    from oracle.quant import dequantize_groups_int4
+    s = np.array([[np.float32(1 + 2.0 ** -9 + 2.0 ** -20)]], dtype=np.float32)
+    q = np.zeros((1, 128), dtype=np.int8)
+    q[0, 0] = 3
+    d = dequantize_groups_int4(q, s)
+    assert d[0, 0] == np.float32(3.0)  # 3.0059 is nearer 3 than 3.015625
+    q[0, 0] = 5  # 5 * s = 5.00977: bf16 neighbours 5.0 and 5.03125
+    assert dequantize_groups_int4(q, s)[0, 0] == np.float32(5.0)
+    q[0, 0] = -7  # -7.01367: neighbours -7.0 and -7.03125, nearer -7.0
+    assert dequantize_groups_int4(q, s)[0, 0] == np.float32(-7.0)
+    s2 = np.array([[np.float32(1 + 2.0 ** -7)]], dtype=np.float32)
+    q[0, 0] = 3  # 3.0234375 exactly: halfway between 3.015625 and 3.03125, ties to even (3.03125)
+    assert dequantize_groups_int4(q, s2)[0, 0] == np.float32(3.03125)
+
+
+def test_int4_packing_layout():
+    """Per 8 consecutive k, byte i holds k = i (low nibble) and k = i + 4
+    (high nibble), codes offset by 8; worked bytes and a round trip."""
+    from oracle.quant import pack_int4, unpack_int4
+    q = np.array([[1, 2, 3, 4, 5, 6, 7, -7, 0, 0, 0, 0, -1, -2, -3, -4]], dtype=np.int8)
+    p = pack_int4(q)
+    assert list(p[0]) == [0xD9, 0xEA, 0xFB, 0x1C, 0x78, 0x68, 0x58, 0x48]
+    rng = np.random.default_rng(3)
+    r = rng.integers(-7, 8, (5, 256)).astype(np.int8)
+    assert np.array_equal(unpack_int4(pack_int4(r)), r)
+
+
+def test_int4_decode_weights_only_projections(tiny64):
+    from oracle.quant import int4_decode_weights, PROJECTIONS
+    cfg, W = tiny64[0], tiny64[1]
+    Wq = int4_decode_weights(W, cfg.n_layers)
+    for k, v in W.items():
+        name = k.split(".", 1)[-1]
+        if k.startswith("L") and name in PROJECTIONS:
+            assert not np.array_equal(Wq[k], v)
+            assert np.abs(Wq[k] - v).max() <= np.abs(v).max() * (1 / 14 + 2.0 ** -8) * 1.0001
+        else:
+            assert Wq[k] is v
