@@ -83,6 +83,7 @@ def parse():
                    help="length of the chunked long prefill (a multiple of 8192; 262144 = the trained length)")
     p.add_argument("--no-verify", action="store_true", help="skip the multi-token verify step")
     p.add_argument("--no-int8", action="store_true", help="skip the weight-only int8 decode")
+    p.add_argument("--no-int4", action="store_true", help="skip the weight-only int4 decode")
     p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return p.parse_args()
 
@@ -114,12 +115,17 @@ def prefill_flops(dims, kinds_exec, T):
     return dict(gemm=gemm, attn=attn, gdn=gdn, head=head, total=gemm + attn + gdn + head)
 
 
-def decode_bytes(dims, kinds_exec, B, L, int8=False):
+def decode_bytes(dims, kinds_exec, B, L, int8=False, int4=False):
     """Per step: each executed layer's weights once (bf16; with int8, one
-    byte per element plus a 4-byte scale per matrix row), the LM head (bf16),
-    all K/V read (L keys) + the appended K/V, GDN state read + write."""
+    byte per element plus a 4-byte scale per matrix row; with int4, half a
+    byte per element plus a 4-byte scale per 128 elements), the LM head
+    (bf16), all K/V read (L keys) + the appended K/V, GDN state read +
+    write."""
     d, F = dims["d_model"], dims["d_ff"]
-    if int8:
+    if int4:
+        weights = sum(layer_matrix_params(d, F, k) // 2 + 4 * (layer_matrix_params(d, F, k) // 128)
+                      for k in kinds_exec)
+    elif int8:
         weights = sum(layer_matrix_params(d, F, k) + 4 * layer_matrix_rows(d, F, k) for k in kinds_exec)
     else:
         weights = sum(2 * layer_matrix_params(d, F, k) for k in kinds_exec)
@@ -147,7 +153,7 @@ def main():
 
     dims = synth.preset("full")
     max_seq = ((DECODE_CTX + args.decode_warmup + args.decode_steps + 1 + VERIFY_K * (VERIFY_STEPS + 1)
-                + INT8_STEPS + INT8_WARMUP + 63) // 64) * 64
+                + 2 * (INT8_STEPS + INT8_WARMUP) + 63) // 64) * 64
     cfg = L.make_config(dims, max_batch=DECODE_B, max_seq=max_seq, max_tokens=PREFILL_T)
     sched = L.loop_schedule(cfg)
     kinds_layer = {}
@@ -285,9 +291,12 @@ def main():
                                "launch_ms": round(a_avg, 4), "launches": a_n,
                                "algorithmic_bytes_per_launch": kv_launch}}
 
-        # weight-only int8 decode: codes of every layer's four projections,
-        # quantized on the device, then the same decode batch continues
-        if not args.no_int8:
+        # weight-only int8 and int4 decode: codes of every layer's four
+        # projections, quantized on the device, then the same decode batch
+        # continues (INT8_STEPS timed steps each)
+        for bits in (8, 4):
+            if (bits == 8 and args.no_int8) or (bits == 4 and args.no_int4):
+                continue
             q_keep, q_layers = [], []
             short = {"w_in": "in", "w_o": "o", "w_gateup": "gateup", "w_down": "down"}
             for l in range(dims["n_layers"]):
@@ -295,13 +304,19 @@ def main():
                 for nm in ("w_in", "w_o", "w_gateup", "w_down"):
                     w = tensors[f"L{l}.{nm}"]
                     N, K = w.shape
-                    q = torch.empty((N, K), dtype=torch.int8, device="cuda")
-                    sc = torch.empty(N, dtype=torch.float32, device="cuda")
-                    L.loop_quantize_int8(w.data_ptr(), N, K, K, q.data_ptr(), sc.data_ptr(), stream)
+                    if bits == 8:
+                        q = torch.empty((N, K), dtype=torch.int8, device="cuda")
+                        sc = torch.empty(N, dtype=torch.float32, device="cuda")
+                        L.loop_quantize_int8(w.data_ptr(), N, K, K, q.data_ptr(), sc.data_ptr(), stream)
+                    else:
+                        q = torch.empty((N, K // 2), dtype=torch.uint8, device="cuda")
+                        sc = torch.empty((N, K // 128), dtype=torch.float32, device="cuda")
+                        L.loop_quantize_int4(w.data_ptr(), N, K, K, q.data_ptr(), sc.data_ptr(), stream)
                     q_keep += [q, sc]
                     dq["w_" + short[nm]], dq["s_" + short[nm]] = q.data_ptr(), sc.data_ptr()
                 q_layers.append(dq)
-            L.loop_model_set_int8(model, q_layers)
+            set_q = L.loop_model_set_int8 if bits == 8 else L.loop_model_set_int4
+            set_q(model, q_layers)
             for _ in range(INT8_WARMUP):
                 decode_step(pos)
                 pos += 1
@@ -314,15 +329,16 @@ def main():
                 pos += 1
             i1.record()
             torch.cuda.synchronize()
-            L.loop_model_set_int8(model, None)
+            set_q(model, None)
             del q_keep
             ims = i0.elapsed_time(i1) / INT8_STEPS
-            by8 = decode_bytes(dims, kinds_exec, DECODE_B, (i_start + pos) // 2, int8=True)
-            decode["int8"] = {"metric": "decode tok/s (weight-only int8 projections)",
-                              "value": round(DECODE_B / (ims / 1e3), 1), "unit": "tok/s",
-                              "ms_per_step": round(ims, 3), "steps": INT8_STEPS, "warmup": INT8_WARMUP,
-                              "hbm_frac_step": round(by8["total"] / (ims / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                              "algorithmic_bytes_per_step": by8["total"], "weight_bytes_per_step": by8["weights"]}
+            byq = decode_bytes(dims, kinds_exec, DECODE_B, (i_start + pos) // 2, int8=bits == 8, int4=bits == 4)
+            decode[f"int{bits}"] = {"metric": f"decode tok/s (weight-only int{bits} projections)",
+                                    "value": round(DECODE_B / (ims / 1e3), 1), "unit": "tok/s",
+                                    "ms_per_step": round(ims, 3), "steps": INT8_STEPS, "warmup": INT8_WARMUP,
+                                    "hbm_frac_step": round(byq["total"] / (ims / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                                    "algorithmic_bytes_per_step": byq["total"],
+                                    "weight_bytes_per_step": byq["weights"]}
 
         # multi-token verify: VERIFY_K drafted tokens per sequence checked in
         # one call (logits and greedy token at every position), continuing

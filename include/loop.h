@@ -271,7 +271,8 @@ int loop_debug_mhc(loop_model* m, float* d_out, void* stream);
  * bf16 matrix; prefill, verify and the head keep bf16.  layers: host
  * [n_layers] (copied); each matrix's codes (int8, the bf16 matrix's shape,
  * row stride = its K) and scales (fp32 [rows]) are device buffers borrowed
- * until the model is destroyed or int8 is turned off.  NULL turns it off.
+ * until the model is destroyed or int8 is turned off.  NULL turns it off
+ * (and so does registering int4 codes).
  * Requires every K (d_model, the mixer widths, d_ff) to be a multiple of 128;
  * decode calls then take at most 64 sequences. */
 typedef struct loop_q8_layer {
@@ -287,6 +288,39 @@ typedef struct loop_q8_layer {
 int loop_quantize_int8(const void* d_w, int64_t N, int64_t K, int64_t ldw, int8_t* d_q, float* d_scale,
                        void* stream);
 int loop_model_set_int8(loop_model* m, const loop_q8_layer* layers);
+
+/* ------------------------------------------------------------ int4 decode
+ * Weight-only INT4 for the decode projections ([P1 section 7] estimates
+ * about 4.5 GB in INT4; the pages give no format).  Group-wise symmetric:
+ * per output row n and group g of 128 consecutive k, scale
+ * s_ng = max |w| over the group / 7 (fp32) and codes q = the nearest integer
+ * to w / s_ng (ties to even; fp32, correctly rounded division) in [-7, 7];
+ * a zero group has s = 0 and q = 0.  The decode projections compute with
+ * the bf16 value nearest to the fp32 product q * s_ng.  Storage: codes + 8
+ * in nibbles, each run of 8 consecutive k in 4 bytes, byte i holding k = i
+ * in its low nibble and k = i + 4 in its high nibble (K / 2 bytes per row);
+ * scales fp32 [N][K / 128].
+ * loop_quantize_int4: codes and scales of one bf16 matrix, on the device.
+ *   d_w bf16 [N][ldw] (device), d_q uint8 [N][K / 2] (device, row stride
+ *   K / 2), d_scale fp32 [N][K / 128] (device).  LOOP_EINVAL for N < 1,
+ *   K < 1 or not a multiple of 128, ldw < K or NULL buffers.
+ * loop_model_set_int4: as loop_model_set_int8, with int4 codes (row stride
+ * K / 2 bytes, 16-byte aligned) and group scales (fp32 [rows][K / 128]).
+ * Registering int4 codes turns int8 off and the reverse; NULL turns int4
+ * off. */
+typedef struct loop_q4_layer {
+  const uint8_t* w_in;
+  const float* s_in;
+  const uint8_t* w_o;
+  const float* s_o;
+  const uint8_t* w_gateup;
+  const float* s_gateup;
+  const uint8_t* w_down;
+  const float* s_down;
+} loop_q4_layer;
+int loop_quantize_int4(const void* d_w, int64_t N, int64_t K, int64_t ldw, uint8_t* d_q, float* d_scale,
+                       void* stream);
+int loop_model_set_int4(loop_model* m, const loop_q4_layer* layers);
 
 const char* loop_last_error(void);
 

@@ -73,6 +73,10 @@ class loop_q8_layer(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("w_in", "s_in", "w_o", "s_o", "w_gateup", "s_gateup", "w_down", "s_down")]
 
 
+class loop_q4_layer(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w_in", "s_in", "w_o", "s_o", "w_gateup", "s_gateup", "w_down", "s_down")]
+
+
 def _load():
     # The library links the HIP runtime that PyTorch-ROCm loads; importing
     # torch first makes that runtime the process's only one.
@@ -99,6 +103,8 @@ def _load():
         "loop_verify_step": (ctypes.c_int, [_vp, P(loop_verify_args), _vp]),
         "loop_model_set_int8": (ctypes.c_int, [_vp, _vp]),
         "loop_quantize_int8": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]),
+        "loop_model_set_int4": (ctypes.c_int, [_vp, _vp]),
+        "loop_quantize_int4": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]),
         "loop_debug_mhc": (ctypes.c_int, [_vp, _vp, _vp]),
         "loop_last_error": (ctypes.c_char_p, []),
         "loop_profile": (ctypes.c_int, [_vp, _i32]),
@@ -119,7 +125,7 @@ _lib = _load()
 EXPORTED = ("loop_kv_bytes", "loop_state_bytes", "loop_arena_bytes", "loop_workspace_bytes",
             "loop_cache_offset", "loop_schedule", "loop_model_create", "loop_model_destroy",
             "loop_prefill", "loop_decode_step", "loop_verify_step", "loop_debug_mhc", "loop_last_error",
-            "loop_model_set_int8", "loop_quantize_int8",
+            "loop_model_set_int8", "loop_quantize_int8", "loop_model_set_int4", "loop_quantize_int4",
             "loop_profile", "loop_profile_read", "loop_op_gemm", "loop_synth_normal",
             "loop_synth_token_ids")
 LOOP_K = dict(gemm_gateup=0, gemm_down=1, gemm_in=2, gemm_o=3, attn_prep=4, flash=5, gdn=6,
@@ -291,6 +297,23 @@ def loop_model_set_int8(model: int, layers) -> None:
         for name, _ in loop_q8_layer._fields_:
             setattr(arr[i], name, d[name])
     _check(_lib.loop_model_set_int8(model, arr))
+
+
+def loop_quantize_int4(d_w: int, N: int, K: int, ldw: int, d_q: int, d_scale: int, stream: int = 0) -> None:
+    _check(_lib.loop_quantize_int4(d_w, N, K, ldw, d_q, d_scale, stream or None))
+
+
+def loop_model_set_int4(model: int, layers) -> None:
+    """layers: list (one per weight layer) of dicts of device pointers with the
+    keys of loop_q4_layer, or None to turn int4 decode off."""
+    if layers is None:
+        _check(_lib.loop_model_set_int4(model, None))
+        return
+    arr = (loop_q4_layer * len(layers))()
+    for i, d in enumerate(layers):
+        for name, _ in loop_q4_layer._fields_:
+            setattr(arr[i], name, d[name])
+    _check(_lib.loop_model_set_int4(model, arr))
 
 
 def loop_debug_mhc(model: int, d_out: int, stream: int = 0) -> None:

@@ -31,7 +31,9 @@ struct GemmArgs {
   int swiglu_F;  // SwiGLU: offset of the up rows in B (= N)
   float* part;   // split-K: fp32 partials [splits][M][N] ([splits][M][2][N] for SwiGLU)
   int kslice;    // split-K: K per split (blockIdx.y)
-  const float* scale = nullptr;  // int8 weights: per-row scale (B is int8 [rows][ldb])
+  const float* scale = nullptr;  // int8 weights: per-row scale (B is int8 [rows][ldb]);
+                                 // int4: [rows][K / 128] group scales (B packed, ldb bytes)
+  uint32_t scale_bytes = 0;      // int4: bytes of the scale array
 };
 
 template <int BM, int BN, int WM, int WN, int EPI, bool SPLIT>
@@ -598,20 +600,42 @@ DEV bf16x8 i8x8_to_bf16(const u32x4& v) {
   return r;
 }
 
-// Q8: int8 weight rows with a per-row scale ([P1 section 7]'s weight-only
-// INT8; codes and scales as the oracle defines them).  Lane group lg then
-// loads bytes 32 lg .. 32 lg + 31 of its row's 128-deep chunk (two 16-byte
-// loads, half the bytes of bf16) and MFMA step q takes the 8 of them at
-// 32 lg + 8 q; the activation operand reads the same k (the reduction order
-// within a chunk is permuted, identically on both operands).  The scale
-// multiplies the row's dot products before the epilogue.  The chunk count
-// needs not be a multiple of the ring depth (chunks past the end are loaded,
-// not multiplied).
-template <int EPI, bool SPLIT, int NW, bool Q8 = false>
+// int4 codes of one group (offset by 8, in nibbles: byte i of each 4-byte
+// word holds k = i low and k = i + 4 high) -> bf16 operand of the bf16 value
+// nearest the float32 product code * s: fma(n, s, -8 s) is that product
+// rounded once (8 s is exact), the conversion rounds it to bf16 (nearest
+// even), as the oracle dequantizes
+DEV bf16x8 i4x8_to_bf16(uint32_t word, float s, float m8s) {
+  const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (bf16)__builtin_fmaf((float)((lo >> (8 * e)) & 0xFFu), s, m8s);
+    r[4 + e] = (bf16)__builtin_fmaf((float)((hi >> (8 * e)) & 0xFFu), s, m8s);
+  }
+  return r;
+}
+
+// QB = 8: int8 weight rows with a per-row scale ([P1 section 7]'s
+// weight-only INT8; codes and scales as the oracle defines them).  Lane group
+// lg then loads bytes 32 lg .. 32 lg + 31 of its row's 128-deep chunk (two
+// 16-byte loads, half the bytes of bf16) and MFMA step q takes the 8 of them
+// at 32 lg + 8 q; the activation operand reads the same k (the reduction
+// order within a chunk is permuted, identically on both operands).  The
+// scale multiplies the row's dot products before the epilogue.
+// QB = 4: int4 codes with one scale per row and 128-deep group (a chunk is
+// one group): lane group lg loads the 16 bytes of k = 32 lg .. 32 lg + 31
+// and the group's scale, and dequantizes to bf16 in registers (same k order
+// as QB = 8).  In both, the chunk count needs not be a multiple of the ring
+// depth (chunks past the end are loaded, not multiplied).
+template <int EPI, bool SPLIT, int NW, int QB = 16>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes) {
   static_assert(NW == 4 || NW == 8, "waves per workgroup");
+  static_assert(QB == 16 || QB == 8 || QB == 4, "weight bits");
+  constexpr bool Q8 = QB == 8, Q4 = QB == 4;
   constexpr int CPW = 16 / NW;  // activation copies per wave per chunk
-  constexpr int WL = Q8 ? 2 : 4;  // weight loads per lane per chunk
+  constexpr int WL = QB == 16 ? 4 : QB == 8 ? 2 : 1;  // 16-byte weight loads per lane per chunk
+  constexpr int WS = Q4 ? 1 : 0;                       // scale loads per lane per chunk
   __shared__ __align__(16) uint8_t sk_smem[SK_NSET * SK_STAGE];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -638,19 +662,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
     const int c = (lane & 15) ^ (row & 15);
     a_off[i] = (min(row, g.M - 1) * (int)g.lda + k0 + c * 8) * 2;
   }
-  const int b_off = Q8 ? wrow * (int)g.ldb + k0 + lg * 32 : (wrow * (int)g.ldb + k0 + lg * 8) * 2;
+  const int b_off = Q4   ? wrow * (int)g.ldb + k0 / 2 + lg * 16
+                    : Q8 ? wrow * (int)g.ldb + k0 + lg * 32
+                         : (wrow * (int)g.ldb + k0 + lg * 8) * 2;
+  const auto s_rsrc = buffer_rsrc(g.scale, g.scale_bytes);
+  const int s_off = Q4 ? (wrow * (g.K / SK_KC) + k0 / SK_KC) * 4 : 0;
 #define SK_COPY(ch_, stage_)                                                                       \
   _Pragma("unroll") for (int i = 0; i < CPW; ++i)                                                  \
       copy16_to_lds(a_rsrc, a_off[i], (ch_) * SK_ROWB,                                             \
                     (lds_void*)(sk_smem + (stage_) * SK_STAGE + (CPW * wave + i) * 1024));
 #define SK_WLOAD(ch_, set_)                                                                        \
   _Pragma("unroll") for (int q = 0; q < WL; ++q) w[set_][q] =                                      \
-      Q8 ? buffer_load16(b_rsrc, b_off + q * 16, (ch_) * SK_KC) : buffer_load16(b_rsrc, b_off + q * 64, (ch_) * SK_ROWB);
+      Q4   ? buffer_load16(b_rsrc, b_off, (ch_) * (SK_KC / 2))                                      \
+      : Q8 ? buffer_load16(b_rsrc, b_off + q * 16, (ch_) * SK_KC)                                   \
+           : buffer_load16(b_rsrc, b_off + q * 64, (ch_) * SK_ROWB);                                \
+  if (Q4) wsc[set_] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_off, (ch_) * 4, 0));
 
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = (f32x4){0, 0, 0, 0};
   u32x4 w[SK_NSET][WL];
+  float wsc[SK_NSET];  // int4: the chunk's group scale
 #pragma unroll
   for (int p = 0; p < SK_NSET - 1; ++p) {
     SK_COPY(min(p, nch - 1), p);
@@ -659,31 +691,34 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
   }
   // Every load is unconditional (past the end the last chunk is loaded again,
   // into the idle stage / registers), so every path has the same loads in
-  // flight and the waits stay exact.  Chunk p's 4 copies are followed by its
-  // 4 weight loads; when chunk c starts, chunks c + 1 and c + 2 (16 loads)
-  // were issued after chunk c's, so vmcnt(16) means chunk c has landed.
+  // flight and the waits stay exact.  Chunk p's CPW copies are followed by
+  // its WL weight loads (and WS scale loads); when chunk c starts, chunks
+  // c + 1 and c + 2 were issued after chunk c's, so a count of twice a
+  // chunk's loads still in flight means chunk c has landed.
   for (int c0 = 0; c0 < nch; c0 += SK_NSET) {
 #pragma unroll
     for (int j = 0; j < SK_NSET; ++j) {
       const int c = c0 + j;
       __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<(CPW + WL) * (SK_NSET - 2)>();
+      wait_vmcnt<(CPW + WL + WS) * (SK_NSET - 2)>();
       lds_barrier();  // chunk c visible; every wave is done with chunk c - 1
       __builtin_amdgcn_sched_barrier(0);
       SK_COPY(min(c + SK_NSET - 1, nch - 1), (j + SK_NSET - 1) % SK_NSET);
       SK_WLOAD(min(c + SK_NSET - 1, nch - 1), (j + SK_NSET - 1) % SK_NSET);
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* st = sk_smem + j * SK_STAGE;
-      if (!Q8 || c < nch) {
+      if (QB == 16 || c < nch) {
+        const float m8s = Q4 ? -8.f * wsc[j] : 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           bf16x8 bfr[4];
-          const int piece = Q8 ? 4 * lg + q : 4 * q + lg;
+          const int piece = QB != 16 ? 4 * lg + q : 4 * q + lg;
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt)
             bfr[mt] = *reinterpret_cast<const bf16x8*>(st + (16 * mt + l16) * SK_ROWB + ((piece ^ l16) << 4));
           bf16x8 wa;
-          if (Q8) wa = (q & 1) ? i8x8_to_bf16<1>(w[j][q >> 1]) : i8x8_to_bf16<0>(w[j][q >> 1]);
+          if (Q4) wa = i4x8_to_bf16(w[j][0][q], wsc[j], m8s);
+          else if (Q8) wa = (q & 1) ? i8x8_to_bf16<1>(w[j][q >> 1]) : i8x8_to_bf16<0>(w[j][q >> 1]);
           else wa = __builtin_bit_cast(bf16x8, w[j][q]);
 #pragma unroll
           for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16x16x32(wa, bfr[mt], acc[mt]);
@@ -901,10 +936,10 @@ hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
   return launch_small<EPI>(g, ws_bytes, s);
 }
 
-// Weight-only int8 (decode, M <= 64): the skinny tiles over int8 rows.
-// Splits as for bf16 (K in 128-deep chunks, any count per split).
-template <int EPI>
-hipError_t launch_q8(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
+// Weight-only int8 / int4 (decode, M <= 64): the skinny tiles over the
+// codes.  Splits as for bf16 (K in 128-deep chunks, any count per split).
+template <int EPI, int QB>
+hipError_t launch_wq(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
   constexpr int NW = SK_WAVES;
   const int per = (EPI == LOOP_EPI_SWIGLU) ? 8 * NW : 16 * NW;
   const int tiles = (g.N + per - 1) / per;
@@ -913,13 +948,13 @@ hipError_t launch_q8(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_b
   const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
   if (splits > 1 && g.part && need <= ws_bytes) {
     g.kslice = g.K / splits;
-    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, NW, true>), dim3(tiles, splits), dim3(64 * NW), 0, s, g, a_bytes,
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, NW, QB>), dim3(tiles, splits), dim3(64 * NW), 0, s, g, a_bytes,
                        b_bytes);
     const int64_t n_out = (int64_t)g.M * g.N;
     const int blocks = (int)std::min<int64_t>((n_out + 255) / 256, 4096);
     hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, splits);
   } else {
-    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, false, NW, true>), dim3(tiles), dim3(64 * NW), 0, s, g, a_bytes,
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, false, NW, QB>), dim3(tiles), dim3(64 * NW), 0, s, g, a_bytes,
                        b_bytes);
   }
   return hipGetLastError();
@@ -946,6 +981,30 @@ __global__ __launch_bounds__(256) void quantize_int8_kernel(const uint16_t* w, i
     const float v = sc > 0.f ? rintf(__fdiv_rn(bf2f(wr[k]), sc)) : 0.f;
     q[n * ldq + k] = (int8_t)fminf(fmaxf(v, -127.f), 127.f);
   }
+}
+
+// per row n and 128-deep group: scale = max |w| / 7, codes = nearest integer
+// to w / scale (ties to even) in [-7, 7], in fp32 with correctly rounded
+// division as the oracle decides them; stored offset by 8 in nibbles, byte
+// i of each 8-k run holding k = i (low) and k = i + 4 (high).  One wave per
+// (row, group): lane l makes byte l of the group's 64.
+__global__ __launch_bounds__(256) void quantize_int4_kernel(const uint16_t* w, int64_t ldw, int64_t N, int G,
+                                                            uint8_t* q, int64_t ldq, float* scale) {
+  const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= N * G) return;  // whole waves
+  const int lane = threadIdx.x & 63;
+  const int64_t n = unit / G;
+  const int grp = (int)(unit % G);
+  const int klo = SK_KC * grp + 8 * (lane >> 2) + (lane & 3);
+  const float vlo = bf2f(w[n * ldw + klo]), vhi = bf2f(w[n * ldw + klo + 4]);
+  float mx = fmaxf(fabsf(vlo), fabsf(vhi));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float sc = __fdiv_rn(mx, 7.0f);
+  const float clo = sc > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(vlo, sc)), -7.f), 7.f) : 0.f;
+  const float chi = sc > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(vhi, sc)), -7.f), 7.f) : 0.f;
+  q[n * ldq + (int64_t)grp * (SK_KC / 2) + lane] = (uint8_t)(((int)clo + 8) | (((int)chi + 8) << 4));
+  if (lane == 0) scale[n * G + grp] = sc;
 }
 
 }  // namespace
@@ -1001,38 +1060,51 @@ hipError_t launch_gemm_norm(const void* A, int64_t lda, const void* B, int64_t l
   return launch_rmsnorm(C, X2, nullptr, ldc, gain, hn, M, N, eps, s);
 }
 
-hipError_t launch_gemm_q8(const void* A, int64_t lda, const int8_t* Bq, int64_t ldb, const float* scale, void* C,
-                          int64_t ldc, const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws,
+static bool wq_args_ok(int bits, int M, int K, int64_t lda, int64_t ldb, const float* scale) {
+  return (bits == 8 || bits == 4) && M >= 1 && M <= 64 && K % SK_KC == 0 && lda % 8 == 0 && ldb % 16 == 0 && scale;
+}
+
+hipError_t launch_gemm_wq(int bits, const void* A, int64_t lda, const void* Bq, int64_t ldb, const float* scale,
+                          void* C, int64_t ldc, const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws,
                           size_t ws_bytes) {
-  if (M < 1 || M > 64 || K % SK_KC || lda % 8 || ldb % 16 || !scale) return hipErrorInvalidValue;
+  if (!wq_args_ok(bits, M, K, lda, ldb, scale)) return hipErrorInvalidValue;
   GemmArgs g{(const uint16_t*)A, lda, (const uint16_t*)Bq, ldb, C, ldc, R, M, N, K, N, ws, K, scale};
   const int64_t rows_b = (epi == LOOP_EPI_SWIGLU) ? 2 * (int64_t)N : N;
   const int64_t a_bytes = (int64_t)M * lda * 2, b_bytes = rows_b * ldb;
-  if (a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31)) return hipErrorInvalidValue;
-  switch (epi) {
-    case LOOP_EPI_BF16: return launch_q8<LOOP_EPI_BF16>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
-    case LOOP_EPI_F32: return launch_q8<LOOP_EPI_F32>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
-    case LOOP_EPI_F32_RES: return launch_q8<LOOP_EPI_F32_RES>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
-    case LOOP_EPI_SWIGLU: return launch_q8<LOOP_EPI_SWIGLU>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
-  }
-  return hipErrorInvalidValue;
+  const int64_t s_bytes = rows_b * (K / SK_KC) * 4;
+  if (a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31) || s_bytes >= (1ll << 31)) return hipErrorInvalidValue;
+  g.scale_bytes = (uint32_t)s_bytes;
+  auto go = [&](auto qb) -> hipError_t {
+    constexpr int QB = decltype(qb)::value;
+    switch (epi) {
+      case LOOP_EPI_BF16: return launch_wq<LOOP_EPI_BF16, QB>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+      case LOOP_EPI_F32: return launch_wq<LOOP_EPI_F32, QB>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+      case LOOP_EPI_F32_RES:
+        return launch_wq<LOOP_EPI_F32_RES, QB>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+      case LOOP_EPI_SWIGLU: return launch_wq<LOOP_EPI_SWIGLU, QB>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+    }
+    return hipErrorInvalidValue;
+  };
+  return bits == 8 ? go(std::integral_constant<int, 8>()) : go(std::integral_constant<int, 4>());
 }
 
-hipError_t launch_gemm_norm_q8(const void* A, int64_t lda, const int8_t* Bq, int64_t ldb, const float* scale,
+hipError_t launch_gemm_norm_wq(int bits, const void* A, int64_t lda, const void* Bq, int64_t ldb, const float* scale,
                                float* C, int64_t ldc, const float* R, const float* X2, const void* gain, void* hn,
                                float eps, int M, int N, int K, hipStream_t s, float* ws, size_t ws_bytes) {
-  if (M < 1 || M > 64 || K % SK_KC || lda % 8 || ldb % 16 || !scale) return hipErrorInvalidValue;
+  if (!wq_args_ok(bits, M, K, lda, ldb, scale)) return hipErrorInvalidValue;
   GemmArgs g{(const uint16_t*)A, lda, (const uint16_t*)Bq, ldb, C, ldc, R, M, N, K, N, ws, K, scale};
-  const int64_t a_bytes = (int64_t)M * lda * 2, b_bytes = (int64_t)N * ldb;
-  if (a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31)) return hipErrorInvalidValue;
+  const int64_t a_bytes = (int64_t)M * lda * 2, b_bytes = (int64_t)N * ldb, s_bytes = (int64_t)N * (K / SK_KC) * 4;
+  if (a_bytes >= (1ll << 31) || b_bytes >= (1ll << 31) || s_bytes >= (1ll << 31)) return hipErrorInvalidValue;
+  g.scale_bytes = (uint32_t)s_bytes;
   const int tiles = (N + 16 * SK_WAVES - 1) / (16 * SK_WAVES);
   int splits = 1;
   while (tiles * splits < 256 && splits < 8 && K % (SK_KC * splits * 2) == 0 && K / (splits * 2) >= 512) splits *= 2;
   if (N <= 4096 && splits > 1 && ws && (size_t)splits * M * N * sizeof(float) <= ws_bytes) {
     g.kslice = K / splits;
-    auto launch = [&](auto epi_tag) {
+    auto launch = [&](auto epi_tag, auto qb) {
       constexpr int EPI = decltype(epi_tag)::value;
-      hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, SK_WAVES, true>), dim3(tiles, splits), dim3(64 * SK_WAVES), 0,
+      constexpr int QB = decltype(qb)::value;
+      hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, SK_WAVES, QB>), dim3(tiles, splits), dim3(64 * SK_WAVES), 0,
                          s, g, (uint32_t)a_bytes, (uint32_t)b_bytes);
       if (splits == 4)
         hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 4>), dim3(M), dim3(1024), 0, s, g, X2,
@@ -1044,12 +1116,19 @@ hipError_t launch_gemm_norm_q8(const void* A, int64_t lda, const int8_t* Bq, int
         hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 8>), dim3(M), dim3(1024), 0, s, g, X2,
                            (const uint16_t*)gain, (uint16_t*)hn, eps);
     };
-    if (R) launch(std::integral_constant<int, LOOP_EPI_F32_RES>());
-    else launch(std::integral_constant<int, LOOP_EPI_F32>());
+    const auto res = std::integral_constant<int, LOOP_EPI_F32_RES>();
+    const auto plain = std::integral_constant<int, LOOP_EPI_F32>();
+    if (bits == 8) {
+      if (R) launch(res, std::integral_constant<int, 8>());
+      else launch(plain, std::integral_constant<int, 8>());
+    } else {
+      if (R) launch(res, std::integral_constant<int, 4>());
+      else launch(plain, std::integral_constant<int, 4>());
+    }
     return hipGetLastError();
   }
-  hipError_t e = launch_gemm_q8(A, lda, Bq, ldb, scale, C, ldc, R, M, N, K, R ? LOOP_EPI_F32_RES : LOOP_EPI_F32, s, ws,
-                                ws_bytes);
+  hipError_t e = launch_gemm_wq(bits, A, lda, Bq, ldb, scale, C, ldc, R, M, N, K, R ? LOOP_EPI_F32_RES : LOOP_EPI_F32,
+                                s, ws, ws_bytes);
   if (e != hipSuccess) return e;
   return launch_rmsnorm(C, X2, nullptr, ldc, gain, hn, M, N, eps, s);
 }
@@ -1059,5 +1138,15 @@ hipError_t launch_quantize_int8(const void* w, int64_t ldw, int64_t N, int K, in
   if (N <= 0 || K <= 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_int8_kernel, dim3((unsigned)N), dim3(256), 0, s, (const uint16_t*)w, ldw, K, q, ldq,
                      scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_int4(const void* w, int64_t ldw, int64_t N, int K, uint8_t* q, int64_t ldq, float* scale,
+                                hipStream_t s) {
+  if (N <= 0 || K <= 0) return hipSuccess;
+  if (K % SK_KC) return hipErrorInvalidValue;
+  const int64_t units = N * (K / SK_KC);
+  hipLaunchKernelGGL(quantize_int4_kernel, dim3((unsigned)((units + 3) / 4)), dim3(256), 0, s, (const uint16_t*)w,
+                     ldw, N, K / SK_KC, q, ldq, scale);
   return hipGetLastError();
 }

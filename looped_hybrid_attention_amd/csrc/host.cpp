@@ -182,6 +182,16 @@ extern "C" int loop_quantize_int8(const void* d_w, int64_t N, int64_t K, int64_t
   return e == hipSuccess ? 0 : loop_hip_fail(e, "quantize_int8");
 }
 
+extern "C" int loop_quantize_int4(const void* d_w, int64_t N, int64_t K, int64_t ldw, uint8_t* d_q, float* d_scale,
+                                  void* stream) {
+  if (!d_w || !d_q || !d_scale) return loop_fail(LOOP_EINVAL, "quantize: NULL buffer");
+  if (N < 1 || K < 1 || K % 128 || ldw < K || K > (1 << 30) || N > (1ll << 31))
+    return loop_fail(LOOP_EINVAL, "quantize_int4: bad shape N %lld K %lld ldw %lld (K a multiple of 128)",
+                     (long long)N, (long long)K, (long long)ldw);
+  hipError_t e = launch_quantize_int4(d_w, ldw, N, (int)K, d_q, K / 2, d_scale, (hipStream_t)stream);
+  return e == hipSuccess ? 0 : loop_hip_fail(e, "quantize_int4");
+}
+
 extern "C" int loop_synth_token_ids(int32_t* dst, int64_t n, uint32_t vocab, uint32_t seed,
                                     uint32_t key, void* stream) {
   if (!dst && n > 0) return loop_fail(LOOP_EINVAL, "synth: null destination");

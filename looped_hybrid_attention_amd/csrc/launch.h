@@ -15,14 +15,18 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, v
 // C = A . B^T (+ R) as launch_gemm (fp32 output), then
 // hn[m] = bf16(RMSNorm(C[m] + X2[m]; gain)) (X2 may be NULL; rows of C and
 // X2 share the stride ldc; hn rows are N apart).
-// Weight-only int8 projections for decode rows (M <= 64): B is int8 [rows][ldb]
-// with a per-row fp32 scale; K a multiple of 128, ldb of 16, lda of 8.
-hipError_t launch_gemm_q8(const void* A, int64_t lda, const int8_t* Bq, int64_t ldb, const float* scale, void* C,
-                          int64_t ldc, const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws,
+// Weight-only projections for decode rows (M <= 64), bits = 8: B is int8
+// [rows][ldb] with a per-row fp32 scale; bits = 4: B is packed int4 codes
+// (ldb bytes per row) with fp32 scales [rows][K / 128].  K a multiple of 128,
+// ldb of 16, lda of 8.
+hipError_t launch_gemm_wq(int bits, const void* A, int64_t lda, const void* Bq, int64_t ldb, const float* scale,
+                          void* C, int64_t ldc, const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws,
                           size_t ws_bytes);
-hipError_t launch_gemm_norm_q8(const void* A, int64_t lda, const int8_t* Bq, int64_t ldb, const float* scale,
+hipError_t launch_gemm_norm_wq(int bits, const void* A, int64_t lda, const void* Bq, int64_t ldb, const float* scale,
                                float* C, int64_t ldc, const float* R, const float* X2, const void* gain, void* hn,
                                float eps, int M, int N, int K, hipStream_t s, float* ws, size_t ws_bytes);
+hipError_t launch_quantize_int4(const void* w, int64_t ldw, int64_t N, int K, uint8_t* q, int64_t ldq, float* scale,
+                                hipStream_t s);
 hipError_t launch_quantize_int8(const void* w, int64_t ldw, int64_t N, int K, int8_t* q, int64_t ldq, float* scale,
                                 hipStream_t s);
 hipError_t launch_gemm_norm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,

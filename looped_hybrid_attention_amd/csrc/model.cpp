@@ -121,8 +121,10 @@ struct loop_model {
   // pass count each sequence slot was started with (0: not started by a
   // prefill from position 0 here)
   std::vector<int32_t> slot_passes;
-  // int8 codes of the layer projections for decode steps (empty: bf16)
+  // int8 or int4 codes of the layer projections for decode steps (both
+  // empty: bf16; at most one of them is set)
   std::vector<loop_q8_layer> q8;
+  std::vector<loop_q4_layer> q4;
   std::vector<int32_t> meta_host;
   // kernel-class timing
   int prof_class = -1;
@@ -305,12 +307,29 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   const int n_in = d.full ? n_in_full(c) : n_in_gdn(c);
 #define SK at<float>(m, L.splitk), L.splitk_bytes
 
-  // decode steps with int8 codes registered use them for the four projections
-  const loop_q8_layer* q8 = (k.decode && !m->q8.empty()) ? &m->q8[d.layer] : nullptr;
+  // decode steps with int8 or int4 codes registered use them for the four
+  // projections (ldq: bytes per code row of a K-deep matrix)
+  struct QW {
+    int bits;
+    const void *w_in, *w_o, *w_gateup, *w_down;
+    const float *s_in, *s_o, *s_gateup, *s_down;
+  } qw{};
+  const QW* q8 = nullptr;
+  if (k.decode && !m->q8.empty()) {
+    const loop_q8_layer& q = m->q8[d.layer];
+    qw = {8, q.w_in, q.w_o, q.w_gateup, q.w_down, q.s_in, q.s_o, q.s_gateup, q.s_down};
+    q8 = &qw;
+  } else if (k.decode && !m->q4.empty()) {
+    const loop_q4_layer& q = m->q4[d.layer];
+    qw = {4, q.w_in, q.w_o, q.w_gateup, q.w_down, q.s_in, q.s_o, q.s_gateup, q.s_down};
+    q8 = &qw;
+  }
+  auto ldq = [&](int K) -> int64_t { return qw.bits == 8 ? K : K / 2; };
   {
     Prof p(m, LOOP_K_GEMM_IN, s);
     if (q8)
-      HIP_TRY(launch_gemm_q8(xn, dm, q8->w_in, dm, q8->s_in, proj, L.n_in_max, nullptr, M, n_in, dm, LOOP_EPI_BF16, s, SK));
+      HIP_TRY(launch_gemm_wq(q8->bits, xn, dm, q8->w_in, ldq(dm), q8->s_in, proj, L.n_in_max, nullptr, M, n_in, dm,
+                             LOOP_EPI_BF16, s, SK));
     else
       HIP_TRY(launch_gemm(xn, dm, w.w_in, dm, proj, L.n_in_max, nullptr, M, n_in, dm, LOOP_EPI_BF16, s, SK));
   }
@@ -384,11 +403,11 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
     // RMSNorm(hmid); loop a = o W_o^T, hn = RMSNorm(x + a)
     Prof p(m, LOOP_K_GEMM_O, s);
     if (q8 && !d.loop)
-      HIP_TRY(launch_gemm_norm_q8(obuf, mix_width, q8->w_o, mix_width, q8->s_o, hmid, dm, h, nullptr, w.ffn_norm, hn,
-                                  c.eps, M, dm, mix_width, s, SK));
+      HIP_TRY(launch_gemm_norm_wq(q8->bits, obuf, mix_width, q8->w_o, ldq(mix_width), q8->s_o, hmid, dm, h, nullptr,
+                                  w.ffn_norm, hn, c.eps, M, dm, mix_width, s, SK));
     else if (q8)
-      HIP_TRY(launch_gemm_norm_q8(obuf, mix_width, q8->w_o, mix_width, q8->s_o, a, dm, nullptr, x, w.ffn_norm, hn,
-                                  c.eps, M, dm, mix_width, s, SK));
+      HIP_TRY(launch_gemm_norm_wq(q8->bits, obuf, mix_width, q8->w_o, ldq(mix_width), q8->s_o, a, dm, nullptr, x,
+                                  w.ffn_norm, hn, c.eps, M, dm, mix_width, s, SK));
     else if (!d.loop)
       HIP_TRY(launch_gemm_norm(obuf, mix_width, w.w_o, mix_width, hmid, dm, h, nullptr, w.ffn_norm, hn, c.eps, M, dm,
                                mix_width, s, SK));
@@ -399,8 +418,8 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   {
     Prof p(m, LOOP_K_GEMM_GATEUP, s);
     if (q8)
-      HIP_TRY(launch_gemm_q8(hn, dm, q8->w_gateup, dm, q8->s_gateup, act, c.d_ff, nullptr, M, c.d_ff, dm,
-                             LOOP_EPI_SWIGLU, s, SK));
+      HIP_TRY(launch_gemm_wq(q8->bits, hn, dm, q8->w_gateup, ldq(dm), q8->s_gateup, act, c.d_ff, nullptr, M, c.d_ff,
+                             dm, LOOP_EPI_SWIGLU, s, SK));
     else
       HIP_TRY(launch_gemm(hn, dm, w.w_gateup, dm, act, c.d_ff, nullptr, M, c.d_ff, dm, LOOP_EPI_SWIGLU, s, SK));
   }
@@ -409,8 +428,8 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
     float* dst = d.loop ? a : h;
     const float* res = d.loop ? a : hmid;
     if (q8)
-      HIP_TRY(launch_gemm_q8(act, c.d_ff, q8->w_down, c.d_ff, q8->s_down, dst, dm, res, M, dm, c.d_ff,
-                             LOOP_EPI_F32_RES, s, SK));
+      HIP_TRY(launch_gemm_wq(q8->bits, act, c.d_ff, q8->w_down, ldq(c.d_ff), q8->s_down, dst, dm, res, M, dm,
+                             c.d_ff, LOOP_EPI_F32_RES, s, SK));
     else
       HIP_TRY(launch_gemm(act, c.d_ff, w.w_down, c.d_ff, dst, dm, res, M, dm, c.d_ff, LOOP_EPI_F32_RES, s, SK));
   }
@@ -607,7 +626,8 @@ extern "C" int loop_decode_step(loop_model* m, const loop_decode_args* a, void* 
   const loop_config& c = m->cfg;
   const int B = a->batch;
   if (B < 1 || B > c.max_batch || B > c.max_tokens) return loop_fail(LOOP_ECAPACITY, "batch %d out of range", B);
-  if (!m->q8.empty() && B > 64) return loop_fail(LOOP_ECAPACITY, "int8 decode takes at most 64 sequences per call");
+  if ((!m->q8.empty() || !m->q4.empty()) && B > 64)
+    return loop_fail(LOOP_ECAPACITY, "int8 / int4 decode takes at most 64 sequences per call");
   if (c.vocab == 0) return loop_fail(LOOP_EINVAL, "decode needs vocab > 0");
   if (!a->d_tokens || !a->pos) return loop_fail(LOOP_EINVAL, "d_tokens and pos are required");
   if (int r = check_slots(c, B, a->slots)) return r;
@@ -699,6 +719,31 @@ extern "C" int loop_model_set_int8(loop_model* m, const loop_q8_layer* layers) {
       return loop_fail(LOOP_EINVAL, "int8 codes of layer %d must be 16-byte aligned", l);
   }
   m->q8.assign(layers, layers + c.n_layers);
+  m->q4.clear();
+  return 0;
+}
+
+extern "C" int loop_model_set_int4(loop_model* m, const loop_q4_layer* layers) {
+  if (!m) return loop_fail(LOOP_EINVAL, "model NULL");
+  const loop_config& c = m->cfg;
+  if (!layers) {
+    m->q4.clear();
+    return 0;
+  }
+  const int mix_full = c.n_q_heads * c.head_dim, mix_gdn = c.gdn_heads * c.gdn_dv;
+  if (c.d_model % 128 || mix_full % 128 || mix_gdn % 128 || c.d_ff % 128)
+    return loop_fail(LOOP_ESHAPE, "int4 decode needs d_model, the mixer widths and d_ff multiples of 128");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const loop_q4_layer& q = layers[l];
+    if (!q.w_in || !q.s_in || !q.w_o || !q.s_o || !q.w_gateup || !q.s_gateup || !q.w_down || !q.s_down)
+      return loop_fail(LOOP_EINVAL, "int4 layer %d misses codes or scales", l);
+    if (((uintptr_t)q.w_in | (uintptr_t)q.w_o | (uintptr_t)q.w_gateup | (uintptr_t)q.w_down) % 16)
+      return loop_fail(LOOP_EINVAL, "int4 codes of layer %d must be 16-byte aligned", l);
+    if (((uintptr_t)q.s_in | (uintptr_t)q.s_o | (uintptr_t)q.s_gateup | (uintptr_t)q.s_down) % 4)
+      return loop_fail(LOOP_EINVAL, "int4 scales of layer %d must be 4-byte aligned", l);
+  }
+  m->q4.assign(layers, layers + c.n_layers);
+  m->q8.clear();
   return 0;
 }
 

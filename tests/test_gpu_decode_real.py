@@ -26,7 +26,8 @@ Then the same step again (GDN states regenerated, the appended position
 rewritten) with the weight-only int8 codes of every projection registered:
 the batch-64 int8 projections with split K (the in / gate-up / down
 widths, and the O-projection's split sum fused with the FFN pre-norm),
-against the oracle decoding with the dequantized codes, 2 sampled sequences.
+against the oracle decoding with the dequantized codes, 2 sampled sequences;
+then once more with the int4 group codes (2 other sampled sequences).
 """
 import numpy as np
 import pytest
@@ -37,7 +38,7 @@ from oracle import model as om
 from gpu_util import torch_cuda, dev, host, say, rel_err
 from model_util import GpuModel
 from parity import bar as parity_bar, argmax_ok
-from oracle.quant import int8_decode_weights
+from oracle.quant import int8_decode_weights, int4_decode_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -152,6 +153,37 @@ def test_decode_b64_ctx32768_group():
             tol_h = parity_bar([e[1] for e in evals])
             el, eh = rel_err(got_l[b], evals[0][0]), rel_err(got_h[b], evals[0][1])
             print("int8 decode seq %d: logits %.4f (bar %.4f), hidden %.4f (bar %.4f)" % (b, el, tol_l, eh, tol_h))
+            assert el <= tol_l and eh <= tol_h, b
+            assert argmax_ok(int(got_n[b]), evals[0][0], tol_l), b
+        del Q32, Q64
+
+        # --- the same step with int4 projections
+        from test_gpu_int4 import device_int4
+        for j in range(n_gdn):
+            L.loop_synth_normal(g.arena.data_ptr() + L.loop_cache_offset(cfg, 2, j, 0), st_n, 0,
+                                synth.SEED_C, synth.fnv1a32(f"test.decode.state.{j}"), 0, 0.1, 0.0, s)
+        layers, keep = device_int4(torch, L, g, dims["n_layers"], s)
+        L.loop_model_set_int4(g.handle, layers)
+        say("decode b64 ctx32768 group, int4 projections")
+        L.loop_decode_step(g.handle, B, list(range(B)), [CTX] * B, d_ids.data_ptr(), d_logits=logits.data_ptr(),
+                           d_next=nxt.data_ptr(), d_hidden_out=hid.data_ptr(), stream=s)
+        torch.cuda.synchronize()
+        got_l, got_h, got_n = host(logits), host(hid), host(nxt)
+        L.loop_model_set_int4(g.handle, None)
+        del keep
+        Q32 = int4_decode_weights(W32, dims["n_layers"], np.float32)
+        Q64 = int4_decode_weights(W32, dims["n_layers"], np.float64)
+        for b in SAMPLE[1:]:
+            say("int4 decode oracle seq", b)
+            evals = []
+            for W, dt in ((Q32, np.float32), (Q64, np.float64)):
+                st = state_of(b, dt)
+                lg, nx, h = om.decode_step(ocfg, W, [st], [int(ids[b])], bf16=True)
+                evals.append((lg[0], h[0]))
+            tol_l = parity_bar([e[0] for e in evals])
+            tol_h = parity_bar([e[1] for e in evals])
+            el, eh = rel_err(got_l[b], evals[0][0]), rel_err(got_h[b], evals[0][1])
+            print("int4 decode seq %d: logits %.4f (bar %.4f), hidden %.4f (bar %.4f)" % (b, el, tol_l, eh, tol_h))
             assert el <= tol_l and eh <= tol_h, b
             assert argmax_ok(int(got_n[b]), evals[0][0], tol_l), b
     finally:
