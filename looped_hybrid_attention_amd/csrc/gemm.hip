@@ -606,7 +606,10 @@ DEV bf16x8 i8x8_to_bf16(const u32x4& v) {
 // rounded once (8 s is exact), the conversion rounds it to bf16 (nearest
 // even), as the oracle dequantizes
 DEV bf16x8 i4x8_to_bf16(uint32_t word, float s, float m8s) {
-  const uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+  uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+  // hide the masks' known zero bits so that each byte converts with one
+  // v_cvt_f32_ubyteN (otherwise the shift and mask are kept per element)
+  asm("" : "+v"(lo), "+v"(hi));
   bf16x8 r;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -938,6 +941,9 @@ hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
 
 // Weight-only int8 / int4 (decode, M <= 64): the skinny tiles over the
 // codes.  Splits as for bf16 (K in 128-deep chunks, any count per split).
+// Measured: twice the workgroups (two per CU) is no faster; with the
+// weights 2-4x smaller, each chunk's activation reads from LDS (16 KB per
+// wave) and its M = 64 MFMAs, not the weight stream, set the time.
 template <int EPI, int QB>
 hipError_t launch_wq(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
   constexpr int NW = SK_WAVES;
