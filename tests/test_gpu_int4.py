@@ -14,6 +14,9 @@
   oracle is closer to the int4 run than the bf16 oracle is.  Registering
   int8 codes afterwards replaces the int4 ones (the next step matches the
   int8 oracle); turning int8 off returns to bf16.
+- A ragged batch (37 sequences, so the tiles' clamped activation rows and
+  guarded stores run) from seeded caches: one int4 step, one int8 step,
+  sampled sequences against the oracle.
 The real-width, split-K variants of the int4 projections are checked in the
 batch-64 decode test at 32K context.
 """
@@ -172,5 +175,89 @@ def test_int4_decode_tiny():
                 assert el < eb, step
             tok = int(o32[1][0])
         del keep, keep8
+    finally:
+        g.close()
+
+
+def test_quantized_decode_ragged_batch():
+    """37 sequences (a ragged M for the weight-streaming tiles) of the tiny
+    model from seeded caches, one decode step with int4 codes, then (GDN
+    states regenerated, the appended position rewritten) one with int8
+    codes; sampled sequences against the oracle in fp32 and fp64."""
+    torch = torch_cuda()
+    dims = synth.preset("tiny")
+    B, max_seq, T = 37, 512, 200
+    g = GpuModel(torch, dims, max_batch=B, max_seq=max_seq, max_tokens=512)
+    try:
+        L, cfg, s = g.L, g.cfg, g.stream()
+        V, d = dims["vocab"], dims["d_model"]
+        rows = L.loop_schedule(cfg)
+        n_full = sum(r[1] for r in rows)
+        n_gdn = len(rows) - n_full
+        Hkv, D = dims["n_kv_heads"], dims["head_dim"]
+        H, Dk, Dv = dims["gdn_heads"], dims["gdn_dk"], dims["gdn_dv"]
+        per, per_s = Hkv * max_seq * D, H * Dv * Dk
+        for f in range(n_full):
+            for which, name in ((0, f"rag.q.k.{f}"), (1, f"rag.q.v.{f}")):
+                L.loop_synth_normal(g.arena.data_ptr() + L.loop_cache_offset(cfg, which, f, 0), B * per, 1,
+                                    synth.SEED_C, synth.fnv1a32(name), 0, 1.0, 0.0, s)
+
+        def fill_states():
+            for j in range(n_gdn):
+                L.loop_synth_normal(g.arena.data_ptr() + L.loop_cache_offset(cfg, 2, j, 0), B * per_s, 0,
+                                    synth.SEED_C, synth.fnv1a32(f"rag.q.state.{j}"), 0, 0.1, 0.0, s)
+
+        def state_of(b, dtype):
+            st = om.SeqState(om_cfg, dtype)
+            for f in range(n_full):
+                kb = synth.normal(synth.SEED_C, f"rag.q.k.{f}", (per,), 1.0, dtype="bf16", start=b * per)
+                vb = synth.normal(synth.SEED_C, f"rag.q.v.{f}", (per,), 1.0, dtype="bf16", start=b * per)
+                K = synth.bf16_bits_to_f32(kb).reshape(Hkv, max_seq, D)[:, :T]
+                Vb = synth.bf16_bits_to_f32(vb).reshape(Hkv, max_seq // 32, D, 32)
+                st.kv[f].k = np.ascontiguousarray(K, dtype)
+                st.kv[f].v = np.ascontiguousarray(Vb.transpose(0, 1, 3, 2).reshape(Hkv, max_seq, D)[:, :T], dtype)
+            for j in range(n_gdn):
+                S = synth.normal(synth.SEED_C, f"rag.q.state.{j}", (per_s,), 0.1, start=b * per_s)
+                st.S[j] = S.reshape(H, Dv, Dk).astype(dtype)
+            st.length = T
+            return st
+
+        om_cfg = oracle.Config.from_dims(dims)
+        W32 = om.to_dtype(g.host_weights, np.float32)
+        nl = dims["n_layers"]
+        ids = synth.token_ids(synth.SEED_X, "rag.q.ids", B, V)
+        d_ids = dev(ids, torch)
+        logits = torch.zeros((B, V), dtype=torch.float32, device="cuda")
+        hid = torch.zeros((B, d), dtype=torch.float32, device="cuda")
+        nxt = torch.zeros(B, dtype=torch.int32, device="cuda")
+        for bits in (4, 8):
+            fill_states()
+            if bits == 4:
+                layers, keep = device_int4(torch, L, g, nl, s)
+                L.loop_model_set_int4(g.handle, layers)
+                Wq = {dt: int4_decode_weights(W32, nl, dt) for dt in (np.float32, np.float64)}
+            else:
+                layers, keep = device_int8(torch, L, g, nl, s)
+                L.loop_model_set_int8(g.handle, layers)
+                Wq = {dt: int8_decode_weights(W32, nl, dt) for dt in (np.float32, np.float64)}
+            say("ragged batch decode, int%d" % bits)
+            L.loop_decode_step(g.handle, B, list(range(B)), [T] * B, d_ids.data_ptr(), d_logits=logits.data_ptr(),
+                               d_next=nxt.data_ptr(), d_hidden_out=hid.data_ptr(), stream=s)
+            torch.cuda.synchronize()
+            got_l, got_h, got_n = host(logits), host(hid), host(nxt)
+            L.loop_model_set_int4(g.handle, None)
+            L.loop_model_set_int8(g.handle, None)
+            del keep
+            for b in (0, 17, 36):
+                outs = []
+                for dt in (np.float32, np.float64):
+                    st = state_of(b, dt)
+                    outs.append(om.decode_step(om_cfg, Wq[dt], [st], [int(ids[b])], bf16=True))
+                tol_l, tol_h = bar([o[0][0] for o in outs]), bar([o[2][0] for o in outs])
+                el, eh = rel_err(got_l[b], outs[0][0][0]), rel_err(got_h[b], outs[0][2][0])
+                print("int%d ragged seq %d: logits %.4f (bar %.4f), hidden %.4f (bar %.4f)"
+                      % (bits, b, el, tol_l, eh, tol_h))
+                assert el <= tol_l and eh <= tol_h, (bits, b)
+                assert argmax_ok(int(got_n[b]), outs[0][0][0], tol_l), (bits, b)
     finally:
         g.close()
