@@ -84,6 +84,7 @@ def parse():
     p.add_argument("--no-verify", action="store_true", help="skip the multi-token verify step")
     p.add_argument("--no-int8", action="store_true", help="skip the weight-only int8 decode")
     p.add_argument("--no-int4", action="store_true", help="skip the weight-only int4 decode")
+    p.add_argument("--no-b1", action="store_true", help="skip the batch-1 decode (bf16 / int8 / int4)")
     p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return p.parse_args()
 
@@ -153,7 +154,7 @@ def main():
 
     dims = synth.preset("full")
     max_seq = ((DECODE_CTX + args.decode_warmup + args.decode_steps + 1 + VERIFY_K * (VERIFY_STEPS + 1)
-                + 2 * (INT8_STEPS + INT8_WARMUP) + 63) // 64) * 64
+                + 5 * (INT8_STEPS + INT8_WARMUP) + 63) // 64) * 64
     cfg = L.make_config(dims, max_batch=DECODE_B, max_seq=max_seq, max_tokens=PREFILL_T)
     sched = L.loop_schedule(cfg)
     kinds_layer = {}
@@ -294,9 +295,9 @@ def main():
         # weight-only int8 and int4 decode: codes of every layer's four
         # projections, quantized on the device, then the same decode batch
         # continues (INT8_STEPS timed steps each)
-        for bits in (8, 4):
-            if (bits == 8 and args.no_int8) or (bits == 4 and args.no_int4):
-                continue
+        def quant_layers(bits):
+            """Codes and scales of every layer's four projections, quantized
+            on the device: (pointer dicts, keep-alive list)."""
             q_keep, q_layers = [], []
             short = {"w_in": "in", "w_o": "o", "w_gateup": "gateup", "w_down": "down"}
             for l in range(dims["n_layers"]):
@@ -315,6 +316,12 @@ def main():
                     q_keep += [q, sc]
                     dq["w_" + short[nm]], dq["s_" + short[nm]] = q.data_ptr(), sc.data_ptr()
                 q_layers.append(dq)
+            return q_layers, q_keep
+
+        for bits in (8, 4):
+            if (bits == 8 and args.no_int8) or (bits == 4 and args.no_int4):
+                continue
+            q_layers, q_keep = quant_layers(bits)
             set_q = L.loop_model_set_int8 if bits == 8 else L.loop_model_set_int4
             set_q(model, q_layers)
             for _ in range(INT8_WARMUP):
@@ -339,6 +346,46 @@ def main():
                                     "hbm_frac_step": round(byq["total"] / (ims / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
                                     "algorithmic_bytes_per_step": byq["total"],
                                     "weight_bytes_per_step": byq["weights"]}
+
+        # batch-1 decode: sequence slot 0 alone at the same context, with the
+        # bf16 matrices, then int8, then int4 codes (weights dominate the step)
+        if not args.no_b1:
+            tok1 = tok[:1].clone()
+            nxt1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+            p1 = pos
+            b1 = {"metric": "decode tok/s at batch 1", "unit": "tok/s", "context": p1, "steps": INT8_STEPS,
+                  "warmup": INT8_WARMUP}
+            for bits in (16, 8, 4):
+                keep = None
+                if bits == 8:
+                    layers, keep = quant_layers(8)
+                    L.loop_model_set_int8(model, layers)
+                elif bits == 4:
+                    layers, keep = quant_layers(4)
+                    L.loop_model_set_int4(model, layers)
+                for _ in range(INT8_WARMUP):
+                    L.loop_decode_step(model, 1, [0], [p1], tok1.data_ptr(), d_next=nxt1.data_ptr(), stream=stream)
+                    tok1.copy_(nxt1)
+                    p1 += 1
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(INT8_STEPS):
+                    L.loop_decode_step(model, 1, [0], [p1], tok1.data_ptr(), d_next=nxt1.data_ptr(), stream=stream)
+                    tok1.copy_(nxt1)
+                    p1 += 1
+                e1.record()
+                torch.cuda.synchronize()
+                L.loop_model_set_int8(model, None)
+                L.loop_model_set_int4(model, None)
+                del keep
+                ms1 = e0.elapsed_time(e1) / INT8_STEPS
+                by1 = decode_bytes(dims, kinds_exec, 1, p1 - INT8_STEPS // 2, int8=bits == 8, int4=bits == 4)
+                b1["bf16" if bits == 16 else f"int{bits}"] = {
+                    "value": round(1e3 / ms1, 1), "ms_per_step": round(ms1, 3),
+                    "hbm_frac_step": round(by1["total"] / (ms1 / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+                    "algorithmic_bytes_per_step": by1["total"]}
+            decode["b1"] = b1
 
         # multi-token verify: VERIFY_K drafted tokens per sequence checked in
         # one call (logits and greedy token at every position), continuing

@@ -631,10 +631,13 @@ DEV bf16x8 i4x8_to_bf16(uint32_t word, float s, float m8s) {
 // and the group's scale, and dequantizes to bf16 in registers (same k order
 // as QB = 8).  In both, the chunk count needs not be a multiple of the ring
 // depth (chunks past the end are loaded, not multiplied).
-template <int EPI, bool SPLIT, int NW, int QB = 16>
+// MT: 16-row tiles of activations multiplied (M <= 16 MT); the copies still
+// fill all 64 rows (clamped), so every wave's load count stays the same.
+template <int EPI, bool SPLIT, int NW, int QB = 16, int MT = 4>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g, uint32_t a_bytes, uint32_t b_bytes) {
   static_assert(NW == 4 || NW == 8, "waves per workgroup");
   static_assert(QB == 16 || QB == 8 || QB == 4, "weight bits");
+  static_assert(MT >= 1 && MT <= 4, "activation row tiles");
   constexpr bool Q8 = QB == 8, Q4 = QB == 4;
   constexpr int CPW = 16 / NW;  // activation copies per wave per chunk
   constexpr int WL = QB == 16 ? 4 : QB == 8 ? 2 : 1;  // 16-byte weight loads per lane per chunk
@@ -681,9 +684,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
            : buffer_load16(b_rsrc, b_off + q * 64, (ch_) * SK_ROWB);                                \
   if (Q4) wsc[set_] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(s_rsrc, s_off, (ch_) * 4, 0));
 
-  f32x4 acc[4];
+  f32x4 acc[MT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = (f32x4){0, 0, 0, 0};
+  for (int i = 0; i < MT; ++i) acc[i] = (f32x4){0, 0, 0, 0};
   u32x4 w[SK_NSET][WL];
   float wsc[SK_NSET];  // int4: the chunk's group scale
 #pragma unroll
@@ -714,17 +717,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
         const float m8s = Q4 ? -8.f * wsc[j] : 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          bf16x8 bfr[4];
+          bf16x8 bfr[MT];
           const int piece = QB != 16 ? 4 * lg + q : 4 * q + lg;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < MT; ++mt)
             bfr[mt] = *reinterpret_cast<const bf16x8*>(st + (16 * mt + l16) * SK_ROWB + ((piece ^ l16) << 4));
           bf16x8 wa;
           if (Q4) wa = i4x8_to_bf16(w[j][0][q], wsc[j], m8s);
           else if (Q8) wa = (q & 1) ? i8x8_to_bf16<1>(w[j][q >> 1]) : i8x8_to_bf16<0>(w[j][q >> 1]);
           else wa = __builtin_bit_cast(bf16x8, w[j][q]);
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma16x16x32(wa, bfr[mt], acc[mt]);
+          for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16x16x32(wa, bfr[mt], acc[mt]);
         }
       }
     }
@@ -745,22 +748,22 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
       }
       const float sc = g.scale[row];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt][r] *= sc;
+      for (int mt = 0; mt < MT; ++mt) acc[mt][r] *= sc;
     }
   }
 
   // lane holds C^T[row 4 lg + r of the wave][m = 16 mt + l16]
   if (EPI == LOOP_EPI_SWIGLU) {
-    float up[4][4];
+    float up[MT][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) up[mt][r] = __shfl_xor(acc[mt][r], 32, 64);
     if (lg >= 2) return;
     uint16_t* C = reinterpret_cast<uint16_t*>(g.C);
     const int col = 8 * NW * tile + 8 * wave + 4 * lg;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
       const int m = 16 * mt + l16;
       if (m >= g.M) continue;
 #pragma unroll
@@ -779,7 +782,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
   }
   const int col = 16 * NW * tile + 16 * wave + 4 * lg;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < MT; ++mt) {
     const int m = 16 * mt + l16;
     if (m >= g.M) continue;
 #pragma unroll
@@ -798,6 +801,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void gemm_skinny_kernel(GemmArgs g
   }
 }
 
+// launch with the fewest 16-row activation tiles that cover M
+template <int EPI, bool SPLIT, int NW, int QB>
+void launch_skinny_mt(dim3 grid, hipStream_t s, const GemmArgs& g, uint32_t a_bytes, uint32_t b_bytes) {
+  if (g.M <= 16)
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, SPLIT, NW, QB, 1>), grid, dim3(64 * NW), 0, s, g, a_bytes, b_bytes);
+  else if (g.M <= 32)
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, SPLIT, NW, QB, 2>), grid, dim3(64 * NW), 0, s, g, a_bytes, b_bytes);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, SPLIT, NW, QB, 4>), grid, dim3(64 * NW), 0, s, g, a_bytes, b_bytes);
+}
+
 // M <= 64, K range of every workgroup a multiple of SK_NSET chunks, operands
 // within 32-bit buffer offsets.
 template <int EPI, int NW>
@@ -809,13 +823,12 @@ hipError_t launch_skinny_w(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32
   const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
   if (splits > 1 && g.part && need <= ws_bytes) {
     g.kslice = g.K / splits;
-    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, NW>), dim3(tiles, splits), dim3(64 * NW), 0, s, g, a_bytes,
-                       b_bytes);
+    launch_skinny_mt<EPI, true, NW, 16>(dim3(tiles, splits), s, g, a_bytes, b_bytes);
     const int64_t n_out = (int64_t)g.M * g.N;
     const int blocks = (int)std::min<int64_t>((n_out + 255) / 256, 4096);
     hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, splits);
   } else {
-    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, false, NW>), dim3(tiles), dim3(64 * NW), 0, s, g, a_bytes, b_bytes);
+    launch_skinny_mt<EPI, false, NW, 16>(dim3(tiles), s, g, a_bytes, b_bytes);
   }
   return hipGetLastError();
 }
@@ -954,14 +967,12 @@ hipError_t launch_wq(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_b
   const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
   if (splits > 1 && g.part && need <= ws_bytes) {
     g.kslice = g.K / splits;
-    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, NW, QB>), dim3(tiles, splits), dim3(64 * NW), 0, s, g, a_bytes,
-                       b_bytes);
+    launch_skinny_mt<EPI, true, NW, QB>(dim3(tiles, splits), s, g, a_bytes, b_bytes);
     const int64_t n_out = (int64_t)g.M * g.N;
     const int blocks = (int)std::min<int64_t>((n_out + 255) / 256, 4096);
     hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, splits);
   } else {
-    hipLaunchKernelGGL((gemm_skinny_kernel<EPI, false, NW, QB>), dim3(tiles), dim3(64 * NW), 0, s, g, a_bytes,
-                       b_bytes);
+    launch_skinny_mt<EPI, false, NW, QB>(dim3(tiles), s, g, a_bytes, b_bytes);
   }
   return hipGetLastError();
 }
@@ -1044,8 +1055,7 @@ hipError_t launch_gemm_norm(const void* A, int64_t lda, const void* B, int64_t l
       g.kslice = K / splits;
       auto launch = [&](auto epi_tag) {
         constexpr int EPI = decltype(epi_tag)::value;
-        hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, SK_WAVES>), dim3(tiles, splits), dim3(64 * SK_WAVES), 0, s,
-                           g, (uint32_t)a_bytes, (uint32_t)b_bytes);
+        launch_skinny_mt<EPI, true, SK_WAVES, 16>(dim3(tiles, splits), s, g, (uint32_t)a_bytes, (uint32_t)b_bytes);
         if (splits == 4)
           hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 4>), dim3(M), dim3(1024), 0, s, g, X2,
                              (const uint16_t*)gain, (uint16_t*)hn, eps);
@@ -1110,8 +1120,7 @@ hipError_t launch_gemm_norm_wq(int bits, const void* A, int64_t lda, const void*
     auto launch = [&](auto epi_tag, auto qb) {
       constexpr int EPI = decltype(epi_tag)::value;
       constexpr int QB = decltype(qb)::value;
-      hipLaunchKernelGGL((gemm_skinny_kernel<EPI, true, SK_WAVES, QB>), dim3(tiles, splits), dim3(64 * SK_WAVES), 0,
-                         s, g, (uint32_t)a_bytes, (uint32_t)b_bytes);
+      launch_skinny_mt<EPI, true, SK_WAVES, QB>(dim3(tiles, splits), s, g, (uint32_t)a_bytes, (uint32_t)b_bytes);
       if (splits == 4)
         hipLaunchKernelGGL((splitk_reduce_norm_kernel<EPI, 4, 4>), dim3(M), dim3(1024), 0, s, g, X2,
                            (const uint16_t*)gain, (uint16_t*)hn, eps);
