@@ -314,21 +314,21 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
     const void *w_in, *w_o, *w_gateup, *w_down;
     const float *s_in, *s_o, *s_gateup, *s_down;
   } qw{};
-  const QW* q8 = nullptr;
+  const QW* wq = nullptr;
   if (k.decode && !m->q8.empty()) {
     const loop_q8_layer& q = m->q8[d.layer];
     qw = {8, q.w_in, q.w_o, q.w_gateup, q.w_down, q.s_in, q.s_o, q.s_gateup, q.s_down};
-    q8 = &qw;
+    wq = &qw;
   } else if (k.decode && !m->q4.empty()) {
     const loop_q4_layer& q = m->q4[d.layer];
     qw = {4, q.w_in, q.w_o, q.w_gateup, q.w_down, q.s_in, q.s_o, q.s_gateup, q.s_down};
-    q8 = &qw;
+    wq = &qw;
   }
   auto ldq = [&](int K) -> int64_t { return qw.bits == 8 ? K : K / 2; };
   {
     Prof p(m, LOOP_K_GEMM_IN, s);
-    if (q8)
-      HIP_TRY(launch_gemm_wq(q8->bits, xn, dm, q8->w_in, ldq(dm), q8->s_in, proj, L.n_in_max, nullptr, M, n_in, dm,
+    if (wq)
+      HIP_TRY(launch_gemm_wq(wq->bits, xn, dm, wq->w_in, ldq(dm), wq->s_in, proj, L.n_in_max, nullptr, M, n_in, dm,
                              LOOP_EPI_BF16, s, SK));
     else
       HIP_TRY(launch_gemm(xn, dm, w.w_in, dm, proj, L.n_in_max, nullptr, M, n_in, dm, LOOP_EPI_BF16, s, SK));
@@ -402,11 +402,11 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
     // O-projection and the FFN pre-norm: plain hmid = h + o W_o^T, hn =
     // RMSNorm(hmid); loop a = o W_o^T, hn = RMSNorm(x + a)
     Prof p(m, LOOP_K_GEMM_O, s);
-    if (q8 && !d.loop)
-      HIP_TRY(launch_gemm_norm_wq(q8->bits, obuf, mix_width, q8->w_o, ldq(mix_width), q8->s_o, hmid, dm, h, nullptr,
+    if (wq && !d.loop)
+      HIP_TRY(launch_gemm_norm_wq(wq->bits, obuf, mix_width, wq->w_o, ldq(mix_width), wq->s_o, hmid, dm, h, nullptr,
                                   w.ffn_norm, hn, c.eps, M, dm, mix_width, s, SK));
-    else if (q8)
-      HIP_TRY(launch_gemm_norm_wq(q8->bits, obuf, mix_width, q8->w_o, ldq(mix_width), q8->s_o, a, dm, nullptr, x,
+    else if (wq)
+      HIP_TRY(launch_gemm_norm_wq(wq->bits, obuf, mix_width, wq->w_o, ldq(mix_width), wq->s_o, a, dm, nullptr, x,
                                   w.ffn_norm, hn, c.eps, M, dm, mix_width, s, SK));
     else if (!d.loop)
       HIP_TRY(launch_gemm_norm(obuf, mix_width, w.w_o, mix_width, hmid, dm, h, nullptr, w.ffn_norm, hn, c.eps, M, dm,
@@ -417,8 +417,8 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
   }
   {
     Prof p(m, LOOP_K_GEMM_GATEUP, s);
-    if (q8)
-      HIP_TRY(launch_gemm_wq(q8->bits, hn, dm, q8->w_gateup, ldq(dm), q8->s_gateup, act, c.d_ff, nullptr, M, c.d_ff,
+    if (wq)
+      HIP_TRY(launch_gemm_wq(wq->bits, hn, dm, wq->w_gateup, ldq(dm), wq->s_gateup, act, c.d_ff, nullptr, M, c.d_ff,
                              dm, LOOP_EPI_SWIGLU, s, SK));
     else
       HIP_TRY(launch_gemm(hn, dm, w.w_gateup, dm, act, c.d_ff, nullptr, M, c.d_ff, dm, LOOP_EPI_SWIGLU, s, SK));
@@ -427,8 +427,8 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
     Prof p(m, LOOP_K_GEMM_DOWN, s);
     float* dst = d.loop ? a : h;
     const float* res = d.loop ? a : hmid;
-    if (q8)
-      HIP_TRY(launch_gemm_wq(q8->bits, act, c.d_ff, q8->w_down, ldq(c.d_ff), q8->s_down, dst, dm, res, M, dm,
+    if (wq)
+      HIP_TRY(launch_gemm_wq(wq->bits, act, c.d_ff, wq->w_down, ldq(c.d_ff), wq->s_down, dst, dm, res, M, dm,
                              c.d_ff, LOOP_EPI_F32_RES, s, SK));
     else
       HIP_TRY(launch_gemm(act, c.d_ff, w.w_down, c.d_ff, dst, dm, res, M, dm, c.d_ff, LOOP_EPI_F32_RES, s, SK));
