@@ -165,6 +165,8 @@ void loop_model_destroy(loop_model* m);
  *   n_taps / tap_exec (host) / d_taps device fp32 [n_taps, batch, d_model]:
  *              hidden state after the listed executions at the last position
  *              (mean of the streams inside the loop), or 0 / NULL.
+ *   taps_all_positions  nonzero: the taps hold every position instead,
+ *              d_taps fp32 [n_taps, batch*seq_len, d_model].
  *   loop_passes number of times the shared block runs in this call: 0 = the
  *              configuration's loop_passes, else 1 .. loop_passes.  A p-pass
  *              call runs the head layers, the block's first p passes (each
@@ -188,6 +190,7 @@ typedef struct loop_prefill_args {
   const int32_t* tap_exec;
   float* d_taps;
   int32_t loop_passes;
+  int32_t taps_all_positions;
 } loop_prefill_args;
 int loop_prefill(loop_model* m, const loop_prefill_args* a, void* stream);
 
@@ -249,6 +252,41 @@ typedef struct loop_verify_args {
   int32_t loop_passes;
 } loop_verify_args;
 int loop_verify_step(loop_model* m, const loop_verify_args* a, void* stream);
+
+/* One execution's sequence mixer on its own, on a given input projection:
+ * the part of an execution between its two projections, run with the
+ * execution's cache slot exactly as loop_prefill (decode = 0) or
+ * loop_decode_step (decode = 1) run it inside the stack, so that the mixer
+ * can be checked on identical inputs.
+ *   full attention ([P1 section 3]): QK-norm over each head's dims, rotary
+ *     on the first rotary_dim dims in adjacent pairs, K / V appended to the
+ *     slot's cache at positions start_pos .. start_pos+seq_len-1 ([P1
+ *     section 4]), causal GQA attention over the cache, output times
+ *     sigmoid(gate);
+ *   Gated-DeltaNet ([P1 section 3]): L2-norm of q, k, gates, the gated
+ *     delta rule from the slot's state (zero at start_pos 0) with the final
+ *     state stored back, RMSNorm of the output times SiLU(z).
+ *   exec       execution index of the configuration's full schedule (its
+ *              weight layer, kind and cache slot)
+ *   batch, seq_len, slots (host [batch]), start_pos (host [batch]) as for
+ *              loop_prefill; decode = 1 requires seq_len = 1
+ *   d_proj     device bf16 [batch*seq_len][ld_proj]: the in-projection
+ *              output, columns [q; g; k; v] (full) or [q; k; v; z; a; b] (GDN)
+ *   d_out      device bf16 [batch*seq_len][ld_out]: the mixer output, the
+ *              input of W_o (n_q_heads*head_dim or gdn_heads*gdn_dv columns)
+ * Uses the model's workspace (calls on one model must not overlap). */
+typedef struct loop_mixer_args {
+  int32_t exec;
+  int32_t batch, seq_len;
+  const int32_t* slots;
+  const int32_t* start_pos;
+  int32_t decode;
+  const void* d_proj;
+  int64_t ld_proj;
+  void* d_out;
+  int64_t ld_out;
+} loop_mixer_args;
+int loop_exec_mixer(loop_model* m, const loop_mixer_args* a, void* stream);
 
 /* Sinkhorn-normalised stream-mix matrices of every loop layer as the device
  * computes them ([P1 section 5]): fp32 [loop_end-loop_start, 2, 2] into

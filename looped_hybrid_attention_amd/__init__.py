@@ -51,7 +51,8 @@ class loop_prefill_args(ctypes.Structure):
     _fields_ = [("batch", _i32), ("seq_len", _i32), ("slots", ctypes.POINTER(_i32)),
                 ("start_pos", ctypes.POINTER(_i32)), ("d_tokens", _vp), ("d_hidden_in", _vp),
                 ("d_logits", _vp), ("d_hidden_out", _vp), ("n_taps", _i32),
-                ("tap_exec", ctypes.POINTER(_i32)), ("d_taps", _vp), ("loop_passes", _i32)]
+                ("tap_exec", ctypes.POINTER(_i32)), ("d_taps", _vp), ("loop_passes", _i32),
+                ("taps_all_positions", _i32)]
 
 
 class loop_decode_args(ctypes.Structure):
@@ -64,6 +65,12 @@ class loop_verify_args(ctypes.Structure):
     _fields_ = [("batch", _i32), ("k", _i32), ("slots", ctypes.POINTER(_i32)), ("pos", ctypes.POINTER(_i32)),
                 ("d_tokens", _vp), ("d_logits", _vp), ("d_next", _vp), ("d_hidden_out", _vp),
                 ("n_taps", _i32), ("tap_exec", ctypes.POINTER(_i32)), ("d_taps", _vp), ("loop_passes", _i32)]
+
+
+class loop_mixer_args(ctypes.Structure):
+    _fields_ = [("exec", _i32), ("batch", _i32), ("seq_len", _i32), ("slots", ctypes.POINTER(_i32)),
+                ("start_pos", ctypes.POINTER(_i32)), ("decode", _i32), ("d_proj", _vp), ("ld_proj", _i64),
+                ("d_out", _vp), ("ld_out", _i64)]
 
 
 LOOP_VERIFY_MAX = 16
@@ -101,6 +108,7 @@ def _load():
         "loop_prefill": (ctypes.c_int, [_vp, P(loop_prefill_args), _vp]),
         "loop_decode_step": (ctypes.c_int, [_vp, P(loop_decode_args), _vp]),
         "loop_verify_step": (ctypes.c_int, [_vp, P(loop_verify_args), _vp]),
+        "loop_exec_mixer": (ctypes.c_int, [_vp, P(loop_mixer_args), _vp]),
         "loop_model_set_int8": (ctypes.c_int, [_vp, _vp]),
         "loop_quantize_int8": (ctypes.c_int, [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]),
         "loop_model_set_int4": (ctypes.c_int, [_vp, _vp]),
@@ -241,9 +249,10 @@ def _i32arr(xs):
 
 def loop_prefill(model: int, batch: int, seq_len: int, slots, start_pos, d_tokens: int = 0,
                  d_hidden_in: int = 0, d_logits: int = 0, d_hidden_out: int = 0, tap_exec=(),
-                 d_taps: int = 0, stream: int = 0, loop_passes: int = 0) -> None:
+                 d_taps: int = 0, stream: int = 0, loop_passes: int = 0, taps_all_positions: bool = False) -> None:
     a = loop_prefill_args()
     a.loop_passes = loop_passes
+    a.taps_all_positions = 1 if taps_all_positions else 0
     a.batch, a.seq_len = batch, seq_len
     sl, sp, te = _i32arr(slots), _i32arr(start_pos), _i32arr(tap_exec)
     a.slots, a.start_pos = sl, sp
@@ -253,6 +262,16 @@ def loop_prefill(model: int, batch: int, seq_len: int, slots, start_pos, d_token
     a.tap_exec = te if len(tap_exec) else None
     a.d_taps = d_taps or None
     _check(_lib.loop_prefill(model, ctypes.byref(a), stream or None))
+
+
+def loop_exec_mixer(model: int, exec_index: int, batch: int, seq_len: int, slots, start_pos, d_proj: int,
+                    ld_proj: int, d_out: int, ld_out: int, decode: bool = False, stream: int = 0) -> None:
+    a = loop_mixer_args()
+    a.exec, a.batch, a.seq_len, a.decode = exec_index, batch, seq_len, 1 if decode else 0
+    sl, sp = _i32arr(slots), _i32arr(start_pos)
+    a.slots, a.start_pos = sl, sp
+    a.d_proj, a.ld_proj, a.d_out, a.ld_out = d_proj, ld_proj, d_out, ld_out
+    _check(_lib.loop_exec_mixer(model, ctypes.byref(a), stream or None))
 
 
 def loop_decode_step(model: int, batch: int, slots, pos, d_tokens: int, d_logits: int = 0,

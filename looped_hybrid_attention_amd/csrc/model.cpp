@@ -290,49 +290,16 @@ struct Call {
 template <typename T>
 T* at(loop_model* m, size_t off) { return reinterpret_cast<T*>(m->ws + off); }
 
-int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
+// The sequence mixer of one execution: from the in-projection output in the
+// workspace (proj, rows of n_in_max) to the gated / normed mixer output
+// (obuf, rows of *mix_width), with the execution's cache slot.
+int run_mixer(loop_model* m, const Call& k, const ExecDesc& d, hipStream_t s, int* mix_width_out) {
   const loop_config& c = m->cfg;
   const Layout& L = m->L;
-  const std::vector<ExecDesc>& sched = *k.sched;
-  const ExecDesc& d = sched[e];
   const loop_layer_weights& w = m->lw[d.layer];
-  const int M = k.M, dm = c.d_model;
-  uint16_t* xn = at<uint16_t>(m, L.xn);
+  const int M = k.M;
   uint16_t* proj = at<uint16_t>(m, L.proj);
   uint16_t* obuf = at<uint16_t>(m, L.obuf);
-  float* h = at<float>(m, L.h);
-  float* hmid = at<float>(m, L.hmid);
-  float* x = at<float>(m, L.x);
-  float* a = at<float>(m, L.a);
-  const int n_in = d.full ? n_in_full(c) : n_in_gdn(c);
-#define SK at<float>(m, L.splitk), L.splitk_bytes
-
-  // decode steps with int8 or int4 codes registered use them for the four
-  // projections (ldq: bytes per code row of a K-deep matrix)
-  struct QW {
-    int bits;
-    const void *w_in, *w_o, *w_gateup, *w_down;
-    const float *s_in, *s_o, *s_gateup, *s_down;
-  } qw{};
-  const QW* wq = nullptr;
-  if (k.decode && !m->q8.empty()) {
-    const loop_q8_layer& q = m->q8[d.layer];
-    qw = {8, q.w_in, q.w_o, q.w_gateup, q.w_down, q.s_in, q.s_o, q.s_gateup, q.s_down};
-    wq = &qw;
-  } else if (k.decode && !m->q4.empty()) {
-    const loop_q4_layer& q = m->q4[d.layer];
-    qw = {4, q.w_in, q.w_o, q.w_gateup, q.w_down, q.s_in, q.s_o, q.s_gateup, q.s_down};
-    wq = &qw;
-  }
-  auto ldq = [&](int K) -> int64_t { return qw.bits == 8 ? K : K / 2; };
-  {
-    Prof p(m, LOOP_K_GEMM_IN, s);
-    if (wq)
-      HIP_TRY(launch_gemm_wq(wq->bits, xn, dm, wq->w_in, ldq(dm), wq->s_in, proj, L.n_in_max, nullptr, M, n_in, dm,
-                             LOOP_EPI_BF16, s, SK));
-    else
-      HIP_TRY(launch_gemm(xn, dm, w.w_in, dm, proj, L.n_in_max, nullptr, M, n_in, dm, LOOP_EPI_BF16, s, SK));
-  }
   int mix_width;
   if (d.full) {
     const int Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim;
@@ -395,6 +362,55 @@ int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
     if (k.decode) HIP_TRY(launch_gdn_recurrent(g, k.B, s));
     else HIP_TRY(launch_gdn_prefill(g, k.B, s));
   }
+  *mix_width_out = mix_width;
+  return 0;
+}
+
+int run_exec(loop_model* m, const Call& k, int e, hipStream_t s) {
+  const loop_config& c = m->cfg;
+  const Layout& L = m->L;
+  const std::vector<ExecDesc>& sched = *k.sched;
+  const ExecDesc& d = sched[e];
+  const loop_layer_weights& w = m->lw[d.layer];
+  const int M = k.M, dm = c.d_model;
+  uint16_t* xn = at<uint16_t>(m, L.xn);
+  uint16_t* proj = at<uint16_t>(m, L.proj);
+  uint16_t* obuf = at<uint16_t>(m, L.obuf);
+  float* h = at<float>(m, L.h);
+  float* hmid = at<float>(m, L.hmid);
+  float* x = at<float>(m, L.x);
+  float* a = at<float>(m, L.a);
+  const int n_in = d.full ? n_in_full(c) : n_in_gdn(c);
+#define SK at<float>(m, L.splitk), L.splitk_bytes
+
+  // decode steps with int8 or int4 codes registered use them for the four
+  // projections (ldq: bytes per code row of a K-deep matrix)
+  struct QW {
+    int bits;
+    const void *w_in, *w_o, *w_gateup, *w_down;
+    const float *s_in, *s_o, *s_gateup, *s_down;
+  } qw{};
+  const QW* wq = nullptr;
+  if (k.decode && !m->q8.empty()) {
+    const loop_q8_layer& q = m->q8[d.layer];
+    qw = {8, q.w_in, q.w_o, q.w_gateup, q.w_down, q.s_in, q.s_o, q.s_gateup, q.s_down};
+    wq = &qw;
+  } else if (k.decode && !m->q4.empty()) {
+    const loop_q4_layer& q = m->q4[d.layer];
+    qw = {4, q.w_in, q.w_o, q.w_gateup, q.w_down, q.s_in, q.s_o, q.s_gateup, q.s_down};
+    wq = &qw;
+  }
+  auto ldq = [&](int K) -> int64_t { return qw.bits == 8 ? K : K / 2; };
+  {
+    Prof p(m, LOOP_K_GEMM_IN, s);
+    if (wq)
+      HIP_TRY(launch_gemm_wq(wq->bits, xn, dm, wq->w_in, ldq(dm), wq->s_in, proj, L.n_in_max, nullptr, M, n_in, dm,
+                             LOOP_EPI_BF16, s, SK));
+    else
+      HIP_TRY(launch_gemm(xn, dm, w.w_in, dm, proj, L.n_in_max, nullptr, M, n_in, dm, LOOP_EPI_BF16, s, SK));
+  }
+  int mix_width = 0;
+  if (int r = run_mixer(m, k, d, s, &mix_width)) return r;
   // O-proj, mid norm, FFN
   uint16_t* hn = at<uint16_t>(m, L.hn);
   uint16_t* act = at<uint16_t>(m, L.act);
@@ -603,6 +619,7 @@ extern "C" int loop_prefill(loop_model* m, const loop_prefill_args* a, void* str
     if (a->tap_exec[i] < 0 || a->tap_exec[i] >= (int)sched.size()) return loop_fail(LOOP_EINVAL, "tap %d out of range", a->tap_exec[i]);
   hipStream_t s = (hipStream_t)stream;
   Call k{B, T, B * T, false, nullptr, nullptr, nullptr, &sched};
+  k.taps_all = a->taps_all_positions != 0;
   const int32_t* meta = at<int32_t>(m, m->L.meta);
   k.d_pos = meta;
   k.d_slot = meta + c.max_batch;
@@ -698,6 +715,46 @@ extern "C" int loop_verify_step(loop_model* m, const loop_verify_args* a, void* 
     if (a->d_next)
       HIP_TRY(launch_argmax(a->d_logits, k.M, c.vocab, at<float>(m, m->L.am_v), at<int>(m, m->L.am_i), a->d_next, s));
   }
+  return 0;
+}
+
+extern "C" int loop_exec_mixer(loop_model* m, const loop_mixer_args* a, void* stream) {
+  if (!m || !a) return loop_fail(LOOP_EINVAL, "model or args NULL");
+  const loop_config& c = m->cfg;
+  const int B = a->batch, T = a->seq_len;
+  if (a->exec < 0 || a->exec >= (int)m->sched.size())
+    return loop_fail(LOOP_EINVAL, "exec %d out of [0, %d)", a->exec, (int)m->sched.size());
+  if (B < 1 || B > c.max_batch) return loop_fail(LOOP_ECAPACITY, "batch %d out of [1, %d]", B, c.max_batch);
+  if (T < 1) return loop_fail(LOOP_EINVAL, "seq_len must be >= 1");
+  if (a->decode && T != 1) return loop_fail(LOOP_EINVAL, "the decode path takes one token per sequence");
+  if (T > 65536) return loop_fail(LOOP_ECAPACITY, "seq_len %d above 65536 tokens per call", T);
+  if ((int64_t)B * T > c.max_tokens) return loop_fail(LOOP_ECAPACITY, "batch*seq_len %lld > max_tokens %d", (long long)B * T, c.max_tokens);
+  if (int r = check_slots(c, B, a->slots)) return r;
+  if (!a->start_pos) return loop_fail(LOOP_EINVAL, "start_pos is NULL");
+  for (int b = 0; b < B; ++b)
+    if (a->start_pos[b] < 0 || (int64_t)a->start_pos[b] + T > c.max_seq)
+      return loop_fail(LOOP_ECAPACITY, "start_pos %d + seq_len %d exceeds max_seq %d", a->start_pos[b], T, c.max_seq);
+  const ExecDesc& d = m->sched[a->exec];
+  const int n_in = d.full ? n_in_full(c) : n_in_gdn(c);
+  const int width = d.full ? c.n_q_heads * c.head_dim : c.gdn_heads * c.gdn_dv;
+  if (!a->d_proj || !a->d_out) return loop_fail(LOOP_EINVAL, "d_proj and d_out are required");
+  if (a->ld_proj < n_in || a->ld_out < width)
+    return loop_fail(LOOP_EINVAL, "ld_proj %lld < %d or ld_out %lld < %d", (long long)a->ld_proj, n_in,
+                     (long long)a->ld_out, width);
+  hipStream_t s = (hipStream_t)stream;
+  Call k{B, T, B * T, a->decode != 0, nullptr, nullptr, nullptr, &m->sched};
+  const int32_t* meta = at<int32_t>(m, m->L.meta);
+  k.d_pos = meta;
+  k.d_slot = meta + c.max_batch;
+  k.d_last = meta + 2 * c.max_batch;
+  if (int r = upload_meta(m, B, T, a->start_pos, a->slots, s)) return r;
+  uint16_t* proj = at<uint16_t>(m, m->L.proj);
+  HIP_TRY(hipMemcpy2DAsync(proj, (size_t)m->L.n_in_max * 2, a->d_proj, (size_t)a->ld_proj * 2, (size_t)n_in * 2,
+                           (size_t)k.M, hipMemcpyDeviceToDevice, s));
+  int mix_width = 0;
+  if (int r = run_mixer(m, k, d, s, &mix_width)) return r;
+  HIP_TRY(hipMemcpy2DAsync(a->d_out, (size_t)a->ld_out * 2, at<uint16_t>(m, m->L.obuf), (size_t)mix_width * 2,
+                           (size_t)mix_width * 2, (size_t)k.M, hipMemcpyDeviceToDevice, s));
   return 0;
 }
 

@@ -62,14 +62,16 @@ def attention_core(q: np.ndarray, K: np.ndarray, V: np.ndarray, q_pos: np.ndarra
     return out
 
 
-def full_attention(xn: np.ndarray, w: dict, cache: KVCache, pos0: int, cfg,
-                   bf16: bool = False) -> np.ndarray:
-    """Mixer output ``a`` [T, d] for one sequence whose new tokens sit at
-    positions pos0 .. pos0+T-1; appends their K, V to ``cache``.  ``bf16``:
-    the backbone precision policy of ``oracle.precision``."""
-    T = xn.shape[0]
+def attention_mixer(proj: np.ndarray, w: dict, cache: KVCache, pos0: int, cfg,
+                    bf16: bool = False) -> np.ndarray:
+    """The mixer between the two projections: from the input projection's
+    output ``proj`` [T, 2 Hq D + 2 Hkv D] (columns q | g | k | v) of one
+    sequence whose new tokens sit at positions pos0 .. pos0+T-1, the gated
+    attention output [T, Hq*D] that enters ``W_o``; appends the new K, V to
+    ``cache``.  ``bf16``: the backbone precision policy of
+    ``oracle.precision`` (``proj`` is then already bf16-valued)."""
+    T = proj.shape[0]
     Hq, Hkv, D = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    proj = maybe_bf16(xn @ w["w_in"].T, bf16)
     q = proj[:, :Hq * D].reshape(T, Hq, D)
     g = proj[:, Hq * D:2 * Hq * D]
     k = proj[:, 2 * Hq * D:2 * Hq * D + Hkv * D].reshape(T, Hkv, D)
@@ -83,5 +85,13 @@ def full_attention(xn: np.ndarray, w: dict, cache: KVCache, pos0: int, cfg,
     assert cache.length == pos0, "cache length must equal the first new position"
     cache.append(k, v)
     o = attention_core(q, cache.k, cache.v, pos, bf16=bf16)
-    o = maybe_bf16(o.reshape(T, Hq * D) * sigmoid(g), bf16)
-    return o @ w["w_o"].T
+    return maybe_bf16(o.reshape(T, Hq * D) * sigmoid(g), bf16)
+
+
+def full_attention(xn: np.ndarray, w: dict, cache: KVCache, pos0: int, cfg,
+                   bf16: bool = False) -> np.ndarray:
+    """Mixer output ``a`` [T, d] for one sequence whose new tokens sit at
+    positions pos0 .. pos0+T-1; appends their K, V to ``cache``.  ``bf16``:
+    the backbone precision policy of ``oracle.precision``."""
+    proj = maybe_bf16(xn @ w["w_in"].T, bf16)
+    return attention_mixer(proj, w, cache, pos0, cfg, bf16=bf16) @ w["w_o"].T

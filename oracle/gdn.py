@@ -87,14 +87,16 @@ def gdn_chunked(q, k, v, log_alpha, beta, S0, chunk: int = 64):
     return o, S
 
 
-def gdn_layer(xn: np.ndarray, w: dict, S0: np.ndarray, cfg, chunked: bool = False,
+def gdn_mixer(proj: np.ndarray, w: dict, S0: np.ndarray, cfg, chunked: bool = False,
               chunk: int = 64, bf16: bool = False):
-    """Mixer output ``a`` [T, d] and the new state for one sequence.  ``bf16``:
-    the backbone precision policy of ``oracle.precision`` (projection outputs
-    and the gated output in bf16; the recurrence and its state in fp32)."""
-    T = xn.shape[0]
+    """The mixer between the two projections: from the input projection's
+    output ``proj`` [T, 2 H Dk + 2 H Dv + 2 H] (columns q | k | v | z | a | b)
+    of one sequence and its entering state ``S0`` [H, Dv, Dk], the gated
+    output [T, H*Dv] that enters ``W_o`` and the new state.  ``bf16``: the
+    backbone precision policy of ``oracle.precision`` (``proj`` is then
+    already bf16-valued; the recurrence and its state stay fp32)."""
+    T = proj.shape[0]
     H, Dk, Dv = cfg.gdn_heads, cfg.gdn_dk, cfg.gdn_dv
-    proj = maybe_bf16(xn @ w["w_in"].T, bf16)
     o0 = 0
     q = proj[:, o0:o0 + H * Dk].reshape(T, H, Dk); o0 += H * Dk
     k = proj[:, o0:o0 + H * Dk].reshape(T, H, Dk); o0 += H * Dk
@@ -112,4 +114,14 @@ def gdn_layer(xn: np.ndarray, w: dict, S0: np.ndarray, cfg, chunked: bool = Fals
     else:
         o, S = gdn_recurrent(qh, kh, v, np.exp(log_alpha), beta, S0)
     o = maybe_bf16(rmsnorm(o, w["o_norm"], cfg.eps) * silu(z), bf16)
-    return o.reshape(T, H * Dv) @ w["w_o"].T, S
+    return o.reshape(T, H * Dv), S
+
+
+def gdn_layer(xn: np.ndarray, w: dict, S0: np.ndarray, cfg, chunked: bool = False,
+              chunk: int = 64, bf16: bool = False):
+    """Mixer output ``a`` [T, d] and the new state for one sequence.  ``bf16``:
+    the backbone precision policy of ``oracle.precision`` (projection outputs
+    and the gated output in bf16; the recurrence and its state in fp32)."""
+    proj = maybe_bf16(xn @ w["w_in"].T, bf16)
+    o, S = gdn_mixer(proj, w, S0, cfg, chunked=chunked, chunk=chunk, bf16=bf16)
+    return o @ w["w_o"].T, S

@@ -80,13 +80,14 @@ def _layer_body(cfg, row, lw, x, st, pos0, chunked_gdn, bf16):
 
 def forward_seq(cfg: Config, W: dict, st: SeqState, ids=None, hidden=None,
                 chunked_gdn: bool = False, write_full: bool = False, taps=(),
-                bf16: bool = False):
+                bf16: bool = False, taps_all: bool = False):
     """One sequence: T new tokens at positions st.length .. st.length+T-1.
     ``bf16``: the backbone precision policy of ``oracle.precision``.
 
     Returns (h [T, d] after the last execution, logits [V] of the last position
     or None, {tap exec: hidden [d] at the last position}).  A tap at a loop
-    execution reports the mean of the streams after its write.
+    execution reports the mean of the streams after its write.  ``taps_all``:
+    the taps hold every position ([T, d]) instead of the last.
     """
     if ids is not None:
         h = W["embed"][np.asarray(ids)]
@@ -103,7 +104,7 @@ def forward_seq(cfg: Config, W: dict, st: SeqState, ids=None, hidden=None,
             a, hmid, f = _layer_body(cfg, row, lw, h, st, pos0, chunked_gdn, bf16)
             h = hmid + f
             if row.e in taps:
-                tapped[row.e] = h[-1].copy()
+                tapped[row.e] = h.copy() if taps_all else h[-1].copy()
             continue
         if row.fork:
             streams = mhc.fork(h, cfg.n_streams)
@@ -115,7 +116,7 @@ def forward_seq(cfg: Config, W: dict, st: SeqState, ids=None, hidden=None,
         if row.merge:
             h = mhc.merge(streams)
         if row.e in taps:
-            tapped[row.e] = mhc.merge(streams)[-1].copy()
+            tapped[row.e] = mhc.merge(streams) if taps_all else mhc.merge(streams)[-1].copy()
     st.length += h.shape[0]
     logits = None
     if cfg.vocab:

@@ -1,6 +1,6 @@
 """Shared set-up of the model-level GPU tests: device weights from the
-seeded host draw, arena / workspace buffers, a model handle.  Marshalling
-only."""
+seeded host draw, arena / workspace buffers, a model handle, and the GPU's
+caches read back into the oracle's cache structures.  Marshalling only."""
 import numpy as np
 
 import synth
@@ -59,3 +59,53 @@ def device_full_weights(torch, L, dims, kinds, stream):
         tensors[name] = t
         ptrs[name] = t.data_ptr()
     return tensors, L.make_weights_struct(dims["n_layers"], ptrs)
+
+
+def state_from_gpu(g, ocfg, seq_slot, length, dtype, slot_map=None):
+    """An oracle SeqState (``oracle.model``) holding the GPU arena's caches of
+    sequence slot ``seq_slot``: K, V of every full-attention execution at
+    positions 0 .. length-1 (V un-blocked from its 32-position transposed
+    blocks) and every Gated-DeltaNet state.  ``slot_map``: {("full" | "gdn",
+    oracle slot): arena slot} when the call's schedule is a part of the
+    configured one (fewer block passes); default the identity."""
+    import torch
+    from oracle import model as om
+    from gpu_util import host
+    L, cfg, dims = g.L, g.cfg, g.dims
+    Hkv, D, S = dims["n_kv_heads"], dims["head_dim"], cfg.max_seq
+    H, Dk, Dv = dims["gdn_heads"], dims["gdn_dk"], dims["gdn_dv"]
+    st = om.SeqState(ocfg, dtype)
+    slot_map = slot_map or {}
+
+    def view(off, n, bf):
+        t = g.arena[off:off + n * (2 if bf else 4)]
+        return host(t.view(torch.bfloat16 if bf else torch.float32))
+
+    for f in range(st.n_full):
+        a = slot_map.get(("full", f), f)
+        K = view(L.loop_cache_offset(cfg, 0, a, seq_slot), Hkv * S * D, True).reshape(Hkv, S, D)
+        Vb = view(L.loop_cache_offset(cfg, 1, a, seq_slot), Hkv * S * D, True).reshape(Hkv, S // 32, D, 32)
+        st.kv[f].k = np.ascontiguousarray(K[:, :length], dtype)
+        st.kv[f].v = np.ascontiguousarray(Vb.transpose(0, 1, 3, 2).reshape(Hkv, S, D)[:, :length], dtype)
+    for j in range(st.n_gdn):
+        a = slot_map.get(("gdn", j), j)
+        st.S[j] = view(L.loop_cache_offset(cfg, 2, a, seq_slot), H * Dv * Dk, False).reshape(H, Dv, Dk).astype(dtype)
+    st.length = length
+    return st
+
+
+def pass_slot_map(L, cfg, passes):
+    """{(kind, slot in the p-pass schedule): slot in the configured schedule}:
+    a call with fewer block passes keeps every execution on its slot of the
+    full schedule."""
+    rows = L.loop_schedule(cfg)
+    ls, le = cfg.loop_start, cfg.loop_end
+    blk = le - ls
+    kept = [r for e, r in enumerate(rows)
+            if not (ls <= e < ls + blk * cfg.loop_passes) or (e - ls) // blk < passes]
+    out, rank = {}, {"full": 0, "gdn": 0}
+    for layer, full, slot, *_ in kept:
+        kind = "full" if full else "gdn"
+        out[(kind, rank[kind])] = slot
+        rank[kind] += 1
+    return out

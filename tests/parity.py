@@ -1,24 +1,41 @@
-"""The whole-model parity bar.
+"""The parity bars.
 
 The pages fix the precision of the backbone (bf16) and of the mHC routing
-(fp32), and the oracle follows that policy.  The synthetic random-weight
-models amplify any rounding difference strongly (a 1e-7 relative input
+(fp32), and the oracle follows that policy.  Two kinds of bar follow from it.
+
+Flat bar (``FLAT`` = 2e-2, max |x - y| / max |y| per tensor): where the
+comparison is well conditioned -- single operations, the first executions of a
+stack (per-execution taps), a decode step's appended K.  The oracle's own
+evaluations (fp32 / fp64, Gated-DeltaNet token by token / chunked) agree there
+to well under 1 %.
+
+Noise-floor bar (``bar``): for whole-stack outputs of the random-weight models.
+They amplify any rounding difference strongly (a 1e-7 relative input
 perturbation grows ~100x over the tiny model at 256 tokens), so evaluations of
 the policy that are identical in exact arithmetic but round in a different
-order (token-by-token vs chunked Gated-DeltaNet, fp32 vs fp64 accumulation)
-already disagree by a few percent once bf16 rounding decisions flip.  The GPU
-path reorders the arithmetic of every kernel, not of one, so its distance to
-any single evaluation is expected to be up to about twice the pairwise spread
-of the oracle's own evaluations.
+order already disagree by a few percent once bf16 rounding decisions flip.  The
+GPU path reorders the arithmetic of every kernel, not of one, so its distance
+to any single evaluation is expected to be up to about twice the pairwise
+spread of the oracle's own evaluations:
+bar = max(2e-2, 2 * max pairwise spread of the oracle evaluations).
 
-bar = max(2e-2, 2 * max pairwise spread of the oracle evaluations), with the
-per-tensor metric max |x - y| / max |y|.
+Greedy tokens (``argmax_ok``): a GPU whose logits are within ``tol`` (of
+max |logit|) of the oracle's can pick another token only where the oracle's
+top-1 / top-2 margin is below about twice that.  So where every oracle
+evaluation picks the same token and its margin exceeds ``tol``, the GPU must
+pick exactly that token; elsewhere (a near-tie that rounding decides) its
+token must be one whose oracle logit lies within ``tol`` of the oracle's best.
+Decode steps are judged from the GPU's own caches, where ``tol`` is the flat
+2e-2, so most decisions are exact ones.
 """
 import itertools
 
+import numpy as np
+
 from gpu_util import rel_err
 
-BASE_TOL = 2e-2
+FLAT = 2e-2
+BASE_TOL = FLAT
 
 
 def noise_floor(evals):
@@ -30,21 +47,29 @@ def bar(evals):
     return max(BASE_TOL, 2.0 * noise_floor(evals))
 
 
-def argmax_ok(gpu_token: int, oracle_logits, tol: float) -> bool:
-    """Exact next-token agreement where the oracle's decision is well
-    conditioned; inside the noise band a near-tie is decided either way.
+def oracle_tokens(evals):
+    """Greedy token (lowest index on ties) of each oracle evaluation."""
+    return [int(np.argmax(np.asarray(e, np.float64).reshape(-1))) for e in evals]
 
-    The oracle's top-1 / top-2 margin (relative to max |logit|) is compared
-    with ``tol`` (the logits bar): above it the GPU must pick the oracle's
-    token exactly; below it the GPU's token must be one of the tokens whose
-    oracle logit lies within tol * max|logit| of the oracle's maximum.
-    """
-    import numpy as np
-    ol = np.asarray(oracle_logits, np.float64).reshape(-1)
-    scale = np.max(np.abs(ol))
-    top = int(np.argmax(ol))
-    srt = np.sort(ol)
-    margin = (srt[-1] - srt[-2]) / scale
-    if margin > tol:
-        return gpu_token == top
-    return ol[gpu_token] >= srt[-1] - tol * scale
+
+def margin(logits) -> float:
+    """Top-1 minus top-2 logit, relative to max |logit|."""
+    x = np.sort(np.asarray(logits, np.float64).reshape(-1))
+    return float((x[-1] - x[-2]) / np.max(np.abs(x)))
+
+
+def exact_required(evals, tol: float) -> bool:
+    return len(set(oracle_tokens(evals))) == 1 and margin(evals[0]) > tol
+
+
+def argmax_ok(gpu_token: int, evals, tol: float) -> bool:
+    """``evals``: the logits of the oracle's evaluations of the same position
+    (a list of 1-D arrays); ``tol``: the logits bar of the comparison."""
+    ref = np.asarray(evals[0], np.float64).reshape(-1)
+    if exact_required(evals, tol):
+        return int(gpu_token) == oracle_tokens(evals)[0]
+    return ref[int(gpu_token)] >= ref.max() - tol * np.max(np.abs(ref))
+
+
+def unanimous(evals) -> bool:
+    return len(set(oracle_tokens(evals))) == 1

@@ -95,3 +95,80 @@ def test_invalid_configuration_is_an_error(full_cfg):
     with pytest.raises(Exception):
         L.loop_schedule(bad)
     assert L.loop_last_error()
+
+
+# ------------------------------------------- loop_model_create's host checks
+# loop_model_create validates its arguments on the host before it queries the
+# device, so every rejection below is reached without a GPU.  The pointers
+# are fake addresses: nothing is dereferenced on the host, and an invalid
+# call enqueues nothing.
+
+LOOP_EINVAL, LOOP_ESHAPE, LOOP_ECAPACITY, LOOP_EHIP, LOOP_EDEVICE = -1, -2, -3, -4, -5
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+def _tiny_create_args(L):
+    dims = synth.preset("tiny")
+    cfg = L.make_config(dims, max_batch=2, max_seq=128, max_tokens=64)
+    kinds = ["full" if l % 4 == 3 else "gdn" for l in range(dims["n_layers"])]
+    from synth.presets import weight_specs
+    ptrs = {name: FAKE + 4096 * i for i, (name, *_r) in enumerate(weight_specs(dims, kinds))}
+    return cfg, ptrs
+
+
+def _create(L, cfg, w, arena, ab, ws, wb, out=True):
+    h = ctypes.c_void_p()
+    code = L._lib.loop_model_create(ctypes.byref(cfg), ctypes.byref(w) if w is not None else None, arena, ab, ws,
+                                    wb, ctypes.byref(h) if out else None)
+    return code, L.loop_last_error()
+
+
+def test_model_create_rejects_bad_arguments_on_host():
+    import looped_hybrid_attention_amd as L
+    cfg, ptrs = _tiny_create_args(L)
+    ab, wb = L.loop_arena_bytes(cfg), L.loop_workspace_bytes(cfg, cfg.max_tokens)
+    assert ab > 0 and wb > 0
+    w = L.make_weights_struct(cfg.n_layers, ptrs)
+    # no output handle
+    assert _create(L, cfg, w, FAKE, ab, FAKE + (1 << 36), wb, out=False)[0] == LOOP_EINVAL
+    # weights missing, a layer's matrix missing, mHC parameters missing
+    code, msg = _create(L, cfg, None, FAKE, ab, FAKE + (1 << 36), wb)
+    assert code == LOOP_EINVAL and "weights" in msg
+    for drop, needle in (("L5.w_in", "layer 5"), ("L3.q_norm", "q_norm"), ("L0.o_norm", "o_norm"),
+                         ("L6.mhc.mix", "mHC"), ("embed", "embed"), ("final_norm", "final_norm")):
+        p = dict(ptrs)
+        del p[drop]
+        code, msg = _create(L, cfg, L.make_weights_struct(cfg.n_layers, p), FAKE, ab, FAKE + (1 << 36), wb)
+        assert code == LOOP_EINVAL and needle in msg, (drop, msg)
+    # n_layers mismatch
+    w_short = L.make_weights_struct(cfg.n_layers - 4, ptrs)
+    assert _create(L, cfg, w_short, FAKE, ab, FAKE + (1 << 36), wb)[0] == LOOP_EINVAL
+    # arena / workspace too small or missing
+    code, msg = _create(L, cfg, w, FAKE, ab - 1, FAKE + (1 << 36), wb)
+    assert code == LOOP_ECAPACITY and "arena" in msg
+    assert _create(L, cfg, w, 0, ab, FAKE + (1 << 36), wb)[0] == LOOP_ECAPACITY
+    code, msg = _create(L, cfg, w, FAKE, ab, FAKE + (1 << 36), wb - 1)
+    assert code == LOOP_ECAPACITY and "workspace" in msg
+    assert _create(L, cfg, w, FAKE, ab, 0, wb)[0] == LOOP_ECAPACITY
+    # misaligned buffers
+    code, msg = _create(L, cfg, w, FAKE + 16, ab, FAKE + (1 << 36), wb)
+    assert code == LOOP_EINVAL and "aligned" in msg
+    assert _create(L, cfg, w, FAKE, ab, FAKE + (1 << 36) + 128, wb)[0] == LOOP_EINVAL
+    # unsupported dimensions are a configuration error
+    bad = L.make_config(dict(synth.preset("tiny"), head_dim=96), max_batch=2, max_seq=128, max_tokens=64)
+    assert _create(L, bad, w, FAKE, ab, FAKE + (1 << 36), wb)[0] in (LOOP_EINVAL, LOOP_ESHAPE)
+
+
+def test_model_create_valid_arguments_reach_the_device_query():
+    """With every argument valid the only remaining check is the device: on a
+    host without a gfx950 GPU the call fails with a HIP or device error (and
+    creates nothing), never a crash."""
+    import looped_hybrid_attention_amd as L
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: creation would succeed")
+    cfg, ptrs = _tiny_create_args(L)
+    ab, wb = L.loop_arena_bytes(cfg), L.loop_workspace_bytes(cfg, cfg.max_tokens)
+    w = L.make_weights_struct(cfg.n_layers, ptrs)
+    code, msg = _create(L, cfg, w, FAKE, ab, FAKE + (1 << 36), wb)
+    assert code in (LOOP_EHIP, LOOP_EDEVICE), (code, msg)

@@ -89,7 +89,7 @@ def test_verify_k5_then_rollback(tiny):
         assert el <= tol_l and eh <= tol_h
         for j in range(K):
             assert int(nx_g[b * K + j]) == int(np.argmax(lg_g[b * K + j]))
-            assert argmax_ok(int(nx_g[b * K + j]), ev[0][0][j], tol_l), (b, j)
+            assert argmax_ok(int(nx_g[b * K + j]), [e[0][j] for e in ev], tol_l), (b, j)
         for i, e in enumerate(TAPS):
             assert rel_err(tp_g[i, b * K:(b + 1) * K], ev[0][2][e]) <= bar([x[2][e] for x in ev]), (b, e)
 
