@@ -398,6 +398,25 @@ int loop_op_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, void* C
                  const float* R, int32_t M, int32_t N, int32_t K, int32_t epi, float* d_ws,
                  size_t ws_bytes, void* stream);
 
+/* GEMM that allocates nothing: loop_op_gemm for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same operands,
+ * epilogues, kernels and results as loop_op_gemm given a large enough d_ws;
+ * the split-K partials of small-M calls live in a static device array of the
+ * library instead (LOOP_GEMM_STATIC_SCRATCH_BYTES, one copy per GPU, held
+ * until the process ends).  Takes at most LOOP_GEMM_STATIC_MAX_ROWS rows
+ * (decode-sized products); a call whose partials would not fit the array is
+ * rejected with LOOP_ECAPACITY (nothing enqueued).  No hipMalloc / hipFree:
+ * the device address of the array is looked up once per device on the
+ * first call there.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other threads) race; calls ordered
+ * on one stream do not.  Every partial a call reads is written by that call
+ * first, so the array needs no clearing. */
+#define LOOP_GEMM_STATIC_SCRATCH_BYTES (32u << 20)
+#define LOOP_GEMM_STATIC_MAX_ROWS 64
+int loop_op_gemm_static(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+                        const float* R, int32_t M, int32_t N, int32_t K, int32_t epi, void* stream);
+
 /* -------------------------------------------------- synthetic inputs
  * Device implementation of the seeded input generator (Philox4x32-10,
  * Salmon et al. SC'11, + Box-Muller in float64): element i of stream

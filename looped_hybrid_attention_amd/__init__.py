@@ -119,6 +119,8 @@ def _load():
         "loop_profile_read": (ctypes.c_int, [_vp, P(_f64), P(_i64)]),
         "loop_op_gemm": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
                                         _i32, _vp, _sz, _vp]),
+        "loop_op_gemm_static": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
+                                               _i32, _vp]),
         "loop_synth_normal": (ctypes.c_int, [_vp, _i64, _i32, _u32, _u32, _i64, _f64, _f64, _vp]),
         "loop_synth_token_ids": (ctypes.c_int, [_vp, _i64, _u32, _u32, _u32, _vp]),
     }
@@ -192,6 +194,15 @@ def loop_op_gemm(A: int, lda: int, B: int, ldb: int, C: int, ldc: int, R: int, M
                  K: int, epi: int, stream: int = 0, ws: int = 0, ws_bytes: int = 0) -> None:
     _check(_lib.loop_op_gemm(A, lda, B, ldb, C, ldc, R or None, M, N, K, epi, ws or None, ws_bytes,
                              stream or None))
+
+
+LOOP_GEMM_STATIC_SCRATCH_BYTES = 32 << 20
+LOOP_GEMM_STATIC_MAX_ROWS = 64
+
+
+def loop_op_gemm_static(A: int, lda: int, B: int, ldb: int, C: int, ldc: int, R: int, M: int, N: int,
+                        K: int, epi: int, stream: int = 0) -> None:
+    _check(_lib.loop_op_gemm_static(A, lda, B, ldb, C, ldc, R or None, M, N, K, epi, stream or None))
 
 
 def loop_synth_normal(dst: int, n: int, dtype: int, seed: int, key: int, start: int, std: float,

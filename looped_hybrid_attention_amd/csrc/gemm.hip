@@ -812,14 +812,25 @@ void launch_skinny_mt(dim3 grid, hipStream_t s, const GemmArgs& g, uint32_t a_by
     hipLaunchKernelGGL((gemm_skinny_kernel<EPI, SPLIT, NW, QB, 4>), grid, dim3(64 * NW), 0, s, g, a_bytes, b_bytes);
 }
 
+// Split-K plans of the small-M paths: the split count a call takes when its
+// partial buffer is large enough (shared by the launchers and
+// gemm_small_m_partial_bytes).
+template <int EPI, int NW>
+int skinny_splits(const GemmArgs& g) {
+  const int per = (EPI == LOOP_EPI_SWIGLU) ? 8 * NW : 16 * NW;  // output columns per workgroup
+  const int tiles = (g.N + per - 1) / per;
+  int splits = 1;
+  while (tiles * splits < 256 && g.K % (SK_KC * SK_NSET * splits * 2) == 0) splits *= 2;
+  return splits;
+}
+
 // M <= 64, K range of every workgroup a multiple of SK_NSET chunks, operands
 // within 32-bit buffer offsets.
 template <int EPI, int NW>
 hipError_t launch_skinny_w(GemmArgs g, size_t ws_bytes, uint32_t a_bytes, uint32_t b_bytes, hipStream_t s) {
   const int per = (EPI == LOOP_EPI_SWIGLU) ? 8 * NW : 16 * NW;  // output columns per workgroup
   const int tiles = (g.N + per - 1) / per;
-  int splits = 1;
-  while (tiles * splits < 256 && g.K % (SK_KC * SK_NSET * splits * 2) == 0) splits *= 2;
+  const int splits = skinny_splits<EPI, NW>(g);
   const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
   if (splits > 1 && g.part && need <= ws_bytes) {
     g.kslice = g.K / splits;
@@ -869,7 +880,7 @@ hipError_t launch_db(const GemmArgs& g, uint32_t a_bytes, uint32_t b_bytes, hipS
 // tiles * splits reaches ~256-512 workgroups, if a large enough partial buffer
 // is given.
 template <int EPI>
-hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
+int small_splits(const GemmArgs& g) {
   constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? 64 : 128;
   const int tiles = ((g.M + 63) / 64) * ((g.N + OUT_BN - 1) / OUT_BN);
   // fewer splits mean fewer fp32 partials to write and sum; measured on the
@@ -885,12 +896,29 @@ hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
   } else {
     while (tiles * splits < target && g.K % (64 * splits * 2) == 0 && g.K / (splits * 2) >= 256) splits *= 2;
   }
+  return splits;
+}
+
+template <int EPI>
+hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
+  const int splits = small_splits<EPI>(g);
   const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
   if (splits > 1 && g.part && need <= ws_bytes) {
     g.kslice = g.K / splits;
     return launch_cfg<64, 128, 2, 2, EPI, true>(g, splits, s);
   }
   return launch_cfg<64, 128, 2, 2, EPI, false>(g, 1, s);
+}
+
+// Measured on the decode shapes (64 rows): the skinny tiles win where the
+// output has at most 4096 columns and K at most 4096; the register-staged
+// 64 x 128 tiles stream the wider and deeper weight matrices faster.
+template <int EPI>
+bool skinny_fits(const GemmArgs& g) {
+  const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
+  const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
+  return g.M <= 64 && g.N <= 4096 && g.K <= 4096 && g.K % (SK_KC * SK_NSET) == 0 && g.lda % 8 == 0 &&
+         g.ldb % 8 == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31);
 }
 
 // Large M: 256 x 256 tiles; small M (decode): 64 x 128 tiles, split K.
@@ -939,17 +967,19 @@ hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
     }
     return launch_cfg<256, 256, 2, 4, EPI, false>(g, 1, s);
   }
-  {
+  if (skinny_fits<EPI>(g)) {
     const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
-    const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
-    // measured on the decode shapes (64 rows): these tiles win where the
-    // output has at most 4096 columns and K at most 4096; the register-staged
-    // 64 x 128 tiles stream the wider and deeper weight matrices faster
-    if (g.M <= 64 && g.N <= 4096 && g.K <= 4096 && g.K % (SK_KC * SK_NSET) == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 && a_bytes < (1ll << 31) &&
-        b_bytes < (1ll << 31))
-      return launch_skinny<EPI>(g, ws_bytes, (uint32_t)a_bytes, (uint32_t)b_bytes, s);
+    return launch_skinny<EPI>(g, ws_bytes, (uint32_t)((int64_t)g.M * g.lda * 2), (uint32_t)(rows_b * g.ldb * 2), s);
   }
   return launch_small<EPI>(g, ws_bytes, s);
+}
+
+// Split-K partial bytes of a call with M < 512 rows when its buffer is large
+// enough (0: the call does not split).
+template <int EPI>
+size_t small_m_partial_bytes(const GemmArgs& g) {
+  const int splits = skinny_fits<EPI>(g) ? skinny_splits<EPI, SK_WAVES>(g) : small_splits<EPI>(g);
+  return splits > 1 ? (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float) : 0;
 }
 
 // Weight-only int8 / int4 (decode, M <= 64): the skinny tiles over the
@@ -1037,6 +1067,18 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, v
     case LOOP_EPI_SWIGLU: return launch_epi<LOOP_EPI_SWIGLU>(g, ws_bytes, s);
   }
   return hipErrorInvalidValue;
+}
+
+size_t gemm_small_m_partial_bytes(int M, int N, int K, int epi, int64_t lda, int64_t ldb) {
+  if (M <= 0 || M >= 512) return 0;
+  GemmArgs g{nullptr, lda, nullptr, ldb, nullptr, N, nullptr, M, N, K, N, nullptr, K};
+  switch (epi) {
+    case LOOP_EPI_BF16: return small_m_partial_bytes<LOOP_EPI_BF16>(g);
+    case LOOP_EPI_F32: return small_m_partial_bytes<LOOP_EPI_F32>(g);
+    case LOOP_EPI_F32_RES: return small_m_partial_bytes<LOOP_EPI_F32_RES>(g);
+    case LOOP_EPI_SWIGLU: return small_m_partial_bytes<LOOP_EPI_SWIGLU>(g);
+  }
+  return 0;
 }
 
 hipError_t launch_gemm_norm(const void* A, int64_t lda, const void* B, int64_t ldb, float* C, int64_t ldc,

@@ -12,6 +12,10 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* B, int64_t ldb, v
                        const float* R, int M, int N, int K, int epi, hipStream_t s, float* ws = nullptr,
                        size_t ws_bytes = 0);
 
+// Split-K partial bytes that launch_gemm uses for a call of M < 512 rows when
+// its buffer is large enough (0: the call does not split; M >= 512: 0).
+size_t gemm_small_m_partial_bytes(int M, int N, int K, int epi, int64_t lda, int64_t ldb);
+
 // C = A . B^T (+ R) as launch_gemm (fp32 output), then
 // hn[m] = bf16(RMSNorm(C[m] + X2[m]; gain)) (X2 may be NULL; rows of C and
 // X2 share the stride ldc; hn rows are N apart).
