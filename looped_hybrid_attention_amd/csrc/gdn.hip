@@ -15,36 +15,43 @@
 //   U = U~ - W S0^T
 //   O = diag(gamma) Q S0^T + (tril(exp(G_r - G_i)) * Q K^T) U
 //   S_C = gamma_C S0 + U^T diag(exp(G_C - G)) K.
-// The chunk-local part runs for all chunks in parallel; the carry of S is
-// sequential over chunks but independent per row of S, so it is split over
-// workgroups along Dv.
+// With q^ = q qs / |q| and k^ = k / |k|, the normalisations become row scales
+// of the raw bf16 projections, which are then exact MFMA operands:
+//   W = (T diag(beta gamma / |k|)) K,  U~ = (T diag(beta)) V,
+//   Mqk[t][i] = exp(G_t - G_i) qs / (|q_t| |k_i|) (q_t . k_i)   (i <= t),
+//   O = diag(gamma qs / |q|) Q S0^T + Mqk U,
+//   S_C = gamma_C S0 + (diag(exp(G_C - G) / |k|) U)^T K.
+// Three kernels: the chunk-local part for all chunks in parallel (prep: W,
+// U~, Mqk and the row scales), the carry of S over the chunks (scan: the rows
+// of S are independent, so a head's rows are split over workgroups; it keeps
+// each chunk's entering state S0 and its U), and the chunk outputs for all
+// chunks in parallel (out: O from S0 and U, then RMSNorm over Dv times
+// SiLU(z)).  Every product runs on the bf16 MFMA with fp32
+// accumulation: a raw projection is an exact bf16 operand, and an fp32
+// operand x enters as three bf16 parts hi = bf16(x), mid = bf16(x - hi),
+// lo = bf16(x - hi - mid) (24 significant bits, the fp32 value up to its last
+// bit): against an exact operand three products, against another split
+// operand the six whose parts' weights reach 2^-24, so the state and the
+// recurrence keep fp32 accuracy.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace {
 
 constexpr int CH = 64;   // chunk length
+constexpr int SCS = 2 * CH + 4;  // row scales per chunk: sq[CH], dk[CH], gC (padded)
 
 DEV float softplusf_(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 
-// fp32 MFMA 16x16x4 tile products from LDS (row-major operands).  Lane l
-// supplies A[m = l%16][k = l/16] and B[k = l/16][n = l%16]; the result D
-// holds rows 4*(l/16) + r (r = 0..3) of column l%16.
-DEV f32x4 mfma16x16x4f32(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-// acc += A[0:16, 0:K] . B[0:16, 0:K]^T
-DEV void mm_nt(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
-  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
-  const float* a = A + i * lda + kk;
-  const float* b = B + i * ldb + kk;
-#pragma unroll
-  for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k], b[k], acc);
-}
-// The same MFMA with its result kept apart from its C operand: C stays live
-// until the result exists, so the registers cannot partially overlap (the
-// compiler otherwise may place a chain's result one register pair off its C
-// operand, which the hardware does not compute correctly).
+// The 16x16 blocks of the chunk inverse use the fp32 MFMA 16x16x4.  Lane l
+// supplies A[m = l%16][k = l/16] and B[k = l/16][n = l%16]; the result D holds
+// rows 4*(l/16) + r (r = 0..3) of column l%16.  The result is kept apart from
+// its C operand: C stays live until the result exists, so the registers cannot
+// partially overlap (the compiler otherwise may place a chain's result one
+// register pair off its C operand, which the hardware does not compute
+// correctly).
 DEV f32x4 mfma16x16x4f32_apart(float a, float b, f32x4 c) {
   const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   asm volatile("" ::"v"(c), "v"(d));
@@ -58,210 +65,147 @@ DEV void mm_nn16_apart(f32x4& acc, const float* A, int lda, const float* B, int 
 #pragma unroll
   for (int k = 0; k < 16; k += 4) acc = mfma16x16x4f32_apart(a[k], b[k * ldb], acc);
 }
-// acc += A[0:16, 0:K] . B[0:K, 0:16]
-DEV void mm_nn(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
-  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
-  const float* a = A + i * lda + kk;
-  const float* b = B + kk * ldb + i;
-#pragma unroll
-  for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k], b[k * ldb], acc);
-}
-// acc += A[0:K, 0:16]^T . B[0:K, 0:16]
-DEV void mm_tn(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
-  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
-  const float* a = A + kk * lda + i;
-  const float* b = B + kk * ldb + i;
-#pragma unroll
-  for (int k = 0; k < K; k += 4) acc = mfma16x16x4f32(a[k * lda], b[k * ldb], acc);
-}
 
-// Two products in one pass (independent MFMA chains, so the second issues
-// while the first is in flight).
-// acc0 += A0[0:16, 0:K] . B[0:16, 0:K]^T, acc1 += A1[0:16, 0:K] . B[0:16, 0:K]^T
-DEV void mm_nt2(f32x4& acc0, f32x4& acc1, const float* A0, const float* A1, int lda, const float* B, int ldb,
-                int K) {
-  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
-  const float* a0 = A0 + i * lda + kk;
-  const float* a1 = A1 + i * lda + kk;
-  const float* b = B + i * ldb + kk;
-#pragma unroll
-  for (int k = 0; k < K; k += 4) {
-    const float bk = b[k];
-    acc0 = mfma16x16x4f32(a0[k], bk, acc0);
-    acc1 = mfma16x16x4f32(a1[k], bk, acc1);
-  }
+// fp32 -> (hi, lo) bf16 pair: hi = bf16(x), lo = bf16(x - hi) (x - hi is exact)
+DEV void split_bf16(float x, bf16& hi, bf16& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - (float)hi);
 }
-// acc0 += A0[0:16, 0:K] . B0[0:K, 0:16], acc1 += A1[0:16, 0:K] . B1[0:K, 0:16]
-DEV void mm_nn2(f32x4& acc0, f32x4& acc1, const float* A0, const float* A1, int lda, const float* B0,
-                const float* B1, int ldb, int K) {
-  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
-  const float* a0 = A0 + i * lda + kk;
-  const float* a1 = A1 + i * lda + kk;
-  const float* b0 = B0 + kk * ldb + i;
-  const float* b1 = B1 + kk * ldb + i;
-#pragma unroll
-  for (int k = 0; k < K; k += 4) {
-    acc0 = mfma16x16x4f32(a0[k], b0[k * ldb], acc0);
-    acc1 = mfma16x16x4f32(a1[k], b1[k * ldb], acc1);
-  }
+// fp32 -> three bf16 parts, x = hi + mid + lo to fp32's last bit (each
+// difference is exact)
+DEV void split3(float x, bf16& hi, bf16& mid, bf16& lo) {
+  hi = f2bf(x);
+  const float r = x - (float)hi;
+  mid = f2bf(r);
+  lo = f2bf(r - (float)mid);
 }
-
-// acc0 += A . B0^T, acc1 += A . B1^T (shared A, [16][K] row-major operands)
-DEV void mm_nt2s(f32x4& acc0, f32x4& acc1, const float* A, int lda, const float* B0, const float* B1, int ldb,
-                 int K) {
-  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
-  const float* a = A + i * lda + kk;
-  const float* b0 = B0 + i * ldb + kk;
-  const float* b1 = B1 + i * ldb + kk;
-#pragma unroll
-  for (int k = 0; k < K; k += 4) {
-    const float ak = a[k];
-    acc0 = mfma16x16x4f32(ak, b0[k], acc0);
-    acc1 = mfma16x16x4f32(ak, b1[k], acc1);
-  }
-}
-// acc += A[0:16, 0:K] . B[0:16, 0:K]^T as two interleaved chains (K % 8 == 0)
-DEV void mm_nt_ilp(f32x4& acc, const float* A, int lda, const float* B, int ldb, int K) {
-  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
-  const float* a = A + i * lda + kk;
-  const float* b = B + i * ldb + kk;
-  f32x4 acc1 = {0, 0, 0, 0};
-#pragma unroll
-  for (int k = 0; k < K; k += 8) {
-    acc = mfma16x16x4f32(a[k], b[k], acc);
-    acc1 = mfma16x16x4f32(a[k + 4], b[k + 4], acc1);
-  }
-  acc += acc1;
-}
-// acc0 += A[0:K, 0:16]^T . B0[0:K, 0:16], acc1 += A[0:K, 0:16]^T . B1[0:K, 0:16]
-DEV void mm_tn2(f32x4& acc0, f32x4& acc1, const float* A, int lda, const float* B0, const float* B1, int ldb,
-                int K) {
-  const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
-  const float* a = A + kk * lda + i;
-  const float* b0 = B0 + kk * ldb + i;
-  const float* b1 = B1 + kk * ldb + i;
-#pragma unroll
-  for (int k = 0; k < K; k += 4) {
-    const float ak = a[k * lda];
-    acc0 = mfma16x16x4f32(ak, b0[k * ldb], acc0);
-    acc1 = mfma16x16x4f32(ak, b1[k * ldb], acc1);
-  }
-}
-
-// Operand staging for the fp32 MFMA with K read ahead: lane group kk takes
-// the contiguous quarter k = kk K/4 .. of K (a permutation of K, applied to
-// both operands of a product), so row operands are 128-bit LDS reads and all
-// reads are issued before the MFMAs.
-// this lane's quarter of row l%16 of a [16][K] row-major operand
-template <int K>
-DEV void row_quarter(float (&v)[K / 4], const float* A, int lda) {
-  const int l = threadIdx.x & 63;
-  const float* r = A + (l & 15) * lda + (l >> 4) * (K / 4);
-#pragma unroll
-  for (int q = 0; q < K / 16; ++q) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(r + 4 * q);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
-  }
-}
-// this lane's quarter of column l%16 of a [K][16] row-major operand
-template <int K>
-DEV void col_quarter(float (&v)[K / 4], const float* B, int ldb) {
-  const int l = threadIdx.x & 63;
-  const float* c = B + (l >> 4) * (K / 4) * ldb + (l & 15);
-#pragma unroll
-  for (int q = 0; q < K / 4; ++q) v[q] = c[q * ldb];
-}
-// acc0 += a0 . b0, acc1 += a1 . b1 over staged quarters (two chains)
-template <int K>
-DEV void mma2(f32x4& acc0, f32x4& acc1, const float (&a0)[K / 4], const float (&b0)[K / 4],
-              const float (&a1)[K / 4], const float (&b1)[K / 4]) {
-#pragma unroll
-  for (int q = 0; q < K / 4; ++q) {
-    acc0 = mfma16x16x4f32(a0[q], b0[q], acc0);
-    acc1 = mfma16x16x4f32(a1[q], b1[q], acc1);
-  }
-}
-
-// Chunk workspace layout, per (seq b, head h, chunk c), fp32:
-//   W, Qp, Up: [CH][DK]; UtT = Ut^T [DV][CH] and KdT = Kd^T [DK][CH]
-//   (transposed: the scan reads them along the chunk's tokens); gC;
-//   S_c (entry state) [DV][DK].
-struct ChunkPtr {
-  float *W, *UtT, *KdT, *Qp, *Up, *S;
-  float* gC;
+DEV uint16_t bits(bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+struct Split8 {
+  bf16x8 h, m, l;
 };
-DEV ChunkPtr chunk_ptr(const GdnArgs& a, int b, int h, int c, int DK) {
-  const int64_t cb = ((int64_t)b * a.H + h) * a.n_chunks + c;
-  const int64_t mat = (int64_t)CH * DK;
-  ChunkPtr p;
-  p.W = a.W + cb * mat;
-  p.UtT = a.Ut + cb * mat;
-  p.KdT = a.Kd + cb * mat;
-  p.Qp = a.Qg + cb * mat;
-  p.Up = a.Mqk + cb * mat;
-  p.S = a.Sc + cb * (int64_t)DK * DK;
-  p.gC = a.gC + cb;
-  return p;
+DEV Split8 split8(const float (&x)[8]) {
+  Split8 s;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bf16 a, b, c;
+    split3(x[e], a, b, c);
+    s.h[e] = a;
+    s.m[e] = b;
+    s.l[e] = c;
+  }
+  return s;
+}
+DEV Split8 split8(const f32x4& x0, const f32x4& x1) {
+  const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  return split8(x);
+}
+// acc += a . b for a split operand and an exact one (three products)
+DEV f32x4 mma_se(const Split8& a, const bf16x8& b, f32x4 acc) {
+  acc = mfma16x16x32(a.h, b, acc);
+  acc = mfma16x16x32(a.m, b, acc);
+  return mfma16x16x32(a.l, b, acc);
+}
+DEV f32x4 mma_es(const bf16x8& a, const Split8& b, f32x4 acc) {
+  acc = mfma16x16x32(a, b.h, acc);
+  acc = mfma16x16x32(a, b.m, acc);
+  return mfma16x16x32(a, b.l, acc);
+}
+// acc += a . b for two split operands: the six products of weight >= 2^-24
+// (smallest first)
+DEV f32x4 mma_ss(const Split8& a, const Split8& b, f32x4 acc) {
+  acc = mfma16x16x32(a.h, b.l, acc);
+  acc = mfma16x16x32(a.l, b.h, acc);
+  acc = mfma16x16x32(a.m, b.m, acc);
+  acc = mfma16x16x32(a.h, b.m, acc);
+  acc = mfma16x16x32(a.m, b.h, acc);
+  return mfma16x16x32(a.h, b.h, acc);
+}
+DEV bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+DEV bf16x8 glb8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// A transposed [DK][CH] bf16 tile (row k holds the chunk's 64 tokens) keeps
+// its 16-byte groups of 8 tokens in the order g ^ kt_swz(k): the transposing
+// 2-byte writes (8 consecutive k of one token per thread) and the 16-byte
+// operand reads (16 consecutive k, one group each) then spread over the LDS
+// banks.
+DEV int kt_swz(int k) { return (k & 7) ^ ((k >> 3) & 7); }
+DEV int kt_at(int k, int t) { return k * CH + 8 * ((t >> 3) ^ kt_swz(k)) + (t & 7); }
+
+// Chunk workspace of (sequence b, head h, chunk c): cb = (b H + h) n_chunks + c.
+DEV int64_t chunk_index(const GdnArgs& a, int b, int h, int c) {
+  return ((int64_t)b * a.H + h) * a.n_chunks + c;
 }
 
 // ------------------------------------------------------- chunk prep
-// grid (chunk, head, seq), eight waves (two per SIMD, so that one's LDS reads
-// overlap the other's MFMAs).  Writes W = T diag(beta gamma) K, Ut = T diag(beta) V,
-// Kd = exp(G_C - G) K, Qp = gamma Q - Mqk W and Up = Mqk Ut, and gC, where
-// Mqk = tril(exp(G_r - G_i)) * Q K^T and T = (I + A)^-1.  In the products
-// wave w takes the 16-row tile w % 4 and half (w / 4) of the column tiles.
-constexpr int PNT = 512;
+// grid (chunk, head, seq), four waves.  From the chunk's raw q, k, v (bf16),
+// a and b: the row norms, the cumulative log-gates G and beta; K K^T and
+// Q K^T on the MFMA (raw operands); A and Mqk with their row / column scales;
+// T = (I + A)^-1 in fp32 (diagonal 16x16 blocks by forward substitution,
+// then the blocks below by block diagonals); W and U~ (T's scaled rows as
+// split operands against the raw K^T, V^T).  Writes W [CH][Dk], U~^T
+// [Dv][CH], Mqk (fp32), the raw K^T tile (bf16, kt_at order) and the row
+// scales sq = gamma qs / |q|,
+// dk = exp(G_C - G) / |k| and gC = exp(G_C).  Rows past the sequence's end
+// are zero (q = k = v = 0, beta = 0, no decay).  The barriers order LDS
+// accesses only: the global stores stay in flight.
+constexpr int PNT = 256;
 template <int DK>
-__global__ __launch_bounds__(PNT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
+constexpr int prep_lds_bytes() {
+  return (2 * CH * (DK + 8) + 2 * DK * CH) * 2 + (2 * CH * (CH + 4) + 4 * 16 * 20 + 6 * CH) * 4;
+}
+template <int DK>
+__global__ __launch_bounds__(PNT, 1) void gdn_prep_kernel(GdnArgs a) {
   constexpr int DV = DK;
-  constexpr int LD = DK + 4;   // [CH][DK] rows
-  constexpr int LC = CH + 4;   // [CH][CH] rows
+  constexpr int LR = DK + 8;   // bf16 stride of the [CH][DK] rows
+  constexpr int LA = CH + 4;   // fp32 stride of the [CH][CH] rows
   constexpr int XS = 20;       // rows of the 16x16 inverse scratch
-  extern __shared__ __align__(16) float gsm[];
-  float* sQ = gsm;                 // q^ ; later unchanged
-  float* sK = sQ + CH * LD;        // k^ ; later W
-  float* sV = sK + CH * LD;        // v  ; later Ut
-  float* sA = sV + CH * LD;        // A ; later T diag(beta gamma)
-  float* sT2 = sA + CH * LC;       // T diag(beta)
-  float* sM = sT2 + CH * LC;       // Mqk
-  float* sG = sM + CH * LC;        // cumulative log alpha
-  float* sB = sG + CH;             // beta
-  float* sEG = sB + CH;            // exp(G_r)
-  float* sEK = sEG + CH;           // exp(G_C - G_r)
-  float* sX = sEK + CH;            // [4][16][XS] products of the blocked inverse
+  constexpr int PPR = DK / 8;  // 16-byte pieces per row
+  constexpr int NP = CH * PPR / PNT;
+  static_assert(NP * PNT == CH * PPR && PPR <= 64, "row pieces");
+  extern __shared__ __align__(16) uint8_t prep_smem[];
+  uint16_t* sQ = reinterpret_cast<uint16_t*>(prep_smem);  // [CH][LR] raw q
+  uint16_t* sK = sQ + CH * LR;                            // [CH][LR] raw k
+  uint16_t* sKt = sK + CH * LR;                           // [DK][CH] raw k transposed (kt_at)
+  uint16_t* sVt = sKt + DK * CH;                          // [DV][CH] raw v transposed (kt_at)
+  float* sA = reinterpret_cast<float*>(sVt + DV * CH);    // [CH][LA] A
+  float* sT = sA + CH * LA;                               // [CH][LA] T
+  float* sX = sT + CH * LA;                               // [4][16][XS]
+  float* sG = sX + 4 * 16 * XS;                           // cumulative log alpha
+  float* sB = sG + CH;                                    // beta
+  float* sNq = sB + CH;                                   // qs / |q|
+  float* sNk = sNq + CH;                                  // 1 / |k|
+  float* sSw = sNk + CH;                                  // beta gamma / |k|
+  float* sSu = sSw + CH;                                  // beta
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int t0 = c * CH;
   const int C = min(CH, a.T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
   const int64_t row0 = (int64_t)b * a.T + t0;
-  const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
+  const int64_t cb = chunk_index(a, b, h, c);
 
-  // q, k, v of the chunk's rows: 8 threads per row, DK/8 dims each, every
-  // load issued before any is used; q and k L2-normalised per row.
+  // q, k, v: all loads issued first; PPR consecutive threads hold a row
   {
-    static_assert(CH * 8 == PNT, "8 threads per row");
-    constexpr int PER = DK / 8;      // dims per thread
-    constexpr int NV = PER / 8;      // 16-byte loads per tensor
-    const int r = tid >> 3, part = tid & 7;
-    const bool ok = r < C;
-    const uint16_t* pr = a.proj + (row0 + min(r, C - 1)) * a.proj_stride;
-    const int d0 = part * PER;
-    u32x4 vq[NV], vk[NV], vv[NV];
+    u32x4 vq[NP], vk[NP], vv[NP];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      vq[i] = *reinterpret_cast<const u32x4*>(pr + a.off_q + h * DK + d0 + 8 * i);
-      vk[i] = *reinterpret_cast<const u32x4*>(pr + a.off_k + h * DK + d0 + 8 * i);
-      vv[i] = *reinterpret_cast<const u32x4*>(pr + a.off_v + h * DV + d0 + 8 * i);
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + i * PNT, r = p / PPR, cp = p % PPR;
+      const uint16_t* pr = a.proj + (row0 + min(r, C - 1)) * a.proj_stride;
+      vq[i] = *reinterpret_cast<const u32x4*>(pr + a.off_q + h * DK + cp * 8);
+      vk[i] = *reinterpret_cast<const u32x4*>(pr + a.off_k + h * DK + cp * 8);
+      vv[i] = *reinterpret_cast<const u32x4*>(pr + a.off_v + h * DV + cp * 8);
     }
     float av = 0.f, bv = 0.f;
-    if (part == 0) {
+    if (tid < CH) {
+      const uint16_t* pr = a.proj + (row0 + min(tid, C - 1)) * a.proj_stride;
       av = bf2f(pr[a.off_a + h]);
       bv = bf2f(pr[a.off_b + h]);
     }
-    float sq = 0.f, sk = 0.f;
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
+    for (int i = 0; i < NP; ++i) {
+      const int p = tid + i * PNT, r = p / PPR, cp = p % PPR;
+      if (r >= C) vq[i] = vk[i] = vv[i] = (u32x4){0, 0, 0, 0};
+      float sq = 0.f, sk = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float q = bf2f((uint16_t)(vq[i][e >> 1] >> ((e & 1) * 16)));
@@ -270,27 +214,28 @@ __global__ __launch_bounds__(PNT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
         sk += k * k;
       }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) {
-      sq += __shfl_xor(sq, o, 64);
-      sk += __shfl_xor(sk, o, 64);
-    }
-    const float iq = ok ? rsqrtf(sq + a.eps) * a.q_scale : 0.f;
-    const float ik = ok ? rsqrtf(sk + a.eps) : 0.f;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
+      for (int o = 1; o < PPR; o <<= 1) {
+        sq += __shfl_xor(sq, o, 64);
+        sk += __shfl_xor(sk, o, 64);
+      }
+      if (cp == 0) {
+        sNq[r] = r < C ? rsqrtf(sq + a.eps) * a.q_scale : 0.f;
+        sNk[r] = r < C ? rsqrtf(sk + a.eps) : 0.f;
+      }
+      *reinterpret_cast<u32x4*>(sQ + r * LR + cp * 8) = vq[i];
+      *reinterpret_cast<u32x4*>(sK + r * LR + cp * 8) = vk[i];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = d0 + 8 * i + e;
-        sQ[r * LD + d] = bf2f((uint16_t)(vq[i][e >> 1] >> ((e & 1) * 16))) * iq;
-        sK[r * LD + d] = bf2f((uint16_t)(vk[i][e >> 1] >> ((e & 1) * 16))) * ik;
-        sV[r * LD + d] = ok ? bf2f((uint16_t)(vv[i][e >> 1] >> ((e & 1) * 16))) : 0.f;
+        sKt[kt_at(cp * 8 + e, r)] = (uint16_t)(vk[i][e >> 1] >> ((e & 1) * 16));
+        sVt[kt_at(cp * 8 + e, r)] = (uint16_t)(vv[i][e >> 1] >> ((e & 1) * 16));
       }
-    if (part == 0) {
-      sG[r] = ok ? -softplusf_(av) : 0.f;
-      sB[r] = ok ? sigmoidf_(bv) : 0.f;
+    }
+    if (tid < CH) {
+      sG[tid] = tid < C ? -softplusf_(av) : 0.f;
+      sB[tid] = tid < C ? sigmoidf_(bv) : 0.f;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (wave == 0) {  // inclusive prefix sum of log alpha over the 64 rows
     float g = sG[lane];
 #pragma unroll
@@ -300,49 +245,69 @@ __global__ __launch_bounds__(PNT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
     }
     sG[lane] = g;
   }
-  __syncthreads();
+  lds_barrier();
+  {  // the raw K^T tile (its swizzled LDS layout) for the scan's stage
+    uint16_t* kt = a.Kt + cb * DK * CH;
+#pragma unroll
+    for (int i = 0; i < DK * CH / 8 / PNT; ++i) {
+      const int p = tid + i * PNT;
+      *reinterpret_cast<u32x4*>(kt + 8 * p) = *reinterpret_cast<const u32x4*>(sKt + 8 * p);
+    }
+  }
   const float GC = sG[C - 1];
   if (tid < CH) {
-    sEG[tid] = __expf(sG[tid]);
-    sEK[tid] = __expf(GC - sG[tid]);
+    const float g = sG[tid];
+    sSw[tid] = sB[tid] * __expf(g) * sNk[tid];
+    sSu[tid] = sB[tid];
+    float* sc = a.sc + cb * SCS;
+    sc[tid] = tid < C ? __expf(g) * sNq[tid] : 0.f;             // sq
+    sc[CH + tid] = tid < C ? __expf(GC - g) * sNk[tid] : 0.f;   // dk
+    if (tid == 0) sc[2 * CH] = __expf(GC);                      // gC
   }
-  if (tid == 0) *P.gC = __expf(GC);
-  // A = beta_r exp(G_r - G_i) k_r.k_i (i < r), Mqk = exp(G_r - G_i) q_r.k_i (i <= r)
-  const int rt = wave & 3, ch = wave >> 2;  // row tile, column half of the products
+  // K K^T -> A (strictly lower), Q K^T -> Mqk (lower incl. diagonal): the 10
+  // lower 16x16 tiles of each; wave w takes jobs w, w + 4, ...
   {
-    const int i16 = lane & 15, kk = lane >> 4;
-    float aK[DK / 4], aQ[DK / 4];
-    row_quarter<DK>(aK, sK + rt * 16 * LD, LD);
-    row_quarter<DK>(aQ, sQ + rt * 16 * LD, LD);
+    float* Mq = a.Mq + cb * CH * CH;
+    for (int job = wave; job < 20; job += 4) {
+      const bool qk = job >= 10;
+      int q = qk ? job - 10 : job, I = 0;
+      while (q > I) { q -= I + 1; ++I; }
+      const int J = q;  // tile (I, J), J <= I
+      const uint16_t* src = qk ? sQ : sK;
+      f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int n2 = 0; n2 < CH / 32; ++n2) {
-      const int nt = ch * (CH / 32) + n2;
-      f32x4 kk_acc = {0, 0, 0, 0}, qk_acc = {0, 0, 0, 0};
-      float bK[DK / 4];
-      row_quarter<DK>(bK, sK + nt * 16 * LD, LD);
-      mma2<DK>(kk_acc, qk_acc, aK, bK, aQ, bK);
+      for (int ks = 0; ks < DK / 32; ++ks)
+        acc = mfma16x16x32(lds8(src + (16 * I + l16) * LR + 32 * ks + 8 * lq),
+                           lds8(sK + (16 * J + l16) * LR + 32 * ks + 8 * lq), acc);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = rt * 16 + 4 * kk + r, col = nt * 16 + i16;
+        const int row = 16 * I + 4 * lq + r, col = 16 * J + l16;
         const float dec = col <= row ? __expf(sG[row] - sG[col]) : 0.f;
-        sA[row * LC + col] = col < row ? sB[row] * dec * kk_acc[r] : 0.f;
-        sM[row * LC + col] = col <= row ? dec * qk_acc[r] : 0.f;
+        if (!qk) {
+          sA[row * LA + col] = col < row ? sB[row] * dec * sNk[row] * sNk[col] * acc[r] : 0.f;
+        } else {
+          Mq[row * CH + col] = dec * sNq[row] * sNk[col] * acc[r];
+        }
+      }
+    }
+    // the upper tiles: zero
+    for (int idx = tid; idx < CH * CH; idx += PNT) {
+      const int r = idx / CH, cc = idx % CH;
+      if ((cc >> 4) > (r >> 4)) {
+        sA[r * LA + cc] = 0.f;
+        sT[r * LA + cc] = 0.f;
+        Mq[idx] = 0.f;
       }
     }
   }
-  __syncthreads();
-  // Kd^T = (exp(G_C - G) k^)^T (rows >= C are zero because k^ is)
-  for (int idx = tid; idx < CH * DK; idx += PNT) {
-    const int d = idx / CH, r = idx % CH;
-    P.KdT[idx] = sEK[r] * sK[r * LD + d];
-  }
-  // T = (I + A)^-1 (unit lower triangular) into sT2, in 16 x 16 blocks.
-  // Diagonal blocks by forward substitution (wave w < 4: block w, lane j <
-  // 16 owns column j); then, by block diagonal d = I - J = 1, 2, 3 (one block
-  // per wave), T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ on the MFMA.
-  if (wave < CH / 16) {
-    const int I = wave, j = lane & 15;
-    const float* Ab = sA + (16 * I) * LC + 16 * I;
+  lds_barrier();
+  // T = (I + A)^-1, unit lower triangular.  Diagonal blocks by forward
+  // substitution (wave w: block w, lane j < 16 owns column j); then, by block
+  // diagonal d = I - J = 1, 2, 3 (one block per wave),
+  // T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ on the fp32 MFMA.
+  {
+    const int I = wave, j = l16;
+    const float* Ab = sA + (16 * I) * LA + 16 * I;
     float t[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) t[i] = (i == j) ? 1.f : 0.f;
@@ -350,406 +315,469 @@ __global__ __launch_bounds__(PNT, 1) void gdn_chunk_prep_kernel(GdnArgs a) {
     for (int r = 1; r < 16; ++r) {
       float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < r; ++i) acc += Ab[r * LC + i] * t[i];
+      for (int i = 0; i < r; ++i) acc += Ab[r * LA + i] * t[i];
       t[r] = (r > j) ? -acc : t[r];
     }
     if (lane < 16) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sT2[(16 * I + i) * LC + 16 * I + j] = t[i];
+      for (int i = 0; i < 16; ++i) sT[(16 * I + i) * LA + 16 * I + j] = t[i];
     }
   }
+  lds_barrier();
   {
-    for (int idx = tid; idx < CH * CH; idx += PNT) {  // blocks above the diagonal
-      const int r = idx / CH, cc = idx % CH;
-      if ((cc >> 4) > (r >> 4)) sT2[r * LC + cc] = 0.f;
-    }
-  }
-  __syncthreads();
-  {
-    const int i16 = lane & 15, kk = lane >> 4;
     float* X = sX + wave * 16 * XS;
     for (int d = 1; d < CH / 16; ++d) {
       if (wave < CH / 16 - d) {
         const int J = wave, I = wave + d;
         f32x4 x = {0, 0, 0, 0};
-        for (int K = J; K < I; ++K) mm_nn16_apart(x, sA + 16 * I * LC + 16 * K, LC, sT2 + 16 * K * LC + 16 * J, LC);
+        for (int K = J; K < I; ++K) mm_nn16_apart(x, sA + 16 * I * LA + 16 * K, LA, sT + 16 * K * LA + 16 * J, LA);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) X[(4 * kk + r) * XS + i16] = x[r];
+        for (int r = 0; r < 4; ++r) X[(4 * lq + r) * XS + l16] = x[r];
         f32x4 y = {0, 0, 0, 0};
-        mm_nn16_apart(y, sT2 + 16 * I * LC + 16 * I, LC, X, XS);
+        mm_nn16_apart(y, sT + 16 * I * LA + 16 * I, LA, X, XS);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sT2[(16 * I + 4 * kk + r) * LC + 16 * J + i16] = -y[r];
+        for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * lq + r) * LA + 16 * J + l16] = -y[r];
       }
-      __syncthreads();
+      lds_barrier();
     }
   }
-  // T diag(beta gamma) -> sA (A is no longer needed), T diag(beta) -> sT2
-  for (int idx = tid; idx < CH * CH; idx += PNT) {
-    const int r = idx / CH, cc = idx % CH;
-    const float tv = sT2[r * LC + cc];
-    sA[r * LC + cc] = tv * sB[cc] * sEG[cc];
-    sT2[r * LC + cc] = tv * sB[cc];
-  }
-  __syncthreads();
-  // W = (T diag(beta gamma)) K^, Ut = (T diag(beta)) V; wave w: rows of tile
-  // w % 4, column tiles of half w / 4
-  constexpr int NTILE = DK / 16 / 2;
-  f32x4 wacc[NTILE], uacc[NTILE];
+  // W = (T diag(beta gamma / |k|)) K and U~ = (T diag(beta)) V: wave w takes
+  // the rows of tile w; its A operands (the scaled rows of T, split in three
+  // bf16 parts) once, then every column tile of W and of U~
   {
-    float a0[CH / 4], a1[CH / 4];
-    row_quarter<CH>(a0, sA + rt * 16 * LC, LC);
-    row_quarter<CH>(a1, sT2 + rt * 16 * LC, LC);
+    Split8 tw_[CH / 32], tu_[CH / 32];
 #pragma unroll
-    for (int n = 0; n < NTILE; ++n) {
-      const int nt = ch * NTILE + n;
-      wacc[n] = (f32x4){0, 0, 0, 0};
-      uacc[n] = (f32x4){0, 0, 0, 0};
-      float b0[CH / 4], b1[CH / 4];
-      col_quarter<CH>(b0, sK + nt * 16, LD);
-      col_quarter<CH>(b1, sV + nt * 16, LD);
-      mma2<CH>(wacc[n], uacc[n], a0, b0, a1, b1);
+    for (int is = 0; is < CH / 32; ++is) {
+      const float* tr = sT + (16 * wave + l16) * LA + 32 * is + 8 * lq;
+      float xw[8], xu[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 32 * is + 8 * lq + e;
+        xw[e] = tr[e] * sSw[i];
+        xu[e] = tr[e] * sSu[i];
+      }
+      tw_[is] = split8(xw);
+      tu_[is] = split8(xu);
     }
-  }
-  __syncthreads();  // sK, sV fully read: reuse them for W and Ut
-  {
-    const int i16 = lane & 15, kk = lane >> 4;
+    float* W = a.W + cb * CH * DK;
+    float* Ut = a.Ut + cb * CH * DV;
+#pragma unroll 2
+    for (int nt = 0; nt < DK / 16; ++nt) {
+      f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int n = 0; n < NTILE; ++n)
+      for (int is = 0; is < CH / 32; ++is) acc = mma_se(tw_[is], lds8(sKt + kt_at(16 * nt + l16, 32 * is + 8 * lq)), acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rt * 16 + 4 * kk + r, col = (ch * NTILE + n) * 16 + i16;
-        const bool ok = row < C;
-        const float w = ok ? wacc[n][r] : 0.f, u = ok ? uacc[n][r] : 0.f;
-        sK[row * LD + col] = w;
-        sV[row * LD + col] = u;
-        P.W[row * DK + col] = w;
-      }
-  }
-  __syncthreads();
-  for (int idx = tid; idx < CH * DV; idx += PNT) {  // Ut^T
-    const int d = idx / CH, r = idx % CH;
-    P.UtT[idx] = sV[r * LD + d];
-  }
-  // Qp = gamma Q - Mqk W, Up = Mqk Ut
-  {
-    const int i16 = lane & 15, kk = lane >> 4;
-    float am[CH / 4];
-    row_quarter<CH>(am, sM + rt * 16 * LC, LC);
+      for (int r = 0; r < 4; ++r) W[(16 * wave + 4 * lq + r) * DK + 16 * nt + l16] = acc[r];
+    }
+#pragma unroll 2
+    for (int nt = 0; nt < DV / 16; ++nt) {
+      f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int n = 0; n < NTILE; ++n) {
-      const int nt = ch * NTILE + n;
-      f32x4 mw = {0, 0, 0, 0}, mu = {0, 0, 0, 0};
-      float b0[CH / 4], b1[CH / 4];
-      col_quarter<CH>(b0, sK + nt * 16, LD);
-      col_quarter<CH>(b1, sV + nt * 16, LD);
-      mma2<CH>(mw, mu, am, b0, am, b1);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = rt * 16 + 4 * kk + r, col = nt * 16 + i16;
-        const bool ok = row < C;
-        P.Qp[row * DK + col] = ok ? sEG[row] * sQ[row * LD + col] - mw[r] : 0.f;
-        P.Up[row * DK + col] = ok ? mu[r] : 0.f;
-      }
+      for (int is = 0; is < CH / 32; ++is) acc = mma_se(tu_[is], lds8(sVt + kt_at(16 * nt + l16, 32 * is + 8 * lq)), acc);
+      // U~^T [DV][CH]: lane (t = 16 wave + 4 lq + r, dv = 16 nt + l16)
+      *reinterpret_cast<f32x4*>(Ut + (16 * nt + l16) * CH + 16 * wave + 4 * lq) = acc;
     }
   }
 }
 
 // ------------------------------------------------------- chunk scan
-// One workgroup (eight waves) per (16 rows of S, head, seq): rows j0 .. j0+15
-// of S carried over the chunks in order,
-//   U = Ut - W S^T,   S <- gC S + U^T Kd.
-// Chunk c + 1's W [CH][DK], Kd^T [DK][CH] and the 16 rows of Ut^T go global ->
-// LDS by buffer_load ... lds while chunk c computes (two-stage ring; 16-byte
-// piece p of row r stored at p ^ (r % 16), so that the 128-bit operand reads
-// of 16 consecutive rows hit distinct banks), and chunk c + 2 is pulled into
-// L2 (one 4-byte copy per 128-byte line, into a scratch corner of LDS) so
-// that the copies of the next step hit L2.  Per chunk, two barriers:
-//   U phase: waves 0..3 compute U for token tile w (32 fp32 MFMAs over all
-//   of K), stored transposed [j][t] (the next phase reads it along t);
-//   update: wave w updates S columns 16w .. 16w+15 from U^T and Kd^T
-//   (16 MFMAs).
-// The entry state of every chunk is written for the output kernel; the final
-// state to the slot.  All Dv/16 row blocks of a (seq, head) read the same W
-// and Kd, so they are placed on one XCD (workgroups go to XCDs round-robin
-// by linear index): index = x + 8 ((g / 8) Dv/16 + jb) for group g = seq*H + head.
+// One workgroup (eight waves) per (16 rows j0 .. j0+15 of S, head, seq),
+// carrying those rows of S over the chunks in order.  Per chunk (S = the
+// entering state, its three bf16 parts in LDS; the fp32 state in registers,
+// wave w < Dk/16 holding S[j][16w .. 16w+15]):
+//   the entering state is stored for the output kernel;
+//   waves 0-3, token tile w:   U = U~ - W S^T (both operands split), stored
+//                              over U~^T for the output kernel, the parts of
+//                              (dk U)^T into LDS;
+//   barrier;
+//   waves w < Dk/16:           S^T <- gC S^T + K^T (dk U)   (raw K^T stage);
+//   the next copies and loads are issued; barrier.
+// The chain over the chunks is bound by memory latency, so operands run
+// ahead: the U waves' register operands (W rows, U~^T, dk) three chunks ahead
+// in three register sets, the raw K^T tile two chunks ahead in three LDS
+// stages (buffer_load ... lds), and a later chunk is warmed into L2.  All
+// Dv/16 row blocks of a (seq, head) read the same W and K, so they are placed
+// on one XCD (workgroups go to XCDs round-robin by linear index): index =
+// x + 8 ((g / 8) Dv/16 + jb) for group g = seq*H + head.
 constexpr int N_XCD = 8;
 constexpr int SCAN_NT = 512;
+constexpr int SCAN_PF = 3;  // chunks of register operands in flight (and K^T stages)
 constexpr int SCAN_MAX_CHUNKS = 1024;  // chunks per sequence and call (65,536 tokens)
-template <int DK, int SCAN_NT_ = SCAN_NT>
-struct ScanLds {
-  static constexpr int W_B = CH * DK * 4;     // W tile
-  static constexpr int K_B = DK * CH * 4;     // Kd^T tile
-  static constexpr int U_B = 16 * CH * 4;     // 16 rows of Ut^T
-  static constexpr int STAGE = W_B + K_B + U_B;
-  static constexpr int LS = DK + 4;           // S rows (floats)
-  static constexpr int LP = CH + 4;           // U^T rows (floats)
-  static constexpr int S_OFF = 2 * STAGE;
-  static constexpr int P_OFF = S_OFF + 16 * LS * 4;
-  static constexpr int X_OFF = P_OFF + 16 * LP * 4;  // L2 warm-up landing (4 bytes per lane)
-  static constexpr int G_OFF = X_OFF + SCAN_NT_ * 4;      // gC of every chunk
-  static constexpr int bytes = G_OFF + SCAN_MAX_CHUNKS * 4;
+// Register operands of one chunk for a U wave: W rows of its token tile, U~^T
+// of row j for four tokens, dk of those tokens.
+template <int DK>
+struct ScanRegs {
+  static constexpr int LOADS = 2 * (DK / 32) + 2;  // vector loads per chunk
+  f32x4 w[DK / 32][2];
+  f32x4 ut, dk;
 };
 template <int DK>
-__global__ __launch_bounds__(SCAN_NT, 1) void gdn_chunk_scan_kernel(GdnArgs a, int n_groups) {
+struct ScanLds {
+  static constexpr int LS = DK + 8;   // bf16 stride of the S rows
+  static constexpr int LU = CH + 8;   // bf16 stride of the (dk U)^T rows
+  static constexpr int S_PART = 16 * LS;
+  static constexpr int U_PART = 16 * LU;
+  static constexpr int K_STAGE = DK * CH;
+  // Dynamic LDS: the SCAN_PF K^T stages (bf16), then the landing area of the
+  // L2 warm-up (4 bytes per thread).  Every LDS target of the asynchronous
+  // copies lies here; the operands the waves write themselves (S, dk U
+  // parts, gC) are separate static arrays, so the compiler sees that those
+  // writes cannot touch a copy in flight and does not wait for the copies.
+  static constexpr int warm_off = SCAN_PF * K_STAGE * 2;
+  static constexpr int bytes = warm_off + SCAN_NT * 4;
+};
+
+DEV uint2 pack4(bf16 a, bf16 b, bf16 c, bf16 d) {
+  return make_uint2((uint32_t)bits(a) | ((uint32_t)bits(b) << 16), (uint32_t)bits(c) | ((uint32_t)bits(d) << 16));
+}
+// the three parts of four consecutive values, stored 8 bytes each at p, p +
+// part, p + 2 part (bf16 elements)
+DEV void put_parts4(uint16_t* p, int part, const f32x4& x) {
+  bf16 h[4], m[4], l[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) split3(x[r], h[r], m[r], l[r]);
+  *reinterpret_cast<uint2*>(p) = pack4(h[0], h[1], h[2], h[3]);
+  *reinterpret_cast<uint2*>(p + part) = pack4(m[0], m[1], m[2], m[3]);
+  *reinterpret_cast<uint2*>(p + 2 * part) = pack4(l[0], l[1], l[2], l[3]);
+}
+DEV Split8 get_parts8(const uint16_t* p, int part) {
+  Split8 v;
+  v.h = lds8(p);
+  v.m = lds8(p + part);
+  v.l = lds8(p + 2 * part);
+  return v;
+}
+
+template <int DK>
+__global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_groups) {
   static_assert(DK == 64 || DK == 128, "scan tiling");
   using L = ScanLds<DK>;
-  constexpr int LS = L::LS, LP = L::LP;
-  constexpr int WI = L::W_B / 1024 / 8;       // W copy instructions per wave
-  constexpr int KI = L::K_B / 1024 / 8;       // Kd^T copy instructions per wave
-  constexpr int WPR = DK / 4;                 // 16-byte pieces per W row
-  extern __shared__ __align__(16) uint8_t scan_smem[];
-  float* sS = reinterpret_cast<float*>(scan_smem + L::S_OFF);
-  float* sP = reinterpret_cast<float*>(scan_smem + L::P_OFF);   // U^T [16][LP]
-  constexpr int NJB = DK / 16;
-  const int xcd = blockIdx.x % N_XCD, q = blockIdx.x / N_XCD;
-  const int g = (q / NJB) * N_XCD + xcd;
+  using R = ScanRegs<DK>;
+  constexpr int DV = DK;
+  constexpr int LS = L::LS, LU = L::LU;
+  constexpr int NKS = DK / 32;      // 32-deep steps over Dk
+  constexpr int NKB = DK / 16;      // column blocks of S (update waves)
+  constexpr int NJB = DV / 16;      // row blocks of S per head (workgroups)
+  constexpr int KCP = DK * CH * 2 / 1024 / 8;  // 1 KB K^T copies per wave
+  static_assert(KCP * 8 * 1024 == DK * CH * 2, "K^T copies");
+  extern __shared__ __align__(16) uint16_t scan_lds[];
+  __shared__ __align__(16) uint16_t sS[3 * L::S_PART];   // parts of S [16][LS]
+  __shared__ __align__(16) uint16_t sD[3 * L::U_PART];   // parts of (dk U)^T [16][LU]
+  __shared__ float sGc[SCAN_MAX_CHUNKS];                 // gC of every chunk
+  uint16_t* sKt = scan_lds;                 // SCAN_PF stages of raw K^T [DK][CH] (kt_at)
+  const int xcd = blockIdx.x % N_XCD, qb = blockIdx.x / N_XCD;
+  const int g = (qb / NJB) * N_XCD + xcd;
   if (g >= n_groups) return;
-  const int j0 = (q % NJB) * 16, h = g % a.H, b = g / a.H;
+  const int jb = qb % NJB, j0 = jb * 16, h = g % a.H, b = g / a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i16 = lane & 15, kk = lane >> 4;
-  float* Sg = a.state + ((int64_t)a.seq_slot[b] * a.H + h) * (int64_t)DK * DK;  // [Dv][Dk]
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int tw = wave & 3;  // token tile of the U phase
+  float* Sg = a.state + ((int64_t)a.seq_slot[b] * a.H + h) * (int64_t)DV * DK;
   const bool fresh = a.pos[b] == 0;
-  for (int idx = tid; idx < 16 * DK; idx += SCAN_NT) {
-    const int j = idx / DK, k = idx % DK;
-    sS[j * LS + k] = fresh ? 0.f : Sg[(int64_t)(j0 + j) * DK + k];
-  }
-  // copy sources (byte offsets within a chunk's tile): W instruction n =
-  // WI wave + i fills rows (64 / WPR) n .., lane l row + l / WPR, piece
-  // l % WPR holding logical piece (l % WPR) ^ (row % 16); Kd^T and Ut^T rows
-  // hold 16 pieces: 4 rows per instruction
-  int w_src[WI], k_src[KI], u_src;
+  const int64_t cb0 = chunk_index(a, b, h, 0);
+  const int n = a.n_chunks;
+
+  // the state: wave w < NKB holds S[j0 + l16][16 w + 4 lq + r]
+  f32x4 S = {0, 0, 0, 0};
+  if (wave < NKB && !fresh) S = *reinterpret_cast<const f32x4*>(Sg + (int64_t)(j0 + l16) * DK + 16 * wave + 4 * lq);
+  auto put_state = [&]() __attribute__((always_inline)) { put_parts4(sS + l16 * LS + 16 * wave + 4 * lq, L::S_PART, S); };
+
+  const __amdgpu_buffer_rsrc_t r_k = buffer_rsrc(a.Kt + cb0 * DK * CH, (uint32_t)(n * DK * CH * 2));
+  auto copy_k = [&](int c, int st) __attribute__((always_inline)) {
+    uint8_t* dst = reinterpret_cast<uint8_t*>(sKt + st * L::K_STAGE);
 #pragma unroll
-  for (int i = 0; i < WI; ++i) {
-    const int row = (64 / WPR) * (wave * WI + i) + lane / WPR, p = lane % WPR;
-    w_src[i] = (row * DK + ((p ^ (row & 15)) * 4)) * 4;
-  }
+    for (int i = 0; i < KCP; ++i)
+      copy16_to_lds(r_k, ((wave * KCP + i) * 64 + lane) * 16, c * DK * CH * 2,
+                    (lds_void*)(dst + (wave * KCP + i) * 1024));
+  };
+  auto load = [&](int c, R& r) __attribute__((always_inline)) {
+    const int64_t cb = cb0 + c;
+    const float* sc = a.sc + cb * SCS;
+    r.dk = *reinterpret_cast<const f32x4*>(sc + CH + 16 * tw + 4 * lq);
+    r.ut = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + (j0 + l16) * CH + 16 * tw + 4 * lq);
+    const float* w = a.W + cb * CH * DK + (16 * tw + l16) * DK + 8 * lq;
 #pragma unroll
-  for (int i = 0; i < KI; ++i) {
-    const int row = 4 * (wave * KI + i) + (lane >> 4), p = lane & 15;
-    k_src[i] = (row * CH + ((p ^ (row & 15)) * 4)) * 4;
-  }
-  {
-    const int row = 4 * (wave & 3) + (lane >> 4), p = lane & 15;  // waves 0..3: Ut^T rows
-    u_src = ((j0 + row) * CH + ((p ^ (row & 15)) * 4)) * 4;
-  }
-  const int64_t cb0 = ((int64_t)b * a.H + h) * a.n_chunks;
-  const int64_t mat = (int64_t)CH * DK;
-  const auto w_rsrc = buffer_rsrc(a.W + cb0 * mat, (uint32_t)(a.n_chunks * mat * 4));
-  const auto k_rsrc = buffer_rsrc(a.Kd + cb0 * mat, (uint32_t)(a.n_chunks * mat * 4));
-  const auto u_rsrc = buffer_rsrc(a.Ut + cb0 * mat, (uint32_t)(a.n_chunks * mat * 4));
-  // L2 warm-up source: the workgroup's share of the chunk (1/8 of the head's
-  // W and Kd^T lines, its own 32 lines of Ut^T), one source tensor per wave
-  // (wave-uniform, w % 3; lanes 32..63 repeat 0..31), so that every wave
-  // issues exactly one copy
-  const int xw = __builtin_amdgcn_readfirstlane(wave) % 3, jb = j0 / 16;
-  const __amdgpu_buffer_rsrc_t x_rsrc = xw == 0 ? w_rsrc : (xw == 1 ? k_rsrc : u_rsrc);
-  const int x_src = xw < 2 ? (jb * 32 + (lane & 31)) * 128 : j0 * CH * 4 + (lane & 31) * 128;
-#define SCAN_WARM(c_)                                                                             \
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lds_void*)(scan_smem + L::X_OFF + wave * 256), 4, \
-                                           x_src, (c_) * (int)mat * 4, 0, 0);
-#define SCAN_COPY(c_, st_)                                                                        \
-  {                                                                                               \
-    uint8_t* S_ = scan_smem + (st_) * L::STAGE;                                                   \
-    const int so_ = (c_) * (int)mat * 4;                                                          \
-    _Pragma("unroll") for (int i = 0; i < WI; ++i)                                                \
-        copy16_to_lds(w_rsrc, w_src[i], so_, (lds_void*)(S_ + (wave * WI + i) * 1024));          \
-    _Pragma("unroll") for (int i = 0; i < KI; ++i)                                                \
-        copy16_to_lds(k_rsrc, k_src[i], so_, (lds_void*)(S_ + L::W_B + (wave * KI + i) * 1024)); \
-    if (wave < 4) copy16_to_lds(u_rsrc, u_src, so_, (lds_void*)(S_ + L::W_B + L::K_B + wave * 1024)); \
-  }
-  float* sG = reinterpret_cast<float*>(scan_smem + L::G_OFF);
-  for (int i = tid; i < a.n_chunks; i += SCAN_NT) sG[i] = a.gC[cb0 + i];
-  // Issue order per chunk c: the copies of chunk c + 1, the warm-up of chunk
-  // c + 2, the entry-state store of chunk c (all unconditional, clamped to
-  // the last chunk, so every wave has the same operations in flight): at the
-  // top of chunk c + 1, vmcnt(2) means its copies have landed.
-  SCAN_COPY(0, 0);
-  SCAN_WARM(min(1, a.n_chunks - 1));
-  for (int c = 0; c < a.n_chunks; ++c) {
-    // chunk c has landed (this wave's copies) and every wave has finished
-    // chunk c - 1
-    wait_vmcnt<2>();
-    lds_barrier();  // (a fence here would drain the warm-up and the store)
-    const uint8_t* st = scan_smem + (c & 1) * L::STAGE;
-    {
-      const int cn = min(c + 1, a.n_chunks - 1);  // past the end: the idle stage, harmlessly
-      SCAN_COPY(cn, (c + 1) & 1);
-      SCAN_WARM(min(c + 2, a.n_chunks - 1));
+    for (int ks = 0; ks < NKS; ++ks) {
+      r.w[ks][0] = *reinterpret_cast<const f32x4*>(w + 32 * ks);
+      r.w[ks][1] = *reinterpret_cast<const f32x4*>(w + 32 * ks + 4);
     }
-    const float gC = sG[c];
-    // entry state of chunk c (every lane stores; for Dk = 64 the second half
-    // of the workgroup repeats the first)
-    {
-      const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
-      const int e = tid % (4 * DK);
-      const int j = e / (DK / 4), k4 = (e % (DK / 4)) * 4;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(sS + j * LS + k4);
-      *reinterpret_cast<f32x4*>(P.S + (int64_t)(j0 + j) * DK + k4) = v;
+  };
+  // L2 warm-up of a later chunk: the head's W, U~^T and K^T lines (128 bytes);
+  // waves 0-2 take one source each, and the Dv/16 workgroups of the head
+  // share its lines.  One 4-byte copy per line into a scratch corner of LDS
+  // (never read).
+  const __amdgpu_buffer_rsrc_t r_w = buffer_rsrc(a.W + cb0 * CH * DK, (uint32_t)(n * CH * DK * 4));
+  const __amdgpu_buffer_rsrc_t r_u = buffer_rsrc(a.Ut + cb0 * CH * DV, (uint32_t)(n * CH * DV * 4));
+  auto warm = [&](int c) __attribute__((always_inline)) {
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    if (wv >= 3) return;
+    lds_void* dst = (lds_void*)(reinterpret_cast<uint8_t*>(scan_lds) + L::warm_off + wv * 256);
+    const int nl = wv == 0 ? CH * DK * 4 / 128 : wv == 1 ? CH * DV * 4 / 128 : DK * CH * 2 / 128;
+    const int per = (nl + NJB - 1) / NJB;
+    const int li = min(jb * per + lane, nl - 1);  // lanes past the share repeat a line
+    // one resource per (wave-uniform) branch: a selected resource would be a
+    // per-lane value
+    if (wv == 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_w, dst, 4, c * CH * DK * 4 + li * 128, 0, 0, 0);
+    else if (wv == 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_u, dst, 4, c * CH * DV * 4 + li * 128, 0, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(r_k, dst, 4, c * DK * CH * 2 + li * 128, 0, 0, 0);
+  };
+
+  // One chunk with register set `cur` (chunk c, c % SCAN_PF == I).  Before
+  // the barrier that publishes the stage, this wave's K^T copies of chunk c
+  // must have landed.  The vector memory counter counts stores as well as
+  // loads, so at least YOUNGER operations were issued after those copies: the
+  // copies of chunk c + 1, the stores of the entering states of chunks c - 1
+  // and c (waves w < Dk/16), and for a U wave the loads of chunks c + 1 and
+  // c + 2 and the stores of U of chunks c - 1 and c (the L2 warm-ups, issued
+  // by three of the four U waves only, are not counted).
+  struct NoRegs {};
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool UW = decltype(role)::value;
+    using RS = std::conditional_t<UW, R, NoRegs>;
+    static_assert(NKB >= 4, "the U waves store the state");
+    constexpr int YOUNGER = UW ? 2 * R::LOADS + KCP + 4 : KCP + (NKB > 4 ? 2 : 0);
+    auto step = [&](auto Ic, RS& cur, int c) __attribute__((always_inline)) {
+      constexpr int I = decltype(Ic)::value;
+      if (wave < NKB)  // the entering state of chunk c, for the output kernel
+        *reinterpret_cast<f32x4*>(a.Sc + (cb0 + c) * DV * DK + (j0 + l16) * DK + 16 * wave + 4 * lq) = S;
+      if constexpr (UW) {
+        // (W S^T)[t][j] for the tile's tokens (two accumulation chains)
+        f32x4 acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks += 2) {
+          acc = mma_ss(split8(cur.w[ks][0], cur.w[ks][1]), get_parts8(sS + l16 * LS + 32 * ks + 8 * lq, L::S_PART), acc);
+          acc2 = mma_ss(split8(cur.w[ks + 1][0], cur.w[ks + 1][1]),
+                        get_parts8(sS + l16 * LS + 32 * (ks + 1) + 8 * lq, L::S_PART), acc2);
+        }
+        // lane: t = 16 tw + 4 lq + r, j = l16: U^T[j][t] over U~^T (read
+        // into registers chunks ago), (dk U)^T[j][t] into LDS
+        f32x4 u, du;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          u[r] = cur.ut[r] - (acc[r] + acc2[r]);
+          du[r] = u[r] * cur.dk[r];
+        }
+        *reinterpret_cast<f32x4*>(a.Ut + (cb0 + c) * DV * CH + (j0 + l16) * CH + 16 * tw + 4 * lq) = u;
+        put_parts4(sD + l16 * LU + 16 * tw + 4 * lq, L::U_PART, du);
+      }
+      wait_vmcnt<YOUNGER>();  // this wave's K^T copies of chunk c have landed
+      lds_barrier();          // the younger loads and stores stay in flight
+      if (wave < NKB) {
+        // S^T <- gC S^T + K^T (dk U) for the rows k = 16 wave ..
+        f32x4 acc = {0, 0, 0, 0};
+        const uint16_t* kt = sKt + I * L::K_STAGE;
+#pragma unroll
+        for (int ts = 0; ts < CH / 32; ++ts)
+          acc = mma_es(lds8(kt + kt_at(16 * wave + l16, 32 * ts + 8 * lq)),
+                       get_parts8(sD + l16 * LU + 32 * ts + 8 * lq, L::U_PART), acc);
+        const float gC = sGc[c];
+        // lane: k = 16 wave + 4 lq + r, j = l16
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[r] = gC * S[r] + acc[r];
+        put_state();
+      }
+      // the operands ahead: K^T of chunk c + 2 into the stage chunk c - 1
+      // used, the U set's chunk c + 3, the L2 warm-up of chunk c + 4 (indices
+      // past the end repeat the last chunk, harmlessly, so every wave of a
+      // role issues the same operations)
+      copy_k(min(c + 2, n - 1), (I + 2) % SCAN_PF);
+      if constexpr (UW) load(min(c + SCAN_PF, n - 1), cur);
+      warm(min(c + SCAN_PF + 1, n - 1));
+      lds_barrier();
+    };
+    static_assert(SCAN_PF == 3, "three register sets");
+    RS r0, r1, r2;  // the U waves' register sets (empty for the others)
+    copy_k(0, 0);
+    if constexpr (UW) load(0, r0);
+    copy_k(min(1, n - 1), 1);
+    if constexpr (UW) {
+      load(min(1, n - 1), r1);
+      load(min(2, n - 1), r2);
     }
-    // U phase (waves 0..3): U^T[j][t] = Ut^T[j][t] - sum_k W[t][k] S[j][k]
-    // for tokens t of tile wave.  Lane group kk takes k = DK/4 kk .. (a
-    // permutation of K applied to both operands): 128-bit reads.
-    if (wave < 4) {
-      constexpr int KQ4 = DK / 4;
-      const int row = 16 * wave + i16;
-      const float* wr = reinterpret_cast<const float*>(st) + row * DK;
-      const float* sr = sS + i16 * LS + KQ4 * kk;
-      float av[KQ4], bv[KQ4];
-#pragma unroll
-      for (int qq = 0; qq < KQ4 / 4; ++qq) {
-        const int pc = (KQ4 * kk) / 4 + qq;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(wr + 4 * (pc ^ (row & 15)));
-        const f32x4 y = *reinterpret_cast<const f32x4*>(sr + 4 * qq);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { av[4 * qq + e] = x[e]; bv[4 * qq + e] = y[e]; }
-      }
-      f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < KQ4; i += 2) {
-        acc0 = mfma16x16x4f32(av[i], bv[i], acc0);
-        acc1 = mfma16x16x4f32(av[i + 1], bv[i + 1], acc1);
-      }
-      acc0 += acc1;
-      // lane holds W S^T [t = 16 wave + 4 kk + r][j = i16]
-      const float* ut = reinterpret_cast<const float*>(st + L::W_B + L::K_B) + i16 * CH;
-      const int pc = 4 * wave + kk;  // Ut^T piece of t = 16 wave + 4 kk ..
-      const f32x4 u = *reinterpret_cast<const f32x4*>(ut + 4 * (pc ^ i16));
-      *reinterpret_cast<f32x4*>(sP + i16 * LP + 16 * wave + 4 * kk) = u - acc0;
+    warm(min(3, n - 1));
+    if (wave < NKB) put_state();
+    for (int i = tid; i < n; i += SCAN_NT) sGc[i] = a.sc[(cb0 + i) * SCS + 2 * CH];
+    // everything issued so far has landed (the first chunk's wait counts
+    // fewer younger operations than the later ones)
+    wait_vmem();
+    __syncthreads();
+    // whole rounds of three chunks, then the last one or two (the loop's only
+    // back edge comes from the third step, so the compiler's waits for each
+    // register set stay exact)
+    int c = 0;
+    for (; c + SCAN_PF <= n; c += SCAN_PF) {
+      step(std::integral_constant<int, 0>(), r0, c);
+      step(std::integral_constant<int, 1>(), r1, c + 1);
+      step(std::integral_constant<int, 2>(), r2, c + 2);
     }
-    lds_barrier();  // the next chunk's copies stay in flight
-    // update: S[j][k] = gC S[j][k] + sum_t U[t][j] Kd[t][k] for the columns
-    // k = 16 wave + i16.  Lane group kk takes t = 16 kk .. + 15.
-    if (wave < DK / 16) {
-      const float* kd = reinterpret_cast<const float*>(st + L::W_B) + (16 * wave + i16) * CH;
-      const float* uu = sP + i16 * LP + 16 * kk;
-      float av[16], bv[16];
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int pc = 4 * kk + qq;
-        const f32x4 u = *reinterpret_cast<const f32x4*>(uu + 4 * qq);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(kd + 4 * (pc ^ i16));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { av[4 * qq + e] = u[e]; bv[4 * qq + e] = y[e]; }
-      }
-      f32x4 acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        acc0 = mfma16x16x4f32(av[i], bv[i], acc0);
-        acc1 = mfma16x16x4f32(av[i + 1], bv[i + 1], acc1);
-      }
-      acc0 += acc1;
-      // lane holds dS[j = 4 kk + r][k = 16 wave + i16]
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float* sp = sS + (4 * kk + r) * LS + 16 * wave + i16;
-        *sp = gC * *sp + acc0[r];
-      }
-    }
-  }
-#undef SCAN_COPY
-#undef SCAN_WARM
+    if (c < n) step(std::integral_constant<int, 0>(), r0, c);
+    if (c + 1 < n) step(std::integral_constant<int, 1>(), r1, c + 1);
+  };
+  if (wave < 4) run(std::true_type());
+  else run(std::false_type());
   wait_vmem();
-  __syncthreads();
-  for (int idx = tid; idx < 16 * DK; idx += SCAN_NT) {
-    const int j = idx / DK, k = idx % DK;
-    Sg[(int64_t)(j0 + j) * DK + k] = sS[j * LS + k];
-  }
+  if (wave < NKB) *reinterpret_cast<f32x4*>(Sg + (int64_t)(j0 + l16) * DK + 16 * wave + 4 * lq) = S;
 }
 
 // ------------------------------------------------------- chunk output
-// grid (chunk, head, seq), eight waves: O = Qp S_c^T + Up, then per token
-// and head y = RMSNorm(o; g_o) * SiLU(z) -> bf16.
+// grid (chunk, head, seq), eight waves: from the chunk's entering state S_c
+// and U (both stored by the scan), O = sq * (Q S_c^T) + Mqk U, then per token
+// y = RMSNorm(O; g_o) * SiLU(z) over Dv -> bf16.  S_c and U^T go to
+// LDS as three bf16 parts (B operands, rows j; 16-byte groups swizzled so the
+// operand reads of 16 consecutive rows and the part writes spread over the
+// banks).  Wave w: token tile w % 4 and half w / 4 of the Dv columns.
 constexpr int ONT = 512;
 template <int DK>
-__global__ __launch_bounds__(ONT, 1) void gdn_chunk_out_kernel(GdnArgs a) {
+struct OutLds {
+  static constexpr int S_PART = DK * DK;   // [Dv][Dk] bf16
+  static constexpr int U_PART = DK * CH;   // [Dv][CH] bf16
+  static constexpr int bytes = (3 * S_PART + 3 * U_PART) * 2 + 2 * CH * 4;
+};
+template <int DK>
+DEV int s_at(int j, int k) {  // element (j, k) of an S part
+  return j * DK + 8 * ((k >> 3) ^ (j & (DK / 8 - 1))) + (k & 7);
+}
+DEV int u_at(int j, int t) {  // element (j, t) of a U^T part
+  return j * CH + 8 * ((t >> 3) ^ ((j >> 1) & 7)) + (t & 7);
+}
+
+template <int DK>
+__global__ __launch_bounds__(ONT, 1) void gdn_out_kernel(GdnArgs a) {
   constexpr int DV = DK;
-  constexpr int LD = DK + 4;
-  constexpr int NQ = CH * DK / 4 / ONT;  // 16-byte pieces of Qp per thread
-  constexpr int NS = DV * DK / 4 / ONT;  // of S_c
-  constexpr int PER = DV / 8;            // output dims per thread (8 threads per row)
-  static_assert(NQ * 4 * ONT == CH * DK && NS * 4 * ONT == DV * DK && CH * 8 == ONT, "thread split");
-  extern __shared__ __align__(16) float gsm[];
-  float* sQ = gsm;             // Qp [CH][LD], later O
-  float* sS = sQ + CH * LD;    // S_c [DV][LD]
+  using L = OutLds<DK>;
+  constexpr int NKS = DK / 32;
+  constexpr int NJT = DV / 32;              // 16-column tiles per wave (half of Dv)
+  constexpr int SP = DV * DK / 4 / ONT;     // S_c pieces (four fp32) per thread
+  static_assert(SP * 4 * ONT == DV * DK, "S_c pieces");
+  extern __shared__ __align__(16) uint16_t out_lds[];
+  uint16_t* sS = out_lds;                   // parts of S_c
+  uint16_t* sU = sS + 3 * L::S_PART;        // parts of U^T
+  float* sN = reinterpret_cast<float*>(sU + 3 * L::U_PART);  // [2][CH] sums of squares
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int C = min(CH, a.T - c * CH);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const ChunkPtr P = chunk_ptr(a, b, h, c, DK);
-  // every global read first: Qp and S_c (for LDS), this thread's row piece
-  // of Up and of the gate z
-  const int r = tid >> 3, d0 = (tid & 7) * PER;
-  const int64_t m = (int64_t)b * a.T + c * CH + min(r, C - 1);
-  u32x4 rq[NQ], rs[NS], ru[PER / 4], rz[PER / 8];
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int tw = wave & 3, jh = wave >> 2;
+  const int64_t cb = chunk_index(a, b, h, c);
+  const int64_t tok = (int64_t)b * a.T + c * CH;
+  const float* sc = a.sc + cb * SCS;
+  // every global read first: S_c pieces; this wave's q and Mqk rows (token
+  // tile), sq, U^T of its columns; z of its outputs
+  f32x4 sv[SP];
 #pragma unroll
-  for (int i = 0; i < NQ; ++i) rq[i] = *reinterpret_cast<const u32x4*>(P.Qp + (tid + i * ONT) * 4);
+  for (int i = 0; i < SP; ++i)
+    sv[i] = *reinterpret_cast<const f32x4*>(a.Sc + cb * DV * DK + (int64_t)(tid + i * ONT) * 4);
+  const int t = 16 * tw + l16;
+  bf16x8 q[NKS];
+  const uint16_t* qr = a.proj + (tok + min(t, C - 1)) * a.proj_stride + a.off_q + h * DK + 8 * lq;
 #pragma unroll
-  for (int i = 0; i < NS; ++i) rs[i] = *reinterpret_cast<const u32x4*>(P.S + (tid + i * ONT) * 4);
+  for (int ks = 0; ks < NKS; ++ks) q[ks] = glb8(qr + 32 * ks);
+  f32x4 mq[CH / 32][2];
+  const float* mr = a.Mq + cb * CH * CH + t * CH + 8 * lq;
 #pragma unroll
-  for (int i = 0; i < PER / 4; ++i) ru[i] = *reinterpret_cast<const u32x4*>(P.Up + r * DK + d0 + 4 * i);
-  const uint16_t* z = a.proj + m * a.proj_stride + a.off_z + h * DV + d0;
-#pragma unroll
-  for (int i = 0; i < PER / 8; ++i) rz[i] = *reinterpret_cast<const u32x4*>(z + 8 * i);
-#pragma unroll
-  for (int i = 0; i < NQ; ++i) {
-    const int e = (tid + i * ONT) * 4;
-    *reinterpret_cast<u32x4*>(sQ + (e / DK) * LD + e % DK) = rq[i];
+  for (int is = 0; is < CH / 32; ++is) {
+    mq[is][0] = *reinterpret_cast<const f32x4*>(mr + 32 * is);
+    mq[is][1] = *reinterpret_cast<const f32x4*>(mr + 32 * is + 4);
   }
+  const f32x4 sq = *reinterpret_cast<const f32x4*>(sc + 16 * tw + 4 * lq);
+  f32x4 ut[NJT];
 #pragma unroll
-  for (int i = 0; i < NS; ++i) {
-    const int e = (tid + i * ONT) * 4;
-    *reinterpret_cast<u32x4*>(sS + (e / DK) * LD + e % DK) = rs[i];
+  for (int jt = 0; jt < NJT; ++jt) {
+    const int j = DV / 2 * jh + 16 * jt + l16;
+    ut[jt] = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + j * CH + 16 * tw + 4 * lq);
   }
-  __syncthreads();
-  // O = Qp S_c^T (+ Up below); wave w: rows of tile w % 4, the column
-  // tiles of half w / 4, in pairs
-  constexpr int NTILE = DV / 16 / 2;
-  static_assert(NTILE % 2 == 0, "tile pairs");
-  const int rt = wave & 3, ch = wave >> 2;
-  f32x4 acc[NTILE];
-  const int i16 = lane & 15, kk = lane >> 4;
+  uint16_t zv[NJT][4];
 #pragma unroll
-  for (int n = 0; n < NTILE; n += 2) {
-    const int nt = ch * NTILE + n;
-    acc[n] = (f32x4){0, 0, 0, 0};
-    acc[n + 1] = (f32x4){0, 0, 0, 0};
-    mm_nt2s(acc[n], acc[n + 1], sQ + rt * 16 * LD, LD, sS + nt * 16 * LD, sS + (nt + 1) * 16 * LD, LD, DK);
+  for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tr = 16 * tw + 4 * lq + r;
+      zv[jt][r] = a.proj[(tok + min(tr, C - 1)) * a.proj_stride + a.off_z + h * DV + DV / 2 * jh + 16 * jt + l16];
+    }
+  // S_c parts into LDS
+#pragma unroll
+  for (int i = 0; i < SP; ++i) {
+    const int p = tid + i * ONT, j = p / (DK / 4), k = (p % (DK / 4)) * 4;
+    bf16 hh[4], mm[4], ll[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) split3(sv[i][r], hh[r], mm[r], ll[r]);
+    const int o = s_at<DK>(j, k);
+    *reinterpret_cast<uint2*>(sS + o) = pack4(hh[0], hh[1], hh[2], hh[3]);
+    *reinterpret_cast<uint2*>(sS + L::S_PART + o) = pack4(mm[0], mm[1], mm[2], mm[3]);
+    *reinterpret_cast<uint2*>(sS + 2 * L::S_PART + o) = pack4(ll[0], ll[1], ll[2], ll[3]);
   }
-  __syncthreads();  // sQ fully read: reuse it for O
+  lds_barrier();
+  auto s_parts = [&](int j, int ks) {
+    Split8 v;
+    const int o = s_at<DK>(j, 32 * ks + 8 * lq);
+    v.h = lds8(sS + o);
+    v.m = lds8(sS + L::S_PART + o);
+    v.l = lds8(sS + 2 * L::S_PART + o);
+    return v;
+  };
+  // the U^T parts of the wave's columns and tokens into LDS; O1 = Q S_c^T for
+  // the wave's column tiles.  Lane: t = 16 tw + 4 lq + r, j = Dv/2 jh + 16 jt
+  // + l16.
 #pragma unroll
-  for (int n = 0; n < NTILE; ++n)
+  for (int jt = 0; jt < NJT; ++jt)
+    put_parts4(sU + u_at(DV / 2 * jh + 16 * jt + l16, 16 * tw + 4 * lq), L::U_PART, ut[jt]);
+  f32x4 o1[NJT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sQ[(rt * 16 + 4 * kk + q) * LD + (ch * NTILE + n) * 16 + i16] = acc[n][q];
-  __syncthreads();
-  // per token and head: y = RMSNorm(O + Up; g_o) * SiLU(z) -> bf16
-  float v[PER];
-  float ss = 0.f;
+  for (int jt = 0; jt < NJT; ++jt) {
+    const int j = DV / 2 * jh + 16 * jt + l16;
+    f32x4 aq = {0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < PER / 4; ++i)
+    for (int ks = 0; ks < NKS; ++ks) aq = mma_es(q[ks], s_parts(j, ks), aq);
+    o1[jt] = aq;
+  }
+  lds_barrier();
+  // O = sq * O1 + Mqk U
+  Split8 ms[CH / 32];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[4 * i + e] = sQ[r * LD + d0 + 4 * i + e] + __uint_as_float(ru[i][e]);
-      ss += v[4 * i + e] * v[4 * i + e];
+  for (int is = 0; is < CH / 32; ++is) ms[is] = split8(mq[is][0], mq[is][1]);
+  f32x4 o[NJT];
+  f32x4 ss = {0, 0, 0, 0};
+#pragma unroll
+  for (int jt = 0; jt < NJT; ++jt) {
+    const int j = DV / 2 * jh + 16 * jt + l16;
+    f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int is = 0; is < CH / 32; ++is) {
+      Split8 up;
+      const int ou = u_at(j, 32 * is + 8 * lq);
+      up.h = lds8(sU + ou);
+      up.m = lds8(sU + L::U_PART + ou);
+      up.l = lds8(sU + 2 * L::U_PART + ou);
+      acc = mma_ss(ms[is], up, acc);
     }
 #pragma unroll
-  for (int o = 1; o < 8; o <<= 1) ss += __shfl_xor(ss, o, 64);
-  const float inv = rsqrtf(ss / DV + a.eps);
-  if (r < C) {
-    uint16_t* y = a.out + m * a.out_stride + h * DV + d0;
+    for (int r = 0; r < 4; ++r) {
+      o[jt][r] = sq[r] * o1[jt][r] + acc[r];
+      ss[r] += o[jt][r] * o[jt][r];
+    }
+  }
+  // per token: sum of squares over Dv (16 lanes x NJT tiles here, then the
+  // other half of Dv through LDS)
 #pragma unroll
-    for (int i = 0; i < PER / 8; ++i) {
-      u32x4 o;
+  for (int r = 0; r < 4; ++r) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        float f[2];
+    for (int m = 1; m < 16; m <<= 1) ss[r] += __shfl_xor(ss[r], m, 64);
+  }
+  if (l16 == 0) *reinterpret_cast<f32x4*>(sN + jh * CH + 16 * tw + 4 * lq) = ss;
+  lds_barrier();
+  const f32x4 s0 = *reinterpret_cast<const f32x4*>(sN + 16 * tw + 4 * lq);
+  const f32x4 s1 = *reinterpret_cast<const f32x4*>(sN + CH + 16 * tw + 4 * lq);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int k = 8 * i + 2 * w + e;
-          const float zf = bf2f((uint16_t)(rz[i][w] >> (16 * e)));
-          f[e] = v[k] * inv * bf2f(a.o_norm[d0 + k]) * siluf_(zf);
-        }
-        o[w] = (uint32_t)f2bf_bits(f[0]) | ((uint32_t)f2bf_bits(f[1]) << 16);
+  for (int r = 0; r < 4; ++r) {
+    const int tr = 16 * tw + 4 * lq + r;
+    const float inv = rsqrtf((s0[r] + s1[r]) / DV + a.eps);
+    if (tr < C) {
+      uint16_t* y = a.out + (tok + tr) * a.out_stride + h * DV + DV / 2 * jh + l16;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        const int j = DV / 2 * jh + 16 * jt + l16;
+        y[16 * jt] = f2bf_bits(o[jt][r] * inv * bf2f(a.o_norm[j]) * siluf_(bf2f(zv[jt][r])));
       }
-      *reinterpret_cast<u32x4*>(y + 8 * i) = o;
     }
   }
 }
@@ -859,21 +887,21 @@ hipError_t set_lds(K k, size_t bytes) {
 template <int DK>
 hipError_t prefill_dk(const GdnArgs& a, int B, hipStream_t s) {
   if (a.n_chunks > SCAN_MAX_CHUNKS) return hipErrorInvalidValue;
-  const size_t lds_prep = (3 * CH * (DK + 4) + 3 * CH * (CH + 4) + 4 * CH + 4 * 16 * 20) * sizeof(float);
-  const size_t lds_out = (CH * (DK + 4) + DK * (DK + 4)) * sizeof(float);
+  constexpr size_t lds_prep = prep_lds_bytes<DK>();
+  constexpr size_t lds_scan = ScanLds<DK>::bytes;
+  constexpr size_t lds_out = OutLds<DK>::bytes;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = set_lds(gdn_chunk_prep_kernel<DK>, lds_prep);
-    if (e == hipSuccess) e = set_lds(gdn_chunk_out_kernel<DK>, lds_out);
-    if (e == hipSuccess) e = set_lds(gdn_chunk_scan_kernel<DK>, ScanLds<DK>::bytes);
+    hipError_t e = set_lds(gdn_prep_kernel<DK>, lds_prep);
+    if (e == hipSuccess) e = set_lds(gdn_scan_kernel<DK>, lds_scan);
+    if (e == hipSuccess) e = set_lds(gdn_out_kernel<DK>, lds_out);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL(gdn_chunk_prep_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(PNT), lds_prep, s, a);
+  hipLaunchKernelGGL(gdn_prep_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(PNT), lds_prep, s, a);
   const int groups = (a.H * B + N_XCD - 1) / N_XCD * N_XCD;
-  hipLaunchKernelGGL(gdn_chunk_scan_kernel<DK>, dim3(groups * (DK / 16)), dim3(SCAN_NT), ScanLds<DK>::bytes, s, a,
-                     a.H * B);
-  hipLaunchKernelGGL(gdn_chunk_out_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(ONT), lds_out, s, a);
+  hipLaunchKernelGGL(gdn_scan_kernel<DK>, dim3(groups * (DK / 16)), dim3(SCAN_NT), lds_scan, s, a, a.H * B);
+  hipLaunchKernelGGL(gdn_out_kernel<DK>, dim3(a.n_chunks, a.H, B), dim3(ONT), lds_out, s, a);
   return hipGetLastError();
 }
 
@@ -886,6 +914,7 @@ hipError_t recurrent_dk(const GdnArgs& a, int B, hipStream_t s) {
 }  // namespace
 
 int gdn_chunks(int T) { return (T + CH - 1) / CH; }
+int gdn_chunk_scales() { return SCS; }
 
 hipError_t launch_gdn_prefill(const GdnArgs& a, int B, hipStream_t s) {
   if (B == 0 || a.T == 0) return hipSuccess;

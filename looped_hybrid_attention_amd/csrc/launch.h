@@ -129,13 +129,17 @@ struct GdnArgs {
   float eps, q_scale;
   const int32_t* pos; const int32_t* seq_slot;
   float* state;  // state block of the exec slot: [max_batch][H][Dv][Dk]
-  // chunk workspace, per (seq, head, chunk): W, Ut, Kd, Qg (= gamma Q - Mqk W),
-  // Mqk (= Mqk Ut) [64][Dk] fp32 each, gC, and Sc, the chunk entry state [Dv][Dk]
-  float* W; float* Ut; float* Qg; float* Kd; float* Mqk; float* gC; float* Sc;
-  float* o;      // [M][H][Dv] fp32
+  // chunk workspace, per (seq, head, chunk) at (seq H + head) n_chunks + chunk:
+  float* W;      // W: fp32 [64][Dk]
+  float* Ut;     // U~^T: fp32 [Dv][64] (prep); the scan overwrites it with U^T
+  float* Mq;     // Mqk: fp32 [64][64]
+  uint16_t* Kt;  // raw k of the chunk transposed: bf16 [Dk][64] (16-byte groups swizzled)
+  float* sc;     // row scales: sq [64], dk [64], gC (gdn_chunk_scales() floats)
+  float* Sc;     // the state entering the chunk: fp32 [Dv][Dk]
   const uint16_t* o_norm;
   uint16_t* out; int64_t out_stride;
 };
 int gdn_chunks(int T);
+int gdn_chunk_scales();
 hipError_t launch_gdn_prefill(const GdnArgs& a, int B, hipStream_t s);
 hipError_t launch_gdn_recurrent(const GdnArgs& a, int B, hipStream_t s);

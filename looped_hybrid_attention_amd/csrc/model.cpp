@@ -35,8 +35,8 @@ constexpr int DEC_SPLIT = DEC_SPLIT_KEYS;  // keys per decode-attention split (d
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t meta, h, hmid, x, a, s0, s1, xn, hn, proj, qbuf, obuf, act, gdn_o;
-  size_t gW, gUt, gQg, gKd, gM, gC, gS;
+  size_t meta, h, hmid, x, a, s0, s1, xn, hn, proj, qbuf, obuf, act;
+  size_t gW, gUt, gM, gKt, gSc, gS;
   size_t xf, logits, am_v, am_i, dec_part, mhc, splitk;
   size_t splitk_bytes;
   size_t total;
@@ -70,17 +70,15 @@ Layout layout(const loop_config& c, int64_t M) {
   L.qbuf = take(M * (int64_t)c.n_q_heads * c.head_dim * 2);
   L.obuf = take(M * (int64_t)std::max(c.n_q_heads * c.head_dim, c.gdn_heads * c.gdn_dv) * 2);
   L.act = take(M * (int64_t)c.d_ff * 2);
-  L.gdn_o = take(M * (int64_t)c.gdn_heads * c.gdn_dv * 4);
   // chunk workspace: (sum over sequences of their chunks) * heads
   L.chunk_slots = (int)((M + 63) / 64 + B);
   const int64_t cs = (int64_t)L.chunk_slots * c.gdn_heads;
   L.gW = take(cs * 64 * c.gdn_dk * 4);
   L.gUt = take(cs * 64 * c.gdn_dv * 4);
-  L.gQg = take(cs * 64 * c.gdn_dk * 4);
-  L.gKd = take(cs * 64 * c.gdn_dk * 4);
-  L.gM = take(cs * 64 * c.gdn_dv * 4);
-  L.gC = take(cs * 4);
+  L.gM = take(cs * 64 * 64 * 4);
+  L.gKt = take(cs * 64 * c.gdn_dk * 2);
   L.gS = take(cs * (int64_t)c.gdn_dv * c.gdn_dk * 4);
+  L.gSc = take(cs * (int64_t)gdn_chunk_scales() * 4);
   // final-norm rows and argmax partials: one per sequence, or up to
   // LOOP_VERIFY_MAX per sequence for a verify step
   const int64_t HR = head_rows(c, M);
@@ -352,10 +350,10 @@ int run_mixer(loop_model* m, const Call& k, const ExecDesc& d, hipStream_t s, in
     g.eps = c.eps; g.q_scale = (float)(1.0 / sqrt((double)Dk));
     g.pos = k.d_pos; g.seq_slot = k.d_slot;
     g.state = (float*)(m->arena + loop_cache_offset(&c, 2, d.slot, 0));
-    g.W = at<float>(m, L.gW); g.Ut = at<float>(m, L.gUt); g.Qg = at<float>(m, L.gQg);
-    g.Kd = at<float>(m, L.gKd); g.Mqk = at<float>(m, L.gM); g.gC = at<float>(m, L.gC);
+    g.W = at<float>(m, L.gW); g.Ut = at<float>(m, L.gUt); g.Mq = at<float>(m, L.gM);
+    g.Kt = at<uint16_t>(m, L.gKt);
+    g.sc = at<float>(m, L.gSc);
     g.Sc = at<float>(m, L.gS);
-    g.o = at<float>(m, L.gdn_o);
     g.o_norm = (const uint16_t*)w.o_norm;
     g.out = obuf; g.out_stride = mix_width;
     Prof pr(m, LOOP_K_GDN, s);
