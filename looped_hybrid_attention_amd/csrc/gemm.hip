@@ -376,48 +376,71 @@ DEV u32x2 pack_bf16x4(float a, float b, float c, float d) {
   return (u32x2){__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
 }
 
-// Epilogue of a wave's 128 x (32 TN) block: lane (lr, half) holds row r0 + 32 i
-// and, for r = 4 q + e, column c0 + 32 j + 8 q + e (c0 includes 4 half);
-// SwiGLU pairs tiles j (gate) and j + 1 (up) into output columns c0 + 32 (j /
-// 2) + 8 q + e.  One row block at a time (sched_barrier), so that only its
-// values are live.
-template <int EPI, int TM, int TN, int WCOLS>
-DEV void db_epilogue(const GemmArgs& g, f32x16 (&acc)[TM][TN], int r0, int c0) {
+// Epilogue of a wave's 128 x (32 TN) block, one 32-row block at a time
+// through the wave's own LDS region `ws` (the stage the last K step read):
+// lane (lr, half) holds row lr and, for r = 4 q + e, column 32 j + 8 q + 4
+// half + e (SwiGLU pairs tiles j (gate) and j + 1 (up) into output column
+// 32 (j / 2) + 8 q + e); it writes its values there (16-byte chunks of a row
+// XOR-swizzled by the row), then reads the block back row-major, so every
+// global access of the wave covers whole rows: 16 bytes per lane, 512 B to
+// 1 KB contiguous per row.  The residual is loaded the same way first.
+template <int EPI, int TM, int TN>
+DEV void db_epilogue(const GemmArgs& g, f32x16 (&acc)[TM][TN], uint8_t* ws, int row0, int col0, int lane) {
+  constexpr bool F32 = EPI == LOOP_EPI_F32 || EPI == LOOP_EPI_F32_RES;
+  constexpr int OCOLS = EPI == LOOP_EPI_SWIGLU ? 16 * TN : 32 * TN;  // output columns of the wave
+  constexpr int RB = OCOLS * (F32 ? 4 : 2);                          // bytes of a block row in LDS
+  constexpr int NCH = RB / 16;                                         // 16-byte chunks per row
+  constexpr int RPI = 1024 / RB;                                       // rows per wave access
+  constexpr int NI = 32 / RPI;                                         // accesses per 32-row block
+  static_assert(NCH <= 32 && RPI * RB == 1024, "epilogue block");
+  const int lr = lane & 31, half = lane >> 5;
+  const int rr = lane / NCH, cc = lane % NCH;  // row-major read back: row rr + RPI k, chunk cc
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
-    const int64_t o0 = (int64_t)(r0 + i * 32) * g.ldc + c0;
-    if (EPI == LOOP_EPI_SWIGLU) {
-      uint16_t* Cr = reinterpret_cast<uint16_t*>(g.C) + o0;
+    const int64_t rb = row0 + 32 * i;
+    if constexpr (F32) {
+      f32x4 rv[NI];
+      if constexpr (EPI == LOOP_EPI_F32_RES) {
 #pragma unroll
-      for (int j = 0; j < TN; j += 2)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = siluf_(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e];
-          *reinterpret_cast<u32x2*>(Cr + (j / 2) * 32 + 8 * q) = pack_bf16x4(o[0], o[1], o[2], o[3]);
-        }
-    } else {
-      f32x4 rv[TN][4];
-      if (EPI == LOOP_EPI_F32_RES) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) rv[j][q] = *reinterpret_cast<const f32x4*>(g.R + o0 + j * 32 + 8 * q);
+        for (int k = 0; k < NI; ++k)
+          rv[k] = *reinterpret_cast<const f32x4*>(g.R + (rb + rr + RPI * k) * g.ldc + col0 + 4 * cc);
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int64_t o = o0 + j * 32 + 8 * q;
-          f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (EPI == LOOP_EPI_BF16) {
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(g.C) + o) = pack_bf16x4(v[0], v[1], v[2], v[3]);
-          } else {
-            if (EPI == LOOP_EPI_F32_RES) v += rv[j][q];
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + o) = v;
-          }
+          const int c = 8 * j + 2 * q + half;
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(ws + lr * RB + ((c ^ lr) % NCH) * 16) = v;
         }
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int r = rr + RPI * k;
+        f32x4 v = *reinterpret_cast<const f32x4*>(ws + r * RB + ((cc ^ r) % NCH) * 16);
+        if constexpr (EPI == LOOP_EPI_F32_RES) v += rv[k];
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(g.C) + (rb + r) * g.ldc + col0 + 4 * cc) = v;
+      }
+    } else {
+      // 8-byte pieces c8 (four bf16) of a row: chunk c8 / 2, half c8 % 2
+#pragma unroll
+      for (int j = 0; j < TN; j += (EPI == LOOP_EPI_SWIGLU ? 2 : 1))
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = EPI == LOOP_EPI_SWIGLU ? siluf_(acc[i][j][4 * q + e]) * acc[i][j + 1][4 * q + e]
+                                          : acc[i][j][4 * q + e];
+          const int c8 = 8 * (EPI == LOOP_EPI_SWIGLU ? j / 2 : j) + 2 * q + half;
+          *reinterpret_cast<u32x2*>(ws + lr * RB + (((c8 >> 1) ^ lr) % NCH) * 16 + (c8 & 1) * 8) =
+              pack_bf16x4(o[0], o[1], o[2], o[3]);
+        }
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int r = rr + RPI * k;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ws + r * RB + ((cc ^ r) % NCH) * 16);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(g.C) + (rb + r) * g.ldc + col0 + 8 * cc) = v;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -556,7 +579,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_db_kernel(GemmArgs g, uint32_
     }
     DB_MFMA((KS - 1) & 1);
 
-    db_epilogue<EPI, TM, TN, OUT_BN / WN>(g, acc, m0 + wm * 128 + lr, n0 + wn * (OUT_BN / WN) + 4 * half);
+    // the stage the last step read is free: each wave's share of it holds
+    // the wave's output blocks; the barrier keeps the next tile's first
+    // copies into that stage behind every wave's epilogue
+    db_epilogue<EPI, TM, TN>(g, acc, db_smem + (s ^ 1) * S::STAGE + wave * (S::STAGE / NW), m0 + wm * 128,
+                             n0 + wn * (OUT_BN / WN), lane);
+    lds_barrier();
   }
   // nothing may still be writing LDS when the workgroup ends
   wait_vmem();
@@ -936,7 +964,8 @@ hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
     const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? (int64_t)g.swiglu_F + g.N : g.N;
     const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
     const int mm = g.M / DB_BM * DB_BM, nm = g.N / OUT_BN * OUT_BN;
-    const bool aligned = (g.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0 &&
+    const int64_t c_align = (EPI == LOOP_EPI_BF16 || EPI == LOOP_EPI_SWIGLU) ? 8 : 4;  // 16-byte rows
+    const bool aligned = g.ldc % c_align == 0 && (reinterpret_cast<uintptr_t>(g.C) & 15) == 0 &&
                          (reinterpret_cast<uintptr_t>(g.R) & 15) == 0 && (g.lda & 7) == 0 && (g.ldb & 7) == 0;
     if (g.K % DB_KB == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31) && aligned && nm > 0) {
       const size_t esz = (EPI == LOOP_EPI_BF16 || EPI == LOOP_EPI_SWIGLU) ? 2 : 4;
