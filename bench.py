@@ -31,6 +31,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 LONG_T = 131072
 VERIFY_K, VERIFY_STEPS = 4, 8
 INT8_STEPS, INT8_WARMUP = 32, 2
+GROUP_T = 4096
 PREFILL_T = 8192
 DECODE_B, DECODE_CTX = 64, 32768
 
@@ -85,6 +86,8 @@ def parse():
     p.add_argument("--no-int8", action="store_true", help="skip the weight-only int8 decode")
     p.add_argument("--no-int4", action="store_true", help="skip the weight-only int4 decode")
     p.add_argument("--no-b1", action="store_true", help="skip the batch-1 decode (bf16 / int8 / int4)")
+    p.add_argument("--no-group", action="store_true",
+                   help="skip the one-group real-width prefill (4 layers, 4096 hidden-state rows)")
     p.add_argument("--cpu-sample-tokens", type=int, default=8192)
     return p.parse_args()
 
@@ -154,7 +157,7 @@ def main():
 
     dims = synth.preset("full")
     max_seq = ((DECODE_CTX + args.decode_warmup + args.decode_steps + 1 + VERIFY_K * (VERIFY_STEPS + 1)
-                + 5 * (INT8_STEPS + INT8_WARMUP) + 63) // 64) * 64
+                + 8 * (INT8_STEPS + INT8_WARMUP) + 63) // 64) * 64
     cfg = L.make_config(dims, max_batch=DECODE_B, max_seq=max_seq, max_tokens=PREFILL_T)
     sched = L.loop_schedule(cfg)
     kinds_layer = {}
@@ -230,6 +233,55 @@ def main():
                     "launch_ms": round(k_avg_ms, 4), "launches": k_n,
                     "algorithmic_flop_per_launch": k_flop}
         step_frac = fl["total"] / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS
+
+    # ------------------------------------------- one group at real width
+    # One shared 4-layer group (GDN, GDN, GDN, full attention) run once as a
+    # loop block (fork, mHC, merge), prefill of 4096 N(0, 1) hidden-state
+    # rows (no embedding or head); its weights are layers 4..7 of the full
+    # model's (the first loop group, which carries the mHC parameters).
+    group = None
+    if not args.no_group:
+        dims_g = synth.preset("group")
+        cfg_g = L.make_config(dims_g, max_batch=1, max_seq=GROUP_T, max_tokens=GROUP_T)
+        kinds_g = ["full" if r[1] else "gdn" for r in L.loop_schedule(cfg_g)]
+        gptrs = {"final_norm": ptrs["final_norm"]}
+        for l in range(dims_g["n_layers"]):
+            for name, ptr in ptrs.items():
+                if name.startswith(f"L{cfg.loop_start + l}."):
+                    gptrs[f"L{l}." + name.split(".", 1)[1]] = ptr
+        ws_g_struct = L.make_weights_struct(dims_g["n_layers"], gptrs)
+        ab_g, wb_g = L.loop_arena_bytes(cfg_g), L.loop_workspace_bytes(cfg_g, GROUP_T)
+        arena_g = torch.empty(ab_g, dtype=torch.uint8, device="cuda")
+        wsp_g = torch.empty(wb_g, dtype=torch.uint8, device="cuda")
+        model_g = L.loop_model_create(cfg_g, ws_g_struct, arena_g.data_ptr(), ab_g, wsp_g.data_ptr(), wb_g)
+        xg = torch.empty((GROUP_T, dims_g["d_model"]), dtype=torch.float32, device="cuda")
+        L.loop_synth_normal(xg.data_ptr(), xg.numel(), 0, synth.SEED_X, synth.fnv1a32("bench.group.x"), 0,
+                            1.0, 0.0, stream)
+        hg = torch.empty_like(xg)
+
+        def group_step():
+            L.loop_prefill(model_g, 1, GROUP_T, [0], [0], d_hidden_in=xg.data_ptr(), d_hidden_out=hg.data_ptr(),
+                           stream=stream)
+
+        for _ in range(args.warmup):
+            group_step()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.steps):
+            group_step()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.steps
+        assert torch.isfinite(hg).all().item(), "non-finite group output"
+        flg = prefill_flops(dims_g, kinds_g, GROUP_T)
+        group = {"metric": "prefill tok/s, one shared 4-layer group at real width", "unit": "tok/s",
+                 "value": round(GROUP_T / (gms / 1e3), 1), "ms_per_step": round(gms, 3), "tokens": GROUP_T,
+                 "steps": args.steps, "warmup": args.warmup,
+                 "mfma_frac_step": round(flg["total"] / (gms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                 "algorithmic_flop_per_step": flg["total"]}
+        L.loop_model_destroy(model_g)
+        del arena_g, wsp_g, xg, hg
 
     # ------------------------------------------------------------- decode
     decode = None
@@ -347,14 +399,48 @@ def main():
                                     "algorithmic_bytes_per_step": byq["total"],
                                     "weight_bytes_per_step": byq["weights"]}
 
-        # batch-1 decode: sequence slot 0 alone at the same context, with the
-        # bf16 matrices, then int8, then int4 codes (weights dominate the step)
+        # multi-token verify: VERIFY_K drafted tokens per sequence checked in
+        # one call (logits and greedy token at every position), continuing
+        # the decode batch's caches
+        if not args.no_verify:
+            vt = torch.empty(DECODE_B * VERIFY_K, dtype=torch.int32, device="cuda")
+            L.loop_synth_token_ids(vt.data_ptr(), vt.numel(), dims["vocab"], synth.SEED_X,
+                                   synth.fnv1a32("bench.verify.ids"), stream)
+            vlog = torch.empty((DECODE_B * VERIFY_K, dims["vocab"]), dtype=torch.float32, device="cuda")
+            vnx = torch.empty(DECODE_B * VERIFY_K, dtype=torch.int32, device="cuda")
+
+            def verify_step(p):
+                L.loop_verify_step(model, DECODE_B, VERIFY_K, slots, [p] * DECODE_B, vt.data_ptr(),
+                                   d_logits=vlog.data_ptr(), d_next=vnx.data_ptr(), stream=stream)
+
+            verify_step(pos)  # warm-up
+            pos += VERIFY_K
+            v_ctx = pos
+            torch.cuda.synchronize()
+            v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            v0.record()
+            for _ in range(VERIFY_STEPS):
+                verify_step(pos)
+                pos += VERIFY_K
+            v1.record()
+            torch.cuda.synchronize()
+            vms = v0.elapsed_time(v1) / VERIFY_STEPS
+            assert torch.isfinite(vlog).all().item(), "non-finite verify logits"
+            decode["verify"] = {"metric": "verified tok/s", "value": round(DECODE_B * VERIFY_K / (vms / 1e3), 1),
+                                "unit": "tok/s", "k": VERIFY_K, "batch": DECODE_B, "ms_per_step": round(vms, 3),
+                                "steps": VERIFY_STEPS, "context": v_ctx}
+
+        # batch-1 decode: sequence slot 0 alone, after the batch legs (its
+        # caches continue from their last position), with the bf16 matrices,
+        # then int8, then int4 codes (weights dominate the step); each timed
+        # as eager calls and as launches of the captured decode graph (one
+        # host call per token; the graph feeds its greedy token back itself)
         if not args.no_b1:
             tok1 = tok[:1].clone()
             nxt1 = torch.zeros(1, dtype=torch.int32, device="cuda")
             p1 = pos
-            b1 = {"metric": "decode tok/s at batch 1", "unit": "tok/s", "context": p1, "steps": INT8_STEPS,
-                  "warmup": INT8_WARMUP}
+            b1 = {"metric": "decode tok/s at batch 1 (decode graph; eager calls beside)", "unit": "tok/s",
+                  "context": p1, "steps": INT8_STEPS, "warmup": INT8_WARMUP}
             for bits in (16, 8, 4):
                 keep = None
                 if bits == 8:
@@ -376,6 +462,19 @@ def main():
                     p1 += 1
                 e1.record()
                 torch.cuda.synchronize()
+                ms_e = e0.elapsed_time(e1) / INT8_STEPS
+                graph = L.loop_decode_graph_create(model, 1, [0], [p1], tok1.data_ptr(), INT8_WARMUP + INT8_STEPS,
+                                                   d_next=tok1.data_ptr())
+                for _ in range(INT8_WARMUP):
+                    L.loop_decode_graph_launch(graph, stream)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(INT8_STEPS):
+                    L.loop_decode_graph_launch(graph, stream)
+                e1.record()
+                torch.cuda.synchronize()
+                L.loop_decode_graph_destroy(graph)
+                p1 += INT8_WARMUP + INT8_STEPS
                 L.loop_model_set_int8(model, None)
                 L.loop_model_set_int4(model, None)
                 del keep
@@ -384,38 +483,10 @@ def main():
                 b1["bf16" if bits == 16 else f"int{bits}"] = {
                     "value": round(1e3 / ms1, 1), "ms_per_step": round(ms1, 3),
                     "hbm_frac_step": round(by1["total"] / (ms1 / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
-                    "algorithmic_bytes_per_step": by1["total"]}
+                    "algorithmic_bytes_per_step": by1["total"],
+                    "eager": {"value": round(1e3 / ms_e, 1), "ms_per_step": round(ms_e, 3),
+                              "hbm_frac_step": round(by1["total"] / (ms_e / 1e3) / 1e9 / PEAK_HBM_GBS, 4)}}
             decode["b1"] = b1
-
-        # multi-token verify: VERIFY_K drafted tokens per sequence checked in
-        # one call (logits and greedy token at every position), continuing
-        # the decode batch's caches
-        if not args.no_verify:
-            vt = torch.empty(DECODE_B * VERIFY_K, dtype=torch.int32, device="cuda")
-            L.loop_synth_token_ids(vt.data_ptr(), vt.numel(), dims["vocab"], synth.SEED_X,
-                                   synth.fnv1a32("bench.verify.ids"), stream)
-            vlog = torch.empty((DECODE_B * VERIFY_K, dims["vocab"]), dtype=torch.float32, device="cuda")
-            vnx = torch.empty(DECODE_B * VERIFY_K, dtype=torch.int32, device="cuda")
-
-            def verify_step(p):
-                L.loop_verify_step(model, DECODE_B, VERIFY_K, slots, [p] * DECODE_B, vt.data_ptr(),
-                                   d_logits=vlog.data_ptr(), d_next=vnx.data_ptr(), stream=stream)
-
-            verify_step(pos)  # warm-up
-            pos += VERIFY_K
-            torch.cuda.synchronize()
-            v0, v1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            v0.record()
-            for _ in range(VERIFY_STEPS):
-                verify_step(pos)
-                pos += VERIFY_K
-            v1.record()
-            torch.cuda.synchronize()
-            vms = v0.elapsed_time(v1) / VERIFY_STEPS
-            assert torch.isfinite(vlog).all().item(), "non-finite verify logits"
-            decode["verify"] = {"metric": "verified tok/s", "value": round(DECODE_B * VERIFY_K / (vms / 1e3), 1),
-                                "unit": "tok/s", "k": VERIFY_K, "batch": DECODE_B, "ms_per_step": round(vms, 3),
-                                "steps": VERIFY_STEPS, "context": DECODE_CTX}
 
     L.loop_model_destroy(model)
 
@@ -485,6 +556,7 @@ def main():
         "algorithmic_flop_per_step": fl["total"] if fl else None,
         "roofline": roofline,
         "decode": decode,
+        "group_prefill": group,
         "long_prefill": long,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),

@@ -215,6 +215,36 @@ typedef struct loop_decode_args {
 } loop_decode_args;
 int loop_decode_step(loop_model* m, const loop_decode_args* a, void* stream);
 
+/* Decode graph: the decode step of a fixed batch captured once into a HIP
+ * graph and replayed, one step per launch, so a token costs one graph launch
+ * on the host instead of ~600 kernel launches ([P1 section 2]: all 56
+ * executions run per generated token; [P2 section 4]: greedy decoding one
+ * token per step).  Each launch computes exactly what loop_decode_step does
+ * at the graph's current positions (same kernels, same launch shapes: the
+ * results are bit-identical), then advances every position by one.
+ *   create: `a` as for loop_decode_step; slots, loop_passes and the device
+ *           buffers d_tokens / d_logits / d_next / d_hidden_out are fixed for
+ *           the graph's life (their contents are read / written at each
+ *           launch: d_tokens may be d_next, so that each step feeds its greedy
+ *           token to the next); a->pos (host) are the first launch's
+ *           positions; max_steps >= 1 launches are allowed, and every
+ *           pos[b] + max_steps must be <= max_seq (LOOP_ECAPACITY).  The
+ *           capture runs on an internal stream and enqueues no work; the
+ *           graph keeps its own positions in device memory (allocated here).
+ *   launch: one step on `stream`; LOOP_ECAPACITY after max_steps launches.
+ *           Calls on the model (prefill, decode, other graphs) may come
+ *           between launches on the same stream; launches must not overlap
+ *           other calls on the model (they share the workspace).
+ *   positions: the next launch's positions (host [batch]).
+ *   destroy: frees the graph; the model must outlive it.
+ * Model changes after create (loop_model_set_int8 / _int4) do not reach the
+ * captured graph. */
+typedef struct loop_decode_graph loop_decode_graph;
+int loop_decode_graph_create(loop_model* m, const loop_decode_args* a, int32_t max_steps, loop_decode_graph** out);
+int loop_decode_graph_launch(loop_decode_graph* g, void* stream);
+int loop_decode_graph_positions(const loop_decode_graph* g, int32_t* pos_out);
+void loop_decode_graph_destroy(loop_decode_graph* g);
+
 /* Verify step: k tokens per sequence (k <= LOOP_VERIFY_MAX) appended at
  * positions pos[b] .. pos[b]+k-1 -- a prefill of k tokens -- with the logits
  * (and greedy next tokens, and taps) of every position, as speculative

@@ -107,6 +107,10 @@ def _load():
         "loop_model_destroy": (None, [_vp]),
         "loop_prefill": (ctypes.c_int, [_vp, P(loop_prefill_args), _vp]),
         "loop_decode_step": (ctypes.c_int, [_vp, P(loop_decode_args), _vp]),
+        "loop_decode_graph_create": (ctypes.c_int, [_vp, P(loop_decode_args), _i32, P(_vp)]),
+        "loop_decode_graph_launch": (ctypes.c_int, [_vp, _vp]),
+        "loop_decode_graph_positions": (ctypes.c_int, [_vp, P(_i32)]),
+        "loop_decode_graph_destroy": (None, [_vp]),
         "loop_verify_step": (ctypes.c_int, [_vp, P(loop_verify_args), _vp]),
         "loop_exec_mixer": (ctypes.c_int, [_vp, P(loop_mixer_args), _vp]),
         "loop_model_set_int8": (ctypes.c_int, [_vp, _vp]),
@@ -134,7 +138,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("loop_kv_bytes", "loop_state_bytes", "loop_arena_bytes", "loop_workspace_bytes",
             "loop_cache_offset", "loop_schedule", "loop_model_create", "loop_model_destroy",
-            "loop_prefill", "loop_decode_step", "loop_verify_step", "loop_debug_mhc", "loop_last_error",
+            "loop_prefill", "loop_decode_step", "loop_decode_graph_create", "loop_decode_graph_launch",
+            "loop_decode_graph_positions", "loop_decode_graph_destroy", "loop_verify_step", "loop_debug_mhc", "loop_last_error",
             "loop_model_set_int8", "loop_quantize_int8", "loop_model_set_int4", "loop_quantize_int4",
             "loop_profile", "loop_profile_read", "loop_op_gemm", "loop_synth_normal",
             "loop_synth_token_ids")
@@ -295,6 +300,36 @@ def loop_decode_step(model: int, batch: int, slots, pos, d_tokens: int, d_logits
     a.d_tokens = d_tokens
     a.d_logits, a.d_next, a.d_hidden_out = d_logits or None, d_next or None, d_hidden_out or None
     _check(_lib.loop_decode_step(model, ctypes.byref(a), stream or None))
+
+
+def loop_decode_graph_create(model: int, batch: int, slots, pos, d_tokens: int, max_steps: int,
+                             d_logits: int = 0, d_next: int = 0, d_hidden_out: int = 0,
+                             loop_passes: int = 0) -> int:
+    """Capture the decode step of this batch into a graph; returns its handle."""
+    a = loop_decode_args()
+    a.loop_passes = loop_passes
+    a.batch = batch
+    sl, ps = _i32arr(slots), _i32arr(pos)
+    a.slots, a.pos = sl, ps
+    a.d_tokens = d_tokens
+    a.d_logits, a.d_next, a.d_hidden_out = d_logits or None, d_next or None, d_hidden_out or None
+    g = _vp()
+    _check(_lib.loop_decode_graph_create(model, ctypes.byref(a), max_steps, ctypes.byref(g)))
+    return g.value
+
+
+def loop_decode_graph_launch(graph: int, stream: int = 0) -> None:
+    _check(_lib.loop_decode_graph_launch(graph, stream or None))
+
+
+def loop_decode_graph_positions(graph: int, batch: int) -> list:
+    out = (_i32 * batch)()
+    _check(_lib.loop_decode_graph_positions(graph, out))
+    return list(out)
+
+
+def loop_decode_graph_destroy(graph: int) -> None:
+    _lib.loop_decode_graph_destroy(graph)
 
 
 def loop_verify_step(model: int, batch: int, k: int, slots, pos, d_tokens: int, d_logits: int = 0,

@@ -78,6 +78,8 @@ struct SinkhornBatch {
 hipError_t launch_sinkhorn_layers(const SinkhornBatch& sb, hipStream_t s);
 int argmax_chunks(int64_t n);
 hipError_t launch_argmax(const float* x, int rows, int64_t n, float* pv, int* pi, int32_t* out, hipStream_t s);
+// pos[b] += 1 for b < B (the positions of a replayed decode graph)
+hipError_t launch_advance_pos(int32_t* pos, int B, hipStream_t s);
 
 // ---- attention
 struct AttnPrepArgs {

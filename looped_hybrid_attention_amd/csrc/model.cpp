@@ -636,7 +636,10 @@ extern "C" int loop_prefill(loop_model* m, const loop_prefill_args* a, void* str
   return 0;
 }
 
-extern "C" int loop_decode_step(loop_model* m, const loop_decode_args* a, void* stream) {
+namespace {
+
+// Host checks of a decode step; the call's pass count on success.
+int check_decode(loop_model* m, const loop_decode_args* a, int* passes) {
   if (!m || !a) return loop_fail(LOOP_EINVAL, "model or args NULL");
   const loop_config& c = m->cfg;
   const int B = a->batch;
@@ -648,15 +651,18 @@ extern "C" int loop_decode_step(loop_model* m, const loop_decode_args* a, void* 
   if (int r = check_slots(c, B, a->slots)) return r;
   for (int b = 0; b < B; ++b)
     if (a->pos[b] < 0 || a->pos[b] >= c.max_seq) return loop_fail(LOOP_ECAPACITY, "pos %d out of [0, %d)", a->pos[b], c.max_seq);
-  int passes = 0;
-  if (int r = call_passes(m, a->loop_passes, B, a->slots, nullptr, &passes)) return r;
-  hipStream_t s = (hipStream_t)stream;
+  return call_passes(m, a->loop_passes, B, a->slots, nullptr, passes);
+}
+
+// The device work of one decode step, with positions / slots / last rows at
+// meta (pos [max_batch], slot [max_batch], last [max_batch]).
+int enqueue_decode(loop_model* m, const loop_decode_args* a, int passes, const int32_t* meta, hipStream_t s) {
+  const loop_config& c = m->cfg;
+  const int B = a->batch;
   Call k{B, 1, B, true, nullptr, nullptr, nullptr, &m->sched_p[passes - 1]};
-  const int32_t* meta = at<int32_t>(m, m->L.meta);
   k.d_pos = meta;
   k.d_slot = meta + c.max_batch;
   k.d_last = meta + 2 * c.max_batch;
-  if (int r = upload_meta(m, B, 1, a->pos, a->slots, s)) return r;
   float* h = at<float>(m, m->L.h);
   HIP_TRY(launch_embed(a->d_tokens, m->embed, h, B, c.d_model, c.vocab, s));
   if (int r = run_forward(m, k, nullptr, 0, nullptr, s)) return r;
@@ -667,6 +673,115 @@ extern "C" int loop_decode_step(loop_model* m, const loop_decode_args* a, void* 
     if (a->d_next)
       HIP_TRY(launch_argmax(logits, B, c.vocab, at<float>(m, m->L.am_v), at<int>(m, m->L.am_i), a->d_next, s));
   }
+  return 0;
+}
+
+}  // namespace
+
+extern "C" int loop_decode_step(loop_model* m, const loop_decode_args* a, void* stream) {
+  int passes = 0;
+  if (int r = check_decode(m, a, &passes)) return r;
+  hipStream_t s = (hipStream_t)stream;
+  if (int r = upload_meta(m, a->batch, 1, a->pos, a->slots, s)) return r;
+  return enqueue_decode(m, a, passes, at<int32_t>(m, m->L.meta), s);
+}
+
+struct loop_decode_graph {
+  loop_model* m = nullptr;
+  int B = 0;
+  int steps_left = 0;
+  std::vector<int32_t> pos;       // positions of the next launch (host mirror)
+  int32_t* meta = nullptr;        // device: pos, slot, last rows [3][max_batch]
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
+extern "C" void loop_decode_graph_destroy(loop_decode_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  if (g->meta) (void)hipFree(g->meta);
+  delete g;
+}
+
+extern "C" int loop_decode_graph_create(loop_model* m, const loop_decode_args* a, int32_t max_steps,
+                                        loop_decode_graph** out) {
+  if (!out) return loop_fail(LOOP_EINVAL, "out is NULL");
+  *out = nullptr;
+  int passes = 0;
+  if (int r = check_decode(m, a, &passes)) return r;
+  const loop_config& c = m->cfg;
+  if (max_steps < 1) return loop_fail(LOOP_EINVAL, "max_steps must be >= 1");
+  for (int b = 0; b < a->batch; ++b)
+    if ((int64_t)a->pos[b] + max_steps > c.max_seq)
+      return loop_fail(LOOP_ECAPACITY, "pos %d + %d steps exceeds max_seq %d", a->pos[b], max_steps, c.max_seq);
+  loop_decode_graph* g = new loop_decode_graph;
+  g->m = m;
+  g->B = a->batch;
+  g->steps_left = max_steps;
+  g->pos.assign(a->pos, a->pos + a->batch);
+  std::vector<int32_t> meta(3 * c.max_batch, 0);
+  for (int b = 0; b < a->batch; ++b) {
+    meta[b] = a->pos[b];
+    meta[c.max_batch + b] = a->slots[b];
+    meta[2 * c.max_batch + b] = b;
+  }
+  hipError_t e = hipMalloc(&g->meta, meta.size() * sizeof(int32_t));
+  if (e == hipSuccess) e = hipMemcpy(g->meta, meta.data(), meta.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    loop_decode_graph_destroy(g);
+    return loop_hip_fail(e, "decode graph positions");
+  }
+  // capture on a stream of our own (default priority); relaxed mode lets the
+  // launchers' one-time kernel attribute calls happen during the capture
+  hipStream_t cs = nullptr;
+  e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    loop_decode_graph_destroy(g);
+    return loop_hip_fail(e, "capture stream");
+  }
+  const int prof = m->prof_class;  // no timing events inside the graph
+  m->prof_class = -1;
+  int r = 0;
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeRelaxed);
+  if (e == hipSuccess) {
+    r = enqueue_decode(m, a, passes, g->meta, cs);
+    if (r == 0) {
+      hipError_t e2 = launch_advance_pos(g->meta, a->batch, cs);
+      if (e2 != hipSuccess) r = loop_hip_fail(e2, "advance positions");
+    }
+    hipGraph_t graph = nullptr;
+    e = hipStreamEndCapture(cs, &graph);
+    g->graph = graph;
+  }
+  m->prof_class = prof;
+  (void)hipStreamDestroy(cs);
+  if (r == 0 && e != hipSuccess) r = loop_hip_fail(e, "decode graph capture");
+  if (r == 0) {
+    e = hipGraphInstantiate(&g->exec, g->graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) r = loop_hip_fail(e, "hipGraphInstantiate");
+  }
+  if (r) {
+    loop_decode_graph_destroy(g);
+    return r;
+  }
+  *out = g;
+  return 0;
+}
+
+extern "C" int loop_decode_graph_launch(loop_decode_graph* g, void* stream) {
+  if (!g) return loop_fail(LOOP_EINVAL, "graph is NULL");
+  if (g->steps_left <= 0) return loop_fail(LOOP_ECAPACITY, "decode graph: all of its steps were launched");
+  hipError_t e = hipGraphLaunch(g->exec, (hipStream_t)stream);
+  if (e != hipSuccess) return loop_hip_fail(e, "hipGraphLaunch");
+  --g->steps_left;
+  for (int32_t& p : g->pos) ++p;
+  return 0;
+}
+
+extern "C" int loop_decode_graph_positions(const loop_decode_graph* g, int32_t* pos_out) {
+  if (!g || !pos_out) return loop_fail(LOOP_EINVAL, "NULL argument");
+  for (int b = 0; b < g->B; ++b) pos_out[b] = g->pos[b];
   return 0;
 }
 

@@ -353,6 +353,12 @@ __global__ __launch_bounds__(NT) void argmax_stage2(const float* pv, const int* 
   if (threadIdx.x == 0) out[row] = bi;
 }
 
+// Positions of the next decode step of a replayed graph: pos[b] += 1.
+__global__ void advance_pos_kernel(int32_t* pos, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < B) pos[b] += 1;
+}
+
 template <typename F>
 hipError_t by_width(int d, F f) {
   if (d <= 256) return f(std::integral_constant<int, 1>());
@@ -411,6 +417,12 @@ hipError_t launch_sinkhorn(const float* mix, int iters, float* out, hipStream_t 
 }
 
 int argmax_chunks(int64_t n) { return (int)((n + 8191) / 8192); }
+
+hipError_t launch_advance_pos(int32_t* pos, int B, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(advance_pos_kernel, dim3((B + 255) / 256), dim3(256), 0, s, pos, B);
+  return hipGetLastError();
+}
 
 hipError_t launch_argmax(const float* x, int rows, int64_t n, float* pv, int* pi, int32_t* out, hipStream_t s) {
   const int nc = argmax_chunks(n);

@@ -172,3 +172,17 @@ def test_model_create_valid_arguments_reach_the_device_query():
     w = L.make_weights_struct(cfg.n_layers, ptrs)
     code, msg = _create(L, cfg, w, FAKE, ab, FAKE + (1 << 36), wb)
     assert code in (LOOP_EHIP, LOOP_EDEVICE), (code, msg)
+
+
+def test_decode_graph_rejects_null_arguments_on_host():
+    # the graph entry points check their handles before any HIP call
+    import looped_hybrid_attention_amd as L
+    lib = L._lib
+    g = ctypes.c_void_p()
+    assert lib.loop_decode_graph_create(None, None, 1, None) == -1  # LOOP_EINVAL
+    assert lib.loop_decode_graph_create(None, None, 1, ctypes.byref(g)) == -1  # LOOP_EINVAL
+    assert g.value is None
+    assert lib.loop_decode_graph_launch(None, None) == -1  # LOOP_EINVAL
+    out = (ctypes.c_int32 * 1)()
+    assert lib.loop_decode_graph_positions(None, out) == -1  # LOOP_EINVAL
+    lib.loop_decode_graph_destroy(None)  # a no-op
