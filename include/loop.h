@@ -390,6 +390,22 @@ int loop_quantize_int4(const void* d_w, int64_t N, int64_t K, int64_t ldw, uint8
                        void* stream);
 int loop_model_set_int4(loop_model* m, const loop_q4_layer* layers);
 
+/* Weight-only quantized GEMM: one decode projection on its own, with the
+ * kernels loop_decode_step runs when int8 / int4 codes are registered.
+ * C[M,N] = A[M,K] . W[N,K]^T with W the dequantized codes of
+ * loop_quantize_int8 (bits 8: W[n][k] = s_n q_nk) or loop_quantize_int4
+ * (bits 4: W[n][k] = the bf16 value nearest to s_ng q_nk); the epilogues of
+ * loop_op_gemm (SwiGLU: the codes and scales hold the gate rows then the up
+ * rows, 2N rows).  A bf16 [M][lda] (device, 16-byte aligned); Bq the codes
+ * (device, ldq bytes per row, 16-byte aligned rows); scale as the quantizer
+ * writes it (device).  Requires 1 <= M <= 64, K % 128 == 0, lda % 8 == 0,
+ * lda >= K, ldq % 16 == 0 and ldq >= the code bytes of a row; LOOP_ESHAPE /
+ * LOOP_EINVAL otherwise (nothing enqueued).  d_ws / ws_bytes as for
+ * loop_op_gemm (split-K partials, summed in split order). */
+int loop_op_gemm_quant(int32_t bits, const void* A, int64_t lda, const void* Bq, int64_t ldq, const float* scale,
+                       void* C, int64_t ldc, const float* R, int32_t M, int32_t N, int32_t K, int32_t epi,
+                       float* d_ws, size_t ws_bytes, void* stream);
+
 const char* loop_last_error(void);
 
 /* Kernel timing of one kernel class inside the model calls: with class c

@@ -125,6 +125,8 @@ def _load():
                                         _i32, _vp, _sz, _vp]),
         "loop_op_gemm_static": (ctypes.c_int, [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _i32, _i32,
                                                _i32, _vp]),
+        "loop_op_gemm_quant": (ctypes.c_int, [_i32, _vp, _i64, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i32,
+                                              _i32, _i32, _vp, _sz, _vp]),
         "loop_synth_normal": (ctypes.c_int, [_vp, _i64, _i32, _u32, _u32, _i64, _f64, _f64, _vp]),
         "loop_synth_token_ids": (ctypes.c_int, [_vp, _i64, _u32, _u32, _u32, _vp]),
     }
@@ -199,6 +201,12 @@ def loop_op_gemm(A: int, lda: int, B: int, ldb: int, C: int, ldc: int, R: int, M
                  K: int, epi: int, stream: int = 0, ws: int = 0, ws_bytes: int = 0) -> None:
     _check(_lib.loop_op_gemm(A, lda, B, ldb, C, ldc, R or None, M, N, K, epi, ws or None, ws_bytes,
                              stream or None))
+
+
+def loop_op_gemm_quant(bits: int, A: int, lda: int, Bq: int, ldq: int, scale: int, C: int, ldc: int, R: int,
+                       M: int, N: int, K: int, epi: int, stream: int = 0, ws: int = 0, ws_bytes: int = 0) -> None:
+    _check(_lib.loop_op_gemm_quant(bits, A, lda, Bq, ldq, scale, C, ldc, R or None, M, N, K, epi, ws or None,
+                                   ws_bytes, stream or None))
 
 
 LOOP_GEMM_STATIC_SCRATCH_BYTES = 32 << 20

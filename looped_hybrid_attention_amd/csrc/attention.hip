@@ -153,6 +153,9 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(AttnPrepArgs a) {
 // sweep).  The loads pick their global source to realise both the swizzle and
 // the K row order.
 constexpr int KT = 64;  // keys per LDS tile
+#ifndef FLASH_FD
+#define FLASH_FD 4
+#endif
 template <int D>
 struct FlashLds {
   static constexpr int KROW = D * 2;                   // bytes per K row
@@ -166,8 +169,8 @@ DEV int k_swz(int r) { return CR >= 16 ? (r & 15) : (r & 7); }
 DEV int v_swz(int d) { return (d >> 1) & 7; }
 
 template <int NDT, int FD, int VROW>
-DEV void flash_pv(f32x16 (&o)[NDT], f32x16 (&s)[2], float& l, float m, float scale, const uint8_t* vr, int h,
-                  int vsw) {
+DEV void flash_pv(f32x16 (&o)[NDT], f32x16 (&s)[2], float& l, float m, float scale, const uint8_t* vr,
+                  const int (&voff)[4]) {
   float lsum = 0.f;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
@@ -184,8 +187,7 @@ DEV void flash_pv(f32x16 (&o)[NDT], f32x16 (&s)[2], float& l, float m, float sca
 #pragma unroll
     for (int e = 0; e < 8; ++e) pf[ks2][e] = f2bf(s[ks2 >> 1][(ks2 & 1) * 8 + e]);
   bf16x8 vf[4 * NDT];
-#define FLASH_VREAD(g_) \
-  vf[g_] = *reinterpret_cast<const bf16x8*>(vr + ((g_) % NDT) * 32 * VROW + (((2 * ((g_) / NDT) + h) ^ vsw) << 4))
+#define FLASH_VREAD(g_) vf[g_] = *reinterpret_cast<const bf16x8*>(vr + ((g_) % NDT) * 32 * VROW + voff[(g_) / NDT])
 #pragma unroll
   for (int g = 0; g < FD; ++g) FLASH_VREAD(g);
 #pragma unroll
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
   constexpr int VI = D * 8 / 64 / W;    // V^T copy instructions per wave and tile
   static_assert(KI * 64 * W == KT * CR && VI * 64 * W == D * 8, "tile / wave split");
   static_assert(CR >= 8, "swizzle needs 8 chunks per row");
-  constexpr int FD = 4;  // LDS operand reads in flight ahead of the MFMAs
+  constexpr int FD = FLASH_FD;  // LDS operand reads in flight ahead of the MFMAs
   using L = FlashLds<D>;
   extern __shared__ __align__(16) uint8_t flash_smem[];
 
@@ -295,6 +297,15 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
   float m_i = -1e30f, l_i = 0.f;
   const float scale = a.scale_log2;
   const int ksw = k_swz<CR>(ql), vsw = v_swz(ql);  // swizzles of the rows this lane reads
+  // Byte offsets of this lane's 16-byte chunk in its K row for the 16-dim
+  // steps G = 0..7; the swizzle (< 16) leaves bit 4 of the chunk index alone,
+  // so step G + 8 sits 256 bytes further (an immediate).  V^T: chunk of key
+  // group q = 0..3.  Few per-lane registers, the rest immediates.
+  int koff[8], voff[4];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) koff[st] = ((2 * st + h) ^ ksw) << 4;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) voff[q] = ((2 * q + h) ^ vsw) << 4;
   const int qpos_lo = p0 + tile * QT + (wave / G) * 32;  // first query of the wave
   FLASH_WAIT_COPIES();
   __syncthreads();
@@ -335,8 +346,9 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
       {
         const uint8_t* kr = sK + ql * L::KROW;
         bf16x8 kf[2 * NKS];
-#define FLASH_KREAD(g_) \
-  kf[g_] = *reinterpret_cast<const bf16x8*>(kr + ((g_) & 1) * 32 * L::KROW + (((2 * ((g_) >> 1) + h) ^ ksw) << 4))
+#define FLASH_KREAD(g_)                                                                  \
+  kf[g_] = *reinterpret_cast<const bf16x8*>(kr + ((g_) & 1) * 32 * L::KROW + koff[((g_) >> 1) & 7] + \
+                                            (((g_) >> 4) << 8))
 #pragma unroll
         for (int g = 0; g < FD; ++g) FLASH_KREAD(g);
 #pragma unroll
@@ -376,7 +388,7 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
       mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * scale;
       bump = mloc > m_i + 8.f;
       if (__builtin_amdgcn_read_exec() & __ballot(bump)) break;
-      flash_pv<NDT, FD, L::VROW>(o, s, l_i, m_i, scale, sK + KT * L::KROW + ql * L::VROW, h, vsw);
+      flash_pv<NDT, FD, L::VROW>(o, s, l_i, m_i, scale, sK + KT * L::KROW + ql * L::VROW, voff);
       FLASH_SYNC(j);
     }
     if (j >= nkt) break;
@@ -389,7 +401,7 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
       m_i = m_new;
     }
     flash_pv<NDT, FD, L::VROW>(o, s, l_i, m_i, scale, flash_smem + (j & 1) * L::STAGE + KT * L::KROW + ql * L::VROW,
-                               h, vsw);
+                               voff);
     FLASH_SYNC(j);
     ++j;
   }

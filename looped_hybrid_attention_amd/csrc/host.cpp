@@ -162,6 +162,25 @@ extern "C" int loop_op_gemm(const void* A, int64_t lda, const void* B, int64_t l
   return e == hipSuccess ? 0 : loop_hip_fail(e, "gemm launch");
 }
 
+extern "C" int loop_op_gemm_quant(int32_t bits, const void* A, int64_t lda, const void* Bq, int64_t ldq,
+                                  const float* scale, void* C, int64_t ldc, const float* R, int32_t M, int32_t N,
+                                  int32_t K, int32_t epi, float* d_ws, size_t ws_bytes, void* stream) {
+  if (bits != 8 && bits != 4) return loop_fail(LOOP_EINVAL, "gemm_quant: bits must be 8 or 4");
+  if (!A || !Bq || !scale || !C) return loop_fail(LOOP_EINVAL, "gemm_quant: null operand");
+  if (epi < 0 || epi > 3) return loop_fail(LOOP_EINVAL, "gemm_quant: bad epilogue %d", epi);
+  if (epi == LOOP_EPI_F32_RES && !R) return loop_fail(LOOP_EINVAL, "gemm_quant: residual epilogue needs R");
+  if (M < 1 || M > 64 || N <= 0 || K <= 0 || K % 128)
+    return loop_fail(LOOP_ESHAPE, "gemm_quant: need 1 <= M <= 64, N > 0, K > 0, K %% 128 == 0");
+  const int64_t row_bytes = bits == 8 ? K : K / 2;
+  if (lda % 8 || lda < K || ldq % 16 || ldq < row_bytes || ldc < N)
+    return loop_fail(LOOP_ESHAPE, "gemm_quant: lda %% 8, lda >= K, ldq %% 16, ldq >= %lld, ldc >= N",
+                     (long long)row_bytes);
+  if (((uintptr_t)A | (uintptr_t)Bq) % 16) return loop_fail(LOOP_EINVAL, "gemm_quant: A and Bq must be 16-byte aligned");
+  hipError_t e = launch_gemm_wq(bits, A, lda, Bq, ldq, scale, C, ldc, R, M, N, K, epi, (hipStream_t)stream, d_ws,
+                                d_ws ? ws_bytes : 0);
+  return e == hipSuccess ? 0 : loop_hip_fail(e, "gemm_quant launch");
+}
+
 // ------------------------------------------------------- synthetic inputs
 
 extern "C" int loop_synth_normal(void* dst, int64_t n, int32_t dtype, uint32_t seed, uint32_t key,

@@ -179,15 +179,17 @@ def test_int4_decode_tiny():
         g.close()
 
 
-def test_quantized_decode_ragged_batch():
-    """29 sequences (a ragged M for the weight-streaming tiles: two 16-row
-    activation tiles, the second part-filled) of the tiny
-    model from seeded caches, one decode step with int4 codes, then (GDN
-    states regenerated, the appended position rewritten) one with int8
-    codes; sampled sequences against the oracle in fp32 and fp64."""
+@pytest.mark.parametrize("B", [9, 29, 37])
+def test_quantized_decode_ragged_batch(B):
+    """B sequences (a ragged M for the weight-streaming tiles: 9, 29 and 37
+    rows reach the one-, two- and four-tile activation variants, the last
+    tile part-filled) of the tiny model from seeded caches, one decode step
+    with int4 codes, then (GDN states regenerated, the appended position
+    rewritten) one with int8 codes; sampled sequences (first, middle, last)
+    against the oracle in fp32 and fp64."""
     torch = torch_cuda()
     dims = synth.preset("tiny")
-    B, max_seq, T = 29, 512, 200
+    max_seq, T = 512, 200
     g = GpuModel(torch, dims, max_batch=B, max_seq=max_seq, max_tokens=512)
     try:
         L, cfg, s = g.L, g.cfg, g.stream()
@@ -249,7 +251,7 @@ def test_quantized_decode_ragged_batch():
             L.loop_model_set_int4(g.handle, None)
             L.loop_model_set_int8(g.handle, None)
             del keep
-            for b in (0, 17, 28):
+            for b in (0, B // 2, B - 1):
                 outs = []
                 for dt in (np.float32, np.float64):
                     st = state_of(b, dt)
