@@ -149,12 +149,19 @@ DEV int64_t chunk_index(const GdnArgs& a, int b, int h, int c) {
 // are zero (q = k = v = 0, beta = 0, no decay).  The barriers order LDS
 // accesses only: the global stores stay in flight.
 constexpr int PNT = 256;
+// LDS: q and k rows, K^T, V^T, A and T, the small arrays.  Where A and T fit
+// in the q and k rows (Dk = 128) they take those bytes (they are formed only
+// after every wave has read q and k): 74 KB, two workgroups per CU.
 template <int DK>
-constexpr int prep_lds_bytes() {
-  return (2 * CH * (DK + 8) + 2 * DK * CH) * 2 + (2 * CH * (CH + 4) + 4 * 16 * 20 + 6 * CH) * 4;
+constexpr bool prep_alias() {
+  return CH * (DK + 8) * 2 >= CH * (CH + 4) * 4;
 }
 template <int DK>
-__global__ __launch_bounds__(PNT, 1) void gdn_prep_kernel(GdnArgs a) {
+constexpr int prep_lds_bytes() {
+  return (2 * CH * (DK + 8) + 2 * DK * CH) * 2 + ((prep_alias<DK>() ? 0 : 2 * CH * (CH + 4)) + 4 * 16 * 20 + 6 * CH) * 4;
+}
+template <int DK>
+__global__ __launch_bounds__(PNT, 2) void gdn_prep_kernel(GdnArgs a) {
   constexpr int DV = DK;
   constexpr int LR = DK + 8;   // bf16 stride of the [CH][DK] rows
   constexpr int LA = CH + 4;   // fp32 stride of the [CH][CH] rows
@@ -167,9 +174,10 @@ __global__ __launch_bounds__(PNT, 1) void gdn_prep_kernel(GdnArgs a) {
   uint16_t* sK = sQ + CH * LR;                            // [CH][LR] raw k
   uint16_t* sKt = sK + CH * LR;                           // [DK][CH] raw k transposed (kt_at)
   uint16_t* sVt = sKt + DK * CH;                          // [DV][CH] raw v transposed (kt_at)
-  float* sA = reinterpret_cast<float*>(sVt + DV * CH);    // [CH][LA] A
-  float* sT = sA + CH * LA;                               // [CH][LA] T
-  float* sX = sT + CH * LA;                               // [4][16][XS]
+  constexpr bool ALIAS = prep_alias<DK>();
+  float* sA = ALIAS ? reinterpret_cast<float*>(sQ) : reinterpret_cast<float*>(sVt + DV * CH);  // [CH][LA] A
+  float* sT = ALIAS ? reinterpret_cast<float*>(sK) : sA + CH * LA;                            // [CH][LA] T
+  float* sX = ALIAS ? reinterpret_cast<float*>(sVt + DV * CH) : sT + CH * LA;                 // [4][16][XS]
   float* sG = sX + 4 * 16 * XS;                           // cumulative log alpha
   float* sB = sG + CH;                                    // beta
   float* sNq = sB + CH;                                   // qs / |q|
@@ -265,10 +273,14 @@ __global__ __launch_bounds__(PNT, 1) void gdn_prep_kernel(GdnArgs a) {
     if (tid == 0) sc[2 * CH] = __expf(GC);                      // gC
   }
   // K K^T -> A (strictly lower), Q K^T -> Mqk (lower incl. diagonal): the 10
-  // lower 16x16 tiles of each; wave w takes jobs w, w + 4, ...
+  // lower 16x16 tiles of each; wave w takes jobs w, w + 4, ... (five each).
+  // All products first, then a barrier: A overwrites the q and k rows.
   {
     float* Mq = a.Mq + cb * CH * CH;
-    for (int job = wave; job < 20; job += 4) {
+    f32x4 accs[5];
+#pragma unroll
+    for (int n = 0; n < 5; ++n) {
+      const int job = wave + 4 * n;
       const bool qk = job >= 10;
       int q = qk ? job - 10 : job, I = 0;
       while (q > I) { q -= I + 1; ++I; }
@@ -279,6 +291,17 @@ __global__ __launch_bounds__(PNT, 1) void gdn_prep_kernel(GdnArgs a) {
       for (int ks = 0; ks < DK / 32; ++ks)
         acc = mfma16x16x32(lds8(src + (16 * I + l16) * LR + 32 * ks + 8 * lq),
                            lds8(sK + (16 * J + l16) * LR + 32 * ks + 8 * lq), acc);
+      accs[n] = acc;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int n = 0; n < 5; ++n) {
+      const int job = wave + 4 * n;
+      const bool qk = job >= 10;
+      int q = qk ? job - 10 : job, I = 0;
+      while (q > I) { q -= I + 1; ++I; }
+      const int J = q;
+      const f32x4 acc = accs[n];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * I + 4 * lq + r, col = 16 * J + l16;
