@@ -57,6 +57,13 @@ DEV f32x4 mfma16x16x4f32_apart(float a, float b, f32x4 c) {
   asm volatile("" ::"v"(c), "v"(d));
   return d;
 }
+// The bf16 16x16x32 MFMA with its result kept apart from its C operand (as
+// above).
+DEV f32x4 mfma16x16x32_apart(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  const f32x4 d = mfma16x16x32(a, b, c);
+  asm volatile("" ::"v"(c), "v"(d));
+  return d;
+}
 // acc += A[0:16, 0:16] . B[0:16, 0:16] with every result apart from its C
 DEV void mm_nn16_apart(f32x4& acc, const float* A, int lda, const float* B, int ldb) {
   const int l = threadIdx.x & 63, i = l & 15, kk = l >> 4;
@@ -289,8 +296,8 @@ __global__ __launch_bounds__(PNT, 2) void gdn_prep_kernel(GdnArgs a) {
       f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks)
-        acc = mfma16x16x32(lds8(src + (16 * I + l16) * LR + 32 * ks + 8 * lq),
-                           lds8(sK + (16 * J + l16) * LR + 32 * ks + 8 * lq), acc);
+        acc = mfma16x16x32_apart(lds8(src + (16 * I + l16) * LR + 32 * ks + 8 * lq),
+                                 lds8(sK + (16 * J + l16) * LR + 32 * ks + 8 * lq), acc);
       accs[n] = acc;
     }
     lds_barrier();
