@@ -652,37 +652,34 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
 // ------------------------------------------------------- chunk output
 // grid (chunk, head, seq), eight waves: from the chunk's entering state S_c
 // and U (both stored by the scan), O = sq * (Q S_c^T) + Mqk U, then per token
-// y = RMSNorm(O; g_o) * SiLU(z) over Dv -> bf16.  S_c and U^T go to
-// LDS as three bf16 parts (B operands, rows j; 16-byte groups swizzled so the
-// operand reads of 16 consecutive rows and the part writes spread over the
-// banks).  Wave w: token tile w % 4 and half w / 4 of the Dv columns.
+// y = RMSNorm(O; g_o) * SiLU(z) over Dv -> bf16.  One 48 KB LDS region holds
+// three-part bf16 B operands (rows j, 64 columns; 16-byte groups swizzled by
+// (j / 2) % 8 so that the operand reads of 16 consecutive rows and the part
+// writes spread over the banks): first S_c's columns 0..63, then 64..127
+// (Q S_c^T accumulates over the two passes), then U^T.  Two workgroups share
+// a CU.  Wave w: token tile w % 4 and half w / 4 of the Dv columns.
 constexpr int ONT = 512;
 template <int DK>
 struct OutLds {
-  static constexpr int S_PART = DK * DK;   // [Dv][Dk] bf16
-  static constexpr int U_PART = DK * CH;   // [Dv][CH] bf16
-  static constexpr int bytes = (3 * S_PART + 3 * U_PART) * 2 + 2 * CH * 4;
+  static constexpr int PART = DK * CH;     // one part of a [Dv][64] region (bf16)
+  static constexpr int bytes = 3 * PART * 2 + 2 * CH * 4;
 };
-template <int DK>
-DEV int s_at(int j, int k) {  // element (j, k) of an S part
-  return j * DK + 8 * ((k >> 3) ^ (j & (DK / 8 - 1))) + (k & 7);
-}
-DEV int u_at(int j, int t) {  // element (j, t) of a U^T part
+DEV int u_at(int j, int t) {  // element (j, t) of a [rows][64] part
   return j * CH + 8 * ((t >> 3) ^ ((j >> 1) & 7)) + (t & 7);
 }
 
 template <int DK>
-__global__ __launch_bounds__(ONT, 1) void gdn_out_kernel(GdnArgs a) {
+__global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
   constexpr int DV = DK;
   using L = OutLds<DK>;
   constexpr int NKS = DK / 32;
+  constexpr int NH = DK / 64;               // passes over 64 columns of S_c
   constexpr int NJT = DV / 32;              // 16-column tiles per wave (half of Dv)
   constexpr int SP = DV * DK / 4 / ONT;     // S_c pieces (four fp32) per thread
-  static_assert(SP * 4 * ONT == DV * DK, "S_c pieces");
+  static_assert(SP * 4 * ONT == DV * DK && ONT % (DK / 4) == 0, "S_c pieces");
   extern __shared__ __align__(16) uint16_t out_lds[];
-  uint16_t* sS = out_lds;                   // parts of S_c
-  uint16_t* sU = sS + 3 * L::S_PART;        // parts of U^T
-  float* sN = reinterpret_cast<float*>(sU + 3 * L::U_PART);  // [2][CH] sums of squares
+  uint16_t* sR = out_lds;                   // the parts region
+  float* sN = reinterpret_cast<float*>(sR + 3 * L::PART);  // [2][CH] sums of squares
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int C = min(CH, a.T - c * CH);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -691,8 +688,10 @@ __global__ __launch_bounds__(ONT, 1) void gdn_out_kernel(GdnArgs a) {
   const int64_t cb = chunk_index(a, b, h, c);
   const int64_t tok = (int64_t)b * a.T + c * CH;
   const float* sc = a.sc + cb * SCS;
-  // every global read first: S_c pieces; this wave's q and Mqk rows (token
-  // tile), sq, U^T of its columns; z of its outputs
+  // S_c pieces (thread: rows tid / (Dk/4) + .., columns 4 (tid % (Dk/4))
+  // .. + 3, so all of one 64-column pass) and the wave's q rows (token tile)
+  // first; its Mqk rows, sq and U^T columns are read under the first pass,
+  // z under the last (registers: two workgroups share a CU)
   f32x4 sv[SP];
 #pragma unroll
   for (int i = 0; i < SP; ++i)
@@ -702,20 +701,58 @@ __global__ __launch_bounds__(ONT, 1) void gdn_out_kernel(GdnArgs a) {
   const uint16_t* qr = a.proj + (tok + min(t, C - 1)) * a.proj_stride + a.off_q + h * DK + 8 * lq;
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) q[ks] = glb8(qr + 32 * ks);
-  f32x4 mq[CH / 32][2];
-  const float* mr = a.Mq + cb * CH * CH + t * CH + 8 * lq;
+  f32x4 mq[CH / 32][2], ut[NJT], sq;
+  auto parts = [&](int j, int col) {
+    Split8 v;
+    const int o = u_at(j, col);
+    v.h = lds8(sR + o);
+    v.m = lds8(sR + L::PART + o);
+    v.l = lds8(sR + 2 * L::PART + o);
+    return v;
+  };
+  // O1 = Q S_c^T for the wave's column tiles, 64 columns of S_c per pass.
+  // Lane: t = 16 tw + 4 lq + r, j = Dv/2 jh + 16 jt + l16.
+  const int kmine = (tid % (DK / 4)) * 4;  // this thread's S_c columns
+  f32x4 o1[NJT];
 #pragma unroll
-  for (int is = 0; is < CH / 32; ++is) {
-    mq[is][0] = *reinterpret_cast<const f32x4*>(mr + 32 * is);
-    mq[is][1] = *reinterpret_cast<const f32x4*>(mr + 32 * is + 4);
-  }
-  const f32x4 sq = *reinterpret_cast<const f32x4*>(sc + 16 * tw + 4 * lq);
-  f32x4 ut[NJT];
+  for (int jt = 0; jt < NJT; ++jt) o1[jt] = (f32x4){0, 0, 0, 0};
 #pragma unroll
-  for (int jt = 0; jt < NJT; ++jt) {
-    const int j = DV / 2 * jh + 16 * jt + l16;
-    ut[jt] = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + j * CH + 16 * tw + 4 * lq);
+  for (int kh = 0; kh < NH; ++kh) {
+    if (kmine / 64 == kh) {
+#pragma unroll
+      for (int i = 0; i < SP; ++i) {
+        const int j = (tid + i * ONT) / (DK / 4);
+        put_parts4(sR + u_at(j, kmine - 64 * kh), L::PART, sv[i]);
+      }
+    }
+    lds_barrier();
+    if (kh == 0) {
+      const float* mr = a.Mq + cb * CH * CH + t * CH + 8 * lq;
+#pragma unroll
+      for (int is = 0; is < CH / 32; ++is) {
+        mq[is][0] = *reinterpret_cast<const f32x4*>(mr + 32 * is);
+        mq[is][1] = *reinterpret_cast<const f32x4*>(mr + 32 * is + 4);
+      }
+      sq = *reinterpret_cast<const f32x4*>(sc + 16 * tw + 4 * lq);
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        const int j = DV / 2 * jh + 16 * jt + l16;
+        ut[jt] = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + j * CH + 16 * tw + 4 * lq);
+      }
+    }
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt) {
+      const int j = DV / 2 * jh + 16 * jt + l16;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) o1[jt] = mma_es(q[2 * kh + ks], parts(j, 32 * ks + 8 * lq), o1[jt]);
+    }
+    lds_barrier();  // every read of this pass done before the region is rewritten
   }
+  // the U^T parts of the wave's columns and tokens into the region
+#pragma unroll
+  for (int jt = 0; jt < NJT; ++jt)
+    put_parts4(sR + u_at(DV / 2 * jh + 16 * jt + l16, 16 * tw + 4 * lq), L::PART, ut[jt]);
+  lds_barrier();
   uint16_t zv[NJT][4];
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt)
@@ -724,43 +761,6 @@ __global__ __launch_bounds__(ONT, 1) void gdn_out_kernel(GdnArgs a) {
       const int tr = 16 * tw + 4 * lq + r;
       zv[jt][r] = a.proj[(tok + min(tr, C - 1)) * a.proj_stride + a.off_z + h * DV + DV / 2 * jh + 16 * jt + l16];
     }
-  // S_c parts into LDS
-#pragma unroll
-  for (int i = 0; i < SP; ++i) {
-    const int p = tid + i * ONT, j = p / (DK / 4), k = (p % (DK / 4)) * 4;
-    bf16 hh[4], mm[4], ll[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) split3(sv[i][r], hh[r], mm[r], ll[r]);
-    const int o = s_at<DK>(j, k);
-    *reinterpret_cast<uint2*>(sS + o) = pack4(hh[0], hh[1], hh[2], hh[3]);
-    *reinterpret_cast<uint2*>(sS + L::S_PART + o) = pack4(mm[0], mm[1], mm[2], mm[3]);
-    *reinterpret_cast<uint2*>(sS + 2 * L::S_PART + o) = pack4(ll[0], ll[1], ll[2], ll[3]);
-  }
-  lds_barrier();
-  auto s_parts = [&](int j, int ks) {
-    Split8 v;
-    const int o = s_at<DK>(j, 32 * ks + 8 * lq);
-    v.h = lds8(sS + o);
-    v.m = lds8(sS + L::S_PART + o);
-    v.l = lds8(sS + 2 * L::S_PART + o);
-    return v;
-  };
-  // the U^T parts of the wave's columns and tokens into LDS; O1 = Q S_c^T for
-  // the wave's column tiles.  Lane: t = 16 tw + 4 lq + r, j = Dv/2 jh + 16 jt
-  // + l16.
-#pragma unroll
-  for (int jt = 0; jt < NJT; ++jt)
-    put_parts4(sU + u_at(DV / 2 * jh + 16 * jt + l16, 16 * tw + 4 * lq), L::U_PART, ut[jt]);
-  f32x4 o1[NJT];
-#pragma unroll
-  for (int jt = 0; jt < NJT; ++jt) {
-    const int j = DV / 2 * jh + 16 * jt + l16;
-    f32x4 aq = {0, 0, 0, 0};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) aq = mma_es(q[ks], s_parts(j, ks), aq);
-    o1[jt] = aq;
-  }
-  lds_barrier();
   // O = sq * O1 + Mqk U
   Split8 ms[CH / 32];
 #pragma unroll
@@ -772,14 +772,7 @@ __global__ __launch_bounds__(ONT, 1) void gdn_out_kernel(GdnArgs a) {
     const int j = DV / 2 * jh + 16 * jt + l16;
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int is = 0; is < CH / 32; ++is) {
-      Split8 up;
-      const int ou = u_at(j, 32 * is + 8 * lq);
-      up.h = lds8(sU + ou);
-      up.m = lds8(sU + L::U_PART + ou);
-      up.l = lds8(sU + 2 * L::U_PART + ou);
-      acc = mma_ss(ms[is], up, acc);
-    }
+    for (int is = 0; is < CH / 32; ++is) acc = mma_ss(ms[is], parts(j, 32 * is + 8 * lq), acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       o[jt][r] = sq[r] * o1[jt][r] + acc[r];
