@@ -138,6 +138,23 @@ DEV bf16x8 glb8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p);
 DEV int kt_swz(int k) { return (k & 7) ^ ((k >> 3) & 7); }
 DEV int kt_at(int k, int t) { return k * CH + 8 * ((t >> 3) ^ kt_swz(k)) + (t & 7); }
 
+// The fp32 chunk workspaces are stored in the order the lanes read them, so
+// that a wave's 16-byte-per-lane access is one contiguous kilobyte:
+//   W [CH][Dk]: element (t, k) at the fragment of (t / 16, k / 32, (k / 4) % 2):
+//     lane t % 16 + 16 ((k % 32) / 8), floats k % 4;
+//   U~^T / U^T [Dv][CH] and S_c [Dv][Dk]: element (j, x) at the fragment of
+//     (j / 16, x / 16): lane j % 16 + 16 ((x % 16) / 4), floats x % 4.
+// Offsets in floats within a chunk's block.
+template <int DK>
+DEV int w_frag(int t, int k) {
+  return ((((t >> 4) * (DK / 32) + (k >> 5)) * 2 + ((k >> 2) & 1)) * 64 + (t & 15) + 16 * ((k & 31) >> 3)) * 4 +
+         (k & 3);
+}
+template <int NX>
+DEV int jx_frag(int j, int x) {  // NX: columns of the matrix (CH or Dk)
+  return (((j >> 4) * (NX / 16) + (x >> 4)) * 64 + (j & 15) + 16 * ((x & 15) >> 2)) * 4 + (x & 3);
+}
+
 // Chunk workspace of (sequence b, head h, chunk c): cb = (b H + h) n_chunks + c.
 DEV int64_t chunk_index(const GdnArgs& a, int b, int h, int c) {
   return ((int64_t)b * a.H + h) * a.n_chunks + c;
@@ -391,13 +408,15 @@ __global__ __launch_bounds__(PNT, 2) void gdn_prep_kernel(GdnArgs a) {
     }
     float* W = a.W + cb * CH * DK;
     float* Ut = a.Ut + cb * CH * DV;
+    // W^T = K^T (T diag(beta gamma / |k|))^T: the lane then holds four
+    // consecutive k of one token row, one 16-byte fragment piece
 #pragma unroll 2
     for (int nt = 0; nt < DK / 16; ++nt) {
       f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-      for (int is = 0; is < CH / 32; ++is) acc = mma_se(tw_[is], lds8(sKt + kt_at(16 * nt + l16, 32 * is + 8 * lq)), acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) W[(16 * wave + 4 * lq + r) * DK + 16 * nt + l16] = acc[r];
+      for (int is = 0; is < CH / 32; ++is) acc = mma_es(lds8(sKt + kt_at(16 * nt + l16, 32 * is + 8 * lq)), tw_[is], acc);
+      // lane: W[t = 16 wave + l16][k = 16 nt + 4 lq + r]
+      *reinterpret_cast<f32x4*>(W + w_frag<DK>(16 * wave + l16, 16 * nt + 4 * lq)) = acc;
     }
 #pragma unroll 2
     for (int nt = 0; nt < DV / 16; ++nt) {
@@ -405,7 +424,7 @@ __global__ __launch_bounds__(PNT, 2) void gdn_prep_kernel(GdnArgs a) {
 #pragma unroll
       for (int is = 0; is < CH / 32; ++is) acc = mma_se(tu_[is], lds8(sVt + kt_at(16 * nt + l16, 32 * is + 8 * lq)), acc);
       // U~^T [DV][CH]: lane (t = 16 wave + 4 lq + r, dv = 16 nt + l16)
-      *reinterpret_cast<f32x4*>(Ut + (16 * nt + l16) * CH + 16 * wave + 4 * lq) = acc;
+      *reinterpret_cast<f32x4*>(Ut + jx_frag<CH>(16 * nt + l16, 16 * wave + 4 * lq)) = acc;
     }
   }
 }
@@ -524,12 +543,12 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
     const int64_t cb = cb0 + c;
     const float* sc = a.sc + cb * SCS;
     r.dk = *reinterpret_cast<const f32x4*>(sc + CH + 16 * tw + 4 * lq);
-    r.ut = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + (j0 + l16) * CH + 16 * tw + 4 * lq);
-    const float* w = a.W + cb * CH * DK + (16 * tw + l16) * DK + 8 * lq;
+    r.ut = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + jx_frag<CH>(j0 + l16, 16 * tw + 4 * lq));
+    const float* w = a.W + cb * CH * DK;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      r.w[ks][0] = *reinterpret_cast<const f32x4*>(w + 32 * ks);
-      r.w[ks][1] = *reinterpret_cast<const f32x4*>(w + 32 * ks + 4);
+      r.w[ks][0] = *reinterpret_cast<const f32x4*>(w + w_frag<DK>(16 * tw + l16, 32 * ks + 8 * lq));
+      r.w[ks][1] = *reinterpret_cast<const f32x4*>(w + w_frag<DK>(16 * tw + l16, 32 * ks + 8 * lq + 4));
     }
   };
   // L2 warm-up of a later chunk: the head's W, U~^T and K^T lines (128 bytes);
@@ -569,7 +588,7 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
     auto step = [&](auto Ic, RS& cur, int c) __attribute__((always_inline)) {
       constexpr int I = decltype(Ic)::value;
       if (wave < NKB)  // the entering state of chunk c, for the output kernel
-        *reinterpret_cast<f32x4*>(a.Sc + (cb0 + c) * DV * DK + (j0 + l16) * DK + 16 * wave + 4 * lq) = S;
+        *reinterpret_cast<f32x4*>(a.Sc + (cb0 + c) * DV * DK + jx_frag<DK>(j0 + l16, 16 * wave + 4 * lq)) = S;
       if constexpr (UW) {
         // (W S^T)[t][j] for the tile's tokens (two accumulation chains)
         f32x4 acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
@@ -587,7 +606,7 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
           u[r] = cur.ut[r] - (acc[r] + acc2[r]);
           du[r] = u[r] * cur.dk[r];
         }
-        *reinterpret_cast<f32x4*>(a.Ut + (cb0 + c) * DV * CH + (j0 + l16) * CH + 16 * tw + 4 * lq) = u;
+        *reinterpret_cast<f32x4*>(a.Ut + (cb0 + c) * DV * CH + jx_frag<CH>(j0 + l16, 16 * tw + 4 * lq)) = u;
         put_parts4(sD + l16 * LU + 16 * tw + 4 * lq, L::U_PART, du);
       }
       wait_vmcnt<YOUNGER>();  // this wave's K^T copies of chunk c have landed
@@ -676,7 +695,7 @@ __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
   constexpr int NH = DK / 64;               // passes over 64 columns of S_c
   constexpr int NJT = DV / 32;              // 16-column tiles per wave (half of Dv)
   constexpr int SP = DV * DK / 4 / ONT;     // S_c pieces (four fp32) per thread
-  static_assert(SP * 4 * ONT == DV * DK && ONT % (DK / 4) == 0, "S_c pieces");
+  static_assert(SP * 4 * ONT == DV * DK && ONT % (DK / 16 * 64) == 0, "S_c pieces");
   extern __shared__ __align__(16) uint16_t out_lds[];
   uint16_t* sR = out_lds;                   // the parts region
   float* sN = reinterpret_cast<float*>(sR + 3 * L::PART);  // [2][CH] sums of squares
@@ -688,8 +707,8 @@ __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
   const int64_t cb = chunk_index(a, b, h, c);
   const int64_t tok = (int64_t)b * a.T + c * CH;
   const float* sc = a.sc + cb * SCS;
-  // S_c pieces (thread: rows tid / (Dk/4) + .., columns 4 (tid % (Dk/4))
-  // .. + 3, so all of one 64-column pass) and the wave's q rows (token tile)
+  // S_c pieces (each thread's all in one 64-column pass) and the wave's q
+  // rows (token tile)
   // first; its Mqk rows, sq and U^T columns are read under the first pass,
   // z under the last (registers: two workgroups share a CU)
   f32x4 sv[SP];
@@ -712,7 +731,10 @@ __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
   };
   // O1 = Q S_c^T for the wave's column tiles, 64 columns of S_c per pass.
   // Lane: t = 16 tw + 4 lq + r, j = Dv/2 jh + 16 jt + l16.
-  const int kmine = (tid % (DK / 4)) * 4;  // this thread's S_c columns
+  // S_c piece p (16 bytes, fragment order): rows 16 (p / (Dk/16 64)) + p % 16,
+  // columns 16 ((p / 64) % (Dk/16)) + 4 ((p % 64) / 16) ..; all of one
+  // thread's pieces share their columns
+  const int kmine = 16 * ((tid / 64) % (DK / 16)) + 4 * ((tid & 63) >> 4);  // this thread's S_c columns
   f32x4 o1[NJT];
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt) o1[jt] = (f32x4){0, 0, 0, 0};
@@ -721,7 +743,8 @@ __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
     if (kmine / 64 == kh) {
 #pragma unroll
       for (int i = 0; i < SP; ++i) {
-        const int j = (tid + i * ONT) / (DK / 4);
+        const int p = tid + i * ONT;
+        const int j = 16 * (p / (DK / 16 * 64)) + (p & 15);
         put_parts4(sR + u_at(j, kmine - 64 * kh), L::PART, sv[i]);
       }
     }
@@ -737,7 +760,7 @@ __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {
         const int j = DV / 2 * jh + 16 * jt + l16;
-        ut[jt] = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + j * CH + 16 * tw + 4 * lq);
+        ut[jt] = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + jx_frag<CH>(j, 16 * tw + 4 * lq));
       }
     }
 #pragma unroll
