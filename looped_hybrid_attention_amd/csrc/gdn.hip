@@ -580,12 +580,25 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
   // c + 2 and the stores of U of chunks c - 1 and c (the L2 warm-ups, issued
   // by three of the four U waves only, are not counted).
   struct NoRegs {};
+  struct NoSplit {};
   auto run = [&](auto role) __attribute__((always_inline)) {
     constexpr bool UW = decltype(role)::value;
     using RS = std::conditional_t<UW, R, NoRegs>;
+    // a U wave's W rows of the next chunk as split operands: split during the
+    // previous chunk's update, off the path from the state to U
+    struct WSplit {
+      Split8 w[NKS];
+    };
+    std::conditional_t<UW, WSplit, NoSplit> ws;
+    auto split_w = [&](const RS& set) __attribute__((always_inline)) {
+      if constexpr (UW) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) ws.w[ks] = split8(set.w[ks][0], set.w[ks][1]);
+      }
+    };
     static_assert(NKB >= 4, "the U waves store the state");
     constexpr int YOUNGER = UW ? 2 * R::LOADS + KCP + 4 : KCP + (NKB > 4 ? 2 : 0);
-    auto step = [&](auto Ic, RS& cur, int c) __attribute__((always_inline)) {
+    auto step = [&](auto Ic, RS& cur, const RS& next, int c) __attribute__((always_inline)) {
       constexpr int I = decltype(Ic)::value;
       if (wave < NKB)  // the entering state of chunk c, for the output kernel
         *reinterpret_cast<f32x4*>(a.Sc + (cb0 + c) * DV * DK + jx_frag<DK>(j0 + l16, 16 * wave + 4 * lq)) = S;
@@ -594,9 +607,8 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
         f32x4 acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < NKS; ks += 2) {
-          acc = mma_ss(split8(cur.w[ks][0], cur.w[ks][1]), get_parts8(sS + l16 * LS + 32 * ks + 8 * lq, L::S_PART), acc);
-          acc2 = mma_ss(split8(cur.w[ks + 1][0], cur.w[ks + 1][1]),
-                        get_parts8(sS + l16 * LS + 32 * (ks + 1) + 8 * lq, L::S_PART), acc2);
+          acc = mma_ss(ws.w[ks], get_parts8(sS + l16 * LS + 32 * ks + 8 * lq, L::S_PART), acc);
+          acc2 = mma_ss(ws.w[ks + 1], get_parts8(sS + l16 * LS + 32 * (ks + 1) + 8 * lq, L::S_PART), acc2);
         }
         // lane: t = 16 tw + 4 lq + r, j = l16: U^T[j][t] over U~^T (read
         // into registers chunks ago), (dk U)^T[j][t] into LDS
@@ -625,6 +637,7 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
         for (int r = 0; r < 4; ++r) S[r] = gC * S[r] + acc[r];
         put_state();
       }
+      split_w(next);  // chunk c + 1's W
       // the operands ahead: K^T of chunk c + 2 into the stage chunk c - 1
       // used, the U set's chunk c + 3, the L2 warm-up of chunk c + 4 (indices
       // past the end repeat the last chunk, harmlessly, so every wave of a
@@ -646,6 +659,7 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
     warm(min(3, n - 1));
     if (wave < NKB) put_state();
     for (int i = tid; i < n; i += SCAN_NT) sGc[i] = a.sc[(cb0 + i) * SCS + 2 * CH];
+    split_w(r0);
     // everything issued so far has landed (the first chunk's wait counts
     // fewer younger operations than the later ones)
     wait_vmem();
@@ -655,12 +669,12 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
     // register set stay exact)
     int c = 0;
     for (; c + SCAN_PF <= n; c += SCAN_PF) {
-      step(std::integral_constant<int, 0>(), r0, c);
-      step(std::integral_constant<int, 1>(), r1, c + 1);
-      step(std::integral_constant<int, 2>(), r2, c + 2);
+      step(std::integral_constant<int, 0>(), r0, r1, c);
+      step(std::integral_constant<int, 1>(), r1, r2, c + 1);
+      step(std::integral_constant<int, 2>(), r2, r0, c + 2);
     }
-    if (c < n) step(std::integral_constant<int, 0>(), r0, c);
-    if (c + 1 < n) step(std::integral_constant<int, 1>(), r1, c + 1);
+    if (c < n) step(std::integral_constant<int, 0>(), r0, r1, c);
+    if (c + 1 < n) step(std::integral_constant<int, 1>(), r1, r2, c + 1);
   };
   if (wave < 4) run(std::true_type());
   else run(std::false_type());
