@@ -941,12 +941,17 @@ hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
 // Measured on the decode shapes (64 rows): the skinny tiles win where the
 // output has at most 4096 columns and K at most 4096; the register-staged
 // 64 x 128 tiles stream the wider and deeper weight matrices faster.
+// Where the weight-streaming tiles beat the 64 x 128 split-K tiles (measured
+// at M = 1 and 64 on the decode projections): up to 4096 columns with K up
+// to 12288 (O and down projections), and very wide products at 16 rows or
+// fewer (the LM head at small batch).
 template <int EPI>
 bool skinny_fits(const GemmArgs& g) {
   const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
   const int64_t a_bytes = (int64_t)g.M * g.lda * 2, b_bytes = rows_b * g.ldb * 2;
-  return g.M <= 64 && g.N <= 4096 && g.K <= 4096 && g.K % (SK_KC * SK_NSET) == 0 && g.lda % 8 == 0 &&
-         g.ldb % 8 == 0 && a_bytes < (1ll << 31) && b_bytes < (1ll << 31);
+  const bool shape = (g.N <= 4096 && g.K <= 12288) || (g.M <= 16 && g.N >= 65536);
+  return g.M <= 64 && shape && g.K % (SK_KC * SK_NSET) == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0 &&
+         a_bytes < (1ll << 31) && b_bytes < (1ll << 31);
 }
 
 // Large M: 256 x 256 tiles; small M (decode): 64 x 128 tiles, split K.

@@ -154,3 +154,19 @@ def test_gemm_split_k(M, N, K, epi):
         assert rel_err(got, ref + r) < 1e-5
     else:
         assert rel_err(got, ref) < (2 ** -8 if epi == 0 else 1e-5)
+
+
+@pytest.mark.parametrize("M,N,K,epi", [(1, 66000, 512, 1), (13, 65600, 1024, 1), (3, 70000, 512, 0)])
+def test_gemm_wide_few_rows(M, N, K, epi):
+    """Very wide products at few rows (the LM head at small batch, a ragged
+    last column tile) on the weight-streaming tiles, against float64."""
+    import looped_hybrid_attention_amd as L
+    torch = torch_cuda()
+    say("gemm wide", M, N, K, epi)
+    a, b = _inputs(M, N, K, f"wide{M}.{N}.{K}")
+    ref = _ref(a, b)
+    A, B = dev(a, torch), dev(b, torch)
+    C = torch.empty((M, N), dtype=torch.bfloat16 if epi == 0 else torch.float32, device="cuda")
+    L.loop_op_gemm(A.data_ptr(), K, B.data_ptr(), K, C.data_ptr(), N, 0, M, N, K, epi, stream(torch))
+    torch.cuda.synchronize()
+    assert rel_err(host(C), ref) < (2 ** -8 if epi == 0 else 1e-5)
