@@ -911,6 +911,9 @@ __global__ __launch_bounds__(64 * DEC_W) void gdn_decode_kernel(GdnArgs a) {
       const int row = row0 + j * RPI;
       const float u = beta * (sv[row] - alpha * p);
       S[j] = alpha * S[j] + u * kk;
+      // the last token's state goes out row by row, while later rows' loads
+      // are still arriving
+      if (t + 1 == a.T) *reinterpret_cast<f32x4*>(Sg + (int64_t)j * RPI * DK) = S[j];
       float o = S[j][0] * qq[0] + S[j][1] * qq[1] + S[j][2] * qq[2] + S[j][3] * qq[3];
 #pragma unroll
       for (int off = 1; off < CPR; off <<= 1) o += __shfl_xor(o, off, 64);
@@ -935,8 +938,6 @@ __global__ __launch_bounds__(64 * DEC_W) void gdn_decode_kernel(GdnArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int j = 0; j < NI; ++j) *reinterpret_cast<f32x4*>(Sg + (int64_t)j * RPI * DK) = S[j];
 }
 
 template <typename K>
