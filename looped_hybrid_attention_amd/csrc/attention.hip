@@ -24,13 +24,104 @@ namespace {
 constexpr int VB = 32;  // positions per block of the transposed V cache
 
 // ---------------------------------------------------------------- prep
-// One workgroup per token: the rotary cos / sin of the token's position are
-// computed once (angle in double, rounded to fp32) into LDS, then the four
-// waves take the Hq query and Hkv key heads in turn; lane holds D/64
-// consecutive dims.
+// QK-norm and partial rotary of one head vector, by one wave.
+// rope_angles: cos / sin of the R/2 rotary frequencies at a position (angle
+// pos * theta^(-2i/R) in double, rounded to fp32), entry i by the caller's
+// thread i.  qk_norm_rope: RMSNorm over the D dims (sum of squares over the
+// wave's lanes)
+// times the gain, then the adjacent pairs (2i, 2i+1), i < R/2, rotated; the
+// bf16 result is stored at dst, the 8-dim group c of the vector at group
+// c ^ sw (sw = 0: in order).  Lane l holds the EPL = D/64 consecutive dims
+// EPL l .. (D = 64: one dim, its rotary partner in the neighbouring lane).
+DEV void rope_angles(int pos, int i, int R, float theta, float* rc, float* rs) {
+  const double th = pow((double)theta, -2.0 * i / R);
+  const double ang = (double)pos * th;
+  rc[i] = (float)cos(ang);
+  rs[i] = (float)sin(ang);
+}
+template <int D>
+struct QkRaw {
+  uint16_t x[D / 64];  // bf16 bits of the lane's dims
+};
+template <int D>
+DEV QkRaw<D> qk_load(const uint16_t* src, int lane) {
+  constexpr int EPL = D / 64;
+  QkRaw<D> r;
+  if constexpr (EPL == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(src + lane * EPL);
+    r.x[0] = (uint16_t)v.x; r.x[1] = (uint16_t)(v.x >> 16);
+    r.x[2] = (uint16_t)v.y; r.x[3] = (uint16_t)(v.y >> 16);
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) r.x[e] = src[lane * EPL + e];
+  }
+  return r;
+}
+template <int D>
+DEV void qk_gain(const uint16_t* gain, int lane, float (&g)[D / 64]) {
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) g[e] = bf2f(gain[lane * (D / 64) + e]);
+}
+template <int D>
+DEV void qk_finish(const QkRaw<D>& r, const float (&g)[D / 64], const float* rc, const float* rs, int R, float eps,
+                   uint16_t* dst, int sw, int lane) {
+  constexpr int EPL = D / 64;
+  const int d0 = lane * EPL;
+  float x[EPL];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] = bf2f(r.x[e]);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
+  ss = wave_sum(ss);
+  const float inv = rsqrtf(ss / D + eps);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] = x[e] * inv * g[e];
+  // rotary on dims < R, adjacent pairs (2i, 2i+1)
+  if (EPL >= 2) {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2) {
+      const int d = d0 + e;
+      if (d < R) {
+        const float c = rc[d >> 1], sn = rs[d >> 1];
+        const float x0 = x[e], x1 = x[e + 1];
+        x[e] = x0 * c - x1 * sn;
+        x[e + 1] = x0 * sn + x1 * c;
+      }
+    }
+  } else {
+    const float partner = __shfl_xor(x[0], 1, 64);
+    if (d0 < R) {
+      const float c = rc[d0 >> 1], sn = rs[d0 >> 1];
+      x[0] = (d0 & 1) ? partner * sn + x[0] * c : x[0] * c - partner * sn;
+    }
+  }
+  uint16_t* o = dst + (((d0 >> 3) ^ sw) << 3) + (d0 & 7);
+  if constexpr (EPL == 4) {
+    uint2 v;
+    v.x = (uint32_t)f2bf_bits(x[0]) | ((uint32_t)f2bf_bits(x[1]) << 16);
+    v.y = (uint32_t)f2bf_bits(x[2]) | ((uint32_t)f2bf_bits(x[3]) << 16);
+    *reinterpret_cast<uint2*>(o) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = f2bf_bits(x[e]);
+  }
+}
+template <int D>
+DEV void qk_norm_rope(const uint16_t* src, const uint16_t* gain, const float* rc, const float* rs, int R,
+                      float eps, uint16_t* dst, int sw, int lane) {
+  float g[D / 64];
+  qk_gain<D>(gain, lane, g);
+  qk_finish<D>(qk_load<D>(src, lane), g, rc, rs, R, eps, dst, sw, lane);
+}
+
+// One workgroup per token: K of every KV head normalised, rotated and
+// appended to the cache (the queries get the same treatment inside the
+// attention kernels).  The rotary cos / sin of the token's position are
+// computed once into LDS, and stored for the attention kernels ([M][R/2]
+// pairs); the four waves take the heads in turn.
 template <int D>
 __global__ __launch_bounds__(256) void qk_prep_kernel(AttnPrepArgs a) {
-  constexpr int EPL = D / 64;
   __shared__ float rc[D / 2], rs[D / 2];
   const int m = blockIdx.x;  // token row
   const int b = m / a.T, t = m % a.T;
@@ -38,66 +129,14 @@ __global__ __launch_bounds__(256) void qk_prep_kernel(AttnPrepArgs a) {
   const int64_t slot_b = a.seq_slot[b];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < a.R / 2) {
-    const double th = pow((double)a.theta, -2.0 * tid / a.R);
-    const double ang = (double)pos * th;
-    rc[tid] = (float)cos(ang);
-    rs[tid] = (float)sin(ang);
+    rope_angles(pos, tid, a.R, a.theta, rc, rs);
+    reinterpret_cast<float2*>(a.rope)[(int64_t)m * (a.R / 2) + tid] = make_float2(rc[tid], rs[tid]);
   }
   __syncthreads();
-  const uint16_t* row = a.proj + (int64_t)m * a.proj_stride;
-  const int d0 = lane * EPL;
-  for (int item = wave; item < a.Hq + a.Hkv; item += 4) {
-    const bool is_q = item < a.Hq;
-    const int head = is_q ? item : item - a.Hq;
-    const uint16_t* src = (is_q ? row + head * D : row + 2 * a.Hq * D + head * D) + d0;
-    const uint16_t* gain = (is_q ? a.q_norm : a.k_norm) + d0;
-    float x[EPL];
-    float ss = 0.f;
-    if constexpr (EPL == 4) {
-      const uint2 v = *reinterpret_cast<const uint2*>(src);
-      x[0] = bf2f((uint16_t)v.x); x[1] = bf2f((uint16_t)(v.x >> 16));
-      x[2] = bf2f((uint16_t)v.y); x[3] = bf2f((uint16_t)(v.y >> 16));
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) x[e] = bf2f(src[e]);
-    }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) ss += x[e] * x[e];
-    ss = wave_sum(ss);
-    const float inv = rsqrtf(ss / D + a.eps);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) x[e] = x[e] * inv * bf2f(gain[e]);
-    // rotary on dims < R, adjacent pairs (2i, 2i+1)
-    if (EPL >= 2) {
-#pragma unroll
-      for (int e = 0; e < EPL; e += 2) {
-        const int d = d0 + e;
-        if (d < a.R) {
-          const float c = rc[d >> 1], sn = rs[d >> 1];
-          const float x0 = x[e], x1 = x[e + 1];
-          x[e] = x0 * c - x1 * sn;
-          x[e + 1] = x0 * sn + x1 * c;
-        }
-      }
-    } else {
-      const float partner = __shfl_xor(x[0], 1, 64);
-      if (d0 < a.R) {
-        const float c = rc[d0 >> 1], sn = rs[d0 >> 1];
-        x[0] = (d0 & 1) ? partner * sn + x[0] * c : x[0] * c - partner * sn;
-      }
-    }
-    uint16_t* dst = is_q ? a.q_out + ((int64_t)m * a.Hq + head) * D + d0
-                         : a.k_cache + ((slot_b * a.Hkv + head) * (int64_t)a.max_seq + pos) * D + d0;
-    if constexpr (EPL == 4) {
-      uint2 o;
-      o.x = (uint32_t)f2bf_bits(x[0]) | ((uint32_t)f2bf_bits(x[1]) << 16);
-      o.y = (uint32_t)f2bf_bits(x[2]) | ((uint32_t)f2bf_bits(x[3]) << 16);
-      *reinterpret_cast<uint2*>(dst) = o;
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) dst[e] = f2bf_bits(x[e]);
-    }
-  }
+  const uint16_t* row = a.proj + (int64_t)m * a.proj_stride + 2 * a.Hq * D;
+  for (int head = wave; head < a.Hkv; head += 4)
+    qk_norm_rope<D>(row + head * D, a.k_norm, rc, rs, a.R, a.eps,
+                    a.k_cache + ((slot_b * a.Hkv + head) * (int64_t)a.max_seq + pos) * D, 0, lane);
 }
 
 // V of a block of 64 tokens of one sequence and KV head into the transposed
@@ -280,16 +319,59 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
   // vmcnt(0): this wave's LDS copies have landed
 #define FLASH_WAIT_COPIES() wait_vmem()
 
-  FLASH_COPY(0, 0);
-
+  // The queries: QK-norm and partial rotary here, from the projection, one
+  // query vector per wave step into a scratch area (stage 1, which the first
+  // tile leaves free; with eight waves both stages, before the first copy),
+  // rows of D bf16 with 8-dim group c of row r at c ^ (r % 16), so that the
+  // fragment reads of 16 rows hit distinct banks; the rotary cos / sin of the
+  // tile's QT positions (from the prep kernel's table) after the stages.
+  constexpr bool QS1 = W * 32 * D * 2 <= L::STAGE;
+  const int RH = a.R / 2;
+  float* rct = reinterpret_cast<float*>(flash_smem + L::bytes);
+  float* rst = rct + QT * RH;
+  uint16_t* qscr = reinterpret_cast<uint16_t*>(flash_smem + (QS1 ? L::STAGE : 0));
+  if (QS1) FLASH_COPY(0, 0);
+  for (int e = tid; e < QT * RH; e += 64 * W) {
+    const int qi = e / RH, i = e % RH;
+    const int tq = min(tile * QT + qi, a.T - 1);  // rows past T: any valid row
+    const float2 cs = reinterpret_cast<const float2*>(a.rope)[((int64_t)b * a.T + tq) * RH + i];
+    rct[qi * RH + i] = cs.x;
+    rst[qi * RH + i] = cs.y;
+  }
+  __syncthreads();
+  {
+    // all 32 rows' loads in flight first (rows past T read as zero, which
+    // the routine turns into zeros)
+    const int q0 = (wave / G) * 32;  // the wave's first query within the tile
+    QkRaw<D> raw[32];
+#pragma unroll
+    for (int qi = 0; qi < 32; ++qi) {
+      const int tq = tile * QT + q0 + qi;
+      if (tq < a.T) {
+        raw[qi] = qk_load<D>(a.q + ((int64_t)b * a.T + tq) * a.q_stride + head * D, lane);
+      } else {
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) raw[qi].x[e] = 0;
+      }
+    }
+    float gq[D / 64];
+    qk_gain<D>(a.q_norm, lane, gq);
+#pragma unroll
+    for (int qi = 0; qi < 32; ++qi)
+      qk_finish<D>(raw[qi], gq, rct + (q0 + qi) * RH, rst + (q0 + qi) * RH, a.R, a.eps, qscr + (wave * 32 + qi) * D,
+                   qi & 15 & (CR - 1), lane);
+  }
+  __syncthreads();
   bf16x8 qf[NKS];
   {
-    const uint16_t* qs = a.q + (m * a.Hq + head) * D;
+    const uint16_t* qr = qscr + (wave * 32 + ql) * D;
+    const int qsw = ql & 15 & (CR - 1);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 v = qvalid ? *reinterpret_cast<const u32x4*>(qs + ks * 16 + h * 8) : (u32x4){0, 0, 0, 0};
-      qf[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int ks = 0; ks < NKS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qr + (((2 * ks + h) ^ qsw) << 3));
+  }
+  if (!QS1) {
+    __syncthreads();  // the scratch is read before the first tile lands there
+    FLASH_COPY(0, 0);
   }
   f32x16 o[NDT];
 #pragma unroll
@@ -470,13 +552,23 @@ __global__ __launch_bounds__(DEC_NT, 2) void decode_attn_kernel(DecodeAttnArgs a
   const int l16 = lane & 15, lg = lane >> 4;
 
   // q^T operand, kept in LDS (registers go to the loads in flight): lane
-  // supplies q[g = l16][32 ks + 8 lg .. +8], zero for g >= G
-  for (int i = threadIdx.x; i < 16 * D / 8; i += DEC_NT) {
-    const int g = i / (D / 8), c = i % (D / 8);
-    sq[i] = g < G ? *reinterpret_cast<const u32x4*>(a.q + ((int64_t)b * a.Hq + kvh * G + g) * D + c * 8)
-                  : (u32x4){0, 0, 0, 0};
+  // supplies q[g = l16][32 ks + 8 lg .. +8], zero for g >= G.  QK-norm and
+  // partial rotary of the G query heads here, from the projection.
+  {
+    __shared__ float rc[D / 2], rs[D / 2];
+    const int lane0 = threadIdx.x & 63, wave0 = threadIdx.x >> 6;
+    if (threadIdx.x < a.R / 2) {
+      const float2 cs = reinterpret_cast<const float2*>(a.rope)[(int64_t)b * (a.R / 2) + threadIdx.x];
+      rc[threadIdx.x] = cs.x;
+      rs[threadIdx.x] = cs.y;
+    }
+    for (int i = G * D / 8 + threadIdx.x; i < 16 * D / 8; i += DEC_NT) sq[i] = (u32x4){0, 0, 0, 0};
+    __syncthreads();
+    for (int g = wave0; g < G; g += DEC_NT / 64)
+      qk_norm_rope<D>(a.q + (int64_t)b * a.q_stride + (kvh * G + g) * D, a.q_norm, rc, rs, a.R, a.eps,
+                      reinterpret_cast<uint16_t*>(sq) + g * D, 0, lane0);
+    __syncthreads();
   }
-  __syncthreads();
   // Buffer loads: one 32-bit lane offset per step, the per-load displacements
   // in the instruction's immediate (K) or a scalar offset (V^T tiles).  The K
   // range ends at key nk, so K rows past it read as zero (and are masked).
@@ -632,16 +724,19 @@ hipError_t prep_d(const AttnPrepArgs& a, int M, hipStream_t s) {
 
 template <int D, int G>
 hipError_t flash_dg(const FlashArgs& a, int B, hipStream_t s) {
-  const size_t lds = FlashLds<D>::bytes;
+  constexpr int W = G < 4 ? 4 : G;
+  constexpr int QT = 32 * W / G;
+  constexpr size_t LDS_MAX = 160 * 1024;
+  // the two stages, then the rotary table of the tile's query positions
+  const size_t lds = FlashLds<D>::bytes + 2 * (size_t)QT * (a.R / 2) * sizeof(float);
+  if (a.R < 0 || a.R > D || a.R % 2 || lds > LDS_MAX) return hipErrorInvalidValue;
   auto k = flash_prefill_kernel<D, G>;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_MAX);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  constexpr int W = G < 4 ? 4 : G;
-  constexpr int QT = 32 * W / G;
   hipLaunchKernelGGL(k, dim3((a.T + QT - 1) / QT, a.Hkv, B), dim3(64 * W), lds, s, a);
   return hipGetLastError();
 }
@@ -659,6 +754,7 @@ hipError_t flash_d(const FlashArgs& a, int B, hipStream_t s) {
 
 template <int D, int G>
 hipError_t decode_dg(const DecodeAttnArgs& a, int B, hipStream_t s) {
+  if (a.R < 0 || a.R > D || a.R % 2) return hipErrorInvalidValue;
   if (a.split_len != DEC_SPLIT || a.n_split > DEC_MAX_SPLITS || (int64_t)a.n_split * DEC_SPLIT < a.max_seq)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_attn_kernel<D, G>), dim3(a.n_split, a.Hkv, B), dim3(DEC_NT), 0, s, a);
@@ -681,6 +777,7 @@ hipError_t decode_d(const DecodeAttnArgs& a, int B, hipStream_t s) {
 
 hipError_t launch_attn_prep(const AttnPrepArgs& a, int M, hipStream_t s) {
   if (M == 0) return hipSuccess;
+  if (a.R < 0 || a.R > a.D || a.R % 2) return hipErrorInvalidValue;
   if (a.D == 256) return prep_d<256>(a, M, s);
   if (a.D == 64) return prep_d<64>(a, M, s);
   return hipErrorInvalidValue;

@@ -88,15 +88,20 @@ struct AttnPrepArgs {
   float theta, eps;
   const int32_t* pos;       // device [B] first position of the call
   const int32_t* seq_slot;  // device [B]
-  const uint16_t* q_norm; const uint16_t* k_norm;
-  uint16_t* q_out;          // [M][Hq][D]
+  const uint16_t* k_norm;
   uint16_t* k_cache;        // K block of the exec slot: [max_batch][Hkv][max_seq][D]
   uint16_t* v_cache;        // V block: [max_batch][Hkv][D][max_seq]
+  float* rope;              // out: [M][R/2] (cos, sin) of each token's position
 };
 hipError_t launch_attn_prep(const AttnPrepArgs& a, int M, hipStream_t s);
 
+// The attention kernels take the queries straight from the projection (row
+// stride q_stride, head h at h * D) and apply QK-norm (gain q_norm, eps) and
+// the partial rotary (first R dims; cos / sin of each token's position from
+// the table the prep kernel wrote, rope [M][R/2]) themselves.
 struct FlashArgs {
-  const uint16_t* q; int T, Hq, Hkv, D, max_seq;
+  const uint16_t* q; int64_t q_stride; const uint16_t* q_norm; int R; float eps; const float* rope;
+  int T, Hq, Hkv, D, max_seq;
   const int32_t* pos; const int32_t* seq_slot;
   const uint16_t* k_cache; const uint16_t* v_cache;
   float scale_log2;
@@ -111,7 +116,8 @@ hipError_t launch_flash_prefill(const FlashArgs& a, int B, hipStream_t s);
 constexpr int DEC_SPLIT_KEYS = 1024;
 constexpr int DEC_MAX_SPLITS = 1024;
 struct DecodeAttnArgs {
-  const uint16_t* q; int Hq, Hkv, D, max_seq;
+  const uint16_t* q; int64_t q_stride; const uint16_t* q_norm; int R; float eps; const float* rope;
+  int Hq, Hkv, D, max_seq;
   const int32_t* pos;  // device [B]: position of the new token (keys 0..pos)
   const int32_t* seq_slot;
   const uint16_t* k_cache; const uint16_t* v_cache;

@@ -35,7 +35,7 @@ constexpr int DEC_SPLIT = DEC_SPLIT_KEYS;  // keys per decode-attention split (d
 size_t up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t meta, h, hmid, x, a, s0, s1, xn, hn, proj, qbuf, obuf, act;
+  size_t meta, h, hmid, x, a, s0, s1, xn, hn, proj, obuf, act, rope;
   size_t gW, gUt, gM, gKt, gSc, gS;
   size_t xf, logits, am_v, am_i, dec_part, mhc, splitk;
   size_t splitk_bytes;
@@ -67,9 +67,9 @@ Layout layout(const loop_config& c, int64_t M) {
   L.xn = take(M * d * 2);
   L.hn = take(M * d * 2);
   L.proj = take(M * (int64_t)L.n_in_max * 2);
-  L.qbuf = take(M * (int64_t)c.n_q_heads * c.head_dim * 2);
   L.obuf = take(M * (int64_t)std::max(c.n_q_heads * c.head_dim, c.gdn_heads * c.gdn_dv) * 2);
   L.act = take(M * (int64_t)c.d_ff * 2);
+  L.rope = take(M * (int64_t)(c.rotary_dim / 2) * 2 * 4);
   // chunk workspace: (sum over sequences of their chunks) * heads
   L.chunk_slots = (int)((M + 63) / 64 + B);
   const int64_t cs = (int64_t)L.chunk_slots * c.gdn_heads;
@@ -309,8 +309,8 @@ int run_mixer(loop_model* m, const Call& k, const ExecDesc& d, hipStream_t s, in
     p.T = k.T; p.Hq = Hq; p.Hkv = Hkv; p.D = D; p.R = c.rotary_dim; p.max_seq = c.max_seq;
     p.theta = c.rope_theta; p.eps = c.eps;
     p.pos = k.d_pos; p.seq_slot = k.d_slot;
-    p.q_norm = (const uint16_t*)w.q_norm; p.k_norm = (const uint16_t*)w.k_norm;
-    p.q_out = at<uint16_t>(m, L.qbuf);
+    p.k_norm = (const uint16_t*)w.k_norm;
+    p.rope = at<float>(m, L.rope);
     p.k_cache = (uint16_t*)(m->arena + kv_off);
     p.v_cache = (uint16_t*)(m->arena + v_off);
     {
@@ -320,7 +320,9 @@ int run_mixer(loop_model* m, const Call& k, const ExecDesc& d, hipStream_t s, in
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     if (!k.decode) {
       FlashArgs f{};
-      f.q = p.q_out; f.T = k.T; f.Hq = Hq; f.Hkv = Hkv; f.D = D; f.max_seq = c.max_seq;
+      f.q = proj; f.q_stride = L.n_in_max; f.q_norm = (const uint16_t*)w.q_norm;
+      f.R = c.rotary_dim; f.eps = c.eps; f.rope = p.rope;
+      f.T = k.T; f.Hq = Hq; f.Hkv = Hkv; f.D = D; f.max_seq = c.max_seq;
       f.pos = k.d_pos; f.seq_slot = k.d_slot; f.k_cache = p.k_cache; f.v_cache = p.v_cache;
       f.scale_log2 = scale_log2;
       f.gate = proj + Hq * D; f.gate_stride = L.n_in_max;
@@ -329,7 +331,9 @@ int run_mixer(loop_model* m, const Call& k, const ExecDesc& d, hipStream_t s, in
       HIP_TRY(launch_flash_prefill(f, k.B, s));
     } else {
       DecodeAttnArgs g{};
-      g.q = p.q_out; g.Hq = Hq; g.Hkv = Hkv; g.D = D; g.max_seq = c.max_seq;
+      g.q = proj; g.q_stride = L.n_in_max; g.q_norm = (const uint16_t*)w.q_norm;
+      g.R = c.rotary_dim; g.eps = c.eps; g.rope = p.rope;
+      g.Hq = Hq; g.Hkv = Hkv; g.D = D; g.max_seq = c.max_seq;
       g.pos = k.d_pos; g.seq_slot = k.d_slot; g.k_cache = p.k_cache; g.v_cache = p.v_cache;
       g.scale_log2 = scale_log2;
       g.split_len = DEC_SPLIT; g.n_split = L.n_split_max;
