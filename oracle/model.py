@@ -62,6 +62,11 @@ def to_dtype(weights: dict, dtype=np.float32) -> dict:
 
 
 def layer_weights(W: dict, l: int) -> dict:
+    """Weights of weight layer ``l`` (keys without the ``L{l}.`` prefix).  A
+    ``W`` with a ``layer`` method supplies them itself (weights drawn per layer
+    on demand, for stacks too large to hold at once)."""
+    if hasattr(W, "layer"):
+        return W.layer(l)
     p = f"L{l}."
     return {k[len(p):]: v for k, v in W.items() if k.startswith(p)}
 
