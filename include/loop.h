@@ -162,6 +162,9 @@ void loop_model_destroy(loop_model* m);
  *   d_logits   device fp32 [batch, vocab] logits of the last position, or NULL
  *   d_hidden_out device fp32 [batch*seq_len, d_model]: h after the last
  *              execution (before the final norm), or NULL
+ *   d_final_out device fp32 [batch*seq_len, d_model]: the final RMSNorm of
+ *              h at every position (gain final_norm; the bf16 values the
+ *              head multiplies, stored as fp32), or NULL
  *   n_taps / tap_exec (host) / d_taps device fp32 [n_taps, batch, d_model]:
  *              hidden state after the listed executions at the last position
  *              (mean of the streams inside the loop), or 0 / NULL.
@@ -191,6 +194,7 @@ typedef struct loop_prefill_args {
   float* d_taps;
   int32_t loop_passes;
   int32_t taps_all_positions;
+  float* d_final_out;
 } loop_prefill_args;
 int loop_prefill(loop_model* m, const loop_prefill_args* a, void* stream);
 

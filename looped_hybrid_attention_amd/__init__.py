@@ -52,7 +52,7 @@ class loop_prefill_args(ctypes.Structure):
                 ("start_pos", ctypes.POINTER(_i32)), ("d_tokens", _vp), ("d_hidden_in", _vp),
                 ("d_logits", _vp), ("d_hidden_out", _vp), ("n_taps", _i32),
                 ("tap_exec", ctypes.POINTER(_i32)), ("d_taps", _vp), ("loop_passes", _i32),
-                ("taps_all_positions", _i32)]
+                ("taps_all_positions", _i32), ("d_final_out", _vp)]
 
 
 class loop_decode_args(ctypes.Structure):
@@ -273,8 +273,10 @@ def _i32arr(xs):
 
 def loop_prefill(model: int, batch: int, seq_len: int, slots, start_pos, d_tokens: int = 0,
                  d_hidden_in: int = 0, d_logits: int = 0, d_hidden_out: int = 0, tap_exec=(),
-                 d_taps: int = 0, stream: int = 0, loop_passes: int = 0, taps_all_positions: bool = False) -> None:
+                 d_taps: int = 0, stream: int = 0, loop_passes: int = 0, taps_all_positions: bool = False,
+                 d_final_out: int = 0) -> None:
     a = loop_prefill_args()
+    a.d_final_out = d_final_out or None
     a.loop_passes = loop_passes
     a.taps_all_positions = 1 if taps_all_positions else 0
     a.batch, a.seq_len = batch, seq_len

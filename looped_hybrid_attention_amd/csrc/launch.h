@@ -47,6 +47,8 @@ hipError_t launch_embed(const int32_t* ids, const void* E, float* h, int M, int 
 // y[i] = bf16(RMSNorm(x[row_i] (+ x2[row_i])) * g); rows = NULL: row i = i.
 hipError_t launch_rmsnorm(const float* x, const float* x2, const int32_t* rows, int64_t x_stride,
                           const void* g, void* y, int M, int d, float eps, hipStream_t s);
+// y fp32 [M][d]: the bf16 values of the RMSNorm above, stored as fp32
+hipError_t launch_rmsnorm_f32(const float* x, const void* g, float* y, int M, int d, float eps, hipStream_t s);
 
 enum { TR_IN_H = 0, TR_IN_WRITE = 1 };
 enum { TR_OUT_NORM = 0, TR_OUT_READ = 1, TR_OUT_NONE = 2 };

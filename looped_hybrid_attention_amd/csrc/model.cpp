@@ -635,6 +635,7 @@ extern "C" int loop_prefill(loop_model* m, const loop_prefill_args* a, void* str
     if (a->start_pos[b] == 0) m->slot_passes[a->slots[b]] = passes;
   if (a->d_hidden_out)
     HIP_TRY(hipMemcpyAsync(a->d_hidden_out, h, (size_t)k.M * c.d_model * 4, hipMemcpyDeviceToDevice, s));
+  if (a->d_final_out) HIP_TRY(launch_rmsnorm_f32(h, m->final_norm, a->d_final_out, k.M, c.d_model, c.eps, s));
   if (a->d_logits)
     if (int r = head_logits(m, k, a->d_logits, s)) return r;
   return 0;

@@ -85,12 +85,13 @@ __global__ __launch_bounds__(NT) void embed_kernel(const int32_t* ids, const uin
   }
 }
 
-// y = bf16(rmsnorm(x [+ x2]) * g) for row blockIdx.x (or rows[blockIdx.x]).
-// With PER a multiple of 4 each thread takes groups of four contiguous
-// columns, 4 (tid + q NT) .. (16-byte loads, all issued before the sums).
-template <int PER>
+// y = bf16(rmsnorm(x [+ x2]) * g) for row blockIdx.x (or rows[blockIdx.x]);
+// F32: the same bf16 values stored as fp32.  With PER a multiple of 4 each
+// thread takes groups of four contiguous columns, 4 (tid + q NT) .. (16-byte
+// loads, all issued before the sums).
+template <int PER, bool F32 = false>
 __global__ __launch_bounds__(NT) void rmsnorm_kernel(const float* x, const float* x2, const int32_t* rows,
-                                                     int64_t x_stride, const uint16_t* g, uint16_t* y,
+                                                     int64_t x_stride, const uint16_t* g, void* y_out,
                                                      int d, float eps) {
   constexpr bool VEC = PER % 4 == 0;
   __shared__ float red[2 * NT / 64];
@@ -124,7 +125,8 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const float* x, const float
   float dummy = 0.f;
   block_sum2(ss, dummy, red);
   const float inv = rsqrtf(ss / d + eps);
-  uint16_t* yr = y + (int64_t)blockIdx.x * d;
+  uint16_t* yr = reinterpret_cast<uint16_t*>(y_out) + (int64_t)blockIdx.x * d;
+  float* yf = reinterpret_cast<float*>(y_out) + (int64_t)blockIdx.x * d;
   if (VEC) {
 #pragma unroll
     for (int q = 0; q < PER / 4; ++q) {
@@ -135,13 +137,19 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const float* x, const float
       uint16_t o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = f2bf_bits(v[4 * q + e] * inv * bf2f(ge[e]));
-      *reinterpret_cast<uint2*>(yr + c) = *reinterpret_cast<const uint2*>(o);
+      if constexpr (F32)
+        *reinterpret_cast<f32x4*>(yf + c) = (f32x4){bf2f(o[0]), bf2f(o[1]), bf2f(o[2]), bf2f(o[3])};
+      else
+        *reinterpret_cast<uint2*>(yr + c) = *reinterpret_cast<const uint2*>(o);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int c = col(i);
-      if (c < d) yr[c] = f2bf_bits(v[i] * inv * bf2f(g[c]));
+      if (c >= d) continue;
+      const uint16_t o = f2bf_bits(v[i] * inv * bf2f(g[c]));
+      if constexpr (F32) yf[c] = bf2f(o);
+      else yr[c] = o;
     }
   }
 }
@@ -381,7 +389,16 @@ hipError_t launch_rmsnorm(const float* x, const float* x2, const int32_t* rows, 
   if (M == 0) return hipSuccess;
   return by_width(d, [&](auto per) {
     hipLaunchKernelGGL(rmsnorm_kernel<decltype(per)::value>, dim3(M), dim3(NT), 0, s, x, x2, rows,
-                       x_stride, (const uint16_t*)g, (uint16_t*)y, d, eps);
+                       x_stride, (const uint16_t*)g, y, d, eps);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_rmsnorm_f32(const float* x, const void* g, float* y, int M, int d, float eps, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  return by_width(d, [&](auto per) {
+    hipLaunchKernelGGL((rmsnorm_kernel<decltype(per)::value, true>), dim3(M), dim3(NT), 0, s, x, nullptr, nullptr,
+                       (int64_t)d, (const uint16_t*)g, (void*)y, d, eps);
     return hipGetLastError();
   });
 }

@@ -91,8 +91,9 @@ def test_prefill_and_greedy_decode(tiny):
     d_ids = dev(ids, torch)
     logits = torch.zeros((1, V), dtype=torch.float32, device="cuda")
     hid = torch.zeros((T, d), dtype=torch.float32, device="cuda")
+    fin = torch.zeros((T, d), dtype=torch.float32, device="cuda")
     g.L.loop_prefill(g.handle, 1, T, [0], [0], d_tokens=d_ids.data_ptr(), d_logits=logits.data_ptr(),
-                     d_hidden_out=hid.data_ptr(), stream=g.stream())
+                     d_hidden_out=hid.data_ptr(), d_final_out=fin.data_ptr(), stream=g.stream())
     torch.cuda.synchronize()
     # four oracle evaluations of the prefill
     runs = []
@@ -107,6 +108,20 @@ def test_prefill_and_greedy_decode(tiny):
           % (rel_err(host(hid), h_ref[0]), tol_h, rel_err(host(logits), lg_ref), tol_l))
     assert rel_err(host(hid), h_ref[0]) <= tol_h
     assert rel_err(host(logits), lg_ref) <= tol_l
+    # the final RMSNorm at every position (d_final_out): the bf16 values the
+    # head multiplies, against each evaluation's final norm (bar from their
+    # spread), and against the GPU's own h normalised on the host in fp64
+    # (one bf16 rounding apart)
+    from oracle.ops import rmsnorm
+    from oracle.precision import round_bf16
+    fins = [round_bf16(rmsnorm(r[2][0].astype(np.float64), W["final_norm"].astype(np.float64), ocfg.eps))
+            for r in runs]
+    tol_f = bar(fins)
+    own = rmsnorm(host(hid).astype(np.float64), W["final_norm"].astype(np.float64), ocfg.eps)
+    print("tiny final norm: gpu-vs-oracle %.4f (bar %.4f), vs its own h %.2e"
+          % (rel_err(host(fin), fins[0]), tol_f, rel_err(host(fin), own)))
+    assert rel_err(host(fin), fins[0]) <= tol_f
+    assert rel_err(host(fin), own) <= 2.0 ** -7
     exact = 0
     ev_l = [r[3][0] for r in runs]
     assert argmax_ok(int(np.argmax(host(logits)[0])), ev_l, tol_l)
