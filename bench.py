@@ -11,7 +11,7 @@ seeded N(0, 1) bf16 KV and N(0, 0.1) fp32 GDN states), one token per sequence
 per step.
 
 Prints one JSON line (see the repository's benchmark contract).  --gpus N
-with N > 1 exits: this build runs on one GPU.
+with N > 1 exits: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -147,7 +147,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence or by heads across GPUs, which this build does not run)",
+              "(the path would shard by sequence or by heads across GPUs; that is not implemented)",
               file=sys.stderr)
         sys.exit(2)
     import torch
