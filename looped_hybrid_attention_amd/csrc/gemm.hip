@@ -333,6 +333,246 @@ hipError_t launch_cfg(const GemmArgs& g, int splits, hipStream_t s) {
 }
 
 
+// ------------------------------------------------- small M, stream over K
+// Rows M <= 64 (decode): the output's 64 x 128 tiles (SwiGLU: 64 output
+// columns, gate and up rows in alternating 32-row blocks) times the 64-deep
+// K steps make U = tiles * nk units of equal work.  A persistent grid of P
+// workgroups (two per CU) takes contiguous ranges [w U / P, (w + 1) U / P),
+// so every workgroup streams the same number of weight bytes, and the
+// register-staged loads run ST_PF units ahead straight across tile
+// boundaries (no refill between tiles).  At the end of a tile (or of its
+// range) a workgroup writes its fp32 partial sum into slot
+// w - (first workgroup of the tile); stream_fixup_kernel adds a tile's slots
+// in slot order (= K order) and applies the epilogue.  The partition depends
+// on N, K and P only, so a row's result does not depend on M.
+constexpr int ST_PF = 3;
+DEV int stream_wg_of(int64_t u, int64_t U, int P) { return (int)(((u + 1) * P - 1) / U); }
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_stream_kernel(GemmArgs g, int P) {
+  constexpr int BM = 64, BN = 128, WN = 2, NT = 256, TM = 1, TN = 2, PF = ST_PF;
+  constexpr int A_CHUNKS = BM * BK / 8 / NT;
+  constexpr int B_CHUNKS = BN * BK / 8 / NT;
+  constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? BN / 2 : BN;
+  constexpr int STAGE = (BM + BN) * LDSK;
+  extern __shared__ __align__(16) uint16_t gemm_smem[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wm = wave / WN, wn = wave % WN;
+  const int nk = g.K / BK;
+  const int tiles = (g.N + OUT_BN - 1) / OUT_BN;
+  const int64_t U = (int64_t)tiles * nk;
+  const int w = blockIdx.x;
+  // U >= P (the launcher's condition): every workgroup owns at least one
+  // unit, so a tile's slots run without gaps from its first workgroup to its
+  // last
+  const int64_t u0 = (int64_t)w * U / P, u1 = (int64_t)(w + 1) * U / P;
+
+  // this thread's 16-byte chunks: A rows (all of M, clamped), B rows of the
+  // tile (row r, K chunk kc); the tile and the K step set the base
+  int a_off[A_CHUNKS], a_lds[A_CHUNKS], b_r[B_CHUNKS], b_kc[B_CHUNKS], b_lds[B_CHUNKS];
+#pragma unroll
+  for (int i = 0; i < A_CHUNKS; ++i) {
+    const int c = tid + i * NT, r = c / (BK / 8), kc = c % (BK / 8);
+    a_off[i] = min(r, g.M - 1) * (int)g.lda + kc * 8;
+    a_lds[i] = r * LDSK + kc * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < B_CHUNKS; ++i) {
+    const int c = tid + i * NT;
+    b_r[i] = c / (BK / 8);
+    b_kc[i] = c % (BK / 8);
+    b_lds[i] = (BM + b_r[i]) * LDSK + b_kc[i] * 8;
+  }
+  auto b_offset = [&](int i, int t, int ks) {
+    const int r = b_r[i];
+    int gn;
+    if (EPI == LOOP_EPI_SWIGLU) {
+      const int blk = r / 32;
+      gn = (blk & 1) * g.swiglu_F + min(t * OUT_BN + (blk >> 1) * 32 + (r & 31), g.N - 1);
+    } else {
+      gn = min(t * OUT_BN + r, g.N - 1);
+    }
+    return gn * (int)g.ldb + ks * BK + b_kc[i] * 8;
+  };
+  u32x4 ra[PF][A_CHUNKS], rb[PF][B_CHUNKS];
+  auto load = [&](int64_t u, u32x4 (&a)[A_CHUNKS], u32x4 (&b)[B_CHUNKS]) __attribute__((always_inline)) {
+    const int t = (int)(u / nk), ks = (int)(u % nk);
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) a[i] = *reinterpret_cast<const u32x4*>(g.A + ks * BK + a_off[i]);
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) b[i] = *reinterpret_cast<const u32x4*>(g.B + b_offset(i, t, ks));
+  };
+  // unit u0 straight into LDS buffer 0; units u0 + 1 .. u0 + PF - 1 into the
+  // register sets 0 .. PF - 2 (set of local unit j: (j - 1) % PF)
+  {
+    u32x4 a0[A_CHUNKS], b0[B_CHUNKS];
+    load(u0, a0, b0);
+#pragma unroll
+    for (int p = 0; p + 1 < PF; ++p) load(min(u0 + 1 + p, u1 - 1), ra[p], rb[p]);
+#pragma unroll
+    for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(gemm_smem + a_lds[i]) = a0[i];
+#pragma unroll
+    for (int i = 0; i < B_CHUNKS; ++i) *reinterpret_cast<u32x4*>(gemm_smem + b_lds[i]) = b0[i];
+  }
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int a_frag = (wm * (BM / 2) + lr) * LDSK + lk;
+  const int b_frag = (BM + wn * (BN / WN) + lr) * LDSK + lk;
+  const int64_t pstride = (int64_t)(EPI == LOOP_EPI_SWIGLU ? 2 : 1) * g.M * g.N;
+  __syncthreads();
+  for (int64_t ub = u0; ub < u1; ub += PF) {
+#pragma unroll
+    for (int jp = 0; jp < PF; ++jp) {
+      const int64_t u = ub + jp;
+      if (u >= u1) break;
+      const int j = (int)(u - u0);
+      const int ld_set = (jp + PF - 1) % PF;
+      load(min(u + PF, u1 - 1), ra[ld_set], rb[ld_set]);
+      const uint16_t* S = gemm_smem + (j & 1) * STAGE;
+      bf16x8 af[2][TM], bfr[2][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[0][i] = *reinterpret_cast<const bf16x8*>(S + a_frag + i * 32 * LDSK);
+#pragma unroll
+      for (int jj = 0; jj < TN; ++jj) bfr[0][jj] = *reinterpret_cast<const bf16x8*>(S + b_frag + jj * 32 * LDSK);
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        if (ks + 1 < BK / 16) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            af[nxt][i] = *reinterpret_cast<const bf16x8*>(S + a_frag + i * 32 * LDSK + (ks + 1) * 16);
+#pragma unroll
+          for (int jj = 0; jj < TN; ++jj)
+            bfr[nxt][jj] = *reinterpret_cast<const bf16x8*>(S + b_frag + jj * 32 * LDSK + (ks + 1) * 16);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < TN; ++jj) acc[i][jj] = mfma32x32x16(af[cur][i], bfr[cur][jj], acc[i][jj]);
+      }
+      uint16_t* D = gemm_smem + ((j + 1) & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < A_CHUNKS; ++i) *reinterpret_cast<u32x4*>(D + a_lds[i]) = ra[jp][i];
+#pragma unroll
+      for (int i = 0; i < B_CHUNKS; ++i) *reinterpret_cast<u32x4*>(D + b_lds[i]) = rb[jp][i];
+      if ((u + 1) % nk == 0 || u + 1 == u1) {
+        // the workgroup's part of this tile: fp32 partials into its slot
+        const int t = (int)(u / nk);
+        const int slot = w - stream_wg_of((int64_t)t * nk, U, P);
+        float* Pp = g.part + slot * pstride;
+        const int row_base = wm * (BM / 2) + 4 * (lane >> 5);
+#pragma unroll
+        for (int jj = 0; jj < TN; ++jj) {
+          int col, part = 0;
+          if (EPI == LOOP_EPI_SWIGLU) {
+            col = t * OUT_BN + (wn * (BN / WN)) / 2 + (jj / 2) * 32 + lr;
+            part = jj & 1;
+          } else {
+            col = t * OUT_BN + wn * (BN / WN) + jj * 32 + lr;
+          }
+          if (col < g.N) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+                if (row >= g.M) continue;
+                if (EPI == LOOP_EPI_SWIGLU) Pp[((int64_t)row * 2 + part) * g.N + col] = acc[i][jj][r];
+                else Pp[(int64_t)row * g.N + col] = acc[i][jj][r];
+              }
+          }
+#pragma unroll
+          for (int i = 0; i < TM; ++i) acc[i][jj] = (f32x16){};
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Sum of each tile's stream partials in slot order, then the epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void stream_fixup_kernel(GemmArgs g, int P) {
+  constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? 64 : 128;
+  const int nk = g.K / BK;
+  const int64_t U = (int64_t)((g.N + OUT_BN - 1) / OUT_BN) * nk;
+  const int64_t n_out = (int64_t)g.M * g.N;
+  const int64_t stride = (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * n_out;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n_out; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / g.N, col = i % g.N;
+    const int t = (int)(col / OUT_BN);
+    const int segs = stream_wg_of((int64_t)(t + 1) * nk - 1, U, P) - stream_wg_of((int64_t)t * nk, U, P) + 1;
+    if (EPI == LOOP_EPI_SWIGLU) {
+      float gt = 0.f, up = 0.f;
+      for (int sp = 0; sp < segs; ++sp) {
+        gt += g.part[sp * stride + (row * 2) * g.N + col];
+        up += g.part[sp * stride + (row * 2 + 1) * g.N + col];
+      }
+      reinterpret_cast<uint16_t*>(g.C)[row * g.ldc + col] = f2bf_bits(siluf_(gt) * up);
+    } else {
+      float v = 0.f;
+      for (int sp = 0; sp < segs; ++sp) v += g.part[sp * stride + i];
+      const int64_t o = row * g.ldc + col;
+      if (EPI == LOOP_EPI_BF16) reinterpret_cast<uint16_t*>(g.C)[o] = f2bf_bits(v);
+      else if (EPI == LOOP_EPI_F32) reinterpret_cast<float*>(g.C)[o] = v;
+      else reinterpret_cast<float*>(g.C)[o] = g.R[o] + v;
+    }
+  }
+}
+
+// Workgroups of the stream grid: two per CU of the 256-CU part (a fixed
+// count, so that the partition, and with it every result, is the same on
+// any device, and the workspace size can be computed without one).  Used
+// where every workgroup gets at least ST_MIN_UNITS units: measured on the
+// decode projections, the stream pays off on gate/up (24 units per
+// workgroup: 51.9 against 55.8 us at 64 rows, 41.7 against 48.0 at one row)
+// and loses on the input projections (8-10 units: the per-workgroup start and
+// the extra partial slots cost more than the balance gains).
+constexpr int ST_P = 512;
+constexpr int ST_MIN_UNITS = 16;
+
+// Partial bytes of the stream path for this call (0: the call cannot use it).
+template <int EPI>
+size_t stream_partial_bytes(const GemmArgs& g) {
+  constexpr int OUT_BN = (EPI == LOOP_EPI_SWIGLU) ? 64 : 128;
+  constexpr int P = ST_P;
+  if (g.M < 1 || g.M > 64 || g.K % BK != 0 || g.N < 1 || g.N > 65536) return 0;
+  const int nk = g.K / BK, tiles = (g.N + OUT_BN - 1) / OUT_BN;
+  const int64_t U = (int64_t)tiles * nk;
+  if (U < (int64_t)ST_MIN_UNITS * P || U > (1ll << 30)) return 0;
+  const int64_t rows_b = (EPI == LOOP_EPI_SWIGLU) ? 2 * (int64_t)g.N : g.N;
+  if (rows_b * g.ldb >= (1ll << 31) || (int64_t)g.M * g.lda >= (1ll << 31)) return 0;
+  int max_segs = 1;
+  for (int t = 0; t < tiles; ++t) {
+    const int64_t a = (int64_t)t * nk, b = (int64_t)(t + 1) * nk - 1;
+    const int segs = (int)(((b + 1) * P - 1) / U) - (int)(((a + 1) * P - 1) / U) + 1;
+    max_segs = std::max(max_segs, segs);
+  }
+  return (size_t)max_segs * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
+}
+
+template <int EPI>
+hipError_t launch_stream(const GemmArgs& g, hipStream_t s) {
+  constexpr int P = ST_P;
+  constexpr size_t lds = 2 * (size_t)(64 + 128) * LDSK * sizeof(uint16_t);
+  auto k = gemm_stream_kernel<EPI>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k, dim3(P), dim3(256), lds, s, g, P);
+  const int64_t n_out = (int64_t)g.M * g.N;
+  const int blocks = (int)std::min<int64_t>((n_out + 255) / 256, 4096);
+  hipLaunchKernelGGL(stream_fixup_kernel<EPI>, dim3(blocks), dim3(256), 0, s, g, P);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------- large-M tiles, LDS copy
 // 256 x 256 output tiles, K in steps of KB, four waves (one per SIMD), each
 // computing 128 x 128 as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 with the
@@ -929,6 +1169,10 @@ int small_splits(const GemmArgs& g) {
 
 template <int EPI>
 hipError_t launch_small(GemmArgs g, size_t ws_bytes, hipStream_t s) {
+  if (g.M <= 64 && g.part) {
+    const size_t need = stream_partial_bytes<EPI>(g);
+    if (need > 0 && need <= ws_bytes) return launch_stream<EPI>(g, s);
+  }
   const int splits = small_splits<EPI>(g);
   const size_t need = (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float);
   if (splits > 1 && g.part && need <= ws_bytes) {
@@ -1012,6 +1256,10 @@ hipError_t launch_epi(GemmArgs g, size_t ws_bytes, hipStream_t s) {
 // enough (0: the call does not split).
 template <int EPI>
 size_t small_m_partial_bytes(const GemmArgs& g) {
+  if (!skinny_fits<EPI>(g) && g.M <= 64) {
+    const size_t st = stream_partial_bytes<EPI>(g);
+    if (st > 0) return st;
+  }
   const int splits = skinny_fits<EPI>(g) ? skinny_splits<EPI, SK_WAVES>(g) : small_splits<EPI>(g);
   return splits > 1 ? (size_t)splits * g.M * g.N * (EPI == LOOP_EPI_SWIGLU ? 2 : 1) * sizeof(float) : 0;
 }
