@@ -509,6 +509,289 @@ __global__ __launch_bounds__(64 * (G < 4 ? 4 : G), 1) void flash_prefill_kernel(
     }
 }
 
+// ------------------------------------------- flash prefill, two waves per SIMD
+// The G = 4 case (four query heads per KV head) with eight waves, two per
+// SIMD, so that one wave's softmax and LDS waits overlap the other's MFMAs.
+// Workgroup = (32-query tile, KV head, sequence); wave w takes query head
+// kvh*4 + w%4 and the 16 queries 16 (w/4) .. of the tile, on
+// v_mfma_f32_16x16x32_bf16: lane (c = lane%16, rg = lane/16) owns query c.
+// S^T = K . Q^T per 16-key block kb of the 64-key tile leaves the lane rows
+// 4 rg + r (r = 0..3) of each block; the PV product O^T += V^T . P^T takes,
+// per 32-key step ks, the keys 8 rg .. 8 rg + 7 of the step in lane group rg.
+// K row i of the LDS tile (block i/16, group (i/4)%4, r = i%4) therefore
+// holds key 32 (kb/2) + 8 rg + 4 (kb%2) + r: blocks 2ks and 2ks + 1 give lane
+// group rg exactly the eight keys its PV operand needs, as they stand.  The
+// running max and sum of a query are shared by its four lanes (reduced over
+// lane ^ 16 and lane ^ 32).  K and V^T tiles as in the kernel above (direct
+// copies, two stages, 16-byte chunks swizzled so that the 16 rows of one
+// operand read hit distinct banks); the queries' QK-norm and rotary in the
+// prologue, through stage 1.
+DEV int f16_key_of_row(int i) { return 32 * (i >> 5) + 8 * ((i >> 2) & 3) + 4 * ((i >> 4) & 1) + (i & 3); }
+template <int CR>
+DEV int f16_kswz(int r) { return CR >= 16 ? (r & 15) : ((r >> 1) & 7); }
+
+template <int NDB, int FD, int VROW>
+DEV void flash16_pv(f32x4 (&o)[NDB], f32x4 (&s)[4], float& l, float m, float scale, const uint8_t* vr, int vsw,
+                    int rg) {
+  float lsum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][r], scale, -m));
+      s[kb][r] = p;
+      lsum += p;
+    }
+  l += lsum;
+  bf16x8 pf[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[ks][e] = f2bf(s[2 * ks + (e >> 2)][e & 3]);
+  bf16x8 vf[2 * NDB];
+  // step g: output block g % NDB, key step g / NDB
+#define F16_VREAD(g_) \
+  vf[g_] = *reinterpret_cast<const bf16x8*>(vr + ((g_) % NDB) * 16 * VROW + (((4 * ((g_) / NDB) + rg) ^ vsw) << 4))
+#pragma unroll
+  for (int g = 0; g < FD; ++g) F16_VREAD(g);
+#pragma unroll
+  for (int g = 0; g < 2 * NDB; ++g) {
+    if (g + FD < 2 * NDB) F16_VREAD(g + FD);
+    o[g % NDB] = mfma16x16x32(vf[g], pf[g / NDB], o[g % NDB]);
+  }
+#undef F16_VREAD
+  __builtin_amdgcn_sched_group_barrier(0x100, FD, 0);
+#pragma unroll
+  for (int g = 0; g < 2 * NDB; ++g) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (g + FD < 2 * NDB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void flash16_prefill_kernel(FlashArgs a) {
+  constexpr int G = 4, W = 8, QT = 32;
+  constexpr int CR = D / 8;    // 16-byte chunks per K row
+  constexpr int NDS = D / 32;  // 32-dim steps of K . Q^T
+  constexpr int NDB = D / 16;  // 16-dim output blocks
+  constexpr int KI = KT * CR / 64 / W;  // K copy instructions per wave and tile
+  constexpr int VI = D * 8 / 64 / W;    // V^T copy instructions per wave and tile
+  static_assert(KI >= 1 && VI >= 1 && KI * 64 * W == KT * CR && VI * 64 * W == D * 8, "tile / wave split");
+  static_assert(CR >= 8, "swizzle needs 8 chunks per row");
+  constexpr int FD = 4;  // LDS operand reads in flight ahead of the MFMAs
+  using L = FlashLds<D>;
+  static_assert(W * 16 * D * 2 <= L::STAGE, "query scratch in stage 1");
+  extern __shared__ __align__(16) uint8_t flash_smem[];
+
+  const int tile = (gridDim.x - 1) - blockIdx.x;  // heaviest (latest) tiles first
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, rg = lane >> 4;
+  const int head = kvh * G + wave % G, qh = wave / G;
+  const int t = tile * QT + qh * 16 + c;
+  const bool qvalid = t < a.T;
+  const int p0 = a.pos[b];
+  const int qpos = p0 + t;
+  const int64_t m = (int64_t)b * a.T + t;
+  const int64_t slot_b = a.seq_slot[b];
+  const uint16_t* Kc = a.k_cache + (slot_b * a.Hkv + kvh) * (int64_t)a.max_seq * D;
+  const uint16_t* Vc = a.v_cache + (slot_b * a.Hkv + kvh) * (int64_t)D * a.max_seq;
+  const int L_valid = p0 + a.T;
+  const int kv_end = p0 + min(a.T, (tile + 1) * QT);
+  const int nkt = (kv_end + KT - 1) / KT;
+
+  int k_src[KI], v_src[VI];
+#pragma unroll
+  for (int i = 0; i < KI; ++i) {
+    const int n = wave * KI + i;
+    const int r = (n * 64 + lane) / CR, p = (n * 64 + lane) % CR;
+    k_src[i] = f16_key_of_row(r) * D + (p ^ f16_kswz<CR>(r)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < VI; ++i) {
+    const int n = wave * VI + i;
+    const int d = (n * 64 + lane) / 8, p = (n * 64 + lane) % 8;
+    const int lp = p ^ v_swz(d);
+    v_src[i] = (lp / 4) * D * VB + d * VB + (lp % 4) * 8;
+  }
+  const auto k_rsrc = buffer_rsrc(Kc, a.max_seq * D * 2);
+  const auto v_rsrc = buffer_rsrc(Vc, a.max_seq * D * 2);
+#define F16_COPY(k0_, stage_)                                                                 \
+  {                                                                                           \
+    uint8_t* S_ = flash_smem + (stage_) * L::STAGE;                                           \
+    _Pragma("unroll") for (int i = 0; i < KI; ++i)                                            \
+        copy16_to_lds(k_rsrc, ((k0_) * D + k_src[i]) * 2, 0, (lds_void*)(S_ + (wave * KI + i) * 1024)); \
+    _Pragma("unroll") for (int i = 0; i < VI; ++i)                                            \
+        copy16_to_lds(v_rsrc, ((k0_) / VB * D * VB + v_src[i]) * 2, 0,                       \
+                      (lds_void*)(S_ + KT * L::KROW + (wave * VI + i) * 1024));               \
+  }
+#define F16_ZERO_TAIL(k0_, stage_)                                                           \
+  {                                                                                          \
+    uint8_t* V_ = flash_smem + (stage_) * L::STAGE + KT * L::KROW;                           \
+    const int first = max(L_valid - (k0_), 0);                                               \
+    for (int d = tid; d < D; d += 64 * W)                                                    \
+      for (int kk = first; kk < KT; ++kk)                                                    \
+        *reinterpret_cast<uint16_t*>(V_ + d * L::VROW + (((kk >> 3) ^ v_swz(d)) << 4) + (kk & 7) * 2) = 0; \
+  }
+
+  // queries: QK-norm and rotary into stage 1 (rows of D bf16, 8-dim group
+  // g of wave row i at g ^ f16_kswz(i)), the rotary table after the stages
+  const int RH = a.R / 2;
+  float* rct = reinterpret_cast<float*>(flash_smem + L::bytes);
+  float* rst = rct + QT * RH;
+  uint16_t* qscr = reinterpret_cast<uint16_t*>(flash_smem + L::STAGE);
+  F16_COPY(0, 0);
+  for (int e = tid; e < QT * RH; e += 64 * W) {
+    const int qi = e / RH, i = e % RH;
+    const int tq = min(tile * QT + qi, a.T - 1);
+    const float2 cs = reinterpret_cast<const float2*>(a.rope)[((int64_t)b * a.T + tq) * RH + i];
+    rct[qi * RH + i] = cs.x;
+    rst[qi * RH + i] = cs.y;
+  }
+  __syncthreads();
+  {
+    QkRaw<D> raw[16];
+#pragma unroll
+    for (int qi = 0; qi < 16; ++qi) {
+      const int tq = tile * QT + qh * 16 + qi;
+      if (tq < a.T) {
+        raw[qi] = qk_load<D>(a.q + ((int64_t)b * a.T + tq) * a.q_stride + head * D, lane);
+      } else {
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) raw[qi].x[e] = 0;
+      }
+    }
+    float gq[D / 64];
+    qk_gain<D>(a.q_norm, lane, gq);
+#pragma unroll
+    for (int qi = 0; qi < 16; ++qi)
+      qk_finish<D>(raw[qi], gq, rct + (qh * 16 + qi) * RH, rst + (qh * 16 + qi) * RH, a.R, a.eps,
+                   qscr + (wave * 16 + qi) * D, f16_kswz<CR>(qi), lane);
+  }
+  __syncthreads();
+  const int ksw = f16_kswz<CR>(c), vsw = v_swz(c);
+  bf16x8 qf[NDS];
+  {
+    const uint16_t* qr = qscr + (wave * 16 + c) * D;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) qf[ds] = *reinterpret_cast<const bf16x8*>(qr + (((4 * ds + rg) ^ ksw) << 3));
+  }
+  f32x4 o[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) o[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float m_i = -1e30f, l_i = 0.f;
+  const float scale = a.scale_log2;
+  const int qpos_lo = p0 + tile * QT + qh * 16;  // first query of the wave
+  wait_vmem();
+  __syncthreads();
+  if (KT > L_valid) {
+    F16_ZERO_TAIL(0, 0);
+    __syncthreads();
+  }
+
+  f32x4 s[4];
+  float mloc;
+  bool bump;
+#define F16_SYNC(j_)                                                   \
+  {                                                                    \
+    wait_vmem();                                                       \
+    __syncthreads();                                                   \
+    if ((j_) + 1 < nkt && ((j_) + 2) * KT > L_valid) {                 \
+      F16_ZERO_TAIL(((j_) + 1) * KT, ((j_) + 1) & 1);                  \
+      __syncthreads();                                                 \
+    }                                                                  \
+  }
+  int j = 0;
+  for (;;) {
+    for (; j < nkt; ++j) {
+      const uint8_t* sK = flash_smem + (j & 1) * L::STAGE;
+      const int k0 = j * KT;
+      if (j + 1 < nkt) F16_COPY(k0 + KT, (j + 1) & 1);
+      // S^T: step g multiplies key block g % 4 by dims 32 (g / 4) ..: four
+      // independent accumulation chains
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      {
+        const uint8_t* kr = sK + c * L::KROW;
+        bf16x8 kf[4 * NDS];
+#define F16_KREAD(g_) \
+  kf[g_] = *reinterpret_cast<const bf16x8*>(kr + ((g_) & 3) * 16 * L::KROW + (((4 * ((g_) >> 2) + rg) ^ ksw) << 4))
+#pragma unroll
+        for (int g = 0; g < FD; ++g) F16_KREAD(g);
+#pragma unroll
+        for (int g = 0; g < 4 * NDS; ++g) {
+          if (g + FD < 4 * NDS) F16_KREAD(g + FD);
+          s[g & 3] = mfma16x16x32(kf[g], qf[g >> 2], s[g & 3]);
+        }
+#undef F16_KREAD
+        __builtin_amdgcn_sched_group_barrier(0x100, FD, 0);
+#pragma unroll
+        for (int g = 0; g < 4 * NDS; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (g + FD < 4 * NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      // causal mask on tiles that reach past the wave's first query:
+      // register r of block kb holds key k0 + f16_key_of_row(16 kb + 4 rg + r)
+      if (k0 + KT - 1 > qpos_lo) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + f16_key_of_row(16 * kb + 4 * rg + r);
+            s[kb][r] = (key <= qpos) ? s[kb][r] : -1e30f;
+          }
+      }
+      // online softmax in log2 units; the reference max m_i moves only when
+      // a tile's max exceeds it by more than 8
+      mloc = -1e30f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mloc = fmaxf(mloc, s[kb][r]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * scale;
+      bump = mloc > m_i + 8.f;
+      if (__builtin_amdgcn_read_exec() & __ballot(bump)) break;
+      flash16_pv<NDB, FD, L::VROW>(o, s, l_i, m_i, scale, sK + KT * L::KROW + c * L::VROW, vsw, rg);
+      F16_SYNC(j);
+    }
+    if (j >= nkt) break;
+    {
+      const float m_new = bump ? mloc : m_i;
+      const float alpha = __builtin_amdgcn_exp2f(m_i - m_new);
+      l_i *= alpha;
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) o[i] *= alpha;
+      m_i = m_new;
+    }
+    flash16_pv<NDB, FD, L::VROW>(o, s, l_i, m_i, scale, flash_smem + (j & 1) * L::STAGE + KT * L::KROW + c * L::VROW,
+                                 vsw, rg);
+    F16_SYNC(j);
+    ++j;
+  }
+#undef F16_SYNC
+#undef F16_COPY
+#undef F16_ZERO_TAIL
+  // the query's sum over its four lanes (each holds the keys of its rows)
+  l_i += __shfl_xor(l_i, 16, 64);
+  l_i += __shfl_xor(l_i, 32, 64);
+  if (!qvalid) return;
+  const float inv_l = 1.f / l_i;
+  const uint16_t* g = a.gate + m * a.gate_stride + head * D;
+  uint16_t* out = a.out + m * a.out_stride + head * D;
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) {
+    const int d = 16 * i + 4 * rg;
+    uint2 gv = *reinterpret_cast<const uint2*>(g + d);
+    const uint16_t* ge = reinterpret_cast<const uint16_t*>(&gv);
+    uint16_t r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = f2bf_bits(o[i][e] * inv_l * sigmoidf_(bf2f(ge[e])));
+    *reinterpret_cast<uint2*>(out + d) = *reinterpret_cast<uint2*>(r);
+  }
+}
+
 // --------------------------------------------------------------- decode
 // Workgroup = (split of DEC_SPLIT keys, KV head, sequence): the G query heads
 // of the KV head against keys [split*DEC_SPLIT, min(pos+1, ...)).  HBM-bound:
@@ -722,8 +1005,28 @@ hipError_t prep_d(const AttnPrepArgs& a, int M, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t flash16_d(const FlashArgs& a, int B, hipStream_t s) {
+  constexpr int QT = 32;
+  constexpr size_t LDS_MAX = 160 * 1024;
+  const size_t lds = FlashLds<D>::bytes + 2 * (size_t)QT * (a.R / 2) * sizeof(float);
+  if (a.R < 0 || a.R > D || a.R % 2 || lds > LDS_MAX) return hipErrorInvalidValue;
+  auto k = flash16_prefill_kernel<D>;
+  // the kernel's static LDS counts against the same 160 KB: the dynamic
+  // limit is raised to what the call asks for
+  static size_t attr = 0;
+  if (lds > attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = lds;
+  }
+  hipLaunchKernelGGL(k, dim3((a.T + QT - 1) / QT, a.Hkv, B), dim3(512), lds, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t flash_dg(const FlashArgs& a, int B, hipStream_t s) {
+  if constexpr (G == 4) return flash16_d<D>(a, B, s);
   constexpr int W = G < 4 ? 4 : G;
   constexpr int QT = 32 * W / G;
   constexpr size_t LDS_MAX = 160 * 1024;

@@ -252,3 +252,45 @@ def test_mixers_prefill_then_decode_path(preset, T):
                 assert max(errs) <= FLAT, (kind, b)
     finally:
         g.close()
+
+
+def test_gdn_mixer_long_call_equals_split_calls():
+    """A long Gated-DeltaNet prefill call (4,100 tokens: 65 chunks, the last
+    one ragged, the state carried through all of them inside one scan) must
+    equal, bit for bit, the same tokens in calls of 1,024 + 1,024 + 1,024 +
+    1,028 (the same chunk boundaries, the state handed from call to call
+    through the cache slot), and the oracle at the flat bar ([P1]
+    hncyxsy.com/news/268323 section 3: 16 heads x 128 at real width)."""
+    torch = torch_cuda()
+    dims = synth.preset("group")
+    ocfg = oracle.Config.from_dims(dims)
+    H, Dk, Dv = dims["gdn_heads"], dims["gdn_dk"], dims["gdn_dv"]
+    n_in, width = 2 * H * Dk + 2 * H * Dv + 2 * H, H * Dv
+    T, parts = 4100, (1024, 1024, 1024, 1028)
+    g = GpuModel(torch, dims, max_batch=2, max_seq=4160, max_tokens=T)
+    try:
+        proj = _proj("mixer.gdn.long", T, n_in)
+        d_x = dev(proj, torch)
+        outs = []
+        for slot, split in ((0, (T,)), (1, parts)):
+            d_o = torch.zeros((T, width), dtype=torch.bfloat16, device="cuda")
+            p0 = 0
+            for n in split:
+                say("gdn mixer slot", slot, "tokens", n, "start", p0)
+                g.L.loop_exec_mixer(g.handle, 0, 1, n, [slot], [p0], d_x.data_ptr() + p0 * n_in * 2, n_in,
+                                    d_o.data_ptr() + p0 * width * 2, width, stream=g.stream())
+                p0 += n
+            torch.cuda.synchronize()
+            outs.append(host(d_o))
+        assert np.array_equal(outs[0], outs[1]), "one long call differs from the split calls"
+        S = [host(_arena_view(g, g.L.loop_cache_offset(g.cfg, 2, 0, s), H * Dv * Dk, "f32")) for s in (0, 1)]
+        assert np.array_equal(S[0], S[1]), "final state differs"
+        W32 = om.layer_weights(om.to_dtype(g.host_weights, np.float32), 0)
+        say("oracle, 4100 tokens")
+        ref, Sref = og.gdn_mixer(synth.bf16_bits_to_f32(proj), W32, np.zeros((H, Dv, Dk), np.float32), ocfg,
+                                 chunked=True, bf16=True)
+        e, es = rel_err(outs[0], ref), rel_err(S[0].reshape(H, Dv, Dk), Sref)
+        print("GDN mixer, 4100 tokens in one call: output %.4f, final state %.2e" % (e, es))
+        assert e <= FLAT and es <= 1e-3
+    finally:
+        g.close()
