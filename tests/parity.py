@@ -25,8 +25,12 @@ top-1 / top-2 margin is below about twice that.  So where every oracle
 evaluation picks the same token and its margin exceeds ``tol``, the GPU must
 pick exactly that token; elsewhere (a near-tie that rounding decides) its
 token must be one whose oracle logit lies within ``tol`` of the oracle's best.
-Decode steps are judged from the GPU's own caches, where ``tol`` is the flat
-2e-2, so most decisions are exact ones.
+On the tiny model the four evaluations (fp32 / fp64, Gated-DeltaNet token by
+token / chunked) span the rounding-order noise of the bf16 policy, so there
+the rule is stricter (``exact_if_unanimous``): wherever they pick the same
+token the GPU must pick it, whatever the margin.  Where only fp32 and fp64
+evaluations of one recurrence are compared their spread does not represent
+that noise, and the margin rule applies.
 """
 import itertools
 
@@ -58,15 +62,15 @@ def margin(logits) -> float:
     return float((x[-1] - x[-2]) / np.max(np.abs(x)))
 
 
-def exact_required(evals, tol: float) -> bool:
-    return len(set(oracle_tokens(evals))) == 1 and margin(evals[0]) > tol
+def exact_required(evals, tol: float, exact_if_unanimous: bool = False) -> bool:
+    return unanimous(evals) and (exact_if_unanimous or margin(evals[0]) > tol)
 
 
-def argmax_ok(gpu_token: int, evals, tol: float) -> bool:
+def argmax_ok(gpu_token: int, evals, tol: float, exact_if_unanimous: bool = False) -> bool:
     """``evals``: the logits of the oracle's evaluations of the same position
     (a list of 1-D arrays); ``tol``: the logits bar of the comparison."""
     ref = np.asarray(evals[0], np.float64).reshape(-1)
-    if exact_required(evals, tol):
+    if exact_required(evals, tol, exact_if_unanimous):
         return int(gpu_token) == oracle_tokens(evals)[0]
     return ref[int(gpu_token)] >= ref.max() - tol * np.max(np.abs(ref))
 

@@ -14,9 +14,9 @@ oracle with token-by-token or chunked Gated-DeltaNet, in fp32 or fp64) land
 max(2e-2, 2 x the largest spread among those evaluations) (``parity.bar``),
 computed here from the oracle alone.
 Next-token argmax (``parity.argmax_ok``): exact wherever the oracle's
-evaluations pick the same token with a top-1 / top-2 margin above the logits
-bar; inside that band (a near-tie rounding decides) the GPU's token must be
-within the bar of the oracle's best.  Every decode step is compared
+evaluations pick the same token; where they disagree (a near-tie that the
+order of rounding decides) the GPU's token must be within the bar of the
+oracle's best.  Every decode step is compared
 with the oracle started from the GPU's own caches (as the prefill and the
 earlier steps left them), so the step is judged on its own arithmetic; its bar
 is the spread of this step's own evaluations (from the GPU's caches in fp32
@@ -34,7 +34,7 @@ import oracle
 from oracle import model as om
 from gpu_util import torch_cuda, dev, host, say, rel_err
 from model_util import GpuModel, state_from_gpu
-from parity import bar, argmax_ok, exact_required
+from parity import bar, argmax_ok, exact_required, oracle_tokens, margin
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
@@ -124,8 +124,10 @@ def test_prefill_and_greedy_decode(tiny):
     assert rel_err(host(fin), own) <= 2.0 ** -7
     exact = 0
     ev_l = [r[3][0] for r in runs]
-    assert argmax_ok(int(np.argmax(host(logits)[0])), ev_l, tol_l)
-    exact += exact_required(ev_l, tol_l)
+    print("tiny prefill greedy: gpu %d, oracle %s, margin %.4f"
+          % (int(np.argmax(host(logits)[0])), oracle_tokens(ev_l), margin(ev_l[0])))
+    assert argmax_ok(int(np.argmax(host(logits)[0])), ev_l, tol_l, exact_if_unanimous=True)
+    exact += exact_required(ev_l, tol_l, exact_if_unanimous=True)
     # against the fp32 definition: no worse than the bf16 policy's own drift
     h32, lg32, _ = om.prefill(ocfg, W, [om.SeqState(ocfg)], ids=ids.reshape(1, -1))
     assert rel_err(host(hid), h32[0]) <= 2 * max(rel_err(r[2][0], h32[0]) for r in runs)
@@ -155,8 +157,10 @@ def test_prefill_and_greedy_decode(tiny):
         assert rel_err(host(logits), lg_o) <= sl, step
         assert rel_err(host(hid)[0], h_o[0]) <= sh, step
         ev_l = [o[0][0] for o in outs]
-        assert argmax_ok(int(host(nxt)[0]), ev_l, sl), step
-        exact += exact_required(ev_l, sl)
+        print("tiny decode %d greedy: gpu %d, oracle %s, margin %.4f"
+              % (step, int(host(nxt)[0]), oracle_tokens(ev_l), margin(ev_l[0])))
+        assert argmax_ok(int(host(nxt)[0]), ev_l, sl, exact_if_unanimous=True), step
+        exact += exact_required(ev_l, sl, exact_if_unanimous=True)
         tok = int(nx_o[0])
     print("tiny greedy decisions required to be exact: %d of 9" % exact)
 
