@@ -24,9 +24,9 @@
 // Three kernels: the chunk-local part for all chunks in parallel (prep: W,
 // U~, Mqk and the row scales), the carry of S over the chunks (scan: the rows
 // of S are independent, so a head's rows are split over workgroups; it keeps
-// each chunk's entering state S0 and its U), and the chunk outputs for all
-// chunks in parallel (out: O from S0 and U, then RMSNorm over Dv times
-// SiLU(z)).  Every product runs on the bf16 MFMA with fp32
+// each chunk's U and the raw-query product Q S0^T with the entering state),
+// and the chunk outputs for all chunks in parallel (out: O from Q S0^T and U,
+// then RMSNorm over Dv times SiLU(z)).  Every product runs on the bf16 MFMA with fp32
 // accumulation: a raw projection is an exact bf16 operand, and an fp32
 // operand x enters as three bf16 parts hi = bf16(x), mid = bf16(x - hi),
 // lo = bf16(x - hi - mid) (24 significant bits, the fp32 value up to its last
@@ -142,8 +142,11 @@ DEV int kt_at(int k, int t) { return k * CH + 8 * ((t >> 3) ^ kt_swz(k)) + (t & 
 // that a wave's 16-byte-per-lane access is one contiguous kilobyte:
 //   W [CH][Dk]: element (t, k) at the fragment of (t / 16, k / 32, (k / 4) % 2):
 //     lane t % 16 + 16 ((k % 32) / 8), floats k % 4;
-//   U~^T / U^T [Dv][CH] and S_c [Dv][Dk]: element (j, x) at the fragment of
-//     (j / 16, x / 16): lane j % 16 + 16 ((x % 16) / 4), floats x % 4.
+//   U~^T / U^T [Dv][CH]: element (j, x) at the fragment of (j / 16, x / 16):
+//     lane j % 16 + 16 ((x % 16) / 4), floats x % 4;
+//   Q S0^T [CH][Dv]: element (t, j) at the fragment of (j / 16, t / 16):
+//     lane j % 16 + 16 ((t % 16) / 4), floats t % 4 (the same form, indexed
+//     jx_frag<CH>(j, t)).
 // Offsets in floats within a chunk's block.
 template <int DK>
 DEV int w_frag(int t, int k) {
@@ -434,16 +437,18 @@ __global__ __launch_bounds__(PNT, 2) void gdn_prep_kernel(GdnArgs a) {
 // carrying those rows of S over the chunks in order.  Per chunk (S = the
 // entering state, its three bf16 parts in LDS; the fp32 state in registers,
 // wave w < Dk/16 holding S[j][16w .. 16w+15]):
-//   the entering state is stored for the output kernel;
 //   waves 0-3, token tile w:   U = U~ - W S^T (both operands split), stored
 //                              over U~^T for the output kernel, the parts of
 //                              (dk U)^T into LDS;
+//   waves 4-7, token tile w-4: Q S^T (raw q rows exact, S split: the output
+//                              kernel's product with the entering state, in
+//                              the same order), stored for it;
 //   barrier;
 //   waves w < Dk/16:           S^T <- gC S^T + K^T (dk U)   (raw K^T stage);
 //   the next copies and loads are issued; barrier.
 // The chain over the chunks is bound by memory latency, so operands run
-// ahead: the U waves' register operands (W rows, U~^T, dk) three chunks ahead
-// in three register sets, the raw K^T tile two chunks ahead in three LDS
+// ahead: the U waves' register operands (W rows, U~^T, dk) and the other
+// waves' q rows three chunks ahead in three register sets, the raw K^T tile two chunks ahead in three LDS
 // stages (buffer_load ... lds), and a later chunk is warmed into L2.  All
 // Dv/16 row blocks of a (seq, head) read the same W and K, so they are placed
 // on one XCD (workgroups go to XCDs round-robin by linear index): index =
@@ -459,6 +464,13 @@ struct ScanRegs {
   static constexpr int LOADS = 2 * (DK / 32) + 2;  // vector loads per chunk
   f32x4 w[DK / 32][2];
   f32x4 ut, dk;
+};
+// Register operands of one chunk for a Q wave: the raw q rows of its token
+// tile (exact bf16 MFMA operands).
+template <int DK>
+struct ScanQRegs {
+  static constexpr int LOADS = DK / 32;
+  bf16x8 q[DK / 32];
 };
 template <int DK>
 struct ScanLds {
@@ -551,6 +563,15 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
       r.w[ks][1] = *reinterpret_cast<const f32x4*>(w + w_frag<DK>(16 * tw + l16, 32 * ks + 8 * lq + 4));
     }
   };
+  // q rows of chunk c for a Q wave (token tile tw; rows past the sequence
+  // repeat its last one)
+  using QR = ScanQRegs<DK>;
+  auto load_q = [&](int c, QR& r) __attribute__((always_inline)) {
+    const int t = min(c * CH + 16 * tw + l16, a.T - 1);
+    const uint16_t* qr = a.proj + ((int64_t)b * a.T + t) * a.proj_stride + a.off_q + h * DK + 8 * lq;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) r.q[ks] = glb8(qr + 32 * ks);
+  };
   // L2 warm-up of a later chunk: the head's W, U~^T and K^T lines (128 bytes);
   // waves 0-2 take one source each, and the Dv/16 workgroups of the head
   // share its lines.  One 4-byte copy per line into a scratch corner of LDS
@@ -575,15 +596,14 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
   // the barrier that publishes the stage, this wave's K^T copies of chunk c
   // must have landed.  The vector memory counter counts stores as well as
   // loads, so at least YOUNGER operations were issued after those copies: the
-  // copies of chunk c + 1, the stores of the entering states of chunks c - 1
-  // and c (waves w < Dk/16), and for a U wave the loads of chunks c + 1 and
-  // c + 2 and the stores of U of chunks c - 1 and c (the L2 warm-ups, issued
-  // by three of the four U waves only, are not counted).
-  struct NoRegs {};
+  // copies of chunk c + 1, the loads of chunks c + 1 and c + 2 of the wave's
+  // register sets and its stores (U of a U wave, Q S^T of a Q wave) of chunks
+  // c - 1 and c (the L2 warm-ups, issued by three of the four U waves only,
+  // are not counted).
   struct NoSplit {};
   auto run = [&](auto role) __attribute__((always_inline)) {
     constexpr bool UW = decltype(role)::value;
-    using RS = std::conditional_t<UW, R, NoRegs>;
+    using RS = std::conditional_t<UW, R, QR>;
     // a U wave's W rows of the next chunk as split operands: split during the
     // previous chunk's update, off the path from the state to U
     struct WSplit {
@@ -596,12 +616,19 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
         for (int ks = 0; ks < NKS; ++ks) ws.w[ks] = split8(set.w[ks][0], set.w[ks][1]);
       }
     };
-    static_assert(NKB >= 4, "the U waves store the state");
-    constexpr int YOUNGER = UW ? 2 * R::LOADS + KCP + 4 : KCP + (NKB > 4 ? 2 : 0);
+    constexpr int YOUNGER = 2 * RS::LOADS + KCP + 2;
     auto step = [&](auto Ic, RS& cur, const RS& next, int c) __attribute__((always_inline)) {
       constexpr int I = decltype(Ic)::value;
-      if (wave < NKB)  // the entering state of chunk c, for the output kernel
-        *reinterpret_cast<f32x4*>(a.Sc + (cb0 + c) * DV * DK + jx_frag<DK>(j0 + l16, 16 * wave + 4 * lq)) = S;
+      if constexpr (!UW) {
+        // (Q S^T)[t][j] for the tile's tokens with the entering state, in
+        // the output kernel's order (three products per 32-deep step)
+        f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          acc = mma_es(cur.q[ks], get_parts8(sS + l16 * LS + 32 * ks + 8 * lq, L::S_PART), acc);
+        // lane: t = 16 tw + 4 lq + r, j = j0 + l16
+        *reinterpret_cast<f32x4*>(a.Oq + (cb0 + c) * CH * DV + jx_frag<CH>(j0 + l16, 16 * tw + 4 * lq)) = acc;
+      }
       if constexpr (UW) {
         // (W S^T)[t][j] for the tile's tokens (two accumulation chains)
         f32x4 acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
@@ -644,17 +671,22 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
       // role issues the same operations)
       copy_k(min(c + 2, n - 1), (I + 2) % SCAN_PF);
       if constexpr (UW) load(min(c + SCAN_PF, n - 1), cur);
+      else load_q(min(c + SCAN_PF, n - 1), cur);
       warm(min(c + SCAN_PF + 1, n - 1));
       lds_barrier();
     };
     static_assert(SCAN_PF == 3, "three register sets");
-    RS r0, r1, r2;  // the U waves' register sets (empty for the others)
+    RS r0, r1, r2;  // the wave's register sets (W rows and U~^T, or q rows)
     copy_k(0, 0);
     if constexpr (UW) load(0, r0);
+    else load_q(0, r0);
     copy_k(min(1, n - 1), 1);
     if constexpr (UW) {
       load(min(1, n - 1), r1);
       load(min(2, n - 1), r2);
+    } else {
+      load_q(min(1, n - 1), r1);
+      load_q(min(2, n - 1), r2);
     }
     warm(min(3, n - 1));
     if (wave < NKB) put_state();
@@ -683,14 +715,13 @@ __global__ __launch_bounds__(SCAN_NT, 1) void gdn_scan_kernel(GdnArgs a, int n_g
 }
 
 // ------------------------------------------------------- chunk output
-// grid (chunk, head, seq), eight waves: from the chunk's entering state S_c
-// and U (both stored by the scan), O = sq * (Q S_c^T) + Mqk U, then per token
-// y = RMSNorm(O; g_o) * SiLU(z) over Dv -> bf16.  One 48 KB LDS region holds
-// three-part bf16 B operands (rows j, 64 columns; 16-byte groups swizzled by
-// (j / 2) % 8 so that the operand reads of 16 consecutive rows and the part
-// writes spread over the banks): first S_c's columns 0..63, then 64..127
-// (Q S_c^T accumulates over the two passes), then U^T.  Two workgroups share
-// a CU.  Wave w: token tile w % 4 and half w / 4 of the Dv columns.
+// grid (chunk, head, seq), eight waves: from Q S_c^T and U (both stored by the
+// scan), O = sq * (Q S_c^T) + Mqk U, then per token y = RMSNorm(O; g_o) *
+// SiLU(z) over Dv -> bf16.  A 48 KB LDS region holds the three-part bf16 B
+// operand U^T (rows j, 64 columns; 16-byte groups swizzled by (j / 2) % 8 so
+// that the operand reads of 16 consecutive rows and the part writes spread
+// over the banks).  Several workgroups share a CU.  Wave w: token tile w % 4
+// and half w / 4 of the Dv columns.
 constexpr int ONT = 512;
 template <int DK>
 struct OutLds {
@@ -705,11 +736,7 @@ template <int DK>
 __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
   constexpr int DV = DK;
   using L = OutLds<DK>;
-  constexpr int NKS = DK / 32;
-  constexpr int NH = DK / 64;               // passes over 64 columns of S_c
   constexpr int NJT = DV / 32;              // 16-column tiles per wave (half of Dv)
-  constexpr int SP = DV * DK / 4 / ONT;     // S_c pieces (four fp32) per thread
-  static_assert(SP * 4 * ONT == DV * DK && ONT % (DK / 16 * 64) == 0, "S_c pieces");
   extern __shared__ __align__(16) uint16_t out_lds[];
   uint16_t* sR = out_lds;                   // the parts region
   float* sN = reinterpret_cast<float*>(sR + 3 * L::PART);  // [2][CH] sums of squares
@@ -721,20 +748,6 @@ __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
   const int64_t cb = chunk_index(a, b, h, c);
   const int64_t tok = (int64_t)b * a.T + c * CH;
   const float* sc = a.sc + cb * SCS;
-  // S_c pieces (each thread's all in one 64-column pass) and the wave's q
-  // rows (token tile)
-  // first; its Mqk rows, sq and U^T columns are read under the first pass,
-  // z under the last (registers: two workgroups share a CU)
-  f32x4 sv[SP];
-#pragma unroll
-  for (int i = 0; i < SP; ++i)
-    sv[i] = *reinterpret_cast<const f32x4*>(a.Sc + cb * DV * DK + (int64_t)(tid + i * ONT) * 4);
-  const int t = 16 * tw + l16;
-  bf16x8 q[NKS];
-  const uint16_t* qr = a.proj + (tok + min(t, C - 1)) * a.proj_stride + a.off_q + h * DK + 8 * lq;
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) q[ks] = glb8(qr + 32 * ks);
-  f32x4 mq[CH / 32][2], ut[NJT], sq;
   auto parts = [&](int j, int col) {
     Split8 v;
     const int o = u_at(j, col);
@@ -743,48 +756,25 @@ __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
     v.l = lds8(sR + 2 * L::PART + o);
     return v;
   };
-  // O1 = Q S_c^T for the wave's column tiles, 64 columns of S_c per pass.
-  // Lane: t = 16 tw + 4 lq + r, j = Dv/2 jh + 16 jt + l16.
-  // S_c piece p (16 bytes, fragment order): rows 16 (p / (Dk/16 64)) + p % 16,
-  // columns 16 ((p / 64) % (Dk/16)) + 4 ((p % 64) / 16) ..; all of one
-  // thread's pieces share their columns
-  const int kmine = 16 * ((tid / 64) % (DK / 16)) + 4 * ((tid & 63) >> 4);  // this thread's S_c columns
-  f32x4 o1[NJT];
+  // Lane: t = 16 tw + 4 lq + r, j = Dv/2 jh + 16 jt + l16: Q S_c^T and U^T of
+  // the wave's tiles, its Mqk rows and row scales
+  f32x4 o1[NJT], ut[NJT], mq[CH / 32][2], sq;
 #pragma unroll
-  for (int jt = 0; jt < NJT; ++jt) o1[jt] = (f32x4){0, 0, 0, 0};
-#pragma unroll
-  for (int kh = 0; kh < NH; ++kh) {
-    if (kmine / 64 == kh) {
-#pragma unroll
-      for (int i = 0; i < SP; ++i) {
-        const int p = tid + i * ONT;
-        const int j = 16 * (p / (DK / 16 * 64)) + (p & 15);
-        put_parts4(sR + u_at(j, kmine - 64 * kh), L::PART, sv[i]);
-      }
-    }
-    lds_barrier();
-    if (kh == 0) {
-      const float* mr = a.Mq + cb * CH * CH + t * CH + 8 * lq;
-#pragma unroll
-      for (int is = 0; is < CH / 32; ++is) {
-        mq[is][0] = *reinterpret_cast<const f32x4*>(mr + 32 * is);
-        mq[is][1] = *reinterpret_cast<const f32x4*>(mr + 32 * is + 4);
-      }
-      sq = *reinterpret_cast<const f32x4*>(sc + 16 * tw + 4 * lq);
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        const int j = DV / 2 * jh + 16 * jt + l16;
-        ut[jt] = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + jx_frag<CH>(j, 16 * tw + 4 * lq));
-      }
-    }
-#pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) {
-      const int j = DV / 2 * jh + 16 * jt + l16;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) o1[jt] = mma_es(q[2 * kh + ks], parts(j, 32 * ks + 8 * lq), o1[jt]);
-    }
-    lds_barrier();  // every read of this pass done before the region is rewritten
+  for (int jt = 0; jt < NJT; ++jt) {
+    const int j = DV / 2 * jh + 16 * jt + l16;
+    o1[jt] = *reinterpret_cast<const f32x4*>(a.Oq + cb * CH * DV + jx_frag<CH>(j, 16 * tw + 4 * lq));
+    ut[jt] = *reinterpret_cast<const f32x4*>(a.Ut + cb * DV * CH + jx_frag<CH>(j, 16 * tw + 4 * lq));
   }
+  const int t = 16 * tw + l16;
+  {
+    const float* mr = a.Mq + cb * CH * CH + t * CH + 8 * lq;
+#pragma unroll
+    for (int is = 0; is < CH / 32; ++is) {
+      mq[is][0] = *reinterpret_cast<const f32x4*>(mr + 32 * is);
+      mq[is][1] = *reinterpret_cast<const f32x4*>(mr + 32 * is + 4);
+    }
+  }
+  sq = *reinterpret_cast<const f32x4*>(sc + 16 * tw + 4 * lq);
   // the U^T parts of the wave's columns and tokens into the region
 #pragma unroll
   for (int jt = 0; jt < NJT; ++jt)

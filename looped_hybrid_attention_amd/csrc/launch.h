@@ -145,7 +145,7 @@ struct GdnArgs {
   float* Mq;     // Mqk: fp32 [64][64]
   uint16_t* Kt;  // raw k of the chunk transposed: bf16 [Dk][64] (16-byte groups swizzled)
   float* sc;     // row scales: sq [64], dk [64], gC (gdn_chunk_scales() floats)
-  float* Sc;     // the state entering the chunk: fp32 [Dv][Dk]
+  float* Oq;     // Q S^T with the state entering the chunk (raw q): fp32 [64][Dv]
   const uint16_t* o_norm;
   uint16_t* out; int64_t out_stride;
 };

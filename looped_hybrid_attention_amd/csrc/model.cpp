@@ -77,7 +77,7 @@ Layout layout(const loop_config& c, int64_t M) {
   L.gUt = take(cs * 64 * c.gdn_dv * 4);
   L.gM = take(cs * 64 * 64 * 4);
   L.gKt = take(cs * 64 * c.gdn_dk * 2);
-  L.gS = take(cs * (int64_t)c.gdn_dv * c.gdn_dk * 4);
+  L.gS = take(cs * 64 * c.gdn_dv * 4);
   L.gSc = take(cs * (int64_t)gdn_chunk_scales() * 4);
   // final-norm rows and argmax partials: one per sequence, or up to
   // LOOP_VERIFY_MAX per sequence for a verify step
@@ -357,7 +357,7 @@ int run_mixer(loop_model* m, const Call& k, const ExecDesc& d, hipStream_t s, in
     g.W = at<float>(m, L.gW); g.Ut = at<float>(m, L.gUt); g.Mq = at<float>(m, L.gM);
     g.Kt = at<uint16_t>(m, L.gKt);
     g.sc = at<float>(m, L.gSc);
-    g.Sc = at<float>(m, L.gS);
+    g.Oq = at<float>(m, L.gS);
     g.o_norm = (const uint16_t*)w.o_norm;
     g.out = obuf; g.out_stride = mix_width;
     Prof pr(m, LOOP_K_GDN, s);
