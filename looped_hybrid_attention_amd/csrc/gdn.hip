@@ -127,6 +127,16 @@ DEV f32x4 mma_ss(const Split8& a, const Split8& b, f32x4 acc) {
   acc = mfma16x16x32(a.m, b.h, acc);
   return mfma16x16x32(a.h, b.h, acc);
 }
+// mma_ss with every result kept apart from its C operand (the chain's
+// registers cannot then partially overlap)
+DEV f32x4 mma_ss_apart(const Split8& a, const Split8& b, f32x4 acc) {
+  acc = mfma16x16x32_apart(a.h, b.l, acc);
+  acc = mfma16x16x32_apart(a.l, b.h, acc);
+  acc = mfma16x16x32_apart(a.m, b.m, acc);
+  acc = mfma16x16x32_apart(a.h, b.m, acc);
+  acc = mfma16x16x32_apart(a.m, b.h, acc);
+  return mfma16x16x32_apart(a.h, b.h, acc);
+}
 DEV bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 DEV bf16x8 glb8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -799,7 +809,7 @@ __global__ __launch_bounds__(ONT, 4) void gdn_out_kernel(GdnArgs a) {
     const int j = DV / 2 * jh + 16 * jt + l16;
     f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-    for (int is = 0; is < CH / 32; ++is) acc = mma_ss(ms[is], parts(j, 32 * is + 8 * lq), acc);
+    for (int is = 0; is < CH / 32; ++is) acc = mma_ss_apart(ms[is], parts(j, 32 * is + 8 * lq), acc);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       o[jt][r] = sq[r] * o1[jt][r] + acc[r];
