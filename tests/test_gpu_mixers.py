@@ -294,3 +294,44 @@ def test_gdn_mixer_long_call_equals_split_calls():
         assert e <= FLAT and es <= 1e-3
     finally:
         g.close()
+
+
+def test_full_attention_mixer_mixed_starts():
+    """One prefill call of two sequences at different start positions (a
+    fresh sequence at 0, and one continuing a 700-token cached prefix at
+    700): every query tile of the call sees its own sequence's key range,
+    causal mask and cache tail, at real width ([P1] hncyxsy.com/news/268323
+    section 3), against the oracle at the flat bar."""
+    torch = torch_cuda()
+    dims = synth.preset("group")
+    ocfg = oracle.Config.from_dims(dims)
+    Hq, Hkv, D = dims["n_q_heads"], dims["n_kv_heads"], dims["head_dim"]
+    n_in, width = 2 * Hq * D + 2 * Hkv * D, Hq * D
+    PRE, T = 700, 300
+    g = GpuModel(torch, dims, max_batch=2, max_seq=1024, max_tokens=2 * PRE)
+    try:
+        W32 = om.layer_weights(om.to_dtype(g.host_weights, np.float32), 3)
+        pre = _proj("mixer.attn.mixed.pre", PRE, n_in)
+        new = [_proj(f"mixer.attn.mixed.{b}", T, n_in) for b in range(2)]
+        d_pre = dev(pre, torch)
+        d_po = torch.zeros((PRE, width), dtype=torch.bfloat16, device="cuda")
+        say("mixer prefix", PRE, "tokens in slot 1")
+        g.L.loop_exec_mixer(g.handle, 3, 1, PRE, [1], [0], d_pre.data_ptr(), n_in, d_po.data_ptr(), width,
+                            stream=g.stream())
+        d_x = dev(np.concatenate(new), torch)
+        d_o = torch.zeros((2 * T, width), dtype=torch.bfloat16, device="cuda")
+        say("mixer, two sequences at starts 0 and", PRE)
+        g.L.loop_exec_mixer(g.handle, 3, 2, T, [0, 1], [0, PRE], d_x.data_ptr(), n_in, d_o.data_ptr(), width,
+                            stream=g.stream())
+        torch.cuda.synchronize()
+        got = host(d_o).reshape(2, T, width)
+        c0 = oa.KVCache(Hkv, D, np.float32)
+        ref0 = oa.attention_mixer(synth.bf16_bits_to_f32(new[0]), W32, c0, 0, ocfg, bf16=True)
+        c1 = oa.KVCache(Hkv, D, np.float32)
+        oa.attention_mixer(synth.bf16_bits_to_f32(pre), W32, c1, 0, ocfg, bf16=True)
+        ref1 = oa.attention_mixer(synth.bf16_bits_to_f32(new[1]), W32, c1, PRE, ocfg, bf16=True)
+        e0, e1 = rel_err(got[0], ref0), rel_err(got[1], ref1)
+        print("attention mixer, mixed starts: seq at 0 %.4f, seq at %d %.4f" % (e0, PRE, e1))
+        assert e0 <= FLAT and e1 <= FLAT
+    finally:
+        g.close()
